@@ -1,0 +1,241 @@
+"""MI355X (gfx950) frozen-NF4 linear with a LoRA side path.
+
+A thin ctypes binding over ``libqlora_nf4.so`` (C ABI in ``include/qlora_nf4.h``).
+Functions carry the C names and only marshal arguments: torch supplies device
+memory and the current HIP stream, every step of the computation runs in the
+library's HIP kernels.  There is no CPU fallback: if the library is missing,
+every call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlora_nf4.so")
+
+QLORA_OK, QLORA_ERR_INVALID_ARG, QLORA_ERR_UNSUPPORTED, QLORA_ERR_WORKSPACE, QLORA_ERR_HIP = range(5)
+QLORA_F32, QLORA_BF16 = 0, 1
+NF4_BLOCK = 64
+DQ_BLOCK = 256
+MAX_RANK = 128
+
+EXPORTS = [
+    "qlora_nf4_codebook", "qlora_status_string", "qlora_quantize_workspace_bytes",
+    "qlora_quantize_nf4", "qlora_dequantize_nf4", "qlora_dequantize_absmax",
+    "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
+]
+
+
+class QloraError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s failed: %s (status %d)" % (what, status_string(status), status))
+        self.status = status
+
+
+class NF4Descriptor(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("block", ctypes.c_int32), ("dq_block", ctypes.c_int32),
+                ("codes", ctypes.c_void_p), ("absmax_q", ctypes.c_void_p),
+                ("absmax_scale", ctypes.c_void_p), ("absmax_mean", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libqlora_nf4.so is not built (run __graft_entry__.build() or "
+                               "python bit_quantized_lora_quant_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32, F, SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
+                              ctypes.c_size_t)
+        D = ctypes.POINTER(NF4Descriptor)
+        L.qlora_nf4_codebook.argtypes = [P]
+        L.qlora_nf4_codebook.restype = None
+        L.qlora_status_string.argtypes = [ctypes.c_int]
+        L.qlora_status_string.restype = ctypes.c_char_p
+        L.qlora_quantize_workspace_bytes.argtypes = [I64, I64]
+        L.qlora_quantize_workspace_bytes.restype = SZ
+        L.qlora_quantize_nf4.argtypes = [P, D, P, SZ, P]
+        L.qlora_dequantize_nf4.argtypes = [D, ctypes.c_int, P, P]
+        L.qlora_dequantize_absmax.argtypes = [D, P, P]
+        L.qlora_linear_workspace_bytes.argtypes = [I64, I64, I64, I32]
+        L.qlora_linear_workspace_bytes.restype = SZ
+        L.qlora_linear_fwd.argtypes = [D, P, I64, P, P, I32, F, P, P, P, SZ, P]
+        L.qlora_linear_bwd.argtypes = [D, P, I64, P, P, I32, F, P, P, P, P, P, P, SZ, P]
+        for name in ("qlora_quantize_nf4", "qlora_dequantize_nf4", "qlora_dequantize_absmax",
+                     "qlora_linear_fwd", "qlora_linear_bwd"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().qlora_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != QLORA_OK:
+        raise QloraError(status, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def qlora_nf4_codebook():
+    """The 16 NF4 levels as a list of floats (host copy)."""
+    buf = (ctypes.c_float * 16)()
+    lib().qlora_nf4_codebook(buf)
+    return [float(v) for v in buf]
+
+
+class NF4Tensor:
+    """Quantised frozen weight: device buffers owned by torch."""
+
+    def __init__(self, rows: int, cols: int, device):
+        n = rows * cols
+        nb = (n + NF4_BLOCK - 1) // NF4_BLOCK
+        nd = (nb + DQ_BLOCK - 1) // DQ_BLOCK
+        self.rows, self.cols = rows, cols
+        self.codes = torch.empty((n + 1) // 2, dtype=torch.uint8, device=device)
+        self.absmax_q = torch.empty(nb, dtype=torch.int8, device=device)
+        self.absmax_scale = torch.empty(nd, dtype=torch.float32, device=device)
+        self.absmax_mean = torch.empty(1, dtype=torch.float32, device=device)
+
+    @property
+    def numel(self):
+        return self.rows * self.cols
+
+    def descriptor(self) -> NF4Descriptor:
+        return NF4Descriptor(self.rows, self.cols, NF4_BLOCK, DQ_BLOCK,
+                             self.codes.data_ptr(), self.absmax_q.data_ptr(),
+                             self.absmax_scale.data_ptr(), self.absmax_mean.data_ptr())
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size()
+                   for t in (self.codes, self.absmax_q, self.absmax_scale, self.absmax_mean))
+
+
+def qlora_quantize_workspace_bytes(rows: int, cols: int) -> int:
+    return int(lib().qlora_quantize_workspace_bytes(rows, cols))
+
+
+def qlora_linear_workspace_bytes(M: int, N: int, K: int, r: int) -> int:
+    return int(lib().qlora_linear_workspace_bytes(M, N, K, r))
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def qlora_quantize_nf4(W: torch.Tensor, q: NF4Tensor = None, ws: torch.Tensor = None):
+    """Quantise a float32 [rows, cols] device tensor; returns (NF4Tensor,
+    workspace).  The workspace's first nb floats hold the exact block absmax."""
+    assert W.dtype == torch.float32 and W.is_contiguous() and W.dim() == 2
+    rows, cols = W.shape
+    if q is None:
+        q = NF4Tensor(rows, cols, W.device)
+    need = qlora_quantize_workspace_bytes(rows, cols)
+    if ws is None:
+        ws = workspace(need, W.device)
+    d = q.descriptor()
+    _check(lib().qlora_quantize_nf4(_ptr(W), ctypes.byref(d), _ptr(ws), ws.numel(), _stream()),
+           "qlora_quantize_nf4")
+    return q, ws
+
+
+def qlora_dequantize_nf4(q: NF4Tensor, dtype=torch.bfloat16, out: torch.Tensor = None):
+    if out is None:
+        out = torch.empty((q.rows, q.cols), dtype=dtype, device=q.codes.device)
+    code = QLORA_BF16 if out.dtype == torch.bfloat16 else QLORA_F32
+    assert out.dtype in (torch.bfloat16, torch.float32) and out.is_contiguous()
+    d = q.descriptor()
+    _check(lib().qlora_dequantize_nf4(ctypes.byref(d), code, _ptr(out), _stream()),
+           "qlora_dequantize_nf4")
+    return out
+
+
+def qlora_dequantize_absmax(q: NF4Tensor, out: torch.Tensor = None):
+    if out is None:
+        out = torch.empty(q.absmax_q.numel(), dtype=torch.float32, device=q.codes.device)
+    d = q.descriptor()
+    _check(lib().qlora_dequantize_absmax(ctypes.byref(d), _ptr(out), _stream()),
+           "qlora_dequantize_absmax")
+    return out
+
+
+def _bf16(t):
+    assert t.dtype == torch.bfloat16 and t.is_contiguous(), "expected contiguous bf16"
+    return t
+
+
+def qlora_linear_fwd(q: NF4Tensor, X, A, B, alpha: float, Y=None, XA_out=None, ws=None,
+                     return_xa: bool = False):
+    """Y = X W'^T + (alpha/r) (X A^T) B^T.  Returns Y, or (Y, XA) with return_xa."""
+    M, K = X.shape
+    r = A.shape[0]
+    _bf16(X), _bf16(A), _bf16(B)
+    assert K == q.cols and A.shape[1] == K and B.shape == (q.rows, r)
+    if Y is None:
+        Y = torch.empty((M, q.rows), dtype=torch.bfloat16, device=X.device)
+    if return_xa and XA_out is None:
+        XA_out = torch.empty((M, r), dtype=torch.bfloat16, device=X.device)
+    if ws is None:
+        ws = workspace(qlora_linear_workspace_bytes(M, q.rows, K, r), X.device)
+    d = q.descriptor()
+    _check(lib().qlora_linear_fwd(ctypes.byref(d), _ptr(X), M, _ptr(A), _ptr(B), r,
+                                  ctypes.c_float(alpha), _ptr(Y), _ptr(XA_out), _ptr(ws),
+                                  ws.numel(), _stream()), "qlora_linear_fwd")
+    return (Y, XA_out) if return_xa else Y
+
+
+def qlora_linear_bwd(q: NF4Tensor, X, A, B, alpha: float, dY, XA_in=None, need_dx: bool = True,
+                     dX=None, dA=None, dB=None, ws=None):
+    """Returns (dX or None, dA float32 [r, K], dB float32 [N, r])."""
+    M, K = X.shape
+    r = A.shape[0]
+    N = q.rows
+    _bf16(X), _bf16(A), _bf16(B), _bf16(dY)
+    assert dY.shape == (M, N)
+    if need_dx and dX is None:
+        dX = torch.empty((M, K), dtype=torch.bfloat16, device=X.device)
+    if dA is None:
+        dA = torch.empty((r, K), dtype=torch.float32, device=X.device)
+    if dB is None:
+        dB = torch.empty((N, r), dtype=torch.float32, device=X.device)
+    if ws is None:
+        ws = workspace(qlora_linear_workspace_bytes(M, N, K, r), X.device)
+    d = q.descriptor()
+    _check(lib().qlora_linear_bwd(ctypes.byref(d), _ptr(X), M, _ptr(A), _ptr(B), r,
+                                  ctypes.c_float(alpha), _ptr(dY), _ptr(XA_in),
+                                  _ptr(dX) if need_dx else None, _ptr(dA), _ptr(dB), _ptr(ws),
+                                  ws.numel(), _stream()), "qlora_linear_bwd")
+    return (dX if need_dx else None), dA, dB
+
+
+class QLoRALinearFn(torch.autograd.Function):
+    """autograd wrapper: frozen NF4 weight, trainable bf16 adapters A and B."""
+
+    @staticmethod
+    def forward(ctx, X, A, B, q, alpha):
+        Y, XA = qlora_linear_fwd(q, X.contiguous(), A.contiguous(), B.contiguous(), alpha,
+                                 return_xa=True)
+        ctx.save_for_backward(X, A, B, XA)
+        ctx.q, ctx.alpha = q, alpha
+        return Y
+
+    @staticmethod
+    def backward(ctx, dY):
+        X, A, B, XA = ctx.saved_tensors
+        dX, dA, dB = qlora_linear_bwd(ctx.q, X, A, B, ctx.alpha, dY.contiguous(), XA_in=XA,
+                                      need_dx=ctx.needs_input_grad[0])
+        return dX, dA.to(A.dtype), dB.to(B.dtype), None, None

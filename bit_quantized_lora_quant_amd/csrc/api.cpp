@@ -1,0 +1,225 @@
+// C ABI of the library (declared in include/qlora_nf4.h): argument checks,
+// workspace carving and the launch sequence of each call.  No device memory
+// is allocated here; everything is enqueued on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/qlora_nf4.h"
+#include "nf4_common.h"
+
+using namespace qnf4;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int64_t nblocks(int64_t n) { return ceil_div(n, kBlock); }
+
+bool valid_tensor(const qlora_nf4_tensor* q) {
+  if (!q || q->rows < 1 || q->cols < 1) return false;
+  if (q->block != QLORA_NF4_BLOCK || q->dq_block != QLORA_DQ_BLOCK) return false;
+  if (!q->codes || !q->absmax_q || !q->absmax_scale || !q->absmax_mean) return false;
+  if (!aligned(q->codes, 4) || !aligned(q->absmax_q, 4) || !aligned(q->absmax_scale, 4) ||
+      !aligned(q->absmax_mean, 4))
+    return false;
+  if (q->rows > INT64_MAX / q->cols) return false;
+  return true;
+}
+
+qlora_status hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP; }
+
+// ----------------------------------------------------- quantise workspace
+struct QuantWs {
+  size_t absmax, pa, pb, total;
+};
+QuantWs quant_layout(int64_t n) {
+  const int64_t nb = nblocks(n);
+  const int64_t c1 = ceil_div(nb, 2048), c2 = ceil_div(c1, 2048);
+  QuantWs w;
+  size_t off = 0;
+  w.absmax = off; off = align_up(off + (size_t)nb * sizeof(float));
+  w.pa = off;     off = align_up(off + (size_t)c1 * sizeof(double));
+  w.pb = off;     off = align_up(off + (size_t)(c2 > 0 ? c2 : 1) * sizeof(double));
+  w.total = off;
+  return w;
+}
+
+// ------------------------------------------------------- linear workspace
+struct LinearWs {
+  int r32;
+  int64_t mp, np;             // token count padded to 32, N padded to 128
+  int gemv_splits, sa, sb;    // split counts
+  size_t ahat_t, xas, gemv_part, bt, gs, gt, xat, part_a, part_b, total;
+};
+
+LinearWs linear_layout(int64_t M, int64_t N, int64_t K, int r) {
+  LinearWs w;
+  w.r32 = (int)ceil_div(r, 32) * 32;
+  w.mp = ceil_div(M, 32) * 32;
+  w.np = ceil_div(N, 128) * 128;
+  w.gemv_splits = M <= 16 ? qnf4::gemv_splits(N, K) : 0;
+  w.sa = lora_grad_splits(M, K);
+  w.sb = lora_grad_splits(M, N);
+  size_t off = 0;
+  w.ahat_t = off;    off = align_up(off + (size_t)(K / kBlock) * N * sizeof(float));
+  w.xas = off;       off = align_up(off + (size_t)M * w.r32 * 2);
+  w.gemv_part = off; off = align_up(off + (size_t)w.gemv_splits * M * N * sizeof(float));
+  w.bt = off;        off = align_up(off + (size_t)r * w.np * 2);
+  w.gs = off;        off = align_up(off + (size_t)M * w.r32 * 2);
+  w.gt = off;        off = align_up(off + (size_t)r * w.mp * 2);
+  w.xat = off;       off = align_up(off + (size_t)r * w.mp * 2);
+  w.part_a = off;    off = align_up(off + (size_t)w.sa * r * K * sizeof(float));
+  w.part_b = off;    off = align_up(off + (size_t)w.sb * N * r * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+qlora_status check_linear(const qlora_nf4_tensor* W, const void* X, int64_t M, const void* A,
+                          const void* B, int32_t r, float alpha) {
+  if (!valid_tensor(W) || !X || !A || !B) return QLORA_ERR_INVALID_ARG;
+  if (M < 1 || r < 1 || r > QLORA_MAX_RANK) return QLORA_ERR_INVALID_ARG;
+  if (!(alpha == alpha)) return QLORA_ERR_INVALID_ARG;
+  if (W->cols % QLORA_NF4_BLOCK != 0) return QLORA_ERR_UNSUPPORTED;
+  if (!aligned(X, 16) || !aligned(A, 16) || !aligned(B, 16)) return QLORA_ERR_INVALID_ARG;
+  return QLORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void qlora_nf4_codebook(float out[16]) {
+  if (out) std::memcpy(out, host_tables().level, sizeof(float) * 16);
+}
+
+const char* qlora_status_string(qlora_status s) {
+  switch (s) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_INVALID_ARG: return "invalid argument";
+    case QLORA_ERR_UNSUPPORTED: return "unsupported shape";
+    case QLORA_ERR_WORKSPACE: return "workspace missing or too small";
+    case QLORA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+size_t qlora_quantize_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 1 || rows > INT64_MAX / cols) return 0;
+  return quant_layout(rows * cols).total;
+}
+
+qlora_status qlora_quantize_nf4(const float* W, const qlora_nf4_tensor* q, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (!W || !valid_tensor(q) || !aligned(W, 16)) return QLORA_ERR_INVALID_ARG;
+  const int64_t n = q->rows * q->cols;
+  const QuantWs L = quant_layout(n);
+  if (!ws || ws_bytes < L.total || !aligned(ws, kAlign)) return QLORA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* absmax = at<float>(ws, L.absmax);
+  hipError_t e = launch_quant_absmax(W, n, q->codes, absmax, s);
+  if (e != hipSuccess) return QLORA_ERR_HIP;
+  e = launch_dq(absmax, nblocks(n), q->absmax_q, q->absmax_scale, q->absmax_mean,
+                at<double>(ws, L.pa), at<double>(ws, L.pb), s);
+  return hip_status(e);
+}
+
+qlora_status qlora_dequantize_nf4(const qlora_nf4_tensor* q, qlora_dtype out_dtype, void* out,
+                                  void* stream) {
+  if (!valid_tensor(q) || !out || !aligned(out, 16)) return QLORA_ERR_INVALID_ARG;
+  if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16) return QLORA_ERR_INVALID_ARG;
+  return hip_status(launch_dequant(q->codes, q->absmax_q, q->absmax_scale, q->absmax_mean,
+                                   q->rows * q->cols, out_dtype == QLORA_BF16, out,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+qlora_status qlora_dequantize_absmax(const qlora_nf4_tensor* q, float* out, void* stream) {
+  if (!valid_tensor(q) || !out) return QLORA_ERR_INVALID_ARG;
+  return hip_status(launch_absmax_recon(q->absmax_q, q->absmax_scale, q->absmax_mean,
+                                        nblocks(q->rows * q->cols), out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
+  if (M < 1 || N < 1 || K < 1 || r < 1 || r > QLORA_MAX_RANK) return 0;
+  return linear_layout(M, N, K, r).total;
+}
+
+qlora_status qlora_linear_fwd(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
+                              const qlora_bf16* A, const qlora_bf16* B, int32_t r, float alpha,
+                              qlora_bf16* Y, qlora_bf16* XA_out, void* ws, size_t ws_bytes,
+                              void* stream) {
+  qlora_status st = check_linear(W, X, M, A, B, r, alpha);
+  if (st != QLORA_OK) return st;
+  if (!Y || !aligned(Y, 16)) return QLORA_ERR_INVALID_ARG;
+  const int64_t N = W->rows, K = W->cols;
+  const LinearWs L = linear_layout(M, N, K, r);
+  if (!ws || ws_bytes < L.total || !aligned(ws, kAlign)) return QLORA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float scale = alpha / (float)r;
+  float* ahat_t = at<float>(ws, L.ahat_t);
+  uint16_t* xas = at<uint16_t>(ws, L.xas);
+  hipError_t e = launch_absmax_recon_t(W->absmax_q, W->absmax_scale, W->absmax_mean, N, K, ahat_t, s);
+  if (e != hipSuccess) return QLORA_ERR_HIP;
+  e = launch_skinny_nt(X, M, K, K, A, r, K, scale, xas, L.r32, XA_out, nullptr, 0, s);
+  if (e != hipSuccess) return QLORA_ERR_HIP;
+  if (M <= 16) {
+    float* part = at<float>(ws, L.gemv_part);
+    e = launch_gemv(X, M, K, W->codes, N, ahat_t, L.gemv_splits, part, s);
+    if (e != hipSuccess) return QLORA_ERR_HIP;
+    e = launch_gemv_finish(part, L.gemv_splits, M, N, xas, r, L.r32, B, Y, s);
+  } else {
+    e = launch_fwd_gemm(X, M, K, W->codes, N, ahat_t, xas, B, r, L.r32, Y, s);
+  }
+  return hip_status(e);
+}
+
+qlora_status qlora_linear_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
+                              const qlora_bf16* A, const qlora_bf16* B, int32_t r, float alpha,
+                              const qlora_bf16* dY, const qlora_bf16* XA_in, qlora_bf16* dX,
+                              float* dA, float* dB, void* ws, size_t ws_bytes, void* stream) {
+  qlora_status st = check_linear(W, X, M, A, B, r, alpha);
+  if (st != QLORA_OK) return st;
+  if (!dY || !dA || !dB || !aligned(dY, 16)) return QLORA_ERR_INVALID_ARG;
+  if (dX && !aligned(dX, 16)) return QLORA_ERR_INVALID_ARG;
+  const int64_t N = W->rows, K = W->cols;
+  const LinearWs L = linear_layout(M, N, K, r);
+  if (!ws || ws_bytes < L.total || !aligned(ws, kAlign)) return QLORA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float scale = alpha / (float)r;
+  float* ahat_t = at<float>(ws, L.ahat_t);
+  uint16_t* bt = at<uint16_t>(ws, L.bt);
+  uint16_t* gs = at<uint16_t>(ws, L.gs);
+  uint16_t* gt = at<uint16_t>(ws, L.gt);
+  uint16_t* xat = at<uint16_t>(ws, L.xat);
+  hipError_t e;
+#define QL_TRY(call) do { e = (call); if (e != hipSuccess) return QLORA_ERR_HIP; } while (0)
+  // XA^T [r, M32] for dB: from the forward's copy, or recomputed
+  if (XA_in) QL_TRY(launch_transpose_bf16(XA_in, M, r, xat, L.mp, s));
+  else QL_TRY(launch_skinny_nt(X, M, K, K, A, r, K, 1.0f, nullptr, 0, nullptr, xat, L.mp, s));
+  // G = dY . B as bf16(s.G) [M, r32] (dX tail) and bf16(G)^T [r, M32] (dA)
+  QL_TRY(launch_transpose_bf16(B, N, r, bt, L.np, s));
+  QL_TRY(launch_skinny_nt(dY, M, N, N, bt, r, L.np, scale, gs, L.r32, nullptr, gt, L.mp, s));
+  if (dX) {
+    QL_TRY(launch_absmax_recon_t(W->absmax_q, W->absmax_scale, W->absmax_mean, N, K, ahat_t, s));
+    QL_TRY(launch_dx_gemm(dY, M, N, W->codes, K, ahat_t, gs, A, r, L.r32, dX, s));
+  }
+  // dA = s . G^T X  (reduce over tokens into [r, K]);  dB = s . dY^T XA  ([N, r])
+  float* pa = at<float>(ws, L.part_a);
+  float* pb = at<float>(ws, L.part_b);
+  QL_TRY(launch_lora_grad(X, M, K, gt, r, L.mp, L.sa, pa, s));
+  QL_TRY(launch_lora_grad_reduce(pa, L.sa, K, r, scale, 1, dA, s));
+  QL_TRY(launch_lora_grad(dY, M, N, xat, r, L.mp, L.sb, pb, s));
+  QL_TRY(launch_lora_grad_reduce(pb, L.sb, N, r, scale, 0, dB, s));
+#undef QL_TRY
+  return QLORA_OK;
+}
+
+}  // extern "C"

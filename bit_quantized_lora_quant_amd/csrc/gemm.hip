@@ -1,0 +1,407 @@
+// Dequantise-in-register bf16 MFMA GEMMs of the frozen NF4 linear.
+//
+//   forward  Y  = X . W'^T + (s.XA) . B^T      inner dim K (+ r)
+//   backward dX = dY . W'  + (s.G)  . A        inner dim N (+ r)
+//
+// W' is never materialised: each workgroup reads the 4-bit codes of its W
+// tile, rebuilds bf16(level[code] * constant) in registers, and feeds them to
+// v_mfma_f32_16x16x32_bf16 as the B operand ("QLoRA: Fine-Tuning a 70B on One
+// GPU", section "Double Quantization": NF4 weights are dequantised on the fly
+// to the compute dtype for the matmul; section "Practical Implementation":
+// bf16 compute dtype).  The LoRA branch rides along as r extra inner columns,
+// so one accumulator holds both terms.
+//
+// Tiling (both kernels): 256 x 256 output tile, 4 waves, each wave owning a
+// 256 x 64 slab (16 x 4 MFMA tiles of 16x16, 256 fp32 accumulators per lane).
+// Every wave needs all 256 rows of the activation tile, which is staged in
+// LDS (double buffered, 16-byte chunks XOR-swizzled by row so the 16-byte
+// reads of 8 consecutive rows hit distinct banks).  Each W element is
+// dequantised exactly once per workgroup, by the one wave whose columns it
+// feeds, so there is no redundant dequant work and no LDS traffic for W.
+//
+// MFMA 16x16x32 bf16 operands: lane l holds row (l % 16) of A / column
+// (l % 16) of B and 8 consecutive inner indices of group (l / 16).  Which
+// actual inner indices a group stands for is free as long as A and B agree;
+// the kernels use that freedom to give each lane a contiguous run of codes.
+#include "nf4_common.h"
+
+namespace qnf4 {
+namespace {
+
+constexpr int kTile = 256;     // output rows and columns per workgroup
+constexpr int kStep = 64;      // inner indices per main-loop step
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint4 dequant8(uint32_t c, float a, const float* lvl) {
+  uint4 r;
+  r.x = pack_bf16x2(lvl[c & 15u] * a, lvl[(c >> 4) & 15u] * a);
+  r.y = pack_bf16x2(lvl[(c >> 8) & 15u] * a, lvl[(c >> 12) & 15u] * a);
+  r.z = pack_bf16x2(lvl[(c >> 16) & 15u] * a, lvl[(c >> 20) & 15u] * a);
+  r.w = pack_bf16x2(lvl[(c >> 24) & 15u] * a, lvl[(c >> 28) & 15u] * a);
+  return r;
+}
+
+// Activation tile [256 rows][64 cols] bf16 -> LDS, chunk c of row i stored at
+// chunk position c ^ (i & 7).  Thread t moves chunk (t & 7) of rows
+// (t >> 3) + 32 * it.  Rows >= rows_valid read row rows_valid-1 (results for
+// them are never stored); columns >= cols_valid read as zero.
+// MODE 0: every chunk in bounds (inner dim a multiple of 64);
+// MODE 1: 16-byte chunks either wholly valid or wholly past cols_valid
+//         (row stride and cols_valid multiples of 8);
+// MODE 2: element-wise bounds (any shape).
+template <int MODE>
+struct TileLoader {
+  uint4 v[8];
+  // element offsets of this thread's 8 rows (row * ld), 32-bit: every operand
+  // here has fewer than 2^32 elements
+  uint32_t roff[8];
+  __device__ __forceinline__ void init(int64_t ld, int64_t row0, int64_t rows_valid) {
+    const int rr = threadIdx.x >> 3;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      int64_t row = row0 + it * 32 + rr;
+      row = row < rows_valid ? row : rows_valid - 1;
+      roff[it] = (uint32_t)(row * ld) + (uint32_t)((threadIdx.x & 7) * 8);
+    }
+  }
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, uint32_t col0,
+                                       uint32_t cols_valid) {
+    const uint32_t col = col0 + (threadIdx.x & 7) * 8;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const uint16_t* p = src + col0 + roff[it];
+      if (MODE == 0) {
+        v[it] = *reinterpret_cast<const uint4*>(p);
+      } else if (MODE == 1) {
+        v[it] = col < cols_valid ? *reinterpret_cast<const uint4*>(p) : make_uint4(0u, 0u, 0u, 0u);
+      } else {
+        uint16_t e[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) e[q] = (col + q < cols_valid) ? p[q] : (uint16_t)0;
+        v[it].x = e[0] | ((uint32_t)e[1] << 16);
+        v[it].y = e[2] | ((uint32_t)e[3] << 16);
+        v[it].z = e[4] | ((uint32_t)e[5] << 16);
+        v[it].w = e[6] | ((uint32_t)e[7] << 16);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* lds) const {
+    const int c = threadIdx.x & 7, rr = threadIdx.x >> 3;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int row = it * 32 + rr;
+      *reinterpret_cast<uint4*>(lds + row * kStep + ((c ^ (row & 7)) * 8)) = v[it];
+    }
+  }
+};
+
+__device__ __forceinline__ uint4 lds_chunk(const uint16_t* lds, int row, int chunk) {
+  return *reinterpret_cast<const uint4*>(lds + row * kStep + ((chunk ^ (row & 7)) * 8));
+}
+
+__device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t& tm, int64_t& tn) {
+  // M-fastest: neighbouring workgroups share one W column tile (L2 reuse).
+  tm = blockIdx.x % tiles_m;
+  tn = blockIdx.x / tiles_m;
+}
+
+// ------------------------------------------------------------------ forward
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(1, 1)))
+void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                    const uint8_t* __restrict__ codes, int64_t N,
+                    const float* __restrict__ ahat_t, NF4Tables tab,
+                    const uint16_t* __restrict__ xas, const uint16_t* __restrict__ B, int r,
+                    int r32, uint16_t* __restrict__ Y) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][kTile * kStep];
+  __shared__ float lvl[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int j16 = lane & 15, g = lane >> 4;
+  int64_t tm, tn;
+  tile_coords(ceil_div(M, kTile), tm, tn);
+  const int64_t m0 = tm * kTile, n0 = tn * kTile;
+  if (tid < 16) lvl[tid] = tab.level[tid];
+
+  // this lane's four W rows (clamped; columns past N are never stored)
+  int64_t nrow[4];
+  uint32_t coff[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int64_t n = n0 + 64 * wv + 16 * nt + j16;
+    nrow[nt] = n < N ? n : N - 1;
+    coff[nt] = (uint32_t)(nrow[nt] * (K / 2)) + (uint32_t)(g * 8);
+  }
+  const uint32_t KT = (uint32_t)(K / kStep);
+  const uint32_t N32 = (uint32_t)N;
+
+  f32x4_t acc[16][4];
+#pragma unroll
+  for (int mt = 0; mt < 16; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  TileLoader<0> ld;
+  ld.init(K, m0, M);
+  uint2 cc[4];
+  float aa[4];
+  ld.load(X, 0, (uint32_t)K);
+  ld.store(xs[0]);
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    cc[nt] = *reinterpret_cast<const uint2*>(codes + coff[nt]);
+    aa[nt] = ahat_t[nrow[nt]];
+  }
+  __syncthreads();
+
+  for (uint32_t kt = 0; kt < KT; ++kt) {
+    // prefetch the next step (the last step re-reads itself; harmless)
+    const uint32_t kn = kt + 1 < KT ? kt + 1 : kt;
+    ld.load(X, kn * kStep, (uint32_t)K);
+    uint2 cn[4];
+    float an[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      cn[nt] = *reinterpret_cast<const uint2*>(codes + coff[nt] + kn * 32);
+      an[nt] = ahat_t[kn * N32 + (uint32_t)nrow[nt]];
+    }
+    // lane's 16 codes cover inner indices 16g .. 16g+15 of this step:
+    // sub-step s takes 16g + 8s .. +7, matching A chunk 2g + s
+    const uint16_t* xb = xs[kt & 1];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      uint4 bop[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) bop[nt] = dequant8(s ? cc[nt].y : cc[nt].x, aa[nt], lvl);
+#pragma unroll
+      for (int mt = 0; mt < 16; ++mt) {
+        const uint4 a = lds_chunk(xb, mt * 16 + j16, 2 * g + s);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma16x16x32(a, bop[nt], acc[mt][nt]);
+      }
+    }
+    ld.store(xs[(kt + 1) & 1]);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) { cc[nt] = cn[nt]; aa[nt] = an[nt]; }
+    __syncthreads();
+  }
+
+  // LoRA up-projection as r32 extra inner columns: A operand s.XA (bf16,
+  // [M, r32], zero padded), B operand rows of B [N, r]
+  const bool bvec = (r % 8) == 0;
+  for (int ts = 0; ts < r32 / 32; ++ts) {
+    const int j0 = ts * 32 + g * 8;
+    uint4 bb[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const uint16_t* p = B + nrow[nt] * r + j0;
+      if (bvec && j0 + 8 <= r) {
+        bb[nt] = *reinterpret_cast<const uint4*>(p);
+      } else {
+        uint16_t e[8];
+        for (int q = 0; q < 8; ++q) e[q] = (j0 + q < r) ? p[q] : (uint16_t)0;
+        bb[nt].x = e[0] | ((uint32_t)e[1] << 16);
+        bb[nt].y = e[2] | ((uint32_t)e[3] << 16);
+        bb[nt].z = e[4] | ((uint32_t)e[5] << 16);
+        bb[nt].w = e[6] | ((uint32_t)e[7] << 16);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt) {
+      int64_t m = m0 + mt * 16 + j16;
+      m = m < M ? m : M - 1;
+      const uint4 a = *reinterpret_cast<const uint4*>(xas + m * r32 + j0);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma16x16x32(a, bb[nt], acc[mt][nt]);
+    }
+  }
+
+  // epilogue: C[row 4g + v][col j16] of each 16x16 tile
+#pragma unroll
+  for (int mt = 0; mt < 16; ++mt) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int64_t n = n0 + 64 * wv + 16 * nt + j16;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t m = m0 + mt * 16 + 4 * g + v;
+        if (m < M && n < N) Y[m * N + n] = (uint16_t)(pack_bf16x2(acc[mt][nt][v], 0.f) & 0xFFFF);
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------- backward
+// dX tile 256 (rows m) x 256 (cols k); inner loop over n in steps of 64.
+// Lane (j16, g) of wave w owns output columns kc = k0 + 64w + 4*j16 + t,
+// t = 0..3, one MFMA per t: so its B operand needs, for each t, 8 consecutive
+// W rows of one column -- exactly the 4 codes of a 16-bit load from each of 8
+// rows.  All four columns sit in one 64-block of each row.
+template <int MODE>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(1, 1)))
+void k_qlora_dx_nn(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
+                   const uint8_t* __restrict__ codes, int64_t K,
+                   const float* __restrict__ ahat_t, NF4Tables tab,
+                   const uint16_t* __restrict__ gs, const uint16_t* __restrict__ A, int r,
+                   int r32, uint16_t* __restrict__ dX) {
+  __shared__ __attribute__((aligned(16))) uint16_t ys[2][kTile * kStep];
+  __shared__ float lvl[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int j16 = lane & 15, g = lane >> 4;
+  int64_t tm, tn;
+  tile_coords(ceil_div(M, kTile), tm, tn);
+  const int64_t m0 = tm * kTile, k0 = tn * kTile;
+  if (tid < 16) lvl[tid] = tab.level[tid];
+
+  const int64_t kc = k0 + 64 * wv + 4 * j16;      // first of this lane's 4 columns
+  const bool kvalid = kc < K;                       // K % 64 == 0: all 4 or none
+  const int64_t kcl = kvalid ? kc : K - 4;
+  const uint32_t kb = (uint32_t)(kcl / kBlock);
+  const uint32_t ldc = (uint32_t)(K / 2);
+  const uint32_t N32 = (uint32_t)N;
+  const uint32_t NT = (uint32_t)ceil_div(N, kStep);
+  const uint32_t ccol = (uint32_t)(kcl / 2);
+  const uint32_t abase = kb * N32;
+
+  f32x4_t acc[16][4];
+#pragma unroll
+  for (int mt = 0; mt < 16; ++mt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // 16 W rows per step (2 sub-steps x 8): rows n0 + 32s + 8g + e
+  auto load_w = [&](uint32_t n0, uint32_t (&c)[16], float (&a)[16]) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t n = n0 + 32 * s + 8 * g + e;
+        n = n < N32 ? n : N32 - 1;
+        c[s * 8 + e] = *reinterpret_cast<const uint16_t*>(codes + n * ldc + ccol);
+        a[s * 8 + e] = ahat_t[abase + n];
+      }
+  };
+
+  TileLoader<MODE> ld;
+  ld.init(N, m0, M);
+  uint32_t cc[16];
+  float aa[16];
+  ld.load(dY, 0, N32);
+  ld.store(ys[0]);
+  load_w(0, cc, aa);
+  __syncthreads();
+
+  for (uint32_t it = 0; it < NT; ++it) {
+    const uint32_t nn = it + 1 < NT ? it + 1 : it;   // last step re-reads itself
+    ld.load(dY, nn * kStep, N32);
+    uint32_t cn[16];
+    float an[16];
+    load_w(nn * kStep, cn, an);
+    const uint16_t* yb = ys[it & 1];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      // B operands of sub-step s: column t, rows e = 0..7 paired (e, e+1)
+      uint4 bop[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = lvl[(cc[s * 8 + e] >> (4 * t)) & 15u] * aa[s * 8 + e];
+        bop[t].x = pack_bf16x2(v[0], v[1]);
+        bop[t].y = pack_bf16x2(v[2], v[3]);
+        bop[t].z = pack_bf16x2(v[4], v[5]);
+        bop[t].w = pack_bf16x2(v[6], v[7]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 16; ++mt) {
+        const uint4 a = lds_chunk(yb, mt * 16 + j16, 4 * s + g);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[mt][t] = mfma16x16x32(a, bop[t], acc[mt][t]);
+      }
+    }
+    ld.store(ys[(it + 1) & 1]);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) { cc[q] = cn[q]; aa[q] = an[q]; }
+    __syncthreads();
+  }
+
+  // LoRA: + (s.G) . A as r32 extra inner indices
+  for (int ts = 0; ts < r32 / 32; ++ts) {
+    const int j0 = ts * 32 + g * 8;
+    uint2 rows[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = j0 + e;
+      rows[e] = (j < r) ? *reinterpret_cast<const uint2*>(A + (int64_t)j * K + kcl)
+                        : make_uint2(0u, 0u);
+    }
+    uint4 bb[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = (t < 2) ? rows[e].x : rows[e].y;
+        h[e] = (t & 1) ? (w >> 16) : (w & 0xFFFFu);
+      }
+      bb[t].x = h[0] | (h[1] << 16);
+      bb[t].y = h[2] | (h[3] << 16);
+      bb[t].z = h[4] | (h[5] << 16);
+      bb[t].w = h[6] | (h[7] << 16);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt) {
+      int64_t m = m0 + mt * 16 + j16;
+      m = m < M ? m : M - 1;
+      const uint4 a = *reinterpret_cast<const uint4*>(gs + m * r32 + j0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[mt][t] = mfma16x16x32(a, bb[t], acc[mt][t]);
+    }
+  }
+
+  // epilogue: lane holds columns kc..kc+3 of rows 4g + v -> one 8-byte store
+  if (kvalid) {
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t m = m0 + mt * 16 + 4 * g + v;
+        if (m < M) {
+          uint2 o;
+          o.x = pack_bf16x2(acc[mt][0][v], acc[mt][1][v]);
+          o.y = pack_bf16x2(acc[mt][2][v], acc[mt][3][v]);
+          *reinterpret_cast<uint2*>(dX + m * K + kc) = o;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes,
+                           int64_t N, const float* ahat_t, const uint16_t* xas, const uint16_t* B,
+                           int r, int r32, uint16_t* Y, hipStream_t s) {
+  const int64_t grid = ceil_div(M, kTile) * ceil_div(N, kTile);
+  hipLaunchKernelGGL(k_qlora_fwd_nt, dim3((unsigned)grid), dim3(kThreads), 0, s, X, M, K, codes,
+                     N, ahat_t, host_tables(), xas, B, r, r32, Y);
+  return hipGetLastError();
+}
+
+hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes,
+                          int64_t K, const float* ahat_t, const uint16_t* gs, const uint16_t* A,
+                          int r, int r32, uint16_t* dX, hipStream_t s) {
+  const int64_t grid = ceil_div(M, kTile) * ceil_div(K, kTile);
+  if (N % kStep == 0)
+    hipLaunchKernelGGL(k_qlora_dx_nn<0>, dim3((unsigned)grid), dim3(kThreads), 0, s, dY, M, N,
+                       codes, K, ahat_t, host_tables(), gs, A, r, r32, dX);
+  else if (N % 8 == 0)
+    hipLaunchKernelGGL(k_qlora_dx_nn<1>, dim3((unsigned)grid), dim3(kThreads), 0, s, dY, M, N,
+                       codes, K, ahat_t, host_tables(), gs, A, r, r32, dX);
+  else
+    hipLaunchKernelGGL(k_qlora_dx_nn<2>, dim3((unsigned)grid), dim3(kThreads), 0, s, dY, M, N,
+                       codes, K, ahat_t, host_tables(), gs, A, r, r32, dX);
+  return hipGetLastError();
+}
+
+}  // namespace qnf4

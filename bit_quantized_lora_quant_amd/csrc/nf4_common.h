@@ -1,0 +1,133 @@
+// Shared device helpers and the internal launcher interface of the gfx950
+// NF4 + LoRA library.  Everything here is CDNA4-specific: wave64, bf16 MFMA
+// (v_mfma_f32_16x16x32_bf16), DPP lane exchanges, v_cvt_pk_bf16_f32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qnf4 {
+
+constexpr int kBlock = 64;     // weights per first-level absmax
+constexpr int kDqBlock = 256;  // first-level constants per second-level scale
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// The 16 levels and the 15 decision thresholds, passed by value in the kernel
+// argument segment (they land in scalar registers).  thresh[j] is the largest
+// float not above the exact midpoint of level[j] and level[j+1], so
+// "x > thresh[j]" is exactly "x is nearer level[j+1], ties to level[j]".
+struct NF4Tables {
+  float level[16];
+  float thresh[15];
+};
+
+// Host-side tables, built once from the normal quantile function.
+const NF4Tables& host_tables();
+
+// ---------------------------------------------------------------- helpers
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};   // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+__device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// DPP lane exchanges inside a row of 16 lanes (no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                             0xF, 0xF, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // reverse each group of 8 lanes
+
+// max over each aligned group of 8 lanes, result in all 8
+__device__ __forceinline__ float group8_max(float v) {
+  v = fmaxf(v, dpp_f32<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  return v;
+}
+
+// Nearest-level index of x in [-1, 1] by a branch-free binary search over
+// the 15 thresholds (4 compares, selects on uniform values).
+__device__ __forceinline__ uint32_t nf4_code(float x, const NF4Tables& t) {
+  const bool b3 = x > t.thresh[7];
+  const float t2 = b3 ? t.thresh[11] : t.thresh[3];
+  const bool b2 = x > t2;
+  const float t1 = b3 ? (b2 ? t.thresh[13] : t.thresh[9]) : (b2 ? t.thresh[5] : t.thresh[1]);
+  const bool b1 = x > t1;
+  const float t0 = b3 ? (b2 ? (b1 ? t.thresh[14] : t.thresh[12]) : (b1 ? t.thresh[10] : t.thresh[8]))
+                      : (b2 ? (b1 ? t.thresh[6] : t.thresh[4]) : (b1 ? t.thresh[2] : t.thresh[0]));
+  const bool b0 = x > t0;
+  return (b3 ? 8u : 0u) | (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
+}
+
+__host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  All pointers are device.
+
+hipError_t launch_quant_absmax(const float* w, int64_t n, uint8_t* codes, float* absmax,
+                               hipStream_t s);
+hipError_t launch_dq(const float* absmax, int64_t nb, int8_t* q, float* scale, float* mean,
+                     double* partial_a, double* partial_b, hipStream_t s);
+hipError_t launch_dequant(const uint8_t* codes, const int8_t* q, const float* scale,
+                          const float* mean, int64_t n, int out_bf16, void* out, hipStream_t s);
+hipError_t launch_absmax_recon(const int8_t* q, const float* scale, const float* mean, int64_t nb,
+                               float* out, hipStream_t s);
+// Reconstructed constants laid out [K/64][N] (block column major) for the GEMMs.
+hipError_t launch_absmax_recon_t(const int8_t* q, const float* scale, const float* mean,
+                                 int64_t N, int64_t K, float* out, hipStream_t s);
+
+// P = T . U^T over the inner dim kin: T [M, kin] (row stride ldt), U [r, kin]
+// (row stride ldu).  Outputs (each nullable):
+//   out_s  bf16(scale * P) [M, r32]   (zero columns r..r32)
+//   out    bf16(P)         [M, r]
+//   out_t  bf16(P)^T       [r, ldo_t] (zero for m in [M, ldo_t))
+hipError_t launch_skinny_nt(const uint16_t* T, int64_t M, int64_t kin, int64_t ldt,
+                            const uint16_t* U, int r, int64_t ldu, float scale,
+                            uint16_t* out_s, int r32, uint16_t* out, uint16_t* out_t,
+                            int64_t ldo_t, hipStream_t s);
+// bf16 transpose [rows, cols] -> [cols, ldo] with zero padding to ldo
+hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
+                                 int64_t ldo, hipStream_t s);
+
+hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes,
+                           int64_t N, const float* ahat_t, const uint16_t* xas, const uint16_t* B,
+                           int r, int r32, uint16_t* Y, hipStream_t s);
+hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes,
+                          int64_t K, const float* ahat_t, const uint16_t* gs, const uint16_t* A,
+                          int r, int r32, uint16_t* dX, hipStream_t s);
+
+// partial[split][p][j] = sum over split's m of T[m][p] * U[j][m];  T [M, P]
+// (row stride P), U [r, ldu] with zero padding for m in [M, ldu).
+int lora_grad_splits(int64_t M, int64_t P);
+hipError_t launch_lora_grad(const uint16_t* T, int64_t M, int64_t P, const uint16_t* U, int r,
+                            int64_t ldu, int splits, float* partial, hipStream_t s);
+// out = scale * sum_split partial; transposed: out[j][p] else out[p][j]
+hipError_t launch_lora_grad_reduce(const float* partial, int splits, int64_t P, int r,
+                                   float scale, int transposed, float* out, hipStream_t s);
+
+// decode path (M <= 16)
+int gemv_splits(int64_t N, int64_t K);
+hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, int64_t N,
+                       const float* ahat_t, int splits, float* partial, hipStream_t s);
+hipError_t launch_gemv_finish(const float* partial, int splits, int64_t M, int64_t N,
+                              const uint16_t* xas, int r, int r32, const uint16_t* B,
+                              uint16_t* Y, hipStream_t s);
+
+}  // namespace qnf4

@@ -1,0 +1,69 @@
+// Host construction of the NF4 levels and decision thresholds.
+//
+// Levels ("QLoRA: Fine-Tuning a 70B on One GPU", section "NF4 Quantization":
+// a 16-entry table built from the normal CDF; inquiringlines note on QLoRA,
+// mechanism paragraph: each bin an equal share of a zero-centred normal):
+// 7 negative levels, an exact zero and 8 positive levels.  Each half sits at
+// normal quantiles of equally spaced probabilities from 1/2 to P = 31/32 (the
+// centre of the outermost sixteenth of the mass), scaled by 1/Phi^-1(P) so the
+// ends are exactly -1 and +1.
+//
+// Phi^-1 here is Newton's method on Phi(x) = erfc(-x/sqrt 2)/2 started at 0;
+// for p >= 1/2 Phi is concave on [0, inf), so the iterates rise monotonically
+// to the root and stop when a step no longer moves x.
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "nf4_common.h"
+
+namespace qnf4 {
+namespace {
+
+double normal_quantile_upper(double p) {  // p in [1/2, 1)
+  const double inv_sqrt_2pi = 0.39894228040143267794;
+  double x = 0.0;
+  for (int it = 0; it < 200; ++it) {
+    const double f = 0.5 * std::erfc(-x / std::sqrt(2.0)) - p;
+    const double d = inv_sqrt_2pi * std::exp(-0.5 * x * x);
+    const double nx = x - f / d;
+    if (nx == x) break;
+    if (it > 8 && std::fabs(nx - x) <= 2e-16 * std::fabs(x)) { x = nx; break; }
+    x = nx;
+  }
+  return x;
+}
+
+NF4Tables build() {
+  NF4Tables t;
+  const double P = 31.0 / 32.0;
+  const double z = normal_quantile_upper(P);
+  t.level[7] = 0.0f;
+  for (int j = 1; j <= 7; ++j) {
+    const double p = 0.5 + (P - 0.5) * j / 7.0;
+    t.level[7 - j] = (float)(-normal_quantile_upper(p) / z);
+  }
+  for (int j = 1; j <= 8; ++j) {
+    const double p = 0.5 + (P - 0.5) * j / 8.0;
+    t.level[7 + j] = (float)(normal_quantile_upper(p) / z);
+  }
+  // thresholds: largest float <= exact midpoint (exact in double)
+  for (int j = 0; j < 15; ++j) {
+    const double m = 0.5 * ((double)t.level[j] + (double)t.level[j + 1]);
+    float f = (float)m;
+    if ((double)f > m) f = std::nextafterf(f, -INFINITY);
+    t.thresh[j] = f;
+  }
+  return t;
+}
+
+}  // namespace
+
+const NF4Tables& host_tables() {
+  static NF4Tables tables;
+  static std::once_flag once;
+  std::call_once(once, [] { tables = build(); });
+  return tables;
+}
+
+}  // namespace qnf4

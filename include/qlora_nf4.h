@@ -1,0 +1,164 @@
+/*
+ * qlora_nf4.h -- C ABI of the MI355X (gfx950) library for the frozen-NF4
+ * linear layer with a LoRA side path.
+ *
+ * The method (QLoRA): the pretrained weight W is quantised once to 4-bit
+ * NormalFloat codes with blockwise absmax constants, the constants are
+ * themselves quantised to 8 bits (double quantisation), and every training
+ * step dequantises W on the fly in the bf16 compute dtype, adds the low-rank
+ * adapter branch and backpropagates through the frozen W into the adapters.
+ * Sources (page title, section):
+ *   - "QLoRA: Fine-Tuning a 70B on One GPU": "NF4 Quantization" (lookup table
+ *     of 16 normal-CDF levels, nearest-level mapping, done once before
+ *     training), "Double Quantization" (the block constants quantised to INT8,
+ *     on-the-fly dequantisation for the matmul), "Practical Implementation"
+ *     (nf4 type, double-quant flag, bf16 compute dtype, LoRA r / lora_alpha).
+ *   - inquiringlines.com note on QLoRA cutting 65B finetuning memory to <48 GB,
+ *     mechanism paragraph (frozen 4-bit base, gradients through it into LoRA
+ *     adapters; equal-share normal bins; quantising the constants themselves).
+ *   - xingyuzhitong guide "Fine-Tuning Memory Requirements", section "LoRA:
+ *     freeze the base, train small adapters" (the r x (d_in + d_out) adapter
+ *     pair beside the frozen weight).
+ * Readings of points the pages leave open (fixed by this library):
+ *   block of 64 weights per absmax, 256 absmax per second-level scale, one
+ *   float32 mean per tensor, signed int8 constants with scale max|d|/127,
+ *   codes packed two per byte with the even element in the low nibble,
+ *   nearest level with ties to the lower level, LoRA scale s = alpha / r.
+ *
+ * Conventions.
+ *   - W is [rows = N, cols = K] row-major (out x in, PyTorch Linear layout);
+ *     X [M, K], A [r, K], B [N, r], Y [M, N], dY [M, N], dX [M, K], all
+ *     row-major and dense.  bf16 tensors are passed as raw uint16 bits.
+ *   - Every pointer argument is device memory owned by the caller, except the
+ *     descriptor structs and the codebook output, which are host memory.  The
+ *     library never allocates or frees device memory; scratch comes from the
+ *     caller's workspace, sized by the *_workspace_bytes queries.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *     enqueued on it and the call returns before it completes; no call
+ *     synchronises the host.  Inputs must stay alive until the stream has
+ *     passed the call.  Calls that share a workspace must be ordered on one
+ *     stream.
+ *   - Errors: argument checks run on the host before anything is enqueued and
+ *     return a status with nothing launched.  A failed launch returns
+ *     QLORA_ERR_HIP.  Outputs are overwritten, never accumulated into.
+ *   - Preconditions not checked on the hot path: W is finite; input and output
+ *     buffers do not overlap.
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_ERR_INVALID_ARG = 1,   /* null pointer, bad size, bad block sizes */
+  QLORA_ERR_UNSUPPORTED = 2,   /* shape outside what the kernels handle (e.g. K % 64) */
+  QLORA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the query says */
+  QLORA_ERR_HIP = 4            /* a HIP launch failed */
+} qlora_status;
+
+typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
+
+typedef uint16_t qlora_bf16;   /* raw bfloat16 bits */
+
+#define QLORA_NF4_BLOCK 64     /* weights per first-level absmax */
+#define QLORA_DQ_BLOCK 256     /* first-level constants per second-level scale */
+#define QLORA_MAX_RANK 128
+
+/* Quantised-weight descriptor (host struct; buffers are device memory the
+ * caller allocates).  With n = rows*cols, nb = ceil(n/64), nd = ceil(nb/256):
+ *   codes        uint8[ceil(n/2)]  element 2i in the low nibble of byte i
+ *   absmax_q     int8[nb]          8-bit first-level constants
+ *   absmax_scale float32[nd]       second-level scale of each 256 constants
+ *   absmax_mean  float32[1]        per-tensor mean of the first-level constants
+ * The reconstructed constant of block b is fma(absmax_q[b], absmax_scale[b/256],
+ * absmax_mean[0]); weight i dequantises to level[code_i] * that constant. */
+typedef struct {
+  int64_t rows, cols;
+  int32_t block;      /* must be 64 */
+  int32_t dq_block;   /* must be 256 */
+  uint8_t* codes;
+  int8_t* absmax_q;
+  float* absmax_scale;
+  float* absmax_mean;
+} qlora_nf4_tensor;
+
+/* Host copy of the 16 NF4 levels, ascending: 7 negative levels, an exact +0.0
+ * and 8 positive levels; level 0 is -1 and level 15 is +1.  Each half takes
+ * normal quantiles at equal probability steps from 1/2 to 31/32, divided by
+ * the 31/32 quantile ("NF4 Quantization" section: levels from the normal CDF;
+ * inquiringlines note: equal share of a zero-centred normal per bin). */
+void qlora_nf4_codebook(float out[16]);
+
+const char* qlora_status_string(qlora_status s);
+
+/* Bytes of workspace qlora_quantize_nf4 needs for a rows x cols tensor. */
+size_t qlora_quantize_workspace_bytes(int64_t rows, int64_t cols);
+
+/* Blockwise NF4 quantisation with double quantisation ("NF4 Quantization" and
+ * "Double Quantization" sections).
+ *   W   float32[rows*cols], device, read-only.
+ *   q   descriptor whose four buffers receive the quantised state.
+ *   ws  device workspace of at least qlora_quantize_workspace_bytes(); on
+ *       return (once the stream passes) its first nb floats hold the exact
+ *       first-level absmax of each 64-block.
+ * Steps: absmax of each block; x = w / absmax (IEEE float division; an all-zero
+ * block gives x = 0); code = nearest level, ties to the lower; then the mean
+ * of all absmax (exact binary tree of pairwise float64 sums, divided by nb and
+ * rounded to float32), deviations d = absmax - mean, per 256 constants
+ * scale = max|d| / 127 and q = clamp(rint(d / scale), -127, 127) (0 when the
+ * scale is 0).  Any rows*cols >= 1 is accepted. */
+qlora_status qlora_quantize_nf4(const float* W, const qlora_nf4_tensor* q, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/* Dequantise to float32 or bf16 (round to nearest even) into out[rows*cols]
+ * ("Double Quantization" section: NF4 weights converted back to the compute
+ * dtype).  The float32 result is the single product level[code] * constant. */
+qlora_status qlora_dequantize_nf4(const qlora_nf4_tensor* q, qlora_dtype out_dtype, void* out,
+                                  void* stream);
+
+/* Reconstructed first-level constants, float32[nb]. */
+qlora_status qlora_dequantize_absmax(const qlora_nf4_tensor* q, float* out, void* stream);
+
+/* Bytes of workspace qlora_linear_fwd / qlora_linear_bwd need. */
+size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
+
+/* Forward of the adapted frozen linear:
+ *     Y = X . W'^T + s . (X . A^T) . B^T,   s = alpha / r,
+ * W' the dequantised W (rows N, cols K), computed in bf16 on the matrix cores
+ * with float32 accumulation and Y rounded to bf16.  W' is rebuilt from the
+ * 4-bit codes inside the kernel and never written to memory.
+ *   X [M, K], A [r, K], B [N, r], Y [M, N] (bf16).  XA_out (nullable) receives
+ *   bf16(X . A^T) [M, r] for reuse by the backward.
+ * Requires K % 64 == 0, M >= 1, 1 <= r <= 128; X, A, B, Y, dY, dX 16-byte
+ * aligned.  M <= 16 takes the
+ * bandwidth-bound decode path (same result definition). */
+qlora_status qlora_linear_fwd(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
+                              const qlora_bf16* A, const qlora_bf16* B, int32_t r, float alpha,
+                              qlora_bf16* Y, qlora_bf16* XA_out, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* Backward of the same layer with W frozen (no gradient for W; the gradient
+ * flows through W' into the adapters):
+ *     G  = dY . B
+ *     dX = dY . W' + s . G . A          (bf16 [M, K]; nullable: skipped)
+ *     dA = s . G^T . X                  (float32 [r, K], overwritten)
+ *     dB = s . dY^T . (X . A^T)         (float32 [N, r], overwritten)
+ * XA_in (nullable) is bf16(X . A^T) [M, r] from the forward; when NULL it is
+ * recomputed.  The reductions over M use a fixed split and order, so results
+ * are identical run to run.  Same shape requirements as the forward. */
+qlora_status qlora_linear_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
+                              const qlora_bf16* A, const qlora_bf16* B, int32_t r, float alpha,
+                              const qlora_bf16* dY, const qlora_bf16* XA_in, qlora_bf16* dX,
+                              float* dA, float* dB, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_NF4_H */

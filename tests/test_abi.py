@@ -1,0 +1,117 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+function include/qlora_nf4.h declares, its codebook equals the oracle's bit for
+bit, and argument errors come back as status codes before anything is
+launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora_nf4.h")
+
+
+@pytest.fixture(scope="module")
+def q():
+    import bit_quantized_lora_quant_amd as q
+    if not os.path.exists(q.LIB_PATH):
+        from bit_quantized_lora_quant_amd import build
+        build.build()
+    return q
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("qlora_quantize_nf4", "qlora_dequantize_nf4", "qlora_linear_fwd", "qlora_linear_bwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(q):
+    lib = q.lib()
+    names = declared_functions()
+    assert names, "no declarations parsed"
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(q.EXPORTS) == names
+
+
+def test_codebook_matches_oracle_bit_exact(q):
+    lib_cb = np.array(q.qlora_nf4_codebook(), dtype=np.float32)
+    assert np.array_equal(lib_cb.view(np.uint32), oracle.codebook().view(np.uint32))
+
+
+def test_status_strings(q):
+    for s in range(5):
+        assert q.status_string(s)
+    assert q.status_string(0) == "ok"
+
+
+def test_workspace_queries(q):
+    assert q.qlora_quantize_workspace_bytes(0, 5) == 0
+    assert q.qlora_quantize_workspace_bytes(1024, 1024) >= (1024 * 1024 // 64) * 4
+    assert q.qlora_linear_workspace_bytes(128, 1024, 1024, 0) == 0
+    assert q.qlora_linear_workspace_bytes(128, 1024, 1024, 129) == 0
+    a = q.qlora_linear_workspace_bytes(128, 1024, 1024, 8)
+    b = q.qlora_linear_workspace_bytes(2048, 4096, 14336, 16)
+    assert 0 < a < b
+
+
+def _desc(q, rows=64, cols=64, block=64, dq=256, null_codes=False):
+    fake = 0x100000  # never dereferenced: validation fails first or shapes are checked
+    return q.NF4Descriptor(rows, cols, block, dq, 0 if null_codes else fake, fake, fake, fake)
+
+
+def test_argument_errors_return_status(q):
+    lib = q.lib()
+    P = ctypes.c_void_p
+    # bad descriptors
+    for d in (_desc(q, block=32), _desc(q, dq=128), _desc(q, rows=0), _desc(q, null_codes=True)):
+        assert lib.qlora_dequantize_nf4(ctypes.byref(d), q.QLORA_F32, P(0x200000), None) == \
+            q.QLORA_ERR_INVALID_ARG
+    d = _desc(q)
+    # null weight / null output
+    assert lib.qlora_quantize_nf4(None, ctypes.byref(d), P(0x200000), 1 << 20, None) == \
+        q.QLORA_ERR_INVALID_ARG
+    assert lib.qlora_dequantize_nf4(ctypes.byref(d), q.QLORA_F32, None, None) == \
+        q.QLORA_ERR_INVALID_ARG
+    # workspace too small
+    assert lib.qlora_quantize_nf4(P(0x200000), ctypes.byref(d), P(0x300000), 16, None) == \
+        q.QLORA_ERR_WORKSPACE
+    # K not a multiple of 64 on the linear path
+    d2 = _desc(q, rows=64, cols=96)
+    X = P(0x400000)
+    st = lib.qlora_linear_fwd(ctypes.byref(d2), X, 4, X, X, 8, ctypes.c_float(16.0), X, None,
+                              X, 1 << 30, None)
+    assert st == q.QLORA_ERR_UNSUPPORTED
+    # rank out of range, M < 1, misaligned activation
+    assert lib.qlora_linear_fwd(ctypes.byref(d), X, 4, X, X, 0, ctypes.c_float(1.0), X, None, X,
+                                1 << 30, None) == q.QLORA_ERR_INVALID_ARG
+    assert lib.qlora_linear_fwd(ctypes.byref(d), X, 0, X, X, 8, ctypes.c_float(1.0), X, None, X,
+                                1 << 30, None) == q.QLORA_ERR_INVALID_ARG
+    assert lib.qlora_linear_fwd(ctypes.byref(d), P(0x400002), 4, X, X, 8, ctypes.c_float(1.0), X,
+                                None, X, 1 << 30, None) == q.QLORA_ERR_INVALID_ARG
+    # backward: missing dA, workspace too small
+    assert lib.qlora_linear_bwd(ctypes.byref(d), X, 4, X, X, 8, ctypes.c_float(1.0), X, None, X,
+                                None, X, X, 1 << 30, None) == q.QLORA_ERR_INVALID_ARG
+    assert lib.qlora_linear_bwd(ctypes.byref(d), X, 4, X, X, 8, ctypes.c_float(1.0), X, None, X,
+                                X, X, X, 64, None) == q.QLORA_ERR_WORKSPACE
+
+
+def test_no_cpu_fallback(q, monkeypatch):
+    """The binding raises when the library is absent instead of computing on
+    the host."""
+    monkeypatch.setattr(q, "_lib", None)
+    monkeypatch.setattr(q, "LIB_PATH", "/nonexistent/libqlora_nf4.so")
+    with pytest.raises(RuntimeError):
+        q.lib()

@@ -1,0 +1,126 @@
+"""GPU parity: NF4 quantisation, double quantisation and dequantisation must
+match the oracle bit for bit (codes, exact absmax, int8 constants, scales,
+mean, reconstructed constants, float32 and bf16 dequantised weights)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import (DEV, compare_quant_state, host, oracle, say, to_dev, workloads)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    import bit_quantized_lora_quant_amd as q
+    q.lib()
+    assert torch.cuda.is_available()
+    return q
+
+
+def _roundtrip(q, w_np, check_dequant=True):
+    n = w_np.size
+    qt = oracle.quantize(w_np)
+    qq, ws = q.qlora_quantize_nf4(to_dev(w_np))
+    torch.cuda.synchronize()
+    compare_quant_state(qq, ws, qt, n)
+    if check_dequant:
+        ahat = oracle.dequant_absmax(qt["absmax_q"], qt["absmax_scale"], qt["absmax_mean"])
+        got_a = host(q.qlora_dequantize_absmax(qq)).numpy()
+        assert np.array_equal(got_a.view(np.uint32), ahat.view(np.uint32)), "reconstructed absmax"
+        wd = oracle.dequantize(qt)
+        f32 = host(q.qlora_dequantize_nf4(qq, torch.float32)).numpy().reshape(-1)
+        assert np.array_equal(f32.view(np.uint32), wd.view(np.uint32)), "fp32 dequant at %s" % (
+            np.nonzero(f32.view(np.uint32) != wd.view(np.uint32))[0][:8],)
+        b16 = host(q.qlora_dequantize_nf4(qq, torch.bfloat16)).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(b16.reshape(-1), oracle.to_bf16_bits(wd)), "bf16 dequant"
+    return qq
+
+
+SHAPES = [(1, 1), (1, 7), (3, 5), (1, 64), (1, 65), (2, 100), (7, 64 * 5 + 3), (64, 64),
+          (100, 1000), (257, 255), (1024, 1024), (333, 4096)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "%dx%d" % s)
+def test_quantize_dequant_bit_exact(q, shape):
+    say("quant %s" % (shape,))
+    rng = np.random.default_rng(shape[0] * 7919 + shape[1])
+    w = (rng.standard_normal(shape) * 0.02).astype(np.float32)
+    _roundtrip(q, w)
+
+
+def test_levels_round_trip(q):
+    say("quant level round trip")
+    cb = oracle.codebook()
+    idx = np.tile(np.arange(16), 4 * 600)
+    for e in (-6, -1, 0, 2):
+        w = (cb[idx] * np.float32(2.0 ** e)).reshape(600, 64)
+        qq = _roundtrip(q, w)
+        back = host(q.qlora_dequantize_nf4(qq, torch.float32)).numpy()
+        assert np.array_equal(back.view(np.uint32), w.view(np.uint32))
+
+
+def test_zero_and_midpoint_blocks(q):
+    say("quant zero + midpoints")
+    cb = oracle.codebook().astype(np.float64)
+    w = np.zeros((40, 64), dtype=np.float32)
+    w[5:7] = -0.0
+    row = 10
+    for j in range(15):
+        m = (cb[j] + cb[j + 1]) / 2.0
+        f = np.float32(m)
+        lo = f if float(f) <= m else np.nextafter(f, np.float32(-2))
+        w[row, 2 * j] = lo
+        w[row, 2 * j + 1] = np.nextafter(lo, np.float32(2))
+    w[row, 63] = 1.0
+    w[20:] = np.random.default_rng(5).uniform(-1, 1, size=(20, 64)).astype(np.float32)
+    _roundtrip(q, w)
+
+
+def test_heavy_tailed_and_wide_range(q):
+    """Constants spanning many magnitudes exercise the int8 clamp, negative
+    reconstructed constants and the float64 tree sum."""
+    say("quant wide range")
+    rng = np.random.default_rng(9)
+    w = (rng.standard_cauchy((512, 512)) * 0.01).astype(np.float32)
+    w[:10] *= np.float32(1e6)
+    w[10:20] *= np.float32(1e-6)
+    _roundtrip(q, w)
+
+
+def test_deterministic_repeat(q):
+    say("quant determinism")
+    w = to_dev((np.random.default_rng(3).standard_normal((512, 2048)) * 0.02).astype(np.float32))
+    a, _ = q.qlora_quantize_nf4(w)
+    b, _ = q.qlora_quantize_nf4(w)
+    torch.cuda.synchronize()
+    for t1, t2 in ((a.codes, b.codes), (a.absmax_q, b.absmax_q), (a.absmax_scale, b.absmax_scale),
+                   (a.absmax_mean, b.absmax_mean)):
+        assert torch.equal(t1, t2)
+
+
+@pytest.mark.parametrize("which", ["embed_tokens", "down_proj"])
+def test_full_weight_set_tensors(q, which):
+    """Full-size tensors of the 8.03B-parameter weight set (drawn on the
+    device), every output compared: the embedding (525M weights, three tree
+    passes for the mean) and one down projection."""
+    spec = [s for s in workloads.llama8b_weight_set() if s[0] == which][0]
+    name, layer, rows, cols = spec
+    say("full tensor %s %dx%d" % (name, rows, cols))
+    w = workloads.device_weight(2, layer, 0 if name == "embed_tokens" else 6, rows, cols)
+    qq, ws = q.qlora_quantize_nf4(w)
+    torch.cuda.synchronize()
+    w_np = host(w).numpy()
+    del w
+    qt = oracle.quantize(w_np)
+    compare_quant_state(qq, ws, qt, w_np.size)
+    del ws
+    wd = oracle.dequantize(qt)
+    out = q.qlora_dequantize_nf4(qq, torch.bfloat16)
+    b16 = host(out).view(torch.int16).numpy().view(np.uint16).reshape(-1)
+    assert np.array_equal(b16, oracle.to_bf16_bits(wd))
+    del out
+    f32 = host(q.qlora_dequantize_nf4(qq, torch.float32)).numpy().reshape(-1)
+    assert np.array_equal(f32.view(np.uint32), wd.view(np.uint32))
+    bits = 8.0 * qq.nbytes() / (rows * cols)
+    assert abs(bits - 4.127) < 1e-3
