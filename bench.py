@@ -1,0 +1,406 @@
+#!/usr/bin/env python
+"""Benchmark of the frozen-NF4 LoRA linear on one MI355X.
+
+Headline step: forward then backward (reverse order) through the seven
+Llama-3.1-8B layer projections (q, k, v, o 4096-wide, k/v 1024, gate/up/down
+14336) at 2048 tokens, LoRA r = 16, alpha = 32, NF4 weights with double
+quantisation.  ``value`` is tokens per second of that step with every input
+resident in HBM.  The JSON line also carries the dominant kernel's roofline
+(HIP-event durations measured on the library's stream during the timed
+region), the CPU oracle timed on a bounded sample, and the other legs of the
+path: quantise + dequantise of the full 8.03B-parameter weight set, the
+70B-shaped decode GEMV at 1 / 4 / 16 tokens, and the 80-layer LLaMA-65B stack.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs all|none]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def log(msg):
+    print("[bench] %s" % msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--legs", choices=["all", "none"], default="all")
+    ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    return ap.parse_args()
+
+
+def src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "bit_quantized_lora_quant_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, launches_flops):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        t = json.load(open(path)).get(kernel)
+    except ValueError:
+        return None
+    if not t or t.get("source_sha") != src_hash(*t.get("sources", [])):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------- headline
+def linear_flops(M, N, K, r):
+    """Algorithmic flops of fwd + bwd of one adapted frozen linear (no dW):
+    fwd 2MNK + 2Mr(K+N); bwd dX 2MNK + 2MrK, G 2MNr, dA 2MrK, dB 2MNr."""
+    return 4 * M * N * K + 6 * M * r * (K + N)
+
+
+def headline(args, q, torch, workloads):
+    wl = workloads.LLAMA8B_LAYER
+    dev = "cuda:0"
+    M, r, alpha = wl.m, wl.r, wl.alpha
+    layers = []
+    host_w = []
+    for t, (name, K, N) in enumerate(wl.linears):
+        w, x, a, b, dy = workloads.linear_inputs(wl, 0, t)
+        qq, _ = q.qlora_quantize_nf4(torch.from_numpy(w).to(dev))
+        host_w.append(w)
+        L = dict(name=name, N=N, K=K, q=qq, X=x.to(dev), A=a.to(dev), B=b.to(dev), dY=dy.to(dev))
+        L["Y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        L["XA"] = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+        L["dX"] = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        L["dA"] = torch.empty((r, K), dtype=torch.float32, device=dev)
+        L["dB"] = torch.empty((N, r), dtype=torch.float32, device=dev)
+        L["ws"] = q.workspace(q.qlora_linear_workspace_bytes(M, N, K, r), dev)
+        layers.append(L)
+    torch.cuda.synchronize()
+    log("headline inputs ready (%d linears)" % len(layers))
+
+    def step():
+        for L in layers:
+            q.qlora_linear_fwd(L["q"], L["X"], L["A"], L["B"], alpha, Y=L["Y"], XA_out=L["XA"],
+                               ws=L["ws"], return_xa=True)
+        for L in reversed(layers):
+            q.qlora_linear_bwd(L["q"], L["X"], L["A"], L["B"], alpha, L["dY"], XA_in=L["XA"],
+                               dX=L["dX"], dA=L["dA"], dB=L["dB"], ws=L["ws"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    q.qlora_trace_begin(["fwd_gemm", "dx_gemm"], capacity=len(layers) * args.steps + 8)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    tr = q.qlora_trace_end()
+    sec = (t1 - t0) / args.steps
+    flops = sum(linear_flops(M, L["N"], L["K"], r) for L in layers)
+    # per-kernel algorithmic flops: fwd GEMM 2MN(K + r), dX GEMM 2MK(N + r)
+    kflops = {"fwd_gemm": sum(2 * M * L["N"] * (L["K"] + r) for L in layers),
+              "dx_gemm": sum(2 * M * L["K"] * (L["N"] + r) for L in layers)}
+    kern = {}
+    for name, (n, ms) in tr.items():
+        avg_ms = ms / n
+        per_launch = kflops[name] / len(layers)
+        kern[name] = {"launches": n, "avg_us": avg_ms * 1e3,
+                      "tflops": kflops[name] * (n / len(layers)) / (ms * 1e-3) / 1e12,
+                      "flops_per_launch": per_launch}
+    dom = max(kern, key=lambda k: kern[k]["avg_us"] * kern[k]["launches"])
+    d = kern[dom]
+    roof = {"kernel": {"fwd_gemm": "k_qlora_fwd_nt", "dx_gemm": "k_qlora_dx_nn"}[dom],
+            "bound": "mfma", "achieved": round(d["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(d["tflops"] / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_for(dom, None),
+            "avg_launch_us": round(d["avg_us"], 2),
+            "flops_per_launch": d["flops_per_launch"]}
+    other = {k: {"avg_launch_us": round(v["avg_us"], 2), "tflops": round(v["tflops"], 2),
+                 "frac": round(v["tflops"] / PEAK_BF16_TFLOPS, 4)} for k, v in kern.items()}
+    res = dict(sec=sec, tokens=M, flops=flops, roofline=roof, kernels=other)
+    log("headline: %.3f ms/step, %.1f TFLOP/s" % (sec * 1e3, flops / sec / 1e12))
+    return res, layers, host_w
+
+
+# ---------------------------------------------------------- cpu baseline
+def cpu_baseline(workloads, layers, host_w, sample_tokens=256):
+    """The oracle as it stands, on a bounded sample of the headline step: the
+    float32 dequantisation of all seven weights (once per step, as the GPU
+    path rebuilds them every step) plus the float64 fwd+bwd of `sample_tokens`
+    tokens; extrapolated to the step's 2048 tokens."""
+    import numpy as np
+    import oracle
+    try:
+        import threadpoolctl
+        blas = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    except Exception:
+        blas = os.cpu_count() or 1
+    wl = workloads.LLAMA8B_LAYER
+    qts = [oracle.quantize(w) for w in host_w]           # load-time, untimed
+    t0 = time.perf_counter()
+    wds = [oracle.dequantize(qt).reshape(w.shape) for qt, w in zip(qts, host_w)]
+    t_deq = time.perf_counter() - t0
+    t_lin = 0.0
+    for t, L in enumerate(layers):
+        _, x, a, b, dy = workloads.linear_inputs(wl, 0, t)
+        xs = workloads.bf16_to_f64(x[:sample_tokens])
+        dys = workloads.bf16_to_f64(dy[:sample_tokens])
+        af, bfl = workloads.bf16_to_f64(a), workloads.bf16_to_f64(b)
+        t1 = time.perf_counter()
+        oracle.linear_fwd(wds[t], xs, af, bfl, wl.alpha)
+        oracle.linear_bwd(wds[t], xs, af, bfl, wl.alpha, dys)
+        t_lin += time.perf_counter() - t1
+    step = t_deq + t_lin * (wl.m / sample_tokens)
+    return {"value": round(wl.m / step, 2), "unit": "tokens/s",
+            "cores": int(max(blas, oracle.threads())), "kind": "oracle",
+            "sample": ("dequantise the 7 Llama-3.1-8B weights (%.2f s) + float64 fwd+bwd of %d of "
+                       "the 2048 tokens (%.2f s), linear part scaled x%d"
+                       % (t_deq, sample_tokens, t_lin, wl.m // sample_tokens))}
+
+
+# -------------------------------------------------------------------- legs
+def leg_quant_dequant(q, torch, workloads, passes=3):
+    """Quantise then dequantise (to bf16) every 2-D weight of the 8.03B set."""
+    dev = "cuda:0"
+    specs = workloads.llama8b_weight_set()
+    ws_max = max(q.qlora_quantize_workspace_bytes(r, c) for _, _, r, c in specs)
+    ws = q.workspace(ws_max, dev)
+    out = torch.empty(max(r * c for _, _, r, c in specs), dtype=torch.bfloat16, device=dev)
+    Ws, Qs = [], []
+    for i, (name, layer, rows, cols) in enumerate(specs):
+        Ws.append(workloads.device_weight(2, layer, i, rows, cols))
+        Qs.append(q.NF4Tensor(rows, cols, dev))
+    params = sum(r * c for _, _, r, c in specs)
+    log("quant leg: %d tensors, %.3fB params on device" % (len(specs), params / 1e9))
+
+    def quant_pass():
+        for W, Q in zip(Ws, Qs):
+            q.qlora_quantize_nf4(W, Q, ws)
+
+    def deq_pass():
+        for Q in Qs:
+            q.qlora_dequantize_nf4(Q, out=out[: Q.numel].view(Q.rows, Q.cols))
+
+    quant_pass(); deq_pass()
+    torch.cuda.synchronize()
+    q.qlora_trace_begin(["quantize", "dequant"], capacity=len(specs) * passes + 4)
+    t0 = time.perf_counter()
+    for _ in range(passes):
+        quant_pass()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(passes):
+        deq_pass()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    tr = q.qlora_trace_end()
+    nbytes = sum(Q.nbytes() for Q in Qs)
+    bpp = 8.0 * nbytes / params
+    tq, td = (t1 - t0) / passes, (t2 - t1) / passes
+    # algorithmic bytes: quantise reads 4 B and writes the 4.127-bit state;
+    # dequantise reads the state and writes 2 B (bf16)
+    qbytes = 4 * params + nbytes
+    dbytes = nbytes + 2 * params
+    res = {"params": params, "bits_per_param": round(bpp, 5),
+           "quantize": {"ms": round(tq * 1e3, 3), "GB/s": round(qbytes / tq / 1e9, 1),
+                        "frac_hbm": round(qbytes / tq / 1e9 / PEAK_HBM_GBS, 4)},
+           "dequantize_bf16": {"ms": round(td * 1e3, 3), "GB/s": round(dbytes / td / 1e9, 1),
+                               "frac_hbm": round(dbytes / td / 1e9 / PEAK_HBM_GBS, 4)}}
+    for name, (n, ms) in tr.items():
+        kb = (4 * params + params / 2) if name == "quantize" else dbytes
+        res[name + "_kernel"] = {"launches": n, "avg_us": round(ms / n * 1e3, 2),
+                                 "GB/s": round(kb * (n / len(specs)) / (ms * 1e-3) / 1e9, 1)}
+    del Ws, Qs, out, ws
+    torch.cuda.empty_cache()
+    log("quant leg: quantise %.2f ms, dequantise %.2f ms, %.4f bits/param" % (tq * 1e3, td * 1e3, bpp))
+    return res
+
+
+def leg_decode(q, torch, workloads, steps=5):
+    """Decode forward through 80 layers x 7 70B-shaped linears (distinct NF4
+    weights, ~35 GB) at M = 1, 4, 16 tokens."""
+    dev = "cuda:0"
+    wl = workloads.LLAMA70B_DECODE
+    r, alpha = wl.r, wl.alpha
+    lin = []
+    qws = q.workspace(max(q.qlora_quantize_workspace_bytes(n, k) for _, k, n in wl.linears), dev)
+    for layer in range(wl.layers):
+        for t, (name, K, N) in enumerate(wl.linears):
+            W = workloads.device_weight(4, layer, t, N, K)
+            Q, _ = q.qlora_quantize_nf4(W, ws=qws)
+            del W
+            lin.append((Q, K, N))
+        if layer % 20 == 19:
+            torch.cuda.synchronize()
+            log("decode leg: %d/%d layers quantised" % (layer + 1, wl.layers))
+    del qws
+    torch.cuda.empty_cache()
+    g = torch.Generator(device=dev)
+    g.manual_seed(4)
+    A = {K: (torch.rand((r, K), generator=g, device=dev) * 2 - 1).mul_(K ** -0.5).to(torch.bfloat16)
+         for _, K, _ in wl.linears}
+    B = {N: (torch.randn((N, r), generator=g, device=dev) * 0.01).to(torch.bfloat16)
+         for _, _, N in wl.linears}
+    out = {}
+    for M in wl.decode_m:
+        X = {K: torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16) for _, K, _ in wl.linears}
+        Y = {N: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _, _, N in wl.linears}
+        ws = q.workspace(max(q.qlora_linear_workspace_bytes(M, N, K, r) for _, K, N in wl.linears), dev)
+
+        def step():
+            for Q, K, N in lin:
+                q.qlora_linear_fwd(Q, X[K], A[K], B[N], alpha, Y=Y[N], ws=ws)
+
+        step()
+        torch.cuda.synchronize()
+        q.qlora_trace_begin(["gemv"], capacity=len(lin) * steps + 4)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / steps
+        tr = q.qlora_trace_end()
+        nb = sum(Q.nbytes() + 2 * r * (K + N) + 2 * M * (K + N) for Q, K, N in lin)
+        code_bytes = sum(Q.nbytes() for Q, _, _ in lin)
+        ent = {"ms_per_token_step": round(sec * 1e3, 3), "tokens/s": round(M / sec, 1),
+               "GB/s": round(nb / sec / 1e9, 1), "frac_hbm": round(nb / sec / 1e9 / PEAK_HBM_GBS, 4)}
+        if "gemv" in tr:
+            n, ms = tr["gemv"]
+            ent["gemv_kernel"] = {"launches": n, "avg_us": round(ms / n * 1e3, 2),
+                                  "GB/s": round(code_bytes * (n / len(lin)) / (ms * 1e-3) / 1e9, 1)}
+        out["M=%d" % M] = ent
+        log("decode leg M=%d: %.3f ms per token step" % (M, sec * 1e3))
+    del lin
+    torch.cuda.empty_cache()
+    return out
+
+
+def leg_65b_stack(q, torch, workloads, steps=2):
+    """fwd + bwd through 80 LLaMA-65B layers (7 linears each, distinct NF4
+    weights ~33 GB), 4096 tokens, r = 64, alpha = 16."""
+    dev = "cuda:0"
+    wl = workloads.LLAMA65B_LAYER
+    M, r, alpha = wl.m, wl.r, wl.alpha
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    qws = q.workspace(max(q.qlora_quantize_workspace_bytes(n, k) for _, k, n in wl.linears), dev)
+    lin = []
+    for layer in range(wl.layers):
+        for t, (name, K, N) in enumerate(wl.linears):
+            W = workloads.device_weight(3, layer, t, N, K)
+            Q, _ = q.qlora_quantize_nf4(W, ws=qws)
+            del W
+            lin.append((Q, K, N))
+        if layer % 20 == 19:
+            torch.cuda.synchronize()
+            log("65B leg: %d/%d layers quantised" % (layer + 1, wl.layers))
+    del qws
+    shp = {(K, N) for _, K, N in wl.linears}
+    X = {K: torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16) for K, _ in shp}
+    dY = {N: torch.randn((M, N), generator=g, device=dev).to(torch.bfloat16) for _, N in shp}
+    A = {K: ((torch.rand((r, K), generator=g, device=dev) * 2 - 1) * K ** -0.5).to(torch.bfloat16)
+         for K, _ in shp}
+    B = {N: (torch.randn((N, r), generator=g, device=dev) * 0.01).to(torch.bfloat16) for _, N in shp}
+    Y = {N: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _, N in shp}
+    dX = {K: torch.empty((M, K), dtype=torch.bfloat16, device=dev) for K, _ in shp}
+    dA = {K: torch.empty((r, K), dtype=torch.float32, device=dev) for K, _ in shp}
+    dB = {N: torch.empty((N, r), dtype=torch.float32, device=dev) for _, N in shp}
+    XA = {K: torch.empty((M, r), dtype=torch.bfloat16, device=dev) for K, _ in shp}
+    ws = q.workspace(max(q.qlora_linear_workspace_bytes(M, N, K, r) for K, N in shp), dev)
+
+    def step():
+        for Q, K, N in lin:
+            q.qlora_linear_fwd(Q, X[K], A[K], B[N], alpha, Y=Y[N], XA_out=XA[K], ws=ws, return_xa=True)
+        for Q, K, N in reversed(lin):
+            q.qlora_linear_bwd(Q, X[K], A[K], B[N], alpha, dY[N], XA_in=XA[K], dX=dX[K], dA=dA[K],
+                               dB=dB[N], ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    flops = sum(linear_flops(M, N, K, r) for _, K, N in lin)
+    del lin
+    torch.cuda.empty_cache()
+    log("65B leg: %.3f s per 80-layer step" % sec)
+    return {"s_per_step": round(sec, 4), "tokens/s": round(M / sec, 1),
+            "TFLOP/s": round(flops / sec / 1e12, 1),
+            "frac_mfma": round(flops / sec / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the path is measured on a single MI355X "
+              "(--gpus %d / WORLD_SIZE %d requested)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_quantized_lora_quant_amd as q
+    import workloads
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    q.lib()
+    head, layers, host_w = headline(args, q, torch, workloads)
+    cpu = None
+    if args.cpu_baseline == "on":
+        cpu = cpu_baseline(workloads, layers, host_w)
+        log("cpu baseline: %s tokens/s on %d threads" % (cpu["value"], cpu["cores"]))
+    del layers, host_w
+    torch.cuda.empty_cache()
+    legs = {}
+    if args.legs == "all":
+        legs["llama8b_weight_set_quant_dequant"] = leg_quant_dequant(q, torch, workloads)
+        legs["llama70b_decode_gemv"] = leg_decode(q, torch, workloads)
+        legs["llama65b_80_layer_stack"] = leg_65b_stack(q, torch, workloads)
+    tokens_s = head["tokens"] / head["sec"]
+    tflops = head["flops"] / head["sec"] / 1e12
+    line = {
+        "metric": "QLoRA linear fwd+bwd tokens/s (TFLOP/s, % MFMA peak); NF4 dequant/GEMV GB/s",
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["sec"] * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; random NF4-quantised weights, no checkpoint)",
+        "config": {"workload": "Llama-3.1-8B layer linears q/k/v/o/gate/up/down, 2048 tokens, "
+                               "LoRA r=16 alpha=32, NF4 + double quant, fwd+bwd",
+                   "tokens": 2048, "rank": 16, "linears": 7},
+        "tflops": round(tflops, 2),
+        "frac_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": head["roofline"],
+        "kernels": head["kernels"],
+        "cpu_baseline": cpu,
+        "legs": legs,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -24,7 +24,9 @@ EXPORTS = [
     "qlora_nf4_codebook", "qlora_status_string", "qlora_quantize_workspace_bytes",
     "qlora_quantize_nf4", "qlora_dequantize_nf4", "qlora_dequantize_absmax",
     "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
+    "qlora_trace_begin", "qlora_trace_end",
 ]
+KERNELS = {"fwd_gemm": 0, "dx_gemm": 1, "quantize": 2, "dequant": 3, "gemv": 4}
 
 
 class QloraError(RuntimeError):
@@ -67,8 +69,11 @@ def lib():
         L.qlora_linear_workspace_bytes.restype = SZ
         L.qlora_linear_fwd.argtypes = [D, P, I64, P, P, I32, F, P, P, P, SZ, P]
         L.qlora_linear_bwd.argtypes = [D, P, I64, P, P, I32, F, P, P, P, P, P, P, SZ, P]
+        L.qlora_trace_begin.argtypes = [ctypes.c_uint32, I32]
+        L.qlora_trace_end.argtypes = [P, P]
         for name in ("qlora_quantize_nf4", "qlora_dequantize_nf4", "qlora_dequantize_absmax",
-                     "qlora_linear_fwd", "qlora_linear_bwd"):
+                     "qlora_linear_fwd", "qlora_linear_bwd", "qlora_trace_begin",
+                     "qlora_trace_end"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -220,6 +225,22 @@ def qlora_linear_bwd(q: NF4Tensor, X, A, B, alpha: float, dY, XA_in=None, need_d
                                   _ptr(dX) if need_dx else None, _ptr(dA), _ptr(dB), _ptr(ws),
                                   ws.numel(), _stream()), "qlora_linear_bwd")
     return (dX if need_dx else None), dA, dB
+
+
+def qlora_trace_begin(kernels, capacity: int = 4096):
+    """Start timing launches of the named kernels (see KERNELS) with HIP events."""
+    mask = 0
+    for k in kernels:
+        mask |= 1 << KERNELS[k]
+    _check(lib().qlora_trace_begin(mask, capacity), "qlora_trace_begin")
+
+
+def qlora_trace_end():
+    """{kernel name: (launches, total_ms)} for the kernels timed since begin."""
+    n = (ctypes.c_int32 * len(KERNELS))()
+    ms = (ctypes.c_double * len(KERNELS))()
+    _check(lib().qlora_trace_end(n, ms), "qlora_trace_end")
+    return {name: (int(n[i]), float(ms[i])) for name, i in KERNELS.items() if n[i] > 0}
 
 
 class QLoRALinearFn(torch.autograd.Function):

@@ -82,6 +82,44 @@ LinearWs linear_layout(int64_t M, int64_t N, int64_t K, int r) {
 template <typename T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
 
+// ------------------------------------------------------ timing instrumentation
+struct Trace {
+  uint32_t mask = 0;
+  int32_t capacity = 0;
+  hipEvent_t* ev[QLORA_KERNEL_COUNT] = {};   // 2 * capacity events per kernel
+  int32_t used[QLORA_KERNEL_COUNT] = {};
+};
+Trace g_trace;
+
+// Runs `launch`, bracketed by a recorded event pair when kernel `k` is traced.
+template <typename F>
+hipError_t traced(int k, hipStream_t s, F&& launch) {
+  const bool on = (g_trace.mask >> k) & 1u && g_trace.used[k] < g_trace.capacity;
+  if (on) {
+    hipError_t e = hipEventRecord(g_trace.ev[k][2 * g_trace.used[k]], s);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch();
+  if (on && e == hipSuccess) {
+    e = hipEventRecord(g_trace.ev[k][2 * g_trace.used[k] + 1], s);
+    ++g_trace.used[k];
+  }
+  return e;
+}
+
+void trace_release() {
+  for (int k = 0; k < QLORA_KERNEL_COUNT; ++k) {
+    if (g_trace.ev[k]) {
+      for (int i = 0; i < 2 * g_trace.capacity; ++i) (void)hipEventDestroy(g_trace.ev[k][i]);
+      delete[] g_trace.ev[k];
+      g_trace.ev[k] = nullptr;
+    }
+    g_trace.used[k] = 0;
+  }
+  g_trace.mask = 0;
+  g_trace.capacity = 0;
+}
+
 qlora_status check_linear(const qlora_nf4_tensor* W, const void* X, int64_t M, const void* A,
                           const void* B, int32_t r, float alpha) {
   if (!valid_tensor(W) || !X || !A || !B) return QLORA_ERR_INVALID_ARG;
@@ -124,7 +162,8 @@ qlora_status qlora_quantize_nf4(const float* W, const qlora_nf4_tensor* q, void*
   if (!ws || ws_bytes < L.total || !aligned(ws, kAlign)) return QLORA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* absmax = at<float>(ws, L.absmax);
-  hipError_t e = launch_quant_absmax(W, n, q->codes, absmax, s);
+  hipError_t e = traced(QLORA_KERNEL_QUANTIZE, s,
+                        [&] { return launch_quant_absmax(W, n, q->codes, absmax, s); });
   if (e != hipSuccess) return QLORA_ERR_HIP;
   e = launch_dq(absmax, nblocks(n), q->absmax_q, q->absmax_scale, q->absmax_mean,
                 at<double>(ws, L.pa), at<double>(ws, L.pb), s);
@@ -135,9 +174,11 @@ qlora_status qlora_dequantize_nf4(const qlora_nf4_tensor* q, qlora_dtype out_dty
                                   void* stream) {
   if (!valid_tensor(q) || !out || !aligned(out, 16)) return QLORA_ERR_INVALID_ARG;
   if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16) return QLORA_ERR_INVALID_ARG;
-  return hip_status(launch_dequant(q->codes, q->absmax_q, q->absmax_scale, q->absmax_mean,
-                                   q->rows * q->cols, out_dtype == QLORA_BF16, out,
-                                   static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(traced(QLORA_KERNEL_DEQUANT, s, [&] {
+    return launch_dequant(q->codes, q->absmax_q, q->absmax_scale, q->absmax_mean,
+                          q->rows * q->cols, out_dtype == QLORA_BF16, out, s);
+  }));
 }
 
 qlora_status qlora_dequantize_absmax(const qlora_nf4_tensor* q, float* out, void* stream) {
@@ -172,11 +213,14 @@ qlora_status qlora_linear_fwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
   if (e != hipSuccess) return QLORA_ERR_HIP;
   if (M <= 16) {
     float* part = at<float>(ws, L.gemv_part);
-    e = launch_gemv(X, M, K, W->codes, N, ahat_t, L.gemv_splits, part, s);
+    e = traced(QLORA_KERNEL_GEMV, s,
+               [&] { return launch_gemv(X, M, K, W->codes, N, ahat_t, L.gemv_splits, part, s); });
     if (e != hipSuccess) return QLORA_ERR_HIP;
     e = launch_gemv_finish(part, L.gemv_splits, M, N, xas, r, L.r32, B, Y, s);
   } else {
-    e = launch_fwd_gemm(X, M, K, W->codes, N, ahat_t, xas, B, r, L.r32, Y, s);
+    e = traced(QLORA_KERNEL_FWD_GEMM, s, [&] {
+      return launch_fwd_gemm(X, M, K, W->codes, N, ahat_t, xas, B, r, L.r32, Y, s);
+    });
   }
   return hip_status(e);
 }
@@ -209,7 +253,9 @@ qlora_status qlora_linear_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
   QL_TRY(launch_skinny_nt(dY, M, N, N, bt, r, L.np, scale, gs, L.r32, nullptr, gt, L.mp, s));
   if (dX) {
     QL_TRY(launch_absmax_recon_t(W->absmax_q, W->absmax_scale, W->absmax_mean, N, K, ahat_t, s));
-    QL_TRY(launch_dx_gemm(dY, M, N, W->codes, K, ahat_t, gs, A, r, L.r32, dX, s));
+    QL_TRY(traced(QLORA_KERNEL_DX_GEMM, s, [&] {
+      return launch_dx_gemm(dY, M, N, W->codes, K, ahat_t, gs, A, r, L.r32, dX, s);
+    }));
   }
   // dA = s . G^T X  (reduce over tokens into [r, K]);  dB = s . dY^T XA  ([N, r])
   float* pa = at<float>(ws, L.part_a);
@@ -220,6 +266,49 @@ qlora_status qlora_linear_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
   QL_TRY(launch_lora_grad_reduce(pb, L.sb, N, r, scale, 0, dB, s));
 #undef QL_TRY
   return QLORA_OK;
+}
+
+qlora_status qlora_trace_begin(uint32_t kernel_mask, int32_t capacity) {
+  if (kernel_mask == 0 || kernel_mask >= (1u << QLORA_KERNEL_COUNT) || capacity < 1 ||
+      capacity > (1 << 20))
+    return QLORA_ERR_INVALID_ARG;
+  trace_release();
+  for (int k = 0; k < QLORA_KERNEL_COUNT; ++k) {
+    if (!((kernel_mask >> k) & 1u)) continue;
+    g_trace.ev[k] = new hipEvent_t[2 * capacity];
+    for (int i = 0; i < 2 * capacity; ++i) {
+      if (hipEventCreate(&g_trace.ev[k][i]) != hipSuccess) {
+        for (int j = 0; j < i; ++j) (void)hipEventDestroy(g_trace.ev[k][j]);
+        delete[] g_trace.ev[k];
+        g_trace.ev[k] = nullptr;
+        trace_release();
+        return QLORA_ERR_HIP;
+      }
+    }
+  }
+  g_trace.mask = kernel_mask;
+  g_trace.capacity = capacity;
+  return QLORA_OK;
+}
+
+qlora_status qlora_trace_end(int32_t* launches, double* total_ms) {
+  if (!launches || !total_ms) return QLORA_ERR_INVALID_ARG;
+  qlora_status st = QLORA_OK;
+  for (int k = 0; k < QLORA_KERNEL_COUNT; ++k) {
+    launches[k] = g_trace.used[k];
+    total_ms[k] = 0.0;
+    for (int i = 0; i < g_trace.used[k]; ++i) {
+      float ms = 0.f;
+      if (hipEventSynchronize(g_trace.ev[k][2 * i + 1]) != hipSuccess ||
+          hipEventElapsedTime(&ms, g_trace.ev[k][2 * i], g_trace.ev[k][2 * i + 1]) != hipSuccess) {
+        st = QLORA_ERR_HIP;
+        break;
+      }
+      total_ms[k] += ms;
+    }
+  }
+  trace_release();
+  return st;
 }
 
 }  // extern "C"

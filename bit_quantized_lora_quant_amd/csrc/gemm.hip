@@ -99,6 +99,64 @@ __device__ __forceinline__ uint4 lds_chunk(const uint16_t* lds, int row, int chu
   return *reinterpret_cast<const uint4*>(lds + row * kStep + ((chunk ^ (row & 7)) * 8));
 }
 
+// acc += A * B on v_mfma_f32_16x16x32_bf16 with the accumulator tied to its
+// AGPRs.  Written as inline asm because, with all 256 AGPRs holding
+// accumulators, the register allocator otherwise migrates tiles between
+// AGPRs and VGPRs every iteration.  Hazards the compiler cannot see here:
+// an AGPR written by VALU must settle before the first MFMA reads it (callers
+// run mfma_settle() after zero-filling), and the MFMA result must settle
+// before a VALU reads it (mfma_settle() after the last one).  A/B source
+// registers are read at issue, so reusing them right after is safe.
+typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void mfma_acc(f32x4_t& acc, const uint4& a, const u32x4v_t& b) {
+  const u32x4v_t av = {a.x, a.y, a.z, a.w};
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(av), "v"(b));
+}
+__device__ __forceinline__ void mfma_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// Global -> LDS copy of an activation tile [256 rows][64 cols] bf16 with the
+// LDS-DMA loads (global_load_lds_dwordx4: no VGPRs, no VALU).  Each load
+// instruction fills 1 KB = 8 rows; wave w issues loads q = 8w .. 8w+7 for
+// rows 8q .. 8q+7.  Lane t lands at row 8q + t/8, chunk position t%8, so it
+// fetches global chunk (t%8) ^ (t/8): the XOR swizzle lds_chunk reads back.
+struct TileDma {
+  uint32_t off[8];   // element offset of this lane's source chunk, per load
+  __device__ __forceinline__ void init(int64_t ld, int64_t row0, int64_t rows_valid) {
+    const int t = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int c = (t & 7) ^ (t >> 3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int64_t row = row0 + 8 * (8 * wv + i) + (t >> 3);
+      row = row < rows_valid ? row : rows_valid - 1;
+      off[i] = (uint32_t)(row * ld) + (uint32_t)(c * 8);
+    }
+  }
+  __device__ __forceinline__ void issue(const uint16_t* __restrict__ src, uint32_t col0,
+                                        uint16_t* lds_tile) const {
+    const int wv = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(src + col0 + off[i]),
+                                       (lds_void_t*)(lds_tile + (8 * wv + i) * 512), 16, 0, 0);
+  }
+};
+
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// The two 32-bit code words of one row for one 64-wide step as used by lane
+// group g: sub-step 0 takes inner indices 8g..8g+7 (bytes 4g..4g+3 of the
+// row's 32-byte segment), sub-step 1 takes 32+8g.. (bytes 16+4g..).  This is
+// the A-operand chunk order 4s + g, which reads LDS without bank conflicts
+// (the order 2g + s costs 4 conflict cycles per read on gfx950).
+__device__ __forceinline__ uint2 load_codes2(const uint8_t* p) {
+  return make_uint2(*reinterpret_cast<const uint32_t*>(p),
+                    *reinterpret_cast<const uint32_t*>(p + 16));
+}
+
 __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t& tm, int64_t& tn) {
   // M-fastest: neighbouring workgroups share one W column tile (L2 reuse).
   tm = blockIdx.x % tiles_m;
@@ -113,7 +171,10 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                     const float* __restrict__ ahat_t, NF4Tables tab,
                     const uint16_t* __restrict__ xas, const uint16_t* __restrict__ B, int r,
                     int r32, uint16_t* __restrict__ Y) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][kTile * kStep];
+  // two distinct LDS objects: the compiler can then prove that the buffer the
+  // DMA fills is not the one being read, and need not drain the DMA first
+  __shared__ __attribute__((aligned(16))) uint16_t xs0[kTile * kStep];
+  __shared__ __attribute__((aligned(16))) uint16_t xs1[kTile * kStep];
   __shared__ float lvl[16];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int j16 = lane & 15, g = lane >> 4;
@@ -129,7 +190,7 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
   for (int nt = 0; nt < 4; ++nt) {
     const int64_t n = n0 + 64 * wv + 16 * nt + j16;
     nrow[nt] = n < N ? n : N - 1;
-    coff[nt] = (uint32_t)(nrow[nt] * (K / 2)) + (uint32_t)(g * 8);
+    coff[nt] = (uint32_t)(nrow[nt] * (K / 2)) + (uint32_t)(g * 4);
   }
   const uint32_t KT = (uint32_t)(K / kStep);
   const uint32_t N32 = (uint32_t)N;
@@ -138,52 +199,118 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
 #pragma unroll
   for (int mt = 0; mt < 16; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < 4; ++nt) {
+      acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      asm volatile("" : "+a"(acc[mt][nt]));   // materialise in AGPRs, in order
+    }
+  mfma_settle();
 
-  TileLoader<0> ld;
-  ld.init(K, m0, M);
-  uint2 cc[4];
-  float aa[4];
-  ld.load(X, 0, (uint32_t)K);
-  ld.store(xs[0]);
+  // Software pipeline, one sub-step (32 inner indices) ahead: while the
+  // MFMAs of sub-step s read operand set bop[s], the VALU rebuilds the next
+  // sub-step's operands into bop[s ^ 1] (free since the previous sub-step),
+  // one 2-weight slice per group of 4 MFMAs.  A step is 32 such groups
+  // (2 sub-steps x 16 row tiles); each group prefetches the next group's A
+  // operand and level lookups, and a scheduling barrier keeps that order so
+  // only two A operands are ever live.  Codes arrive two steps ahead; the X
+  // tile of step kt+1 streams into the other LDS buffer by DMA.  One barrier
+  // per step.
+  // X tiles stream global -> LDS by DMA one step ahead
+  TileDma dma;
+  dma.init(K, m0, M);
+  dma.issue(X, 0, xs0);
+  uint32_t coff32[4], arow[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) { coff32[nt] = coff[nt]; arow[nt] = (uint32_t)nrow[nt]; }
+  uint2 cc[4], cn[4], cnn[4];
+  float ac[4], an[4], ann[4];
+  const uint32_t k1 = KT > 1 ? 1 : 0;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
-    cc[nt] = *reinterpret_cast<const uint2*>(codes + coff[nt]);
-    aa[nt] = ahat_t[nrow[nt]];
+    cc[nt] = load_codes2(codes + coff32[nt]);            // step 0
+    ac[nt] = ahat_t[arow[nt]];
+    cn[nt] = load_codes2(codes + coff32[nt] + k1 * 32);  // step 1
+    an[nt] = ahat_t[k1 * N32 + arow[nt]];
   }
-  __syncthreads();
+  wait_vmem_all();
+  __syncthreads();   // level table and X tile 0 visible
+  uint32_t bop[2][4][4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int dw = 0; dw < 4; ++dw)
+      bop[0][nt][dw] = pack_bf16x2(lvl[(cc[nt].x >> (8 * dw)) & 15u] * ac[nt],
+                                   lvl[(cc[nt].x >> (8 * dw + 4)) & 15u] * ac[nt]);
 
-  for (uint32_t kt = 0; kt < KT; ++kt) {
-    // prefetch the next step (the last step re-reads itself; harmless)
-    const uint32_t kn = kt + 1 < KT ? kt + 1 : kt;
-    ld.load(X, kn * kStep, (uint32_t)K);
-    uint2 cn[4];
-    float an[4];
+  // slice j (0..31) of a step builds bop[(j >> 4) ^ 1][nt][dw] (nt = (j>>2)&3,
+  // dw = j&3) from code word (j < 16 ? this step's .y : next step's .x);
+  // slices 32.. are the next step's 0.. (word: next step's .y = cn.y).
+  // Group i's A operand and slice i's level lookups are fetched kD groups
+  // ahead into small rings, so LDS latency hides behind 4*kD MFMAs.
+  constexpr int kD = 4;
+  uint4 aq[kD];
+  float lq0[kD], lq1[kD];
+#pragma unroll
+  for (int d = 0; d < kD; ++d) {
+    aq[d] = lds_chunk(xs0, d * 16 + j16, g);
+    const int nt = (d >> 2) & 3, dw = d & 3;
+    lq0[d] = lvl[(cc[nt].y >> (8 * dw)) & 15u];
+    lq1[d] = lvl[(cc[nt].y >> (8 * dw + 4)) & 15u];
+  }
+
+  // one step: MFMAs read X tile kt from `xb`, the DMA fills `xn` with tile kt+1
+  auto step = [&](uint32_t kt, const uint16_t* xb, uint16_t* xn) {
+    const uint32_t kn = kt + 1 < KT ? kt + 1 : kt;        // last step re-reads itself
+    const uint32_t kn2 = kt + 2 < KT ? kt + 2 : KT - 1;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      cn[nt] = *reinterpret_cast<const uint2*>(codes + coff[nt] + kn * 32);
-      an[nt] = ahat_t[kn * N32 + (uint32_t)nrow[nt]];
+      cnn[nt] = load_codes2(codes + coff32[nt] + kn2 * 32);
+      ann[nt] = ahat_t[kn2 * N32 + arow[nt]];
     }
-    // lane's 16 codes cover inner indices 16g .. 16g+15 of this step:
-    // sub-step s takes 16g + 8s .. +7, matching A chunk 2g + s
-    const uint16_t* xb = xs[kt & 1];
+    compiler_fence();
+    dma.issue(X, kn * kStep, xn);
+    compiler_fence();   // keep the loads here, ahead of the MFMAs
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      uint4 bop[4];
+    for (int i = 0; i < 32; ++i) {
+      const int s = i >> 4, mt = i & 15, q = i % kD;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) bop[nt] = dequant8(s ? cc[nt].y : cc[nt].x, aa[nt], lvl);
-#pragma unroll
-      for (int mt = 0; mt < 16; ++mt) {
-        const uint4 a = lds_chunk(xb, mt * 16 + j16, 2 * g + s);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma16x16x32(a, bop[nt], acc[mt][nt]);
+      for (int nt = 0; nt < 4; ++nt)
+        mfma_acc(acc[mt][nt], aq[q],
+                 u32x4v_t{bop[s][nt][0], bop[s][nt][1], bop[s][nt][2], bop[s][nt][3]});
+      // finish slice i (its lookups arrived kD groups ago)
+      {
+        const int nt = (i >> 2) & 3, dw = i & 3;
+        const float sc = s ? an[nt] : ac[nt];
+        bop[s ^ 1][nt][dw] = pack_bf16x2(lq0[q] * sc, lq1[q] * sc);
       }
+      // fetch group i+kD's A operand (this step only) and slice i+kD's lookups
+      const int ia = i + kD;
+      if (ia < 32) aq[q] = lds_chunk(xb, (ia & 15) * 16 + j16, 4 * (ia >> 4) + g);
+      {
+        const int j = ia & 31, nt = (j >> 2) & 3, dw = j & 3;
+        const uint32_t c = (ia >= 32) ? cn[nt].y : (j < 16 ? cc[nt].y : cn[nt].x);
+        lq0[q] = lvl[(c >> (8 * dw)) & 15u];
+        lq1[q] = lvl[(c >> (8 * dw + 4)) & 15u];
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    ld.store(xs[(kt + 1) & 1]);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) { cc[nt] = cn[nt]; aa[nt] = an[nt]; }
+    for (int nt = 0; nt < 4; ++nt) {
+      cc[nt] = cn[nt]; ac[nt] = an[nt];
+      cn[nt] = cnn[nt]; an[nt] = ann[nt];
+    }
+    wait_vmem_all();   // the DMA of tile kt+1 has landed
     __syncthreads();
+#pragma unroll
+    for (int d = 0; d < kD; ++d) aq[d] = lds_chunk(xn, d * 16 + j16, g);
+  };
+  uint32_t kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    step(kt, xs0, xs1);
+    step(kt + 1, xs1, xs0);
   }
+  if (kt < KT) step(kt, xs0, xs1);
+  mfma_settle();
 
   // LoRA up-projection as r32 extra inner columns: A operand s.XA (bf16,
   // [M, r32], zero padded), B operand rows of B [N, r]
@@ -215,7 +342,8 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
     }
   }
 
-  // epilogue: C[row 4g + v][col j16] of each 16x16 tile
+  // epilogue: C[row 4g + v][col j16] of each 16x16 tile, one row tile at a
+  // time so only 16 accumulators are in flight
 #pragma unroll
   for (int mt = 0; mt < 16; ++mt) {
 #pragma unroll
@@ -227,6 +355,7 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
         if (m < M && n < N) Y[m * N + n] = (uint16_t)(pack_bf16x2(acc[mt][nt][v], 0.f) & 0xFFFF);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 

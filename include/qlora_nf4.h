@@ -157,6 +157,29 @@ qlora_status qlora_linear_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
                               const qlora_bf16* dY, const qlora_bf16* XA_in, qlora_bf16* dX,
                               float* dA, float* dB, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Kernel timing (benchmark instrumentation; not part of the method).
+ * Between qlora_trace_begin and qlora_trace_end, every launch of a kernel whose
+ * bit is set in `kernel_mask` (1 << qlora_kernel) is bracketed by a pair of HIP
+ * events recorded on the launch's stream, for at most `capacity` launches per
+ * kernel.  qlora_trace_end waits for those events (host synchronisation on
+ * them only), writes the number of timed launches and their summed duration in
+ * milliseconds into launches[QLORA_KERNEL_COUNT] / total_ms[QLORA_KERNEL_COUNT],
+ * and releases the events.  Process-global state: not for concurrent use from
+ * several host threads.  Returns QLORA_ERR_INVALID_ARG for a bad mask or
+ * capacity, QLORA_ERR_HIP if an event call fails. */
+typedef enum {
+  QLORA_KERNEL_FWD_GEMM = 0,   /* dequant-fused forward GEMM (M > 16) */
+  QLORA_KERNEL_DX_GEMM = 1,    /* dequant-fused dX GEMM */
+  QLORA_KERNEL_QUANTIZE = 2,   /* first-level absmax + NF4 codes */
+  QLORA_KERNEL_DEQUANT = 3,    /* dequantise to float32 / bf16 */
+  QLORA_KERNEL_GEMV = 4,       /* decode forward (M <= 16), main kernel */
+  QLORA_KERNEL_COUNT = 5
+} qlora_kernel;
+
+qlora_status qlora_trace_begin(uint32_t kernel_mask, int32_t capacity);
+qlora_status qlora_trace_end(int32_t* launches, double* total_ms);
+
 #ifdef __cplusplus
 }
 #endif
