@@ -506,6 +506,198 @@ void k_qlora_dx_nn(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
   }
 }
 
+// Fast dX path for N % 64 == 0 (every step full): the dY tile streams into
+// LDS by DMA, the W' operands of the next sub-step are rebuilt between the
+// MFMA groups of the current one (as in the forward kernel), accumulators are
+// pinned in AGPRs.
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(1, 1)))
+void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
+                       const uint8_t* __restrict__ codes, int64_t K,
+                       const float* __restrict__ ahat_t, NF4Tables tab,
+                       const uint16_t* __restrict__ gs, const uint16_t* __restrict__ A, int r,
+                       int r32, uint16_t* __restrict__ dX) {
+  __shared__ __attribute__((aligned(16))) uint16_t ys0[kTile * kStep];
+  __shared__ __attribute__((aligned(16))) uint16_t ys1[kTile * kStep];
+  __shared__ float lvl[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int j16 = lane & 15, g = lane >> 4;
+  int64_t tm, tn;
+  tile_coords(ceil_div(M, kTile), tm, tn);
+  const int64_t m0 = tm * kTile, k0 = tn * kTile;
+  if (tid < 16) lvl[tid] = tab.level[tid];
+
+  const int64_t kc = k0 + 64 * wv + 4 * j16;      // first of this lane's 4 columns
+  const bool kvalid = kc < K;                       // K % 64 == 0: all 4 or none
+  const int64_t kcl = kvalid ? kc : K - 4;
+  const uint32_t ldc = (uint32_t)(K / 2);
+  const uint32_t NT = (uint32_t)(N / kStep);
+  const uint32_t ccol = (uint32_t)(kcl / 2);
+  const uint32_t abase = (uint32_t)(kcl / kBlock) * (uint32_t)N + 8 * g;
+
+  f32x4_t acc[16][4];
+#pragma unroll
+  for (int mt = 0; mt < 16; ++mt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      acc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      asm volatile("" : "+a"(acc[mt][t]));
+    }
+  mfma_settle();
+
+  // W rows of step n0: n0 + 32s + 8g + e (s = 0, 1; e = 0..7): 16 codes words
+  // (4 codes each, columns kc..kc+3) and their 16 block constants
+  struct WStep { uint32_t c[16]; float a[16]; };
+  auto load_w = [&](uint32_t n0, WStep& w) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        w.c[s2 * 8 + e] =
+            *reinterpret_cast<const uint16_t*>(codes + (n0 + 32 * s2 + 8 * g + e) * ldc + ccol);
+      const float4 lo = *reinterpret_cast<const float4*>(ahat_t + abase + n0 + 32 * s2);
+      const float4 hi = *reinterpret_cast<const float4*>(ahat_t + abase + n0 + 32 * s2 + 4);
+      w.a[s2 * 8 + 0] = lo.x; w.a[s2 * 8 + 1] = lo.y; w.a[s2 * 8 + 2] = lo.z; w.a[s2 * 8 + 3] = lo.w;
+      w.a[s2 * 8 + 4] = hi.x; w.a[s2 * 8 + 5] = hi.y; w.a[s2 * 8 + 6] = hi.z; w.a[s2 * 8 + 7] = hi.w;
+    }
+  };
+
+  TileDma dma;
+  dma.init(N, m0, M);
+  dma.issue(dY, 0, ys0);
+  WStep wc, wn, wnn;
+  load_w(0, wc);
+  load_w(NT > 1 ? kStep : 0, wn);
+  wait_vmem_all();
+  __syncthreads();   // level table and dY tile 0 visible
+
+  // operand set of sub-step s: bop[s][t][q] = bf16 pair of W' rows (2q, 2q+1)
+  // at column kc + t
+  uint32_t bop[2][4][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      bop[0][t][q] = pack_bf16x2(lvl[(wc.c[2 * q] >> (4 * t)) & 15u] * wc.a[2 * q],
+                                 lvl[(wc.c[2 * q + 1] >> (4 * t)) & 15u] * wc.a[2 * q + 1]);
+
+  // slice j (0..31): target bop[(j >> 4) ^ 1][t = (j >> 2) & 3][q = j & 3];
+  // rows: j < 16 -> this step's sub-step 1 (wc, words 8 + 2q, 9 + 2q);
+  // j >= 16 -> next step's sub-step 0 (wn, words 2q, 2q + 1); slices 32..
+  // are the next step's 0.. (wn, words 8 + 2q ..).
+  constexpr int kD = 4;
+  uint4 aq[kD];
+  float lq0[kD], lq1[kD];
+#pragma unroll
+  for (int d = 0; d < kD; ++d) {
+    aq[d] = lds_chunk(ys0, d * 16 + j16, g);
+    const int t = (d >> 2) & 3, q = d & 3;
+    lq0[d] = lvl[(wc.c[8 + 2 * q] >> (4 * t)) & 15u];
+    lq1[d] = lvl[(wc.c[9 + 2 * q] >> (4 * t)) & 15u];
+  }
+
+  auto step = [&](uint32_t it, const uint16_t* yb, uint16_t* yn) {
+    const uint32_t nn = it + 1 < NT ? it + 1 : it;       // last step re-reads itself
+    const uint32_t nn2 = it + 2 < NT ? it + 2 : NT - 1;
+    load_w(nn2 * kStep, wnn);
+    compiler_fence();
+    dma.issue(dY, nn * kStep, yn);
+    compiler_fence();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int s = i >> 4, mt = i & 15, qd = i % kD;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        mfma_acc(acc[mt][t], aq[qd],
+                 u32x4v_t{bop[s][t][0], bop[s][t][1], bop[s][t][2], bop[s][t][3]});
+      {
+        const int t = (i >> 2) & 3, q = i & 3;
+        const float a0 = s ? wn.a[2 * q] : wc.a[8 + 2 * q];
+        const float a1 = s ? wn.a[2 * q + 1] : wc.a[9 + 2 * q];
+        bop[s ^ 1][t][q] = pack_bf16x2(lq0[qd] * a0, lq1[qd] * a1);
+      }
+      const int ia = i + kD;
+      if (ia < 32) aq[qd] = lds_chunk(yb, (ia & 15) * 16 + j16, 4 * (ia >> 4) + g);
+      {
+        const int j = ia & 31, t = (j >> 2) & 3, q = j & 3;
+        uint32_t w0, w1;
+        if (ia >= 32) { w0 = wn.c[8 + 2 * q]; w1 = wn.c[9 + 2 * q]; }
+        else if (j < 16) { w0 = wc.c[8 + 2 * q]; w1 = wc.c[9 + 2 * q]; }
+        else { w0 = wn.c[2 * q]; w1 = wn.c[2 * q + 1]; }
+        lq0[qd] = lvl[(w0 >> (4 * t)) & 15u];
+        lq1[qd] = lvl[(w1 >> (4 * t)) & 15u];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wc = wn;
+    wn = wnn;
+    wait_vmem_all();   // the DMA of the next dY tile has landed
+    __syncthreads();
+#pragma unroll
+    for (int d = 0; d < kD; ++d) aq[d] = lds_chunk(yn, d * 16 + j16, g);
+  };
+  uint32_t it = 0;
+  for (; it + 1 < NT; it += 2) {
+    step(it, ys0, ys1);
+    step(it + 1, ys1, ys0);
+  }
+  if (it < NT) step(it, ys0, ys1);
+  mfma_settle();
+
+  // LoRA: + (s.G) . A as r32 extra inner indices
+  for (int ts = 0; ts < r32 / 32; ++ts) {
+    const int j0 = ts * 32 + g * 8;
+    uint2 rows[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = j0 + e;
+      rows[e] = (j < r) ? *reinterpret_cast<const uint2*>(A + (int64_t)j * K + kcl)
+                        : make_uint2(0u, 0u);
+    }
+    uint4 bb[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = (t < 2) ? rows[e].x : rows[e].y;
+        h[e] = (t & 1) ? (w >> 16) : (w & 0xFFFFu);
+      }
+      bb[t].x = h[0] | (h[1] << 16);
+      bb[t].y = h[2] | (h[3] << 16);
+      bb[t].z = h[4] | (h[5] << 16);
+      bb[t].w = h[6] | (h[7] << 16);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt) {
+      int64_t m = m0 + mt * 16 + j16;
+      m = m < M ? m : M - 1;
+      const uint4 a = *reinterpret_cast<const uint4*>(gs + m * r32 + j0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[mt][t] = mfma16x16x32(a, bb[t], acc[mt][t]);
+    }
+  }
+
+  // epilogue: lane holds columns kc..kc+3 of rows 4g + v -> one 8-byte store
+  if (kvalid) {
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t m = m0 + mt * 16 + 4 * g + v;
+        if (m < M) {
+          uint2 o;
+          o.x = pack_bf16x2(acc[mt][0][v], acc[mt][1][v]);
+          o.y = pack_bf16x2(acc[mt][2][v], acc[mt][3][v]);
+          *reinterpret_cast<uint2*>(dX + m * K + kc) = o;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes,
@@ -522,7 +714,7 @@ hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t N, const uint8_
                           int r, int r32, uint16_t* dX, hipStream_t s) {
   const int64_t grid = ceil_div(M, kTile) * ceil_div(K, kTile);
   if (N % kStep == 0)
-    hipLaunchKernelGGL(k_qlora_dx_nn<0>, dim3((unsigned)grid), dim3(kThreads), 0, s, dY, M, N,
+    hipLaunchKernelGGL(k_qlora_dx_nn_dma, dim3((unsigned)grid), dim3(kThreads), 0, s, dY, M, N,
                        codes, K, ahat_t, host_tables(), gs, A, r, r32, dX);
   else if (N % 8 == 0)
     hipLaunchKernelGGL(k_qlora_dx_nn<1>, dim3((unsigned)grid), dim3(kThreads), 0, s, dY, M, N,
