@@ -3,6 +3,7 @@
 // is allocated here; everything is enqueued on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 
@@ -54,7 +55,8 @@ struct LinearWs {
   int r32;
   int64_t mp, np;             // token count padded to 32, N padded to 128
   int gemv_splits, sa, sb;    // split counts
-  size_t ahat_t, xas, gemv_part, bt, gs, gt, xat, part_a, part_b, total;
+  int sf, sx;                 // split-K slices of the forward / dX GEMM
+  size_t ahat_t, xas, gemv_part, bt, gs, gt, xat, part_a, part_b, gemm_part, total;
 };
 
 LinearWs linear_layout(int64_t M, int64_t N, int64_t K, int r) {
@@ -65,6 +67,8 @@ LinearWs linear_layout(int64_t M, int64_t N, int64_t K, int r) {
   w.gemv_splits = M <= 16 ? qnf4::gemv_splits(N, K) : 0;
   w.sa = lora_grad_splits(M, K);
   w.sb = lora_grad_splits(M, N);
+  w.sf = M > 16 ? fwd_splits(M, N, K) : 1;
+  w.sx = dx_splits(M, N, K);
   size_t off = 0;
   w.ahat_t = off;    off = align_up(off + (size_t)(K / kBlock) * N * sizeof(float));
   w.xas = off;       off = align_up(off + (size_t)M * w.r32 * 2);
@@ -75,6 +79,9 @@ LinearWs linear_layout(int64_t M, int64_t N, int64_t K, int r) {
   w.xat = off;       off = align_up(off + (size_t)r * w.mp * 2);
   w.part_a = off;    off = align_up(off + (size_t)w.sa * r * K * sizeof(float));
   w.part_b = off;    off = align_up(off + (size_t)w.sb * N * r * sizeof(float));
+  const size_t gp = std::max((size_t)(w.sf > 1 ? w.sf : 0) * M * N,
+                             (size_t)(w.sx > 1 ? w.sx : 0) * M * K);
+  w.gemm_part = off; off = align_up(off + gp * sizeof(float));
   w.total = off;
   return w;
 }
@@ -219,7 +226,8 @@ qlora_status qlora_linear_fwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
     e = launch_gemv_finish(part, L.gemv_splits, M, N, xas, r, L.r32, B, Y, s);
   } else {
     e = traced(QLORA_KERNEL_FWD_GEMM, s, [&] {
-      return launch_fwd_gemm(X, M, K, W->codes, N, ahat_t, xas, B, r, L.r32, Y, s);
+      return launch_fwd_gemm(X, M, K, W->codes, N, ahat_t, xas, B, r, L.r32, Y,
+                             at<float>(ws, L.gemm_part), s);
     });
   }
   return hip_status(e);
@@ -254,7 +262,8 @@ qlora_status qlora_linear_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
   if (dX) {
     QL_TRY(launch_absmax_recon_t(W->absmax_q, W->absmax_scale, W->absmax_mean, N, K, ahat_t, s));
     QL_TRY(traced(QLORA_KERNEL_DX_GEMM, s, [&] {
-      return launch_dx_gemm(dY, M, N, W->codes, K, ahat_t, gs, A, r, L.r32, dX, s);
+      return launch_dx_gemm(dY, M, N, W->codes, K, ahat_t, gs, A, r, L.r32, dX,
+                            at<float>(ws, L.gemm_part), s);
     }));
   }
   // dA = s . G^T X  (reduce over tokens into [r, K]);  dB = s . dY^T XA  ([N, r])

@@ -157,6 +157,17 @@ __device__ __forceinline__ uint2 load_codes2(const uint8_t* p) {
                     *reinterpret_cast<const uint32_t*>(p + 16));
 }
 
+// Workgroup -> (split, tile): the split slices of one tile are adjacent
+// workgroups; tiles are M-fastest as in tile_coords.
+__device__ __forceinline__ void tile_coords_split(int64_t tiles_m, int splits, int64_t& tm,
+                                                  int64_t& tn, int& split) {
+  const int64_t b = blockIdx.x;
+  split = (int)(b % splits);
+  const int64_t t = b / splits;
+  tm = t % tiles_m;
+  tn = t / tiles_m;
+}
+
 __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t& tm, int64_t& tn) {
   // M-fastest: neighbouring workgroups share one W column tile (L2 reuse).
   tm = blockIdx.x % tiles_m;
@@ -170,7 +181,8 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                     const uint8_t* __restrict__ codes, int64_t N,
                     const float* __restrict__ ahat_t, NF4Tables tab,
                     const uint16_t* __restrict__ xas, const uint16_t* __restrict__ B, int r,
-                    int r32, uint16_t* __restrict__ Y) {
+                    int r32, uint16_t* __restrict__ Y, int splits, int ksteps,
+                    float* __restrict__ part) {
   // two distinct LDS objects: the compiler can then prove that the buffer the
   // DMA fills is not the one being read, and need not drain the DMA first
   __shared__ __attribute__((aligned(16))) uint16_t xs0[kTile * kStep];
@@ -179,7 +191,8 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int j16 = lane & 15, g = lane >> 4;
   int64_t tm, tn;
-  tile_coords(ceil_div(M, kTile), tm, tn);
+  int split;
+  tile_coords_split(ceil_div(M, kTile), splits, tm, tn, split);
   const int64_t m0 = tm * kTile, n0 = tn * kTile;
   if (tid < 16) lvl[tid] = tab.level[tid];
 
@@ -192,7 +205,10 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
     nrow[nt] = n < N ? n : N - 1;
     coff[nt] = (uint32_t)(nrow[nt] * (K / 2)) + (uint32_t)(g * 4);
   }
-  const uint32_t KT = (uint32_t)(K / kStep);
+  // this workgroup's steps [kt0, kt1) of the K loop (split-K slice)
+  const uint32_t KTall = (uint32_t)(K / kStep);
+  const uint32_t kt0 = (uint32_t)split * (uint32_t)ksteps;
+  const uint32_t kt1 = kt0 + (uint32_t)ksteps < KTall ? kt0 + (uint32_t)ksteps : KTall;
   const uint32_t N32 = (uint32_t)N;
 
   f32x4_t acc[16][4];
@@ -217,18 +233,18 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
   // X tiles stream global -> LDS by DMA one step ahead
   TileDma dma;
   dma.init(K, m0, M);
-  dma.issue(X, 0, xs0);
+  dma.issue(X, kt0 * kStep, xs0);
   uint32_t coff32[4], arow[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) { coff32[nt] = coff[nt]; arow[nt] = (uint32_t)nrow[nt]; }
   uint2 cc[4], cn[4], cnn[4];
   float ac[4], an[4], ann[4];
-  const uint32_t k1 = KT > 1 ? 1 : 0;
+  const uint32_t k1 = kt0 + 1 < kt1 ? kt0 + 1 : kt0;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
-    cc[nt] = load_codes2(codes + coff32[nt]);            // step 0
-    ac[nt] = ahat_t[arow[nt]];
-    cn[nt] = load_codes2(codes + coff32[nt] + k1 * 32);  // step 1
+    cc[nt] = load_codes2(codes + coff32[nt] + kt0 * 32);   // first step
+    ac[nt] = ahat_t[kt0 * N32 + arow[nt]];
+    cn[nt] = load_codes2(codes + coff32[nt] + k1 * 32);    // second step
     an[nt] = ahat_t[k1 * N32 + arow[nt]];
   }
   wait_vmem_all();
@@ -259,8 +275,12 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
 
   // one step: MFMAs read X tile kt from `xb`, the DMA fills `xn` with tile kt+1
   auto step = [&](uint32_t kt, const uint16_t* xb, uint16_t* xn) {
-    const uint32_t kn = kt + 1 < KT ? kt + 1 : kt;        // last step re-reads itself
-    const uint32_t kn2 = kt + 2 < KT ? kt + 2 : KT - 1;
+    // Free in steady state (the previous step ended drained), but it tells
+    // the wait-count pass that the loop-carried code words have landed, so
+    // it does not drain the in-flight DMA in the middle of the step.
+    wait_vmem_all();
+    const uint32_t kn = kt + 1 < kt1 ? kt + 1 : kt;        // last step re-reads itself
+    const uint32_t kn2 = kt + 2 < kt1 ? kt + 2 : kt1 - 1;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       cnn[nt] = load_codes2(codes + coff32[nt] + kn2 * 32);
@@ -304,18 +324,19 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
 #pragma unroll
     for (int d = 0; d < kD; ++d) aq[d] = lds_chunk(xn, d * 16 + j16, g);
   };
-  uint32_t kt = 0;
-  for (; kt + 1 < KT; kt += 2) {
+  uint32_t kt = kt0;
+  for (; kt + 1 < kt1; kt += 2) {
     step(kt, xs0, xs1);
     step(kt + 1, xs1, xs0);
   }
-  if (kt < KT) step(kt, xs0, xs1);
+  if (kt < kt1) step(kt, xs0, xs1);
   mfma_settle();
 
   // LoRA up-projection as r32 extra inner columns: A operand s.XA (bf16,
-  // [M, r32], zero padded), B operand rows of B [N, r]
+  // [M, r32], zero padded), B operand rows of B [N, r]; last K slice only
   const bool bvec = (r % 8) == 0;
-  for (int ts = 0; ts < r32 / 32; ++ts) {
+  const int tail = split == splits - 1 ? r32 / 32 : 0;
+  for (int ts = 0; ts < tail; ++ts) {
     const int j0 = ts * 32 + g * 8;
     uint4 bb[4];
 #pragma unroll
@@ -343,7 +364,9 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
   }
 
   // epilogue: C[row 4g + v][col j16] of each 16x16 tile, one row tile at a
-  // time so only 16 accumulators are in flight
+  // time so only 16 accumulators are in flight.  Split-K slices write float32
+  // partials [split][M][N] that a second kernel adds in split order.
+  float* pbase = part + (int64_t)split * M * N;
 #pragma unroll
   for (int mt = 0; mt < 16; ++mt) {
 #pragma unroll
@@ -352,7 +375,10 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int64_t m = m0 + mt * 16 + 4 * g + v;
-        if (m < M && n < N) Y[m * N + n] = (uint16_t)(pack_bf16x2(acc[mt][nt][v], 0.f) & 0xFFFF);
+        if (m < M && n < N) {
+          if (splits == 1) Y[m * N + n] = (uint16_t)(pack_bf16x2(acc[mt][nt][v], 0.f) & 0xFFFF);
+          else pbase[m * N + n] = acc[mt][nt][v];
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -516,14 +542,16 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
                        const uint8_t* __restrict__ codes, int64_t K,
                        const float* __restrict__ ahat_t, NF4Tables tab,
                        const uint16_t* __restrict__ gs, const uint16_t* __restrict__ A, int r,
-                       int r32, uint16_t* __restrict__ dX) {
+                       int r32, uint16_t* __restrict__ dX, int splits, int nsteps,
+                       float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint16_t ys0[kTile * kStep];
   __shared__ __attribute__((aligned(16))) uint16_t ys1[kTile * kStep];
   __shared__ float lvl[16];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int j16 = lane & 15, g = lane >> 4;
   int64_t tm, tn;
-  tile_coords(ceil_div(M, kTile), tm, tn);
+  int split;
+  tile_coords_split(ceil_div(M, kTile), splits, tm, tn, split);
   const int64_t m0 = tm * kTile, k0 = tn * kTile;
   if (tid < 16) lvl[tid] = tab.level[tid];
 
@@ -531,7 +559,10 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
   const bool kvalid = kc < K;                       // K % 64 == 0: all 4 or none
   const int64_t kcl = kvalid ? kc : K - 4;
   const uint32_t ldc = (uint32_t)(K / 2);
-  const uint32_t NT = (uint32_t)(N / kStep);
+  // this workgroup's inner steps [it0, it1) (split over N)
+  const uint32_t NTall = (uint32_t)(N / kStep);
+  const uint32_t it0 = (uint32_t)split * (uint32_t)nsteps;
+  const uint32_t it1 = it0 + (uint32_t)nsteps < NTall ? it0 + (uint32_t)nsteps : NTall;
   const uint32_t ccol = (uint32_t)(kcl / 2);
   const uint32_t abase = (uint32_t)(kcl / kBlock) * (uint32_t)N + 8 * g;
 
@@ -564,10 +595,10 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
 
   TileDma dma;
   dma.init(N, m0, M);
-  dma.issue(dY, 0, ys0);
+  dma.issue(dY, it0 * kStep, ys0);
   WStep wc, wn, wnn;
-  load_w(0, wc);
-  load_w(NT > 1 ? kStep : 0, wn);
+  load_w(it0 * kStep, wc);
+  load_w((it0 + 1 < it1 ? it0 + 1 : it0) * kStep, wn);
   wait_vmem_all();
   __syncthreads();   // level table and dY tile 0 visible
 
@@ -597,8 +628,9 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
   }
 
   auto step = [&](uint32_t it, const uint16_t* yb, uint16_t* yn) {
-    const uint32_t nn = it + 1 < NT ? it + 1 : it;       // last step re-reads itself
-    const uint32_t nn2 = it + 2 < NT ? it + 2 : NT - 1;
+    wait_vmem_all();   // see the forward kernel: keeps the wait pass from draining the DMA
+    const uint32_t nn = it + 1 < it1 ? it + 1 : it;       // last step re-reads itself
+    const uint32_t nn2 = it + 2 < it1 ? it + 2 : it1 - 1;
     load_w(nn2 * kStep, wnn);
     compiler_fence();
     dma.issue(dY, nn * kStep, yn);
@@ -637,16 +669,17 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
 #pragma unroll
     for (int d = 0; d < kD; ++d) aq[d] = lds_chunk(yn, d * 16 + j16, g);
   };
-  uint32_t it = 0;
-  for (; it + 1 < NT; it += 2) {
+  uint32_t it = it0;
+  for (; it + 1 < it1; it += 2) {
     step(it, ys0, ys1);
     step(it + 1, ys1, ys0);
   }
-  if (it < NT) step(it, ys0, ys1);
+  if (it < it1) step(it, ys0, ys1);
   mfma_settle();
 
-  // LoRA: + (s.G) . A as r32 extra inner indices
-  for (int ts = 0; ts < r32 / 32; ++ts) {
+  // LoRA: + (s.G) . A as r32 extra inner indices (last slice only)
+  const int tail = split == splits - 1 ? r32 / 32 : 0;
+  for (int ts = 0; ts < tail; ++ts) {
     const int j0 = ts * 32 + g * 8;
     uint2 rows[8];
 #pragma unroll
@@ -679,7 +712,9 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
     }
   }
 
-  // epilogue: lane holds columns kc..kc+3 of rows 4g + v -> one 8-byte store
+  // epilogue: lane holds columns kc..kc+3 of rows 4g + v -> one 8-byte
+  // store (bf16), or float32 partials [split][M][K] when split
+  float* pbase = part + (int64_t)split * M * K;
   if (kvalid) {
 #pragma unroll
     for (int mt = 0; mt < 16; ++mt) {
@@ -687,10 +722,15 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
       for (int v = 0; v < 4; ++v) {
         const int64_t m = m0 + mt * 16 + 4 * g + v;
         if (m < M) {
-          uint2 o;
-          o.x = pack_bf16x2(acc[mt][0][v], acc[mt][1][v]);
-          o.y = pack_bf16x2(acc[mt][2][v], acc[mt][3][v]);
-          *reinterpret_cast<uint2*>(dX + m * K + kc) = o;
+          if (splits == 1) {
+            uint2 o;
+            o.x = pack_bf16x2(acc[mt][0][v], acc[mt][1][v]);
+            o.y = pack_bf16x2(acc[mt][2][v], acc[mt][3][v]);
+            *reinterpret_cast<uint2*>(dX + m * K + kc) = o;
+          } else {
+            *reinterpret_cast<float4*>(pbase + m * K + kc) =
+                make_float4(acc[mt][0][v], acc[mt][1][v], acc[mt][2][v], acc[mt][3][v]);
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -698,29 +738,87 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
   }
 }
 
+// out[i] = bf16(sum over s of part[s][i]), s in order; 4 elements per thread
+__global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ part, int splits,
+                                                      int64_t count,
+                                                      uint16_t* __restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= count) return;
+  if (i + 4 <= count) {
+    float4 acc = *reinterpret_cast<const float4*>(part + i);
+    for (int s = 1; s < splits; ++s) {
+      const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)s * count + i);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    uint2 o;
+    o.x = pack_bf16x2(acc.x, acc.y);
+    o.y = pack_bf16x2(acc.z, acc.w);
+    *reinterpret_cast<uint2*>(out + i) = o;
+  } else {
+    for (int64_t j = i; j < count; ++j) {
+      float a = part[j];
+      for (int s = 1; s < splits; ++s) a += part[(int64_t)s * count + j];
+      out[j] = (uint16_t)(pack_bf16x2(a, 0.f) & 0xFFFF);
+    }
+  }
+}
+
 }  // namespace
+
+int fwd_splits(int64_t M, int64_t N, int64_t K) {
+  // Split K only when the output tiles cannot fill the chip; keep >= 8 steps
+  // per slice.
+  const int64_t tiles = ceil_div(M, kTile) * ceil_div(N, kTile);
+  const int64_t steps = K / kStep;
+  int64_t s = 1;
+  while (s < 8 && tiles * s * 2 <= 256 && steps / (s * 2) >= 8) s *= 2;
+  return (int)s;
+}
+
+int dx_splits(int64_t M, int64_t N, int64_t K) {
+  if (N % kStep != 0) return 1;   // ragged inner dim: single-slice kernel
+  return fwd_splits(M, K, N);
+}
 
 hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes,
                            int64_t N, const float* ahat_t, const uint16_t* xas, const uint16_t* B,
-                           int r, int r32, uint16_t* Y, hipStream_t s) {
-  const int64_t grid = ceil_div(M, kTile) * ceil_div(N, kTile);
+                           int r, int r32, uint16_t* Y, float* part, hipStream_t s) {
+  const int64_t steps = K / kStep;
+  const int ksteps = (int)ceil_div(steps, part ? fwd_splits(M, N, K) : 1);
+  const int splits = (int)ceil_div(steps, ksteps);   // every slice non-empty
+  const int64_t grid = ceil_div(M, kTile) * ceil_div(N, kTile) * splits;
   hipLaunchKernelGGL(k_qlora_fwd_nt, dim3((unsigned)grid), dim3(kThreads), 0, s, X, M, K, codes,
-                     N, ahat_t, host_tables(), xas, B, r, r32, Y);
+                     N, ahat_t, host_tables(), xas, B, r, r32, Y, splits, ksteps, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const int64_t count = M * N;
+  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)ceil_div(ceil_div(count, 4), 256)), dim3(256),
+                     0, s, part, splits, count, Y);
   return hipGetLastError();
 }
 
 hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes,
                           int64_t K, const float* ahat_t, const uint16_t* gs, const uint16_t* A,
-                          int r, int r32, uint16_t* dX, hipStream_t s) {
-  const int64_t grid = ceil_div(M, kTile) * ceil_div(K, kTile);
-  if (N % kStep == 0)
-    hipLaunchKernelGGL(k_qlora_dx_nn_dma, dim3((unsigned)grid), dim3(kThreads), 0, s, dY, M, N,
-                       codes, K, ahat_t, host_tables(), gs, A, r, r32, dX);
-  else if (N % 8 == 0)
-    hipLaunchKernelGGL(k_qlora_dx_nn<1>, dim3((unsigned)grid), dim3(kThreads), 0, s, dY, M, N,
+                          int r, int r32, uint16_t* dX, float* part, hipStream_t s) {
+  const int64_t grid1 = ceil_div(M, kTile) * ceil_div(K, kTile);
+  if (N % kStep == 0) {
+    const int nsteps = (int)ceil_div(N / kStep, part ? dx_splits(M, N, K) : 1);
+    const int splits = (int)ceil_div(N / kStep, nsteps);   // every slice non-empty
+    hipLaunchKernelGGL(k_qlora_dx_nn_dma, dim3((unsigned)(grid1 * splits)), dim3(kThreads), 0, s,
+                       dY, M, N, codes, K, ahat_t, host_tables(), gs, A, r, r32, dX, splits,
+                       nsteps, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    const int64_t count = M * K;
+    hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)ceil_div(ceil_div(count, 4), 256)),
+                       dim3(256), 0, s, part, splits, count, dX);
+    return hipGetLastError();
+  }
+  if (N % 8 == 0)
+    hipLaunchKernelGGL(k_qlora_dx_nn<1>, dim3((unsigned)grid1), dim3(kThreads), 0, s, dY, M, N,
                        codes, K, ahat_t, host_tables(), gs, A, r, r32, dX);
   else
-    hipLaunchKernelGGL(k_qlora_dx_nn<2>, dim3((unsigned)grid), dim3(kThreads), 0, s, dY, M, N,
+    hipLaunchKernelGGL(k_qlora_dx_nn<2>, dim3((unsigned)grid1), dim3(kThreads), 0, s, dY, M, N,
                        codes, K, ahat_t, host_tables(), gs, A, r, r32, dX);
   return hipGetLastError();
 }

@@ -73,6 +73,9 @@ RAGGED = [  # M, N, K, r
     (17, 64, 64, 1), (33, 100, 128, 8), (300, 192, 192, 16), (257, 300, 320, 64),
     (513, 520, 256, 5), (64, 1000, 640, 100), (40, 72, 128, 128), (2, 130, 192, 8),
     (16, 4096, 512, 64), (1, 77, 64, 3), (5, 640, 1024, 16), (600, 264, 64, 33),
+    # few output tiles: the inner loop is split across workgroups, with uneven
+    # slices (17 = 9 + 8, 65 = 7 x 9 + 2, 19 = 10 + 9 steps of 64)
+    (300, 1216, 1088, 24), (70, 512, 4160, 16), (40, 4096, 256, 8),
 ]
 
 
