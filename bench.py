@@ -39,7 +39,24 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--legs", choices=["all", "none"], default="all")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run 3 plain device-to-device copies of MIB MiB (the known-size "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def calibrate_copy(torch, mib):
+    """Three device-to-device copies of `mib` MiB: reads and writes exactly
+    mib MiB each, so a counter pass over it gives the counter's bytes per KiB."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copy calibration: 3 x %d MiB device-to-device" % mib)
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 def src_hash(*names):
@@ -50,9 +67,10 @@ def src_hash(*names):
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel, launches_flops):
-    """HBM bytes per launch of `kernel` from the committed counter summary,
-    if it was taken on the current kernel source; else None."""
+def traffic_for(kernel):
+    """HBM bytes per launch of `kernel` (FETCH_SIZE + WRITE_SIZE, each scaled by
+    a plain copy's reading) from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -104,7 +122,8 @@ def headline(args, q, torch, workloads):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    q.qlora_trace_begin(["fwd_gemm", "dx_gemm"], capacity=len(layers) * args.steps + 8)
+    q.qlora_trace_begin(["fwd_gemm", "dx_gemm", "split_reduce"],
+                        capacity=2 * len(layers) * args.steps + 8)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -119,6 +138,8 @@ def headline(args, q, torch, workloads):
               "dx_gemm": sum(2 * M * L["K"] * (L["N"] + r) for L in layers)}
     kern = {}
     for name, (n, ms) in tr.items():
+        if name not in kflops:
+            continue
         avg_ms = ms / n
         per_launch = kflops[name] / len(layers)
         kern[name] = {"launches": n, "avg_us": avg_ms * 1e3,
@@ -126,14 +147,20 @@ def headline(args, q, torch, workloads):
                       "flops_per_launch": per_launch}
     dom = max(kern, key=lambda k: kern[k]["avg_us"] * kern[k]["launches"])
     d = kern[dom]
-    roof = {"kernel": {"fwd_gemm": "k_qlora_fwd_nt", "dx_gemm": "k_qlora_dx_nn"}[dom],
+    # the dX GEMM with N % 64 == 0 (all seven Llama linears) runs k_qlora_dx_nn_dma
+    roof = {"kernel": {"fwd_gemm": "k_qlora_fwd_nt", "dx_gemm": "k_qlora_dx_nn_dma"}[dom],
             "bound": "mfma", "achieved": round(d["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(d["tflops"] / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic_for(dom, None),
+            "traffic": None,
             "avg_launch_us": round(d["avg_us"], 2),
             "flops_per_launch": d["flops_per_launch"]}
+    roof["traffic"] = traffic_for(roof["kernel"])
     other = {k: {"avg_launch_us": round(v["avg_us"], 2), "tflops": round(v["tflops"], 2),
                  "frac": round(v["tflops"] / PEAK_BF16_TFLOPS, 4)} for k, v in kern.items()}
+    for k, (n, ms) in tr.items():   # per-step time of every timed kernel
+        if n:
+            other.setdefault(k, {})["us_per_step"] = round(ms * 1e3 / args.steps, 2)
+            other[k].setdefault("avg_launch_us", round(ms * 1e3 / n, 2))
     res = dict(sec=sec, tokens=M, flops=flops, roofline=roof, kernels=other)
     log("headline: %.3f ms/step, %.1f TFLOP/s" % (sec * 1e3, flops / sec / 1e12))
     return res, layers, host_w
@@ -362,6 +389,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     q.lib()
+    if args.calibrate_copy:
+        calibrate_copy(torch, args.calibrate_copy)
     head, layers, host_w = headline(args, q, torch, workloads)
     cpu = None
     if args.cpu_baseline == "on":

@@ -26,7 +26,8 @@ EXPORTS = [
     "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_trace_begin", "qlora_trace_end",
 ]
-KERNELS = {"fwd_gemm": 0, "dx_gemm": 1, "quantize": 2, "dequant": 3, "gemv": 4}
+KERNELS = {"fwd_gemm": 0, "dx_gemm": 1, "quantize": 2, "dequant": 3, "gemv": 4,
+           "split_reduce": 5}
 
 
 class QloraError(RuntimeError):

@@ -225,10 +225,13 @@ qlora_status qlora_linear_fwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
     if (e != hipSuccess) return QLORA_ERR_HIP;
     e = launch_gemv_finish(part, L.gemv_splits, M, N, xas, r, L.r32, B, Y, s);
   } else {
+    float* part = at<float>(ws, L.gemm_part);
     e = traced(QLORA_KERNEL_FWD_GEMM, s, [&] {
-      return launch_fwd_gemm(X, M, K, W->codes, N, ahat_t, xas, B, r, L.r32, Y,
-                             at<float>(ws, L.gemm_part), s);
+      return launch_fwd_gemm(X, M, K, W->codes, N, ahat_t, xas, B, r, L.r32, Y, L.sf, part, s);
     });
+    if (e == hipSuccess && L.sf > 1)
+      e = traced(QLORA_KERNEL_SPLIT_REDUCE, s,
+                 [&] { return launch_split_reduce(part, L.sf, M * N, Y, s); });
   }
   return hip_status(e);
 }
@@ -261,10 +264,13 @@ qlora_status qlora_linear_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
   QL_TRY(launch_skinny_nt(dY, M, N, N, bt, r, L.np, scale, gs, L.r32, nullptr, gt, L.mp, s));
   if (dX) {
     QL_TRY(launch_absmax_recon_t(W->absmax_q, W->absmax_scale, W->absmax_mean, N, K, ahat_t, s));
+    float* part = at<float>(ws, L.gemm_part);
     QL_TRY(traced(QLORA_KERNEL_DX_GEMM, s, [&] {
-      return launch_dx_gemm(dY, M, N, W->codes, K, ahat_t, gs, A, r, L.r32, dX,
-                            at<float>(ws, L.gemm_part), s);
+      return launch_dx_gemm(dY, M, N, W->codes, K, ahat_t, gs, A, r, L.r32, dX, L.sx, part, s);
     }));
+    if (L.sx > 1)
+      QL_TRY(traced(QLORA_KERNEL_SPLIT_REDUCE, s,
+                    [&] { return launch_split_reduce(part, L.sx, M * K, dX, s); }));
   }
   // dA = s . G^T X  (reduce over tokens into [r, K]);  dB = s . dY^T XA  ([N, r])
   float* pa = at<float>(ws, L.part_a);

@@ -767,12 +767,12 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ 
 
 int fwd_splits(int64_t M, int64_t N, int64_t K) {
   // Split K only when the output tiles cannot fill the chip; keep >= 8 steps
-  // per slice.
+  // per slice, and make every slice non-empty.
   const int64_t tiles = ceil_div(M, kTile) * ceil_div(N, kTile);
   const int64_t steps = K / kStep;
   int64_t s = 1;
   while (s < 8 && tiles * s * 2 <= 256 && steps / (s * 2) >= 8) s *= 2;
-  return (int)s;
+  return (int)ceil_div(steps, ceil_div(steps, s));
 }
 
 int dx_splits(int64_t M, int64_t N, int64_t K) {
@@ -782,44 +782,39 @@ int dx_splits(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes,
                            int64_t N, const float* ahat_t, const uint16_t* xas, const uint16_t* B,
-                           int r, int r32, uint16_t* Y, float* part, hipStream_t s) {
-  const int64_t steps = K / kStep;
-  const int ksteps = (int)ceil_div(steps, part ? fwd_splits(M, N, K) : 1);
-  const int splits = (int)ceil_div(steps, ksteps);   // every slice non-empty
+                           int r, int r32, uint16_t* Y, int splits, float* part, hipStream_t s) {
+  const int ksteps = (int)ceil_div(K / kStep, splits);
   const int64_t grid = ceil_div(M, kTile) * ceil_div(N, kTile) * splits;
   hipLaunchKernelGGL(k_qlora_fwd_nt, dim3((unsigned)grid), dim3(kThreads), 0, s, X, M, K, codes,
                      N, ahat_t, host_tables(), xas, B, r, r32, Y, splits, ksteps, part);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || splits == 1) return e;
-  const int64_t count = M * N;
-  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)ceil_div(ceil_div(count, 4), 256)), dim3(256),
-                     0, s, part, splits, count, Y);
   return hipGetLastError();
 }
 
 hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes,
                           int64_t K, const float* ahat_t, const uint16_t* gs, const uint16_t* A,
-                          int r, int r32, uint16_t* dX, float* part, hipStream_t s) {
+                          int r, int r32, uint16_t* dX, int splits, float* part, hipStream_t s) {
   const int64_t grid1 = ceil_div(M, kTile) * ceil_div(K, kTile);
   if (N % kStep == 0) {
-    const int nsteps = (int)ceil_div(N / kStep, part ? dx_splits(M, N, K) : 1);
-    const int splits = (int)ceil_div(N / kStep, nsteps);   // every slice non-empty
+    const int nsteps = (int)ceil_div(N / kStep, splits);
     hipLaunchKernelGGL(k_qlora_dx_nn_dma, dim3((unsigned)(grid1 * splits)), dim3(kThreads), 0, s,
                        dY, M, N, codes, K, ahat_t, host_tables(), gs, A, r, r32, dX, splits,
                        nsteps, part);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || splits == 1) return e;
-    const int64_t count = M * K;
-    hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)ceil_div(ceil_div(count, 4), 256)),
-                       dim3(256), 0, s, part, splits, count, dX);
-    return hipGetLastError();
-  }
-  if (N % 8 == 0)
+  } else if (splits != 1) {
+    return hipErrorInvalidValue;
+  } else if (N % 8 == 0) {
     hipLaunchKernelGGL(k_qlora_dx_nn<1>, dim3((unsigned)grid1), dim3(kThreads), 0, s, dY, M, N,
                        codes, K, ahat_t, host_tables(), gs, A, r, r32, dX);
-  else
+  } else {
     hipLaunchKernelGGL(k_qlora_dx_nn<2>, dim3((unsigned)grid1), dim3(kThreads), 0, s, dY, M, N,
                        codes, K, ahat_t, host_tables(), gs, A, r, r32, dX);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_split_reduce(const float* part, int splits, int64_t count, uint16_t* out,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)ceil_div(ceil_div(count, 4), 256)), dim3(256),
+                     0, s, part, splits, count, out);
   return hipGetLastError();
 }
 

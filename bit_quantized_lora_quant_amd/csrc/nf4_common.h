@@ -106,17 +106,21 @@ hipError_t launch_skinny_nt(const uint16_t* T, int64_t M, int64_t kin, int64_t l
 hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
                                  int64_t ldo, hipStream_t s);
 
-// The GEMMs split their inner loop across workgroups when the output tiles
-// alone cannot fill the chip; `part` (nullable: never split) then holds
-// splits x M x (N or K) float32 partials, added in split order.
+// The GEMMs split their inner loop into `splits` slices (one workgroup per
+// tile and slice) when the output tiles alone cannot fill the chip; with
+// splits > 1 each slice writes float32 partials [splits][M][N or K] to `part`
+// and launch_split_reduce adds them in slice order into the bf16 output.
+// The *_splits functions return the slice count (every slice non-empty).
 int fwd_splits(int64_t M, int64_t N, int64_t K);
 int dx_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes,
                            int64_t N, const float* ahat_t, const uint16_t* xas, const uint16_t* B,
-                           int r, int r32, uint16_t* Y, float* part, hipStream_t s);
+                           int r, int r32, uint16_t* Y, int splits, float* part, hipStream_t s);
 hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes,
                           int64_t K, const float* ahat_t, const uint16_t* gs, const uint16_t* A,
-                          int r, int r32, uint16_t* dX, float* part, hipStream_t s);
+                          int r, int r32, uint16_t* dX, int splits, float* part, hipStream_t s);
+hipError_t launch_split_reduce(const float* part, int splits, int64_t count, uint16_t* out,
+                               hipStream_t s);
 
 // partial[split][p][j] = sum over split's m of T[m][p] * U[j][m];  T [M, P]
 // (row stride P), U [r, ldu] with zero padding for m in [M, ldu).

@@ -174,7 +174,8 @@ typedef enum {
   QLORA_KERNEL_QUANTIZE = 2,   /* first-level absmax + NF4 codes */
   QLORA_KERNEL_DEQUANT = 3,    /* dequantise to float32 / bf16 */
   QLORA_KERNEL_GEMV = 4,       /* decode forward (M <= 16), main kernel */
-  QLORA_KERNEL_COUNT = 5
+  QLORA_KERNEL_SPLIT_REDUCE = 5, /* sum of split-K GEMM partials -> bf16 */
+  QLORA_KERNEL_COUNT = 6
 } qlora_kernel;
 
 qlora_status qlora_trace_begin(uint32_t kernel_mask, int32_t capacity);
