@@ -56,7 +56,9 @@ struct LinearWs {
   int64_t mp, np;             // token count padded to 32, N padded to 128
   int gemv_splits, sa, sb;    // split counts
   int sf, sx;                 // split-K slices of the forward / dX GEMM
-  size_t ahat_t, xas, gemv_part, bt, gs, gt, xat, part_a, part_b, gemm_part, total;
+  size_t ahat_t, xas, gemv_part, bt, gs, gt, xat, part_a, part_b, gemm_part;
+  size_t sk_k, sk_n;          // skinny-product slice partials (inner dim K / N)
+  size_t total;
 };
 
 LinearWs linear_layout(int64_t M, int64_t N, int64_t K, int r) {
@@ -82,6 +84,8 @@ LinearWs linear_layout(int64_t M, int64_t N, int64_t K, int r) {
   const size_t gp = std::max((size_t)(w.sf > 1 ? w.sf : 0) * M * N,
                              (size_t)(w.sx > 1 ? w.sx : 0) * M * K);
   w.gemm_part = off; off = align_up(off + gp * sizeof(float));
+  w.sk_k = off;      off = align_up(off + skinny_part_floats(M, K, r) * sizeof(float));
+  w.sk_n = off;      off = align_up(off + skinny_part_floats(M, N, r) * sizeof(float));
   w.total = off;
   return w;
 }
@@ -98,19 +102,31 @@ struct Trace {
 };
 Trace g_trace;
 
-// Runs `launch`, bracketed by a recorded event pair when kernel `k` is traced.
+}  // namespace
+
+namespace qnf4 {
+PendingTiming& pending_timing() {
+  static PendingTiming t;
+  return t;
+}
+}  // namespace qnf4
+
+namespace {
+
+// Runs `launch` (one kernel); when kernel `k` is traced, that dispatch records
+// its own start and end into the next event pair.
 template <typename F>
 hipError_t traced(int k, hipStream_t s, F&& launch) {
+  (void)s;
   const bool on = (g_trace.mask >> k) & 1u && g_trace.used[k] < g_trace.capacity;
   if (on) {
-    hipError_t e = hipEventRecord(g_trace.ev[k][2 * g_trace.used[k]], s);
-    if (e != hipSuccess) return e;
+    pending_timing().start = g_trace.ev[k][2 * g_trace.used[k]];
+    pending_timing().stop = g_trace.ev[k][2 * g_trace.used[k] + 1];
   }
   hipError_t e = launch();
-  if (on && e == hipSuccess) {
-    e = hipEventRecord(g_trace.ev[k][2 * g_trace.used[k] + 1], s);
-    ++g_trace.used[k];
-  }
+  const bool consumed = on && pending_timing().start == nullptr;
+  pending_timing() = PendingTiming{};
+  if (consumed && e == hipSuccess) ++g_trace.used[k];
   return e;
 }
 
@@ -214,9 +230,12 @@ qlora_status qlora_linear_fwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
   const float scale = alpha / (float)r;
   float* ahat_t = at<float>(ws, L.ahat_t);
   uint16_t* xas = at<uint16_t>(ws, L.xas);
-  hipError_t e = launch_absmax_recon_t(W->absmax_q, W->absmax_scale, W->absmax_mean, N, K, ahat_t, s);
-  if (e != hipSuccess) return QLORA_ERR_HIP;
-  e = launch_skinny_nt(X, M, K, K, A, r, K, scale, xas, L.r32, XA_out, nullptr, 0, s);
+  // X.A^T -> bf16(s.XA) [M, r32] (GEMM tail) and bf16(XA) [M, r] (caller),
+  // with the block constants reconstructed in the same launch
+  SkinnyJob xa{X, K, K, A, K, 0, 0, at<float>(ws, L.sk_k), scale, xas, XA_out, nullptr, 0};
+  skinny_plan(&xa, M);
+  const ReconJob rc{W->absmax_q, W->absmax_scale, W->absmax_mean, N, K / kBlock, ahat_t};
+  hipError_t e = launch_skinny(&xa, 1, M, r, L.r32, &rc, s);
   if (e != hipSuccess) return QLORA_ERR_HIP;
   if (M <= 16) {
     float* part = at<float>(ws, L.gemv_part);
@@ -256,14 +275,26 @@ qlora_status qlora_linear_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
   uint16_t* xat = at<uint16_t>(ws, L.xat);
   hipError_t e;
 #define QL_TRY(call) do { e = (call); if (e != hipSuccess) return QLORA_ERR_HIP; } while (0)
-  // XA^T [r, M32] for dB: from the forward's copy, or recomputed
-  if (XA_in) QL_TRY(launch_transpose_bf16(XA_in, M, r, xat, L.mp, s));
-  else QL_TRY(launch_skinny_nt(X, M, K, K, A, r, K, 1.0f, nullptr, 0, nullptr, xat, L.mp, s));
-  // G = dY . B as bf16(s.G) [M, r32] (dX tail) and bf16(G)^T [r, M32] (dA)
-  QL_TRY(launch_transpose_bf16(B, N, r, bt, L.np, s));
-  QL_TRY(launch_skinny_nt(dY, M, N, N, bt, r, L.np, scale, gs, L.r32, nullptr, gt, L.mp, s));
+  // one launch: B^T [r, N128] for G = dY.B; XA^T [r, M32] for dB from the
+  // forward's copy; the block constants for the dX GEMM
+  TransposeJob tj[2];
+  int nt = 0;
+  tj[nt++] = TransposeJob{B, N, r, bt, L.np};
+  if (XA_in) tj[nt++] = TransposeJob{XA_in, M, r, xat, L.mp};
+  const ReconJob rc{W->absmax_q, W->absmax_scale, W->absmax_mean, N, K / kBlock, ahat_t};
+  QL_TRY(launch_prep(tj, nt, dX ? &rc : nullptr, s));
+  // G = dY.B as bf16(s.G) [M, r32] (dX tail) and bf16(G)^T [r, M32] (dA);
+  // without the forward's XA, X.A^T is recomputed beside it
+  SkinnyJob sj[2];
+  int nj = 0;
+  sj[nj++] = SkinnyJob{dY, N, N, bt, L.np, 0, 0, at<float>(ws, L.sk_n), scale, gs, nullptr, gt,
+                       L.mp};
+  if (!XA_in)
+    sj[nj++] = SkinnyJob{X, K, K, A, K, 0, 0, at<float>(ws, L.sk_k), 1.0f, nullptr, nullptr, xat,
+                         L.mp};
+  for (int i = 0; i < nj; ++i) skinny_plan(&sj[i], M);
+  QL_TRY(launch_skinny(sj, nj, M, r, L.r32, nullptr, s));
   if (dX) {
-    QL_TRY(launch_absmax_recon_t(W->absmax_q, W->absmax_scale, W->absmax_mean, N, K, ahat_t, s));
     float* part = at<float>(ws, L.gemm_part);
     QL_TRY(traced(QLORA_KERNEL_DX_GEMM, s, [&] {
       return launch_dx_gemm(dY, M, N, W->codes, K, ahat_t, gs, A, r, L.r32, dX, L.sx, part, s);
@@ -273,12 +304,10 @@ qlora_status qlora_linear_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
                     [&] { return launch_split_reduce(part, L.sx, M * K, dX, s); }));
   }
   // dA = s . G^T X  (reduce over tokens into [r, K]);  dB = s . dY^T XA  ([N, r])
-  float* pa = at<float>(ws, L.part_a);
-  float* pb = at<float>(ws, L.part_b);
-  QL_TRY(launch_lora_grad(X, M, K, gt, r, L.mp, L.sa, pa, s));
-  QL_TRY(launch_lora_grad_reduce(pa, L.sa, K, r, scale, 1, dA, s));
-  QL_TRY(launch_lora_grad(dY, M, N, xat, r, L.mp, L.sb, pb, s));
-  QL_TRY(launch_lora_grad_reduce(pb, L.sb, N, r, scale, 0, dB, s));
+  const GradJob gj[2] = {
+      GradJob{X, K, gt, L.mp, L.sa, at<float>(ws, L.part_a), scale, 1, dA},
+      GradJob{dY, N, xat, L.mp, L.sb, at<float>(ws, L.part_b), scale, 0, dB}};
+  QL_TRY(launch_lora_grads(gj, 2, M, r, s));
 #undef QL_TRY
   return QLORA_OK;
 }

@@ -785,9 +785,8 @@ hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_
                            int r, int r32, uint16_t* Y, int splits, float* part, hipStream_t s) {
   const int ksteps = (int)ceil_div(K / kStep, splits);
   const int64_t grid = ceil_div(M, kTile) * ceil_div(N, kTile) * splits;
-  hipLaunchKernelGGL(k_qlora_fwd_nt, dim3((unsigned)grid), dim3(kThreads), 0, s, X, M, K, codes,
-                     N, ahat_t, host_tables(), xas, B, r, r32, Y, splits, ksteps, part);
-  return hipGetLastError();
+  return launch_kernel(k_qlora_fwd_nt, dim3((unsigned)grid), dim3(kThreads), s, X, M, K, codes, N,
+                       ahat_t, host_tables(), xas, B, r, r32, Y, splits, ksteps, part);
 }
 
 hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes,
@@ -796,25 +795,24 @@ hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t N, const uint8_
   const int64_t grid1 = ceil_div(M, kTile) * ceil_div(K, kTile);
   if (N % kStep == 0) {
     const int nsteps = (int)ceil_div(N / kStep, splits);
-    hipLaunchKernelGGL(k_qlora_dx_nn_dma, dim3((unsigned)(grid1 * splits)), dim3(kThreads), 0, s,
-                       dY, M, N, codes, K, ahat_t, host_tables(), gs, A, r, r32, dX, splits,
-                       nsteps, part);
+    launch_kernel(k_qlora_dx_nn_dma, dim3((unsigned)(grid1 * splits)), dim3(kThreads), s, dY, M, N,
+                  codes, K, ahat_t, host_tables(), gs, A, r, r32, dX, splits, nsteps, part);
   } else if (splits != 1) {
     return hipErrorInvalidValue;
   } else if (N % 8 == 0) {
-    hipLaunchKernelGGL(k_qlora_dx_nn<1>, dim3((unsigned)grid1), dim3(kThreads), 0, s, dY, M, N,
-                       codes, K, ahat_t, host_tables(), gs, A, r, r32, dX);
+    launch_kernel(k_qlora_dx_nn<1>, dim3((unsigned)grid1), dim3(kThreads), s, dY, M, N, codes, K,
+                  ahat_t, host_tables(), gs, A, r, r32, dX);
   } else {
-    hipLaunchKernelGGL(k_qlora_dx_nn<2>, dim3((unsigned)grid1), dim3(kThreads), 0, s, dY, M, N,
-                       codes, K, ahat_t, host_tables(), gs, A, r, r32, dX);
+    launch_kernel(k_qlora_dx_nn<2>, dim3((unsigned)grid1), dim3(kThreads), s, dY, M, N, codes, K,
+                  ahat_t, host_tables(), gs, A, r, r32, dX);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_split_reduce(const float* part, int splits, int64_t count, uint16_t* out,
                                hipStream_t s) {
-  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)ceil_div(ceil_div(count, 4), 256)), dim3(256),
-                     0, s, part, splits, count, out);
+  launch_kernel(k_split_reduce, dim3((unsigned)ceil_div(ceil_div(count, 4), 256)), dim3(256), s,
+                part, splits, count, out);
   return hipGetLastError();
 }
 

@@ -104,9 +104,8 @@ hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* c
                        const float* ahat_t, int splits, float* partial, hipStream_t s) {
   // split boundaries on 128 so each lane-group step stays inside one split
   const int64_t kchunk = ceil_div(ceil_div(K, splits), kKStep) * kKStep;
-  hipLaunchKernelGGL(k_qlora_gemv, dim3((unsigned)ceil_div(N, kRowsPerWg), (unsigned)splits),
-                     dim3(256), 0, s, X, M, K, codes, N, ahat_t, host_tables(), kchunk, partial);
-  return hipGetLastError();
+  return launch_kernel(k_qlora_gemv, dim3((unsigned)ceil_div(N, kRowsPerWg), (unsigned)splits),
+                       dim3(256), s, X, M, K, codes, N, ahat_t, host_tables(), kchunk, partial);
 }
 
 hipError_t launch_gemv_finish(const float* partial, int splits, int64_t M, int64_t N,

@@ -4,12 +4,19 @@
 // section "LoRA: freeze the base, train small adapters"; r and lora_alpha are
 // the PEFT knobs of "QLoRA: Fine-Tuning a 70B on One GPU", section "Practical
 // Implementation").  All contractions run on v_mfma_f32_16x16x32_bf16 with
-// float32 accumulation; reductions over tokens use a fixed split and a fixed
-// summation order, so results repeat bit for bit.
+// float32 accumulation; reductions over the inner dimension or the tokens use
+// fixed slices and a fixed summation order, so results repeat bit for bit.
+//
+// These steps stream one activation tensor each and are bound by HBM; they
+// are cut into enough workgroups to cover the chip, and independent small
+// steps share a launch.
 #include "nf4_common.h"
 
 namespace qnf4 {
 namespace {
+
+constexpr int kSkStep = 128;    // inner indices per wave step (4 lane groups x 32)
+constexpr int kSkWaves = 8;     // waves per skinny workgroup (512 threads)
 
 __device__ __forceinline__ uint4 load8_bf16(const uint16_t* __restrict__ p, int64_t idx,
                                             int64_t limit, bool vec) {
@@ -26,51 +33,106 @@ __device__ __forceinline__ uint4 load8_bf16(const uint16_t* __restrict__ p, int6
   return v;
 }
 
+__device__ __forceinline__ uint16_t to_bf16(float v) {
+  return (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFF);
+}
+
+// One thread per element of [KB][N]: out[kb * N + n] = â(n * KB + kb).
+__device__ __forceinline__ void recon_elems(const ReconJob& J, int64_t b) {
+  const int64_t e = b * blockDim.x + threadIdx.x;
+  if (e >= J.N * J.KB) return;
+  const int64_t kb = e / J.N, n = e - kb * J.N;
+  J.out[e] = absmax_recon(J.q, J.scale, *J.mean, n * J.KB + kb);
+}
+
+
 // ------------------------------------------------------------ skinny NT
-// P[m][j] = sum_k T[m][k] U[j][k] for 16 rows m per workgroup.  The 8 waves
-// take interleaved 128-wide inner steps; lane (j16, g) reads the 32
-// contiguous inner indices 32g..32g+31 of the step from both operands (four
-// MFMA sub-steps).  The wave partials are summed in wave order through LDS.
+// Workgroup (row group, slice): 16 rows of T, inner indices [kbeg, kend).
+// The 4 waves take interleaved 128-wide steps; lane (j16, g) reads the 32
+// contiguous inner indices 32g..32g+31 of a step from both operands (four
+// MFMA sub-steps).  Wave partials are added in wave order through LDS.
 template <int RT>
-__global__ __launch_bounds__(512) void k_skinny_nt(const uint16_t* __restrict__ T, int64_t M,
-                                                   int64_t kin, int64_t ldt,
-                                                   const uint16_t* __restrict__ U, int r,
-                                                   int64_t ldu, float scale,
-                                                   uint16_t* __restrict__ out_s, int r32,
-                                                   uint16_t* __restrict__ out,
-                                                   uint16_t* __restrict__ out_t, int64_t ldo_t,
-                                                   int vec) {
-  __shared__ float red[8][RT][4][64];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+__device__ __forceinline__ void skinny_slice(const SkinnyJob& J, int64_t M, int r, int r32,
+                                             int64_t b) {
+  __shared__ float red[kSkWaves][RT][4][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int j16 = lane & 15, g = lane >> 4;
-  const int64_t m0 = (int64_t)blockIdx.x * 16;
+  const int ks = (int)(b % J.ks);
+  const int64_t m0 = (b / J.ks) * 16;
   int64_t mrow = m0 + j16;
   mrow = mrow < M ? mrow : M - 1;
-  const bool tv = vec && (ldt % 8) == 0;
-  const bool uv = vec && (ldu % 8) == 0;
+  const int64_t kbeg = (int64_t)ks * J.kslice;
+  int64_t kend = kbeg + J.kslice;
+  kend = kend < J.kin ? kend : J.kin;
+  const bool tv = (J.ldt % 8) == 0;
+  const bool uv = (J.ldu % 8) == 0;
+  const uint16_t* trow = J.T + mrow * J.ldt;
 
   f32x4_t acc[RT];
 #pragma unroll
   for (int jt = 0; jt < RT; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t k = (int64_t)wv * 128; k < kin; k += 8 * 128) {
-    const int64_t kk = k + 32 * g;
-    uint4 a[4];
+  // Operands of one step: sub-step s takes inner indices k + 32 s + 8 g ..
+  // + 7 from lane group g, so each load instruction reads 64 contiguous bytes
+  // per row.
+  auto load_step = [&](int64_t k, uint4 (&a)[4], uint4 (&bv)[RT][4]) {
+    if (tv && uv && k + kSkStep <= J.kin) {
+      // whole step in range (wave-uniform): plain vector loads; adapter rows
+      // past r are loaded clamped and zeroed by a select
 #pragma unroll
-    for (int s = 0; s < 4; ++s) a[s] = load8_bf16(T + mrow * ldt, kk + 8 * s, kin, tv);
+      for (int s = 0; s < 4; ++s)
+        a[s] = *reinterpret_cast<const uint4*>(trow + k + 32 * s + 8 * g);
 #pragma unroll
-    for (int jt = 0; jt < RT; ++jt) {
-      const int u = jt * 16 + j16;
-      uint4 b[4];
-      if (u < r) {
+      for (int jt = 0; jt < RT; ++jt) {
+        const int u = jt * 16 + j16;
+        const uint16_t* urow = J.U + (int64_t)(u < r ? u : r - 1) * J.ldu + k + 8 * g;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) b[s] = load8_bf16(U + (int64_t)u * ldu, kk + 8 * s, kin, uv);
-      } else {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) b[s] = make_uint4(0u, 0u, 0u, 0u);
+        for (int s = 0; s < 4; ++s) {
+          const uint4 v = *reinterpret_cast<const uint4*>(urow + 32 * s);
+          bv[jt][s] = u < r ? v : make_uint4(0u, 0u, 0u, 0u);
+        }
       }
+    } else {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc[jt] = mfma16x16x32(a[s], b[s], acc[jt]);
+      for (int s = 0; s < 4; ++s) a[s] = load8_bf16(trow, k + 32 * s + 8 * g, J.kin, tv);
+#pragma unroll
+      for (int jt = 0; jt < RT; ++jt) {
+        const int u = jt * 16 + j16;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          bv[jt][s] = u < r ? load8_bf16(J.U + (int64_t)u * J.ldu, k + 32 * s + 8 * g, J.kin, uv)
+                            : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  };
+  constexpr int64_t stride = (int64_t)kSkWaves * kSkStep;
+  int64_t k = kbeg + (int64_t)wv * kSkStep;
+  auto mfmas = [&](const uint4 (&a)[4], const uint4 (&bv)[RT][4]) {
+#pragma unroll
+    for (int jt = 0; jt < RT; ++jt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc[jt] = mfma16x16x32(a[s], bv[jt][s], acc[jt]);
+  };
+  if constexpr (RT <= 4) {
+    // two steps in flight: the next step's loads are issued before this
+    // step's MFMAs
+    uint4 a0[4], b0[RT][4], a1[4], b1[RT][4];
+    if (k < kend) load_step(k, a0, b0);
+    while (k < kend) {
+      if (k + stride < kend) load_step(k + stride, a1, b1);
+      mfmas(a0, b0);
+      k += stride;
+      if (k >= kend) break;
+      if (k + stride < kend) load_step(k + stride, a0, b0);
+      mfmas(a1, b1);
+      k += stride;
+    }
+  } else {
+    for (; k < kend; k += stride) {   // r > 64: one step at a time
+      uint4 a0[4], b0[RT][4];
+      load_step(k, a0, b0);
+      mfmas(a0, b0);
     }
   }
 #pragma unroll
@@ -79,65 +141,144 @@ __global__ __launch_bounds__(512) void k_skinny_nt(const uint16_t* __restrict__ 
     for (int v = 0; v < 4; ++v) red[wv][jt][v][lane] = acc[jt][v];
   __syncthreads();
   if (wv != 0) return;
-  // lane holds P[m0 + 4g + v][16 jt + j16]
+  // lane holds P[m0 + 4g + v][16 jt + j16]; a single slice writes the final
+  // outputs, several write float32 partials for the finish step
+  float* part = J.part + (int64_t)ks * M * (RT * 16);
 #pragma unroll
-  for (int jt = 0; jt < RT; ++jt) {
+  for (int jt = 0; jt < RT; ++jt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      float sum = 0.f;
+      float sum = red[0][jt][v][lane];
 #pragma unroll
-      for (int w = 0; w < 8; ++w) sum += red[w][jt][v][lane];
+      for (int w = 1; w < kSkWaves; ++w) sum += red[w][jt][v][lane];
       const int64_t m = m0 + 4 * g + v;
       const int j = jt * 16 + j16;
-      if (m < M) {
-        if (out_s && j < r32) out_s[m * r32 + j] = (uint16_t)(pack_bf16x2(j < r ? scale * sum : 0.f, 0.f) & 0xFFFF);
-        if (out && j < r) out[m * r + j] = (uint16_t)(pack_bf16x2(sum, 0.f) & 0xFFFF);
+      if (J.ks > 1) {
+        if (m < M) part[m * (RT * 16) + j] = sum;
+        continue;
       }
-      if (out_t && j < r && m < ldo_t)
-        out_t[(int64_t)j * ldo_t + m] = m < M ? (uint16_t)(pack_bf16x2(sum, 0.f) & 0xFFFF) : (uint16_t)0;
+      if (m < M) {
+        if (J.out_s && j < r32) J.out_s[m * r32 + j] = to_bf16(j < r ? J.scale * sum : 0.f);
+        if (J.out && j < r) J.out[m * r + j] = to_bf16(sum);
+      }
+      if (J.out_t && j < r && m < J.ldo_t)
+        J.out_t[(int64_t)j * J.ldo_t + m] = m < M ? to_bf16(sum) : 0;
     }
-  }
-  // zero padding columns of out_s beyond the computed tiles
-  if (out_s) {
+  if (J.ks == 1 && J.out_s) {   // padding columns of out_s past the computed tiles
     for (int j = RT * 16 + j16; j < r32; j += 16)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int64_t m = m0 + 4 * g + v;
-        if (m < M) out_s[m * r32 + j] = 0;
+        if (m < M) J.out_s[m * r32 + j] = 0;
       }
   }
 }
 
-__global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ in,
-                                                        int64_t rows, int64_t cols,
-                                                        uint16_t* __restrict__ out, int64_t ldo) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // output index along ldo
-  const int64_t j = blockIdx.y;                                  // output row (= input column)
-  if (i < ldo) out[j * ldo + i] = (i < rows) ? in[i * cols + j] : (uint16_t)0;
+// Row groups of a job: past M only when out_t needs zero padding.
+__device__ __host__ __forceinline__ int64_t skinny_rows(const SkinnyJob& J, int64_t M) {
+  return (J.ks == 1 && J.out_t && J.ldo_t > M) ? J.ldo_t : M;
+}
+
+__device__ __forceinline__ int64_t skinny_blocks(const SkinnyJob& J, int64_t M) {
+  return ceil_div(skinny_rows(J, M), 16) * J.ks;
+}
+
+template <int RT>
+__global__ __launch_bounds__(512) void k_skinny_slices(SkinnyJob j0, SkinnyJob j1, int nj,
+                                                       int64_t M, int r, int r32, ReconJob rc,
+                                                       int has_rc) {
+  int64_t b = blockIdx.x;
+  const int64_t b0 = skinny_blocks(j0, M);
+  if (b < b0) { skinny_slice<RT>(j0, M, r, r32, b); return; }
+  b -= b0;
+  if (nj > 1) {
+    const int64_t b1 = skinny_blocks(j1, M);
+    if (b < b1) { skinny_slice<RT>(j1, M, r, r32, b); return; }
+    b -= b1;
+  }
+  if (has_rc) recon_elems(rc, b);
+}
+
+// Thread per (row m, column j < r32) of one job: adds the slices in order.
+__device__ __forceinline__ void skinny_finish_elem(const SkinnyJob& J, int64_t M, int r, int r32,
+                                                   int rpad, int64_t e) {
+  const int64_t rows = (J.out_t && J.ldo_t > M) ? J.ldo_t : M;
+  if (e >= rows * r32) return;
+  const int64_t m = e / r32;
+  const int j = (int)(e - m * r32);
+  float sum = 0.f;
+  if (m < M && j < r) {
+    sum = J.part[m * rpad + j];
+    for (int k = 1; k < J.ks; ++k) sum += J.part[((int64_t)k * M + m) * rpad + j];
+  }
+  if (m < M) {
+    if (J.out_s) J.out_s[m * r32 + j] = to_bf16(j < r ? J.scale * sum : 0.f);
+    if (J.out && j < r) J.out[m * r + j] = to_bf16(sum);
+  }
+  if (J.out_t && j < r && m < J.ldo_t) J.out_t[(int64_t)j * J.ldo_t + m] = m < M ? to_bf16(sum) : 0;
+}
+
+// (jobs run as a single slice wrote their outputs directly: no finish)
+__device__ __host__ __forceinline__ int64_t finish_blocks(const SkinnyJob& J, int64_t M,
+                                                          int r32) {
+  if (J.ks == 1) return 0;
+  const int64_t rows = (J.out_t && J.ldo_t > M) ? J.ldo_t : M;
+  return ceil_div(rows * r32, 256);
+}
+
+__global__ __launch_bounds__(256) void k_skinny_finish(SkinnyJob j0, SkinnyJob j1, int nj,
+                                                       int64_t M, int r, int r32, int rpad) {
+  int64_t b = blockIdx.x;
+  const int64_t b0 = finish_blocks(j0, M, r32);
+  if (b < b0) { skinny_finish_elem(j0, M, r, r32, rpad, b * 256 + threadIdx.x); return; }
+  b -= b0;
+  if (nj > 1) skinny_finish_elem(j1, M, r, r32, rpad, b * 256 + threadIdx.x);
+}
+
+// ------------------------------------------------------------------ prep
+__device__ __forceinline__ void transpose_elem(const TransposeJob& J, int64_t e) {
+  if (e >= J.cols * J.ldo) return;
+  const int64_t j = e / J.ldo, i = e - j * J.ldo;   // output row j (= input column), column i
+  J.out[e] = (i < J.rows) ? J.in[i * J.cols + j] : (uint16_t)0;
+}
+
+__global__ __launch_bounds__(256) void k_prep(TransposeJob t0, TransposeJob t1, int nt,
+                                              ReconJob rc, int has_rc) {
+  int64_t b = blockIdx.x;
+  if (nt > 0) {
+    const int64_t n0 = ceil_div(t0.cols * t0.ldo, 256);
+    if (b < n0) { transpose_elem(t0, b * 256 + threadIdx.x); return; }
+    b -= n0;
+  }
+  if (nt > 1) {
+    const int64_t n1 = ceil_div(t1.cols * t1.ldo, 256);
+    if (b < n1) { transpose_elem(t1, b * 256 + threadIdx.x); return; }
+    b -= n1;
+  }
+  if (has_rc) recon_elems(rc, b);
 }
 
 // ------------------------------------------------------- adapter gradients
-// partial[split][p][j] = sum_{m in split} T[m][p] U[j][m]
-// T [M, P] row-major, U [r, ldu] (U[j][m] = 0 for m >= M).  Wave = 128
-// consecutive p.  Lane (i16, g) loads 8 rows m (8g..8g+7 of a 32-step) x 8
-// consecutive p (8 i16 .. 8 i16 + 7) and regroups them into the A operands of
-// 8 MFMAs: MFMA t handles p = p0 + 8 i + t, so the transpose of T costs one
-// 16-bit regroup per pair of rows, no LDS.
+// Workgroup (128 consecutive p, token slice): the 4 waves take interleaved
+// 32-token steps.  Lane (i16, g) loads 8 rows m (8g..8g+7 of a step) x 8
+// consecutive p (8 i16 .. 8 i16 + 7) of T and regroups them into the A
+// operands of 8 MFMAs: MFMA t handles p = p0 + 8 i + t, so the transpose of T
+// costs one 16-bit regroup per pair of rows, no LDS.  Wave partials are added
+// in wave order through LDS, one MFMA column t at a time.
 template <int RT>
-__global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ T, int64_t M,
-                                                   int64_t P, const uint16_t* __restrict__ U,
-                                                   int r, int64_t ldu, int64_t mchunk,
-                                                   float* __restrict__ partial, int vec) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+__device__ __forceinline__ void grad_slice(const GradJob& J, int64_t M, int r, int64_t b) {
+  __shared__ float red[4][RT][4][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int i16 = lane & 15, g = lane >> 4;
-  const int64_t p0 = ((int64_t)blockIdx.x * 4 + wv) * 128;
-  if (p0 >= P) return;
-  const int split = blockIdx.y;
+  const int split = (int)(b % J.splits);
+  const int64_t p0 = (b / J.splits) * 128;
+  const int64_t mchunk = ceil_div(ceil_div(M, J.splits), 32) * 32;
   const int64_t mbeg = (int64_t)split * mchunk;
   int64_t mend = mbeg + mchunk;
   mend = mend < M ? mend : M;
   const int64_t pc = p0 + 8 * i16;
-  const bool pv = vec && (P % 8) == 0;
+  const bool pv = (J.P % 8) == 0;
 
   f32x4_t acc[8][RT];
 #pragma unroll
@@ -145,21 +286,32 @@ __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ 
 #pragma unroll
     for (int jt = 0; jt < RT; ++jt) acc[t][jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t mb = mbeg; mb < mend; mb += 32) {
-    uint4 rows[8];
+  const bool fast = pv && p0 + 128 <= J.P;   // workgroup-uniform
+  auto load_step = [&](int64_t mb, uint4 (&rows)[8], uint4 (&bu)[RT]) {
+    if (fast) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      int64_t m = mb + 8 * g + e;
-      m = m < M ? m : M - 1;                // U is zero there
-      rows[e] = load8_bf16(T + m * P, pc, P, pv);
+      for (int e = 0; e < 8; ++e) {
+        int64_t m = mb + 8 * g + e;
+        m = m < M ? m : M - 1;              // U is zero there
+        rows[e] = *reinterpret_cast<const uint4*>(J.T + m * J.P + pc);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        int64_t m = mb + 8 * g + e;
+        m = m < M ? m : M - 1;
+        rows[e] = load8_bf16(J.T + m * J.P, pc, J.P, pv);
+      }
     }
-    uint4 bu[RT];
 #pragma unroll
     for (int jt = 0; jt < RT; ++jt) {
       const int u = jt * 16 + i16;
-      bu[jt] = (u < r) ? *reinterpret_cast<const uint4*>(U + (int64_t)u * ldu + mb + 8 * g)
-                       : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 v =
+          *reinterpret_cast<const uint4*>(J.U + (int64_t)(u < r ? u : r - 1) * J.ldu + mb + 8 * g);
+      bu[jt] = u < r ? v : make_uint4(0u, 0u, 0u, 0u);
     }
+  };
+  auto mfmas = [&](const uint4 (&rows)[8], const uint4 (&bu)[RT]) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       uint32_t h[8];
@@ -176,95 +328,193 @@ __global__ __launch_bounds__(256) void k_lora_grad(const uint16_t* __restrict__ 
 #pragma unroll
       for (int jt = 0; jt < RT; ++jt) acc[t][jt] = mfma16x16x32(a, bu[jt], acc[t][jt]);
     }
+  };
+  constexpr int64_t stride = 4 * 32;
+  int64_t mb = mbeg + 32 * wv;
+  if constexpr (RT <= 2) {
+    // two steps in flight, as in the skinny product
+    uint4 r0[8], u0[RT], r1[8], u1[RT];
+    if (mb < mend) load_step(mb, r0, u0);
+    while (mb < mend) {
+      if (mb + stride < mend) load_step(mb + stride, r1, u1);
+      mfmas(r0, u0);
+      mb += stride;
+      if (mb >= mend) break;
+      if (mb + stride < mend) load_step(mb + stride, r0, u0);
+      mfmas(r1, u1);
+      mb += stride;
+    }
+  } else {
+    // wide ranks: the accumulators fill the register file, one step at a time
+    for (; mb < mend; mb += stride) {
+      uint4 r0[8], u0[RT];
+      load_step(mb, r0, u0);
+      mfmas(r0, u0);
+    }
   }
   // D[i = 4g + v][j16] of MFMA (t, jt): p = p0 + 8 (4g + v) + t, j = 16 jt + j16
-  float* base = partial + (int64_t)split * P * r;
+  float* base = J.partial + (int64_t)split * J.P * r;
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+  for (int t = 0; t < 8; ++t) {
 #pragma unroll
     for (int jt = 0; jt < RT; ++jt)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t p = p0 + 8 * (4 * g + v) + t;
-        const int j = jt * 16 + i16;
-        if (p < P && j < r) base[p * r + j] = acc[t][jt][v];
-      }
+      for (int v = 0; v < 4; ++v) red[wv][jt][v][lane] = acc[t][jt][v];
+    __syncthreads();
+    if (wv == 0) {
+#pragma unroll
+      for (int jt = 0; jt < RT; ++jt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float s = red[0][jt][v][lane];
+#pragma unroll
+          for (int w = 1; w < 4; ++w) s += red[w][jt][v][lane];
+          const int64_t p = p0 + 8 * (4 * g + v) + t;
+          const int j = jt * 16 + i16;
+          if (p < J.P && j < r) base[p * r + j] = s;
+        }
+    }
+    __syncthreads();
+  }
 }
 
-__global__ __launch_bounds__(256) void k_lora_grad_reduce(const float* __restrict__ partial,
-                                                          int splits, int64_t P, int r,
-                                                          float scale, int transposed,
-                                                          float* __restrict__ out) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= P * r) return;
-  int64_t p, j;
-  if (transposed) { j = idx / P; p = idx % P; } else { p = idx / r; j = idx % r; }
-  float s = 0.f;
-  for (int k = 0; k < splits; ++k) s += partial[(int64_t)k * P * r + p * r + j];
-  out[idx] = scale * s;
+__device__ __forceinline__ int64_t grad_blocks(const GradJob& J) {
+  return ceil_div(J.P, 128) * J.splits;
 }
 
 template <int RT>
-hipError_t skinny_rt(const uint16_t* T, int64_t M, int64_t kin, int64_t ldt, const uint16_t* U,
-                     int r, int64_t ldu, float scale, uint16_t* out_s, int r32, uint16_t* out,
-                     uint16_t* out_t, int64_t ldo_t, hipStream_t s) {
-  int64_t rows = M;
-  if (out_t && ldo_t > rows) rows = ldo_t;
-  hipLaunchKernelGGL(k_skinny_nt<RT>, dim3((unsigned)ceil_div(rows, 16)), dim3(512), 0, s, T, M,
-                     kin, ldt, U, r, ldu, scale, out_s, r32, out, out_t, ldo_t, 1);
+__global__ __launch_bounds__(256) void k_lora_grads(GradJob j0, GradJob j1, int nj, int64_t M,
+                                                    int r) {
+  int64_t b = blockIdx.x;
+  const int64_t b0 = grad_blocks(j0);
+  if (b < b0) { grad_slice<RT>(j0, M, r, b); return; }
+  if (nj > 1) grad_slice<RT>(j1, M, r, b - b0);
+}
+
+__device__ __forceinline__ void grad_reduce_elem(const GradJob& J, int r, int64_t idx) {
+  if (idx >= J.P * r) return;
+  int64_t p, j;
+  if (J.transposed) { j = idx / J.P; p = idx - j * J.P; } else { p = idx / r; j = idx - p * r; }
+  float s = J.partial[p * r + j];
+  for (int k = 1; k < J.splits; ++k) s += J.partial[(int64_t)k * J.P * r + p * r + j];
+  J.out[idx] = J.scale * s;
+}
+
+__global__ __launch_bounds__(256) void k_lora_grad_reduce(GradJob j0, GradJob j1, int nj, int r) {
+  const int64_t b0 = ceil_div(j0.P * r, 256);
+  const int64_t b = blockIdx.x;
+  if (b < b0) { grad_reduce_elem(j0, r, b * 256 + threadIdx.x); return; }
+  if (nj > 1) grad_reduce_elem(j1, r, (b - b0) * 256 + threadIdx.x);
+}
+
+template <int RT>
+hipError_t skinny_rt(const SkinnyJob* jobs, int nj, int64_t M, int r, int r32, const ReconJob* rc,
+                     hipStream_t s) {
+  int64_t blocks = 0;
+  for (int i = 0; i < nj; ++i) blocks += ceil_div(skinny_rows(jobs[i], M), 16) * jobs[i].ks;
+  blocks += rc ? ceil_div(rc->N * rc->KB, kSkWaves * 64) : 0;
+  const ReconJob none{};
+  hipLaunchKernelGGL(k_skinny_slices<RT>, dim3((unsigned)blocks), dim3(kSkWaves * 64), 0, s,
+                     jobs[0], nj > 1 ? jobs[1] : jobs[0], nj, M, r, r32, rc ? *rc : none,
+                     rc ? 1 : 0);
   return hipGetLastError();
 }
 
 template <int RT>
-hipError_t grad_rt(const uint16_t* T, int64_t M, int64_t P, const uint16_t* U, int r, int64_t ldu,
-                   int splits, float* partial, hipStream_t s) {
-  const int64_t mchunk = ceil_div(ceil_div(M, splits), 32) * 32;
-  hipLaunchKernelGGL(k_lora_grad<RT>, dim3((unsigned)ceil_div(P, 512), (unsigned)splits), dim3(256),
-                     0, s, T, M, P, U, r, ldu, mchunk, partial, 1);
+hipError_t grads_rt(const GradJob* jobs, int nj, int64_t M, int r, hipStream_t s) {
+  int64_t blocks = 0;
+  for (int i = 0; i < nj; ++i) blocks += ceil_div(jobs[i].P, 128) * jobs[i].splits;
+  hipLaunchKernelGGL(k_lora_grads<RT>, dim3((unsigned)blocks), dim3(256), 0, s, jobs[0],
+                     nj > 1 ? jobs[1] : jobs[0], nj, M, r);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_skinny_nt(const uint16_t* T, int64_t M, int64_t kin, int64_t ldt,
-                            const uint16_t* U, int r, int64_t ldu, float scale, uint16_t* out_s,
-                            int r32, uint16_t* out, uint16_t* out_t, int64_t ldo_t,
-                            hipStream_t s) {
-  if (r <= 16) return skinny_rt<1>(T, M, kin, ldt, U, r, ldu, scale, out_s, r32, out, out_t, ldo_t, s);
-  if (r <= 32) return skinny_rt<2>(T, M, kin, ldt, U, r, ldu, scale, out_s, r32, out, out_t, ldo_t, s);
-  if (r <= 64) return skinny_rt<4>(T, M, kin, ldt, U, r, ldu, scale, out_s, r32, out, out_t, ldo_t, s);
-  return skinny_rt<8>(T, M, kin, ldt, U, r, ldu, scale, out_s, r32, out, out_t, ldo_t, s);
+int skinny_rpad(int r) { return r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : 128; }
+
+int skinny_slices(int64_t M, int64_t kin) {
+  // one slice once there are enough row groups to spread over the chip (no
+  // finish step then); else about 256 workgroups, at least one 128-wide
+  // step per wave
+  const int64_t groups = ceil_div(M, 16);
+  if (groups >= 64) return 1;
+  int64_t ks = ceil_div(256, groups);
+  const int64_t maxs = ceil_div(kin, (int64_t)kSkWaves * kSkStep);
+  if (ks > maxs) ks = maxs;
+  if (ks < 1) ks = 1;
+  return (int)ks;
 }
 
-hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
-                                 int64_t ldo, hipStream_t s) {
-  hipLaunchKernelGGL(k_transpose_bf16, dim3((unsigned)ceil_div(ldo, 256), (unsigned)cols),
-                     dim3(256), 0, s, in, rows, cols, out, ldo);
+size_t skinny_part_floats(int64_t M, int64_t kin, int r) {
+  return (size_t)skinny_slices(M, kin) * (size_t)M * (size_t)skinny_rpad(r);
+}
+
+void skinny_plan(SkinnyJob* j, int64_t M) {
+  const int ks = skinny_slices(M, j->kin);
+  // slice length a multiple of the wave step; every slice non-empty
+  j->kslice = ceil_div(ceil_div(j->kin, ks), kSkStep) * kSkStep;
+  j->ks = (int)ceil_div(j->kin, j->kslice);
+}
+
+hipError_t launch_skinny(const SkinnyJob* jobs, int nj, int64_t M, int r, int r32,
+                         const ReconJob* recon, hipStream_t s) {
+  const int rpad = skinny_rpad(r);
+  hipError_t e;
+  switch (rpad) {
+    case 16: e = skinny_rt<1>(jobs, nj, M, r, r32, recon, s); break;
+    case 32: e = skinny_rt<2>(jobs, nj, M, r, r32, recon, s); break;
+    case 64: e = skinny_rt<4>(jobs, nj, M, r, r32, recon, s); break;
+    default: e = skinny_rt<8>(jobs, nj, M, r, r32, recon, s); break;
+  }
+  if (e != hipSuccess) return e;
+  bool finish = false;
+  for (int i = 0; i < nj; ++i) finish |= jobs[i].ks > 1;
+  if (!finish) return hipSuccess;
+  int64_t blocks = 0;
+  for (int i = 0; i < nj; ++i) blocks += finish_blocks(jobs[i], M, r32);
+  hipLaunchKernelGGL(k_skinny_finish, dim3((unsigned)blocks), dim3(256), 0, s, jobs[0],
+                     nj > 1 ? jobs[1] : jobs[0], nj, M, r, r32, rpad);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const TransposeJob* t, int nt, const ReconJob* recon, hipStream_t s) {
+  int64_t blocks = 0;
+  for (int i = 0; i < nt; ++i) blocks += ceil_div(t[i].cols * t[i].ldo, 256);
+  blocks += recon ? ceil_div(recon->N * recon->KB, 256) : 0;
+  if (blocks == 0) return hipSuccess;
+  const TransposeJob tn{};
+  const ReconJob rn{};
+  hipLaunchKernelGGL(k_prep, dim3((unsigned)blocks), dim3(256), 0, s, nt > 0 ? t[0] : tn,
+                     nt > 1 ? t[1] : tn, nt, recon ? *recon : rn, recon ? 1 : 0);
   return hipGetLastError();
 }
 
 int lora_grad_splits(int64_t M, int64_t P) {
-  // enough workgroups to cover the chip, at least 256 tokens per split
-  const int64_t groups = ceil_div(P, 512);
-  int64_t splits = ceil_div(1024, groups);
+  // about 512 workgroups over the chip, at least 256 tokens per split (two
+  // steps per wave)
+  const int64_t groups = ceil_div(P, 128);
+  int64_t splits = ceil_div(512, groups);
   const int64_t maxs = ceil_div(M, 256);
   if (splits > maxs) splits = maxs;
   if (splits < 1) splits = 1;
   return (int)splits;
 }
 
-hipError_t launch_lora_grad(const uint16_t* T, int64_t M, int64_t P, const uint16_t* U, int r,
-                            int64_t ldu, int splits, float* partial, hipStream_t s) {
-  if (r <= 16) return grad_rt<1>(T, M, P, U, r, ldu, splits, partial, s);
-  if (r <= 32) return grad_rt<2>(T, M, P, U, r, ldu, splits, partial, s);
-  if (r <= 64) return grad_rt<4>(T, M, P, U, r, ldu, splits, partial, s);
-  return grad_rt<8>(T, M, P, U, r, ldu, splits, partial, s);
-}
-
-hipError_t launch_lora_grad_reduce(const float* partial, int splits, int64_t P, int r, float scale,
-                                   int transposed, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(k_lora_grad_reduce, dim3((unsigned)ceil_div(P * r, 256)), dim3(256), 0, s,
-                     partial, splits, P, r, scale, transposed, out);
+hipError_t launch_lora_grads(const GradJob* jobs, int nj, int64_t M, int r, hipStream_t s) {
+  hipError_t e;
+  const int rpad = skinny_rpad(r);
+  switch (rpad) {
+    case 16: e = grads_rt<1>(jobs, nj, M, r, s); break;
+    case 32: e = grads_rt<2>(jobs, nj, M, r, s); break;
+    case 64: e = grads_rt<4>(jobs, nj, M, r, s); break;
+    default: e = grads_rt<8>(jobs, nj, M, r, s); break;
+  }
+  if (e != hipSuccess) return e;
+  int64_t blocks = 0;
+  for (int i = 0; i < nj; ++i) blocks += ceil_div(jobs[i].P * r, 256);
+  hipLaunchKernelGGL(k_lora_grad_reduce, dim3((unsigned)blocks), dim3(256), 0, s, jobs[0],
+                     nj > 1 ? jobs[1] : jobs[0], nj, r);
   return hipGetLastError();
 }
 

@@ -3,11 +3,35 @@
 // (v_mfma_f32_16x16x32_bf16), DPP lane exchanges, v_cvt_pk_bf16_f32.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace qnf4 {
+
+// Benchmark instrumentation: when an event pair is pending, the next launch
+// through launch_kernel records its own start and end into it (from the
+// dispatch itself, so no extra packets sit between kernels).  Set and cleared
+// by the tracer around one launcher call; process-global, single host thread.
+struct PendingTiming {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+PendingTiming& pending_timing();
+
+template <typename... Params, typename... Args>
+inline hipError_t launch_kernel(void (*k)(Params...), dim3 grid, dim3 block, hipStream_t s,
+                                Args... args) {
+  PendingTiming& t = pending_timing();
+  if (t.start) {
+    const hipEvent_t a = t.start, b = t.stop;
+    t.start = t.stop = nullptr;
+    hipExtLaunchKernelGGL(k, grid, block, 0, s, a, b, 0, static_cast<Params>(args)...);
+  } else {
+    hipLaunchKernelGGL(k, grid, block, 0, s, static_cast<Params>(args)...);
+  }
+  return hipGetLastError();
+}
 
 constexpr int kBlock = 64;     // weights per first-level absmax
 constexpr int kDqBlock = 256;  // first-level constants per second-level scale
@@ -78,6 +102,12 @@ __device__ __forceinline__ uint32_t nf4_code(float x, const NF4Tables& t) {
 
 __host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Reconstructed block constant b: one fused multiply-add, q * S + mean.
+__device__ __forceinline__ float absmax_recon(const int8_t* q, const float* scale, float mu,
+                                              int64_t b) {
+  return __builtin_fmaf((float)q[b], scale[b / kDqBlock], mu);
+}
+
 // ---------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  All pointers are device.
 
@@ -89,22 +119,79 @@ hipError_t launch_dequant(const uint8_t* codes, const int8_t* q, const float* sc
                           const float* mean, int64_t n, int out_bf16, void* out, hipStream_t s);
 hipError_t launch_absmax_recon(const int8_t* q, const float* scale, const float* mean, int64_t nb,
                                float* out, hipStream_t s);
-// Reconstructed constants laid out [K/64][N] (block column major) for the GEMMs.
-hipError_t launch_absmax_recon_t(const int8_t* q, const float* scale, const float* mean,
-                                 int64_t N, int64_t K, float* out, hipStream_t s);
 
-// P = T . U^T over the inner dim kin: T [M, kin] (row stride ldt), U [r, kin]
-// (row stride ldu).  Outputs (each nullable):
+// ------------------------------------------------ side-path job launches
+// Several small independent steps share one launch (each is a few
+// microseconds of work; separate launches would cost more than the work).
+
+// Reconstructed constants laid out [K/64][N]: out[kb * N + n] = â of block
+// (n, kb).
+struct ReconJob {
+  const int8_t* q;
+  const float* scale;
+  const float* mean;
+  int64_t N, KB;
+  float* out;
+};
+// bf16 transpose [rows, cols] -> [cols, ldo], zero for i in [rows, ldo)
+struct TransposeJob {
+  const uint16_t* in;
+  int64_t rows, cols;
+  uint16_t* out;
+  int64_t ldo;
+};
+// Skinny product P = T . U^T over the inner dim kin: T [M, kin] (row stride
+// ldt), U [r, kin] (row stride ldu).  The inner dim is cut into `ks` slices
+// whose float32 partials [ks][M][rpad] go to `part`; the finish step adds
+// them in slice order and writes (each output nullable)
 //   out_s  bf16(scale * P) [M, r32]   (zero columns r..r32)
 //   out    bf16(P)         [M, r]
 //   out_t  bf16(P)^T       [r, ldo_t] (zero for m in [M, ldo_t))
-hipError_t launch_skinny_nt(const uint16_t* T, int64_t M, int64_t kin, int64_t ldt,
-                            const uint16_t* U, int r, int64_t ldu, float scale,
-                            uint16_t* out_s, int r32, uint16_t* out, uint16_t* out_t,
-                            int64_t ldo_t, hipStream_t s);
-// bf16 transpose [rows, cols] -> [cols, ldo] with zero padding to ldo
-hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
-                                 int64_t ldo, hipStream_t s);
+struct SkinnyJob {
+  const uint16_t* T;
+  int64_t kin, ldt;
+  const uint16_t* U;
+  int64_t ldu;
+  int ks;
+  int64_t kslice;
+  float* part;
+  float scale;
+  uint16_t* out_s;
+  uint16_t* out;
+  uint16_t* out_t;
+  int64_t ldo_t;
+};
+// Padded rank of the partial rows (16, 32, 64 or 128).
+int skinny_rpad(int r);
+int skinny_slices(int64_t M, int64_t kin);
+// Floats of `part` a job with these sizes needs.
+size_t skinny_part_floats(int64_t M, int64_t kin, int r);
+// Fills ks / kslice of each job from its kin.
+void skinny_plan(SkinnyJob* j, int64_t M);
+// Slice launch (jobs + optional recon), then the finish launch.
+hipError_t launch_skinny(const SkinnyJob* jobs, int njobs, int64_t M, int r, int r32,
+                         const ReconJob* recon, hipStream_t s);
+// Up to two transposes and a recon in one launch.
+hipError_t launch_prep(const TransposeJob* t, int nt, const ReconJob* recon, hipStream_t s);
+
+// Adapter gradient: out = scale * sum_m T[m][p] U[j][m], T [M, P] (row stride
+// P), U [r, ldu] (zero for m in [M, ldu)).  Token range cut into `splits`
+// slices with float32 partials [splits][P][r]; out is [r][P] when
+// `transposed`, else [P][r].
+struct GradJob {
+  const uint16_t* T;
+  int64_t P;
+  const uint16_t* U;
+  int64_t ldu;
+  int splits;
+  float* partial;
+  float scale;
+  int transposed;
+  float* out;
+};
+int lora_grad_splits(int64_t M, int64_t P);
+// Both jobs' partial launch, then both reductions.
+hipError_t launch_lora_grads(const GradJob* jobs, int njobs, int64_t M, int r, hipStream_t s);
 
 // The GEMMs split their inner loop into `splits` slices (one workgroup per
 // tile and slice) when the output tiles alone cannot fill the chip; with
@@ -121,15 +208,6 @@ hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t N, const uint8_
                           int r, int r32, uint16_t* dX, int splits, float* part, hipStream_t s);
 hipError_t launch_split_reduce(const float* part, int splits, int64_t count, uint16_t* out,
                                hipStream_t s);
-
-// partial[split][p][j] = sum over split's m of T[m][p] * U[j][m];  T [M, P]
-// (row stride P), U [r, ldu] with zero padding for m in [M, ldu).
-int lora_grad_splits(int64_t M, int64_t P);
-hipError_t launch_lora_grad(const uint16_t* T, int64_t M, int64_t P, const uint16_t* U, int r,
-                            int64_t ldu, int splits, float* partial, hipStream_t s);
-// out = scale * sum_split partial; transposed: out[j][p] else out[p][j]
-hipError_t launch_lora_grad_reduce(const float* partial, int splits, int64_t P, int r,
-                                   float scale, int transposed, float* out, hipStream_t s);
 
 // decode path (M <= 16)
 int gemv_splits(int64_t N, int64_t K);

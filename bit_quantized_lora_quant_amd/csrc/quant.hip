@@ -139,9 +139,6 @@ __global__ __launch_bounds__(kThreads) void k_dq_blocks(const float* __restrict_
 }
 
 // ------------------------------------------------------------- dequantise
-__device__ __forceinline__ float recon(const int8_t* q, const float* scale, float mu, int64_t b) {
-  return __builtin_fmaf((float)q[b], scale[b / kDqBlock], mu);
-}
 
 // One thread per 8 weights (one 32-bit word of codes, all inside one block).
 template <bool BF16>
@@ -157,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_nf4(const uint8_t* __restr
   const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int64_t e0 = g * 8;
   if (e0 >= n) return;
-  const float a = recon(q, scale, *mean, e0 / kBlock);
+  const float a = absmax_recon(q, scale, *mean, e0 / kBlock);
   const bool full = e0 + 8 <= n;
   uint32_t c;
   if (full) {
@@ -195,21 +192,12 @@ __global__ __launch_bounds__(kThreads) void k_absmax_recon(const int8_t* __restr
                                                            const float* __restrict__ mean,
                                                            int64_t nb, float* __restrict__ out) {
   const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (b < nb) out[b] = recon(q, scale, *mean, b);
+  if (b < nb) out[b] = absmax_recon(q, scale, *mean, b);
 }
 
 // Constants rebuilt into [K/64][N]: out[kb * N + n] is the constant of row n,
 // column block kb (block index n * K/64 + kb).  Threads run along n so the
 // stores are contiguous.
-__global__ __launch_bounds__(kThreads) void k_absmax_recon_t(const int8_t* __restrict__ q,
-                                                             const float* __restrict__ scale,
-                                                             const float* __restrict__ mean,
-                                                             int64_t N, int64_t KB,
-                                                             float* __restrict__ out) {
-  const int64_t n = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t kb = blockIdx.y;
-  if (n < N) out[kb * N + n] = recon(q, scale, *mean, n * KB + kb);
-}
 
 }  // namespace
 
@@ -217,7 +205,7 @@ hipError_t launch_quant_absmax(const float* w, int64_t n, uint8_t* codes, float*
                                hipStream_t s) {
   const int64_t threads = ceil_div(n, 8);
   const int64_t grid = ceil_div(threads, kThreads);
-  hipLaunchKernelGGL(k_quant_absmax_nf4, dim3((unsigned)grid), dim3(kThreads), 0, s, w, n,
+  launch_kernel(k_quant_absmax_nf4, dim3((unsigned)grid), dim3(kThreads), s, w, n,
                      host_tables(), codes, absmax);
   return hipGetLastError();
 }
@@ -247,10 +235,10 @@ hipError_t launch_dequant(const uint8_t* codes, const int8_t* q, const float* sc
                           const float* mean, int64_t n, int out_bf16, void* out, hipStream_t s) {
   const int64_t grid = ceil_div(ceil_div(n, 8), kThreads);
   if (out_bf16)
-    hipLaunchKernelGGL(k_dequant_nf4<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, codes, q,
+    launch_kernel(k_dequant_nf4<true>, dim3((unsigned)grid), dim3(kThreads), s, codes, q,
                        scale, mean, n, host_tables(), out);
   else
-    hipLaunchKernelGGL(k_dequant_nf4<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, codes, q,
+    launch_kernel(k_dequant_nf4<false>, dim3((unsigned)grid), dim3(kThreads), s, codes, q,
                        scale, mean, n, host_tables(), out);
   return hipGetLastError();
 }
@@ -262,12 +250,5 @@ hipError_t launch_absmax_recon(const int8_t* q, const float* scale, const float*
   return hipGetLastError();
 }
 
-hipError_t launch_absmax_recon_t(const int8_t* q, const float* scale, const float* mean,
-                                 int64_t N, int64_t K, float* out, hipStream_t s) {
-  const int64_t KB = K / kBlock;
-  hipLaunchKernelGGL(k_absmax_recon_t, dim3((unsigned)ceil_div(N, kThreads), (unsigned)KB),
-                     dim3(kThreads), 0, s, q, scale, mean, N, KB, out);
-  return hipGetLastError();
-}
 
 }  // namespace qnf4

@@ -160,9 +160,10 @@ qlora_status qlora_linear_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
 /* ------------------------------------------------------------------------
  * Kernel timing (benchmark instrumentation; not part of the method).
  * Between qlora_trace_begin and qlora_trace_end, every launch of a kernel whose
- * bit is set in `kernel_mask` (1 << qlora_kernel) is bracketed by a pair of HIP
- * events recorded on the launch's stream, for at most `capacity` launches per
- * kernel.  qlora_trace_end waits for those events (host synchronisation on
+ * bit is set in `kernel_mask` (1 << qlora_kernel) records its own start and end
+ * into a pair of HIP events (hipExtLaunchKernel: the dispatch itself takes the
+ * timestamps, so no extra packets sit between kernels), for at most `capacity`
+ * launches per kernel.  qlora_trace_end waits for those events (host synchronisation on
  * them only), writes the number of timed launches and their summed duration in
  * milliseconds into launches[QLORA_KERNEL_COUNT] / total_ms[QLORA_KERNEL_COUNT],
  * and releases the events.  Process-global state: not for concurrent use from
