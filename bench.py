@@ -37,7 +37,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", choices=["all", "none"], default="all")
+    ap.add_argument("--legs", default="all",
+                    help="all, none, or a comma list of quant, decode, stack65b")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run 3 plain device-to-device copies of MIB MiB (the known-size "
@@ -81,6 +82,31 @@ def traffic_for(kernel):
     if not t or t.get("source_sha") != src_hash(*t.get("sources", [])):
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def graph_of(torch, fn):
+    """Capture the launches `fn` makes (on torch's current stream, which the
+    library enqueues on) into a HIP graph; one eager run first, off-capture."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def timed(torch, fn, reps):
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / reps
 
 
 # ---------------------------------------------------------------- headline
@@ -227,29 +253,30 @@ def leg_quant_dequant(q, torch, workloads, passes=3):
 
     quant_pass(); deq_pass()
     torch.cuda.synchronize()
+    # eager passes, kernel durations traced
     q.qlora_trace_begin(["quantize", "dequant"], capacity=len(specs) * passes + 4)
-    t0 = time.perf_counter()
-    for _ in range(passes):
-        quant_pass()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for _ in range(passes):
-        deq_pass()
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
+    tq_eager = timed(torch, quant_pass, passes)
+    td_eager = timed(torch, deq_pass, passes)
     tr = q.qlora_trace_end()
+    # the same passes replayed from HIP graphs: one host call per pass, so the
+    # many small tensors do not leave the GPU waiting on the host
+    gq, gd = graph_of(torch, quant_pass), graph_of(torch, deq_pass)
+    tq = timed(torch, gq.replay, passes)
+    td = timed(torch, gd.replay, passes)
+    del gq, gd
     nbytes = sum(Q.nbytes() for Q in Qs)
     bpp = 8.0 * nbytes / params
-    tq, td = (t1 - t0) / passes, (t2 - t1) / passes
     # algorithmic bytes: quantise reads 4 B and writes the 4.127-bit state;
     # dequantise reads the state and writes 2 B (bf16)
     qbytes = 4 * params + nbytes
     dbytes = nbytes + 2 * params
     res = {"params": params, "bits_per_param": round(bpp, 5),
            "quantize": {"ms": round(tq * 1e3, 3), "GB/s": round(qbytes / tq / 1e9, 1),
-                        "frac_hbm": round(qbytes / tq / 1e9 / PEAK_HBM_GBS, 4)},
+                        "frac_hbm": round(qbytes / tq / 1e9 / PEAK_HBM_GBS, 4),
+                        "launch": "hip graph", "eager_ms": round(tq_eager * 1e3, 3)},
            "dequantize_bf16": {"ms": round(td * 1e3, 3), "GB/s": round(dbytes / td / 1e9, 1),
-                               "frac_hbm": round(dbytes / td / 1e9 / PEAK_HBM_GBS, 4)}}
+                               "frac_hbm": round(dbytes / td / 1e9 / PEAK_HBM_GBS, 4),
+                               "launch": "hip graph", "eager_ms": round(td_eager * 1e3, 3)}}
     for name, (n, ms) in tr.items():
         kb = (4 * params + params / 2) if name == "quantize" else dbytes
         res[name + "_kernel"] = {"launches": n, "avg_us": round(ms / n * 1e3, 2),
@@ -298,16 +325,17 @@ def leg_decode(q, torch, workloads, steps=5):
         step()
         torch.cuda.synchronize()
         q.qlora_trace_begin(["gemv"], capacity=len(lin) * steps + 4)
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            step()
-        torch.cuda.synchronize()
-        sec = (time.perf_counter() - t0) / steps
+        sec_eager = timed(torch, step, steps)
         tr = q.qlora_trace_end()
+        # the 560 calls of a token step replayed from one HIP graph
+        gstep = graph_of(torch, step)
+        sec = timed(torch, gstep.replay, steps)
+        del gstep
         nb = sum(Q.nbytes() + 2 * r * (K + N) + 2 * M * (K + N) for Q, K, N in lin)
         code_bytes = sum(Q.nbytes() for Q, _, _ in lin)
         ent = {"ms_per_token_step": round(sec * 1e3, 3), "tokens/s": round(M / sec, 1),
-               "GB/s": round(nb / sec / 1e9, 1), "frac_hbm": round(nb / sec / 1e9 / PEAK_HBM_GBS, 4)}
+               "GB/s": round(nb / sec / 1e9, 1), "frac_hbm": round(nb / sec / 1e9 / PEAK_HBM_GBS, 4),
+               "launch": "hip graph", "eager_ms_per_token_step": round(sec_eager * 1e3, 3)}
         if "gemv" in tr:
             n, ms = tr["gemv"]
             ent["gemv_kernel"] = {"launches": n, "avg_us": round(ms / n * 1e3, 2),
@@ -399,9 +427,13 @@ def main():
     del layers, host_w
     torch.cuda.empty_cache()
     legs = {}
-    if args.legs == "all":
+    want = {"quant", "decode", "stack65b"} if args.legs == "all" else (
+        set() if args.legs == "none" else set(args.legs.split(",")))
+    if "quant" in want:
         legs["llama8b_weight_set_quant_dequant"] = leg_quant_dequant(q, torch, workloads)
+    if "decode" in want:
         legs["llama70b_decode_gemv"] = leg_decode(q, torch, workloads)
+    if "stack65b" in want:
         legs["llama65b_80_layer_stack"] = leg_65b_stack(q, torch, workloads)
     tokens_s = head["tokens"] / head["sec"]
     tflops = head["flops"] / head["sec"] / 1e12

@@ -16,7 +16,11 @@ namespace qnf4 {
 namespace {
 
 constexpr int kSkStep = 128;    // inner indices per wave step (4 lane groups x 32)
-constexpr int kSkWaves = 8;     // waves per skinny workgroup (512 threads)
+constexpr int kSkWaves = 8;     // waves per skinny workgroup at ranks above 16
+// rank <= 16 keeps few registers per lane: 16 waves (1024 threads) put twice
+// the loads in flight per CU
+template <int RT>
+constexpr int sk_waves() { return RT == 1 ? 16 : kSkWaves; }
 
 __device__ __forceinline__ uint4 load8_bf16(const uint16_t* __restrict__ p, int64_t idx,
                                             int64_t limit, bool vec) {
@@ -54,7 +58,8 @@ __device__ __forceinline__ void recon_elems(const ReconJob& J, int64_t b) {
 template <int RT>
 __device__ __forceinline__ void skinny_slice(const SkinnyJob& J, int64_t M, int r, int r32,
                                              int64_t b) {
-  __shared__ float red[kSkWaves][RT][4][64];
+  constexpr int W = sk_waves<RT>();
+  __shared__ float red[W][RT][4][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int j16 = lane & 15, g = lane >> 4;
@@ -106,7 +111,7 @@ __device__ __forceinline__ void skinny_slice(const SkinnyJob& J, int64_t M, int 
       }
     }
   };
-  constexpr int64_t stride = (int64_t)kSkWaves * kSkStep;
+  constexpr int64_t stride = (int64_t)W * kSkStep;
   int64_t k = kbeg + (int64_t)wv * kSkStep;
   auto mfmas = [&](const uint4 (&a)[4], const uint4 (&bv)[RT][4]) {
 #pragma unroll
@@ -150,7 +155,7 @@ __device__ __forceinline__ void skinny_slice(const SkinnyJob& J, int64_t M, int 
     for (int v = 0; v < 4; ++v) {
       float sum = red[0][jt][v][lane];
 #pragma unroll
-      for (int w = 1; w < kSkWaves; ++w) sum += red[w][jt][v][lane];
+      for (int w = 1; w < W; ++w) sum += red[w][jt][v][lane];
       const int64_t m = m0 + 4 * g + v;
       const int j = jt * 16 + j16;
       if (J.ks > 1) {
@@ -184,7 +189,7 @@ __device__ __forceinline__ int64_t skinny_blocks(const SkinnyJob& J, int64_t M) 
 }
 
 template <int RT>
-__global__ __launch_bounds__(512) void k_skinny_slices(SkinnyJob j0, SkinnyJob j1, int nj,
+__global__ __launch_bounds__(sk_waves<RT>() * 64) void k_skinny_slices(SkinnyJob j0, SkinnyJob j1, int nj,
                                                        int64_t M, int r, int r32, ReconJob rc,
                                                        int has_rc) {
   int64_t b = blockIdx.x;
@@ -412,9 +417,9 @@ hipError_t skinny_rt(const SkinnyJob* jobs, int nj, int64_t M, int r, int r32, c
                      hipStream_t s) {
   int64_t blocks = 0;
   for (int i = 0; i < nj; ++i) blocks += ceil_div(skinny_rows(jobs[i], M), 16) * jobs[i].ks;
-  blocks += rc ? ceil_div(rc->N * rc->KB, kSkWaves * 64) : 0;
+  blocks += rc ? ceil_div(rc->N * rc->KB, sk_waves<RT>() * 64) : 0;
   const ReconJob none{};
-  hipLaunchKernelGGL(k_skinny_slices<RT>, dim3((unsigned)blocks), dim3(kSkWaves * 64), 0, s,
+  hipLaunchKernelGGL(k_skinny_slices<RT>, dim3((unsigned)blocks), dim3(sk_waves<RT>() * 64), 0, s,
                      jobs[0], nj > 1 ? jobs[1] : jobs[0], nj, M, r, r32, rc ? *rc : none,
                      rc ? 1 : 0);
   return hipGetLastError();

@@ -47,6 +47,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 struct NF4Tables {
   float level[16];
   float thresh[15];
+  int bucket_ok;   // the thresholds suit the quantiser's 256-bucket search
 };
 
 // Host-side tables, built once from the normal quantile function.
@@ -77,6 +78,7 @@ __device__ __forceinline__ float dpp_f32(float v) {
 constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // reverse each group of 8 lanes
+constexpr int kDppRowMirror = 0x140;  // reverse each row of 16 lanes
 
 // max over each aligned group of 8 lanes, result in all 8
 __device__ __forceinline__ float group8_max(float v) {
@@ -84,20 +86,6 @@ __device__ __forceinline__ float group8_max(float v) {
   v = fmaxf(v, dpp_f32<kDppQuadXor2>(v));
   v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
   return v;
-}
-
-// Nearest-level index of x in [-1, 1] by a branch-free binary search over
-// the 15 thresholds (4 compares, selects on uniform values).
-__device__ __forceinline__ uint32_t nf4_code(float x, const NF4Tables& t) {
-  const bool b3 = x > t.thresh[7];
-  const float t2 = b3 ? t.thresh[11] : t.thresh[3];
-  const bool b2 = x > t2;
-  const float t1 = b3 ? (b2 ? t.thresh[13] : t.thresh[9]) : (b2 ? t.thresh[5] : t.thresh[1]);
-  const bool b1 = x > t1;
-  const float t0 = b3 ? (b2 ? (b1 ? t.thresh[14] : t.thresh[12]) : (b1 ? t.thresh[10] : t.thresh[8]))
-                      : (b2 ? (b1 ? t.thresh[6] : t.thresh[4]) : (b1 ? t.thresh[2] : t.thresh[0]));
-  const bool b0 = x > t0;
-  return (b3 ? 8u : 0u) | (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
 }
 
 __host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -17,46 +17,114 @@ namespace {
 constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------- quantise
-// One thread per 8 consecutive weights, 8 threads per 64-block (an aligned
-// group of 8 lanes), so the block absmax is three DPP max steps.  Loads are
-// two 16-byte vectors per thread; the 8 codes leave as one 32-bit store.
+// A wave takes 1024-weight chunks (grid-stride).  In load i (0..3) lane l
+// reads the float4 at chunk + 256 i + 4 l, so each load instruction covers 1
+// KB contiguously; the 16 lanes of a DPP row then hold exactly one 64-block,
+// whose absmax is four DPP max steps.  The 4 codes of a lane leave as one
+// 16-bit store (128 contiguous bytes per wave).
+constexpr int kQChunk = 1024;
+
+// Nearest-level code of x in [-1, 1] = number of thresholds below x, found
+// through 256 equal buckets of [-1, 1]: bucket b holds the count of
+// thresholds under its interval and the one threshold inside it (+inf if
+// none), so the code is base + (x > thr).  Built per workgroup in LDS (one
+// entry per thread) from the thresholds in the argument segment.
+struct Bucket {
+  uint32_t base;
+  float thr;
+};
+
+__device__ __forceinline__ void build_buckets(Bucket* lds, const NF4Tables& tab) {
+  const int b = threadIdx.x;                 // kThreads == 256 buckets
+  const float lo = (float)b * (1.0f / 128.0f) - 1.0f;          // exact
+  const float hi = (float)(b + 1) * (1.0f / 128.0f) - 1.0f;    // exact
+  uint32_t base = 0;
+  float thr = __builtin_inff();
+#pragma unroll
+  for (int j = 0; j < 15; ++j) {
+    const float t = tab.thresh[j];
+    base += t < lo ? 1u : 0u;
+    if (t >= lo && t < hi) thr = t;
+  }
+  lds[b] = Bucket{base, thr};
+}
+
+__device__ __forceinline__ uint32_t nf4_code(float x, const Bucket* lds) {
+  // 128 x is exact, so t is 128 x + 128 rounded once; x in [-1, 1] gives
+  // t in [0, 256]
+  const float t = __builtin_fmaf(x, 128.0f, 128.0f);
+  int b = (int)t;
+  b = b < 255 ? b : 255;
+  const Bucket e = lds[b];
+  return e.base + (x > e.thr ? 1u : 0u);
+}
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
+  return v;
+}
+
 __global__ __launch_bounds__(kThreads) void k_quant_absmax_nf4(const float* __restrict__ w,
                                                                int64_t n, NF4Tables tab,
                                                                uint8_t* __restrict__ codes,
                                                                float* __restrict__ absmax) {
-  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t e0 = g * 8;
-  float v[8];
-  if (e0 + 8 <= n) {
-    const float4 a = *reinterpret_cast<const float4*>(w + e0);
-    const float4 b = *reinterpret_cast<const float4*>(w + e0 + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
+  __shared__ Bucket buckets[256];
+  build_buckets(buckets, tab);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
+  const int64_t nchunks = ceil_div(n, kQChunk);
+  for (int64_t c = wave; c < nchunks; c += nwaves) {
+    const int64_t base = c * kQChunk;
+    const bool full = base + kQChunk <= n;
+    float v[4][4];
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = (e0 + i < n) ? w[e0 + i] : 0.0f;
-  }
-  float m = 0.0f;
+      for (int i = 0; i < 4; ++i) {
+        const float4 t = *reinterpret_cast<const float4*>(w + base + 256 * i + 4 * lane);
+        v[i][0] = t.x; v[i][1] = t.y; v[i][2] = t.z; v[i][3] = t.w;
+      }
+    } else {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-  const float a = group8_max(m);
-  const int64_t blk = g >> 3;
-  if ((threadIdx.x & 7) == 0 && blk * kBlock < n) absmax[blk] = a;
-  if (e0 >= n) return;
-  uint32_t packed = 0;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float x = (a == 0.0f) ? 0.0f : v[i] / a;
-    packed |= nf4_code(x, tab) << (4 * i);
-  }
-  if (e0 + 8 <= n) {
-    *reinterpret_cast<uint32_t*>(codes + (e0 >> 1)) = packed;
-  } else {
-    const int64_t cnt = n - e0;            // 1..7 elements
-    for (int64_t i = 0; i < (cnt + 1) / 2; ++i) {
-      uint8_t byte = (uint8_t)(packed >> (8 * i));
-      if (2 * i + 1 >= cnt) byte &= 0x0F;   // missing odd element: high nibble 0
-      codes[(e0 >> 1) + i] = byte;
+        for (int e = 0; e < 4; ++e) {
+          const int64_t idx = base + 256 * i + 4 * lane + e;
+          v[i][e] = idx < n ? w[idx] : 0.0f;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float m = fmaxf(fmaxf(fabsf(v[i][0]), fabsf(v[i][1])), fmaxf(fabsf(v[i][2]), fabsf(v[i][3])));
+      const float a = row16_max(m);
+      const int64_t e0 = base + 256 * i + 4 * lane;          // first element of this lane
+      const int64_t blk = e0 / kBlock;
+      if ((lane & 15) == 0 && e0 < n) absmax[blk] = a;
+      uint32_t packed = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = (a == 0.0f) ? 0.0f : v[i][e] / a;
+        packed |= nf4_code(x, buckets) << (4 * e);
+      }
+      if (full) {
+        *reinterpret_cast<uint16_t*>(codes + (e0 >> 1)) = (uint16_t)packed;
+      } else {
+        // bytes holding elements (e0, e0+1) and (e0+2, e0+3); a missing odd
+        // element leaves its high nibble 0
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int64_t el = e0 + 2 * k;
+          if (el < n) {
+            uint8_t byte = (uint8_t)(packed >> (8 * k));
+            if (el + 1 >= n) byte &= 0x0F;
+            codes[el >> 1] = byte;
+          }
+        }
+      }
     }
   }
 }
@@ -140,7 +208,12 @@ __global__ __launch_bounds__(kThreads) void k_dq_blocks(const float* __restrict_
 
 // ------------------------------------------------------------- dequantise
 
-// One thread per 8 weights (one 32-bit word of codes, all inside one block).
+// A wave takes 2048-weight chunks (grid-stride): in sub-step i (0..3) lane l
+// rebuilds the 8 weights at chunk + 512 i + 8 l from one 32-bit word of codes
+// (256 contiguous bytes per load instruction, 1 KB of bf16 per store), with
+// all four code loads of a chunk in flight together.
+constexpr int kDqChunk = 2048;
+
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_dequant_nf4(const uint8_t* __restrict__ codes,
                                                           const int8_t* __restrict__ q,
@@ -151,38 +224,57 @@ __global__ __launch_bounds__(kThreads) void k_dequant_nf4(const uint8_t* __restr
   __shared__ float lvl[16];
   if (threadIdx.x < 16) lvl[threadIdx.x] = tab.level[threadIdx.x];
   __syncthreads();
-  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t e0 = g * 8;
-  if (e0 >= n) return;
-  const float a = absmax_recon(q, scale, *mean, e0 / kBlock);
-  const bool full = e0 + 8 <= n;
-  uint32_t c;
-  if (full) {
-    c = *reinterpret_cast<const uint32_t*>(codes + (e0 >> 1));
-  } else {
-    c = 0;
-    for (int64_t i = 0; i < (n - e0 + 1) / 2; ++i) c |= (uint32_t)codes[(e0 >> 1) + i] << (8 * i);
-  }
-  float v[8];
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
+  const int64_t nchunks = ceil_div(n, kDqChunk);
+  const float mu = *mean;
+  for (int64_t c = wave; c < nchunks; c += nwaves) {
+    const int64_t base = c * kDqChunk;
+    const bool full = base + kDqChunk <= n;
+    uint32_t cw[4];
+    float a[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = lvl[(c >> (4 * i)) & 15u] * a;
-  if (BF16) {
-    uint16_t* o = reinterpret_cast<uint16_t*>(out) + e0;
-    if (full) {
-      uint4 p;
-      p.x = pack_bf16x2(v[0], v[1]); p.y = pack_bf16x2(v[2], v[3]);
-      p.z = pack_bf16x2(v[4], v[5]); p.w = pack_bf16x2(v[6], v[7]);
-      *reinterpret_cast<uint4*>(o) = p;
-    } else {
-      for (int64_t i = 0; i < n - e0; ++i) o[i] = (uint16_t)(pack_bf16x2(v[i], 0.0f) & 0xFFFF);
+    for (int i = 0; i < 4; ++i) {
+      const int64_t e0 = base + 512 * i + 8 * lane;
+      if (full) {
+        cw[i] = *reinterpret_cast<const uint32_t*>(codes + (e0 >> 1));
+      } else {
+        cw[i] = 0;
+        for (int64_t k = 0; k < 4; ++k)
+          if (e0 + 2 * k < n) cw[i] |= (uint32_t)codes[(e0 >> 1) + k] << (8 * k);
+      }
+      const int64_t b = (e0 < n ? e0 : n - 1) / kBlock;
+      a[i] = absmax_recon(q, scale, mu, b);
     }
-  } else {
-    float* o = reinterpret_cast<float*>(out) + e0;
-    if (full) {
-      *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
-      *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
-    } else {
-      for (int64_t i = 0; i < n - e0; ++i) o[i] = v[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t e0 = base + 512 * i + 8 * lane;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = lvl[(cw[i] >> (4 * e)) & 15u] * a[i];
+      if (full || e0 + 8 <= n) {
+        if (BF16) {
+          uint4 p;
+          p.x = pack_bf16x2(v[0], v[1]); p.y = pack_bf16x2(v[2], v[3]);
+          p.z = pack_bf16x2(v[4], v[5]); p.w = pack_bf16x2(v[6], v[7]);
+          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + e0) = p;
+        } else {
+          float* o = reinterpret_cast<float*>(out) + e0;
+          *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+          *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (e0 + e < n) {
+            if (BF16)
+              reinterpret_cast<uint16_t*>(out)[e0 + e] = (uint16_t)(pack_bf16x2(v[e], 0.0f) & 0xFFFF);
+            else
+              reinterpret_cast<float*>(out)[e0 + e] = v[e];
+          }
+        }
+      }
     }
   }
 }
@@ -201,13 +293,17 @@ __global__ __launch_bounds__(kThreads) void k_absmax_recon(const int8_t* __restr
 
 }  // namespace
 
+// Grid-stride launches: about 32 waves per CU, fewer for small tensors.
+static int64_t stream_grid(int64_t chunks) {
+  const int64_t waves = chunks < 8192 ? chunks : 8192;
+  return ceil_div(waves > 0 ? waves : 1, kThreads / 64);
+}
+
 hipError_t launch_quant_absmax(const float* w, int64_t n, uint8_t* codes, float* absmax,
                                hipStream_t s) {
-  const int64_t threads = ceil_div(n, 8);
-  const int64_t grid = ceil_div(threads, kThreads);
-  launch_kernel(k_quant_absmax_nf4, dim3((unsigned)grid), dim3(kThreads), s, w, n,
-                     host_tables(), codes, absmax);
-  return hipGetLastError();
+  if (!host_tables().bucket_ok) return hipErrorInvalidValue;
+  return launch_kernel(k_quant_absmax_nf4, dim3((unsigned)stream_grid(ceil_div(n, kQChunk))),
+                       dim3(kThreads), s, w, n, host_tables(), codes, absmax);
 }
 
 hipError_t launch_dq(const float* absmax, int64_t nb, int8_t* q, float* scale, float* mean,
@@ -233,14 +329,12 @@ hipError_t launch_dq(const float* absmax, int64_t nb, int8_t* q, float* scale, f
 
 hipError_t launch_dequant(const uint8_t* codes, const int8_t* q, const float* scale,
                           const float* mean, int64_t n, int out_bf16, void* out, hipStream_t s) {
-  const int64_t grid = ceil_div(ceil_div(n, 8), kThreads);
+  const dim3 grid((unsigned)stream_grid(ceil_div(n, kDqChunk)));
   if (out_bf16)
-    launch_kernel(k_dequant_nf4<true>, dim3((unsigned)grid), dim3(kThreads), s, codes, q,
-                       scale, mean, n, host_tables(), out);
-  else
-    launch_kernel(k_dequant_nf4<false>, dim3((unsigned)grid), dim3(kThreads), s, codes, q,
-                       scale, mean, n, host_tables(), out);
-  return hipGetLastError();
+    return launch_kernel(k_dequant_nf4<true>, grid, dim3(kThreads), s, codes, q, scale, mean, n,
+                         host_tables(), out);
+  return launch_kernel(k_dequant_nf4<false>, grid, dim3(kThreads), s, codes, q, scale, mean, n,
+                       host_tables(), out);
 }
 
 hipError_t launch_absmax_recon(const int8_t* q, const float* scale, const float* mean, int64_t nb,

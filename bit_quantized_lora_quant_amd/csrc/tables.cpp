@@ -54,6 +54,19 @@ NF4Tables build() {
     if ((double)f > m) f = std::nextafterf(f, -INFINITY);
     t.thresh[j] = f;
   }
+  // The quantiser finds codes through 256 buckets of [-1, 1] (bucket
+  // floor(128 x + 128)); that is exact when no threshold lies near a bucket
+  // edge (the bucket index is off by at most 2^-16 there) and no bucket holds
+  // two thresholds.
+  t.bucket_ok = 1;
+  int prev = -1;
+  for (int j = 0; j < 15; ++j) {
+    const double u = 128.0 * (double)t.thresh[j] + 128.0;
+    if (std::fabs(u - std::nearbyint(u)) < 1.0 / 1024.0) t.bucket_ok = 0;
+    const int b = (int)std::floor(u);
+    if (b == prev) t.bucket_ok = 0;
+    prev = b;
+  }
   return t;
 }
 
