@@ -58,6 +58,7 @@ struct LinearWs {
   int sf, sx;                 // split-K slices of the forward / dX GEMM
   size_t ahat_t, xas, gemv_part, bt, gs, gt, xat, part_a, part_b, gemm_part;
   size_t sk_k, sk_n;          // skinny-product slice partials (inner dim K / N)
+  size_t dec_xa;              // decode: down-projection slice partials
   size_t total;
 };
 
@@ -86,6 +87,9 @@ LinearWs linear_layout(int64_t M, int64_t N, int64_t K, int r) {
   w.gemm_part = off; off = align_up(off + gp * sizeof(float));
   w.sk_k = off;      off = align_up(off + skinny_part_floats(M, K, r) * sizeof(float));
   w.sk_n = off;      off = align_up(off + skinny_part_floats(M, N, r) * sizeof(float));
+  w.dec_xa = off;
+  if (M <= 16)
+    off = align_up(off + (size_t)decode_xa_slices(K) * M * skinny_rpad(r) * sizeof(float));
   w.total = off;
   return w;
 }
@@ -228,6 +232,17 @@ qlora_status qlora_linear_fwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
   if (!ws || ws_bytes < L.total || !aligned(ws, kAlign)) return QLORA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float scale = alpha / (float)r;
+  hipError_t e;
+  if (M <= 16) {
+    const NF4Ref w{W->codes, W->absmax_q, W->absmax_scale, W->absmax_mean};
+    float* part = at<float>(ws, L.gemv_part);
+    float* xa_part = at<float>(ws, L.dec_xa);
+    e = traced(QLORA_KERNEL_GEMV, s, [&] {
+      return launch_decode(X, M, K, w, N, A, B, r, scale, L.gemv_splits, part, xa_part, Y,
+                           XA_out, s);
+    });
+    return hip_status(e);
+  }
   float* ahat_t = at<float>(ws, L.ahat_t);
   uint16_t* xas = at<uint16_t>(ws, L.xas);
   // X.A^T -> bf16(s.XA) [M, r32] (GEMM tail) and bf16(XA) [M, r] (caller),
@@ -235,23 +250,15 @@ qlora_status qlora_linear_fwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
   SkinnyJob xa{X, K, K, A, K, 0, 0, at<float>(ws, L.sk_k), scale, xas, XA_out, nullptr, 0};
   skinny_plan(&xa, M);
   const ReconJob rc{W->absmax_q, W->absmax_scale, W->absmax_mean, N, K / kBlock, ahat_t};
-  hipError_t e = launch_skinny(&xa, 1, M, r, L.r32, &rc, s);
+  e = launch_skinny(&xa, 1, M, r, L.r32, &rc, s);
   if (e != hipSuccess) return QLORA_ERR_HIP;
-  if (M <= 16) {
-    float* part = at<float>(ws, L.gemv_part);
-    e = traced(QLORA_KERNEL_GEMV, s,
-               [&] { return launch_gemv(X, M, K, W->codes, N, ahat_t, L.gemv_splits, part, s); });
-    if (e != hipSuccess) return QLORA_ERR_HIP;
-    e = launch_gemv_finish(part, L.gemv_splits, M, N, xas, r, L.r32, B, Y, s);
-  } else {
-    float* part = at<float>(ws, L.gemm_part);
-    e = traced(QLORA_KERNEL_FWD_GEMM, s, [&] {
-      return launch_fwd_gemm(X, M, K, W->codes, N, ahat_t, xas, B, r, L.r32, Y, L.sf, part, s);
-    });
-    if (e == hipSuccess && L.sf > 1)
-      e = traced(QLORA_KERNEL_SPLIT_REDUCE, s,
-                 [&] { return launch_split_reduce(part, L.sf, M * N, Y, s); });
-  }
+  float* part = at<float>(ws, L.gemm_part);
+  e = traced(QLORA_KERNEL_FWD_GEMM, s, [&] {
+    return launch_fwd_gemm(X, M, K, W->codes, N, ahat_t, xas, B, r, L.r32, Y, L.sf, part, s);
+  });
+  if (e == hipSuccess && L.sf > 1)
+    e = traced(QLORA_KERNEL_SPLIT_REDUCE, s,
+               [&] { return launch_split_reduce(part, L.sf, M * N, Y, s); });
   return hip_status(e);
 }
 

@@ -1,118 +1,362 @@
 // Decode path (M <= 16 tokens): the forward streams the 4-bit weights once
-// and is bound by HBM bandwidth, not by the matrix cores.  Tokens are padded
-// to the 16 rows of one MFMA; each lane rebuilds bf16(level[code] * constant)
-// for 32 contiguous weights of one row per step, so every weight byte is read
-// once and dequantised once.  The inner dimension is split across
-// workgroups to put enough loads in flight; the float32 partial sums are
-// added in split order by a second small kernel, which also adds the LoRA
-// branch and rounds to bf16.
-#include "nf4_common.h"
+// and is bound by HBM bandwidth, not by the matrix cores.
+//
+// Two launches per call.  The first holds two kinds of workgroup:
+//  * LoRA down-projection slices: X . A^T over inner-index slices (first in
+//    the grid, so they start early and leave no tail);
+//  * weight streamers: 64 rows of W by at most 16 64-blocks (1024 inner
+//    indices).  A streamer issues all its code loads at once, stages its
+//    slice of X in LDS meanwhile, then per 64-block turns each lane's 16
+//    codes into bf16 levels through a 256-entry LDS table of level pairs
+//    (one lookup per code byte, no multiply); two MFMAs (tokens padded to
+//    16) give the block's dot products, and the block constant -- rebuilt in
+//    registers from its int8 code, the scale and the mean -- scales them as
+//    they are accumulated.  No dequantised weight and no constant table is
+//    written.
+// The second launch adds the float32 partials in split order, adds
+// bf16(s XA) . B^T and rounds to bf16.
+//
+// The per-block factoring computes sum_b a_b (sum_k x_k bf16(level_k)), where
+// the GEMMs compute sum_k x_k bf16(level_k a_b): both round each weight once
+// to bf16, and both stay inside the forward's tolerance.
+#include "skinny.h"
 
 namespace qnf4 {
 namespace {
 
-constexpr int kRowsPerWg = 64;   // 4 waves x 16 rows
-constexpr int kKStep = 128;      // inner indices per lane-group step (4 x 32)
+constexpr int kDecRows = 64;      // weight rows per streaming workgroup (4 waves x 16)
+constexpr int kDecBlocks = 16;    // 64-blocks per streaming workgroup (at most)
+constexpr int kDecXStride = kDecBlocks * 64 + 8;   // LDS row of X (bf16), padded
+constexpr int kXaWaves = 4;
 
-__device__ __forceinline__ uint4 dequant8(uint32_t c, float a, const float* lvl) {
+struct DecodeArgs {
+  const uint16_t* X;
+  int64_t M, K, N;
+  const uint8_t* codes;
+  const int8_t* q;
+  const float* scale;
+  const float* mean;
+  int splits;                   // 64-block ranges of kDecBlocks
+  float* partial;               // [splits][M][N]
+  int64_t xa_blocks;            // workgroups of X . A^T slices (first in the grid)
+  SkinnyJob xa;                 // X . A^T slices (partials only)
+};
+
+__device__ __forceinline__ void build_pairs(uint32_t* pairs, const NF4Tables& tab) {
+  // entry v: bf16(level[v & 15]) | bf16(level[v >> 4]) << 16 (256 threads)
+  const int v = threadIdx.x;
+  float lo = 0.f, hi = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    lo = (v & 15) == i ? tab.level[i] : lo;
+    hi = (v >> 4) == i ? tab.level[i] : hi;
+  }
+  pairs[v] = pack_bf16x2(lo, hi);
+}
+
+// 8 codes (one 32-bit word) -> 8 bf16 levels as an MFMA operand
+__device__ __forceinline__ uint4 levels8(uint32_t c, const uint32_t* pairs) {
   uint4 r;
-  r.x = pack_bf16x2(lvl[c & 15u] * a, lvl[(c >> 4) & 15u] * a);
-  r.y = pack_bf16x2(lvl[(c >> 8) & 15u] * a, lvl[(c >> 12) & 15u] * a);
-  r.z = pack_bf16x2(lvl[(c >> 16) & 15u] * a, lvl[(c >> 20) & 15u] * a);
-  r.w = pack_bf16x2(lvl[(c >> 24) & 15u] * a, lvl[(c >> 28) & 15u] * a);
+  r.x = pairs[c & 0xFFu];
+  r.y = pairs[(c >> 8) & 0xFFu];
+  r.z = pairs[(c >> 16) & 0xFFu];
+  r.w = pairs[c >> 24];
   return r;
 }
 
-// partial[split][m][n] = sum over the split's inner range of X[m][k] W'[n][k]
-__global__ __launch_bounds__(256) void k_qlora_gemv(const uint16_t* __restrict__ X, int64_t M,
-                                                    int64_t K, const uint8_t* __restrict__ codes,
-                                                    int64_t N, const float* __restrict__ ahat_t,
-                                                    NF4Tables tab, int64_t kchunk,
-                                                    float* __restrict__ partial) {
-  __shared__ float lvl[16];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int j16 = lane & 15, g = lane >> 4;
-  if (tid < 16) lvl[tid] = tab.level[tid];
-  __syncthreads();
-  const int64_t n = (int64_t)blockIdx.x * kRowsPerWg + 16 * wv + j16;
-  const int64_t nl = n < N ? n : N - 1;
-  const int split = blockIdx.y;
-  const int64_t kbeg = (int64_t)split * kchunk;
-  int64_t kend = kbeg + kchunk;
-  kend = kend < K ? kend : K;
-  const bool tok = j16 < M;                      // A operand row = token j16
-  const uint16_t* xrow = X + (int64_t)(tok ? j16 : 0) * K;
-  const uint8_t* crow = codes + nl * (K / 2);
+// v if keep (an all-ones mask), else 0: a value select the compiler cannot
+// turn into a select of load addresses
+__device__ __forceinline__ uint4 keep_if(uint4 v, uint32_t keep) {
+  return make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+}
 
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t k = kbeg; k < kend; k += kKStep) {
-    // this lane's 32 inner indices; a final half step (K % 128 == 64) leaves
-    // groups 2 and 3 idle, as zero operands (MFMA needs the whole wave)
-    const int64_t kk = k + 32 * g;
-    const bool in = kk < kend;
-    const uint4 c = in ? *reinterpret_cast<const uint4*>(crow + kk / 2) : make_uint4(0u, 0u, 0u, 0u);
-    const float a = in ? ahat_t[(kk / kBlock) * N + nl] : 0.f;
-    uint4 xa[4];
+__device__ __forceinline__ void decode_rows(const DecodeArgs& a, const uint32_t* pairs,
+                                            uint16_t* xs, int64_t b) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j16 = lane & 15, g = lane >> 4;
+  const int split = (int)(b % a.splits);
+  const int64_t n = (b / a.splits) * kDecRows + 16 * wv + j16;
+  const int64_t nl = n < a.N ? n : a.N - 1;
+  const int64_t KB = a.K / kBlock;
+  const int64_t kb0 = (int64_t)split * kDecBlocks;
+  const int nblk = (int)(KB - kb0 < kDecBlocks ? KB - kb0 : kDecBlocks);   // >= 1
+  const uint8_t* crow = a.codes + nl * (a.K / 2) + 32 * kb0 + 8 * g;
+  const int64_t qrow = nl * KB + kb0;
+  const float mu = *a.mean;
+  // Loads: constants, codes, then X, with no per-lane branch around them
+  // (indices past the range are clamped and the values ignored).
+  const bool grouped = (KB & 3) == 0;   // int8 constants four to a word
+  uint32_t qw[kDecBlocks / 4];
+  float sc[kDecBlocks / 4];
+  if (grouped) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      xa[s] = (tok && in) ? *reinterpret_cast<const uint4*>(xrow + kk + 8 * s)
-                          : make_uint4(0u, 0u, 0u, 0u);
-    acc = mfma16x16x32(xa[0], dequant8(c.x, a, lvl), acc);
-    acc = mfma16x16x32(xa[1], dequant8(c.y, a, lvl), acc);
-    acc = mfma16x16x32(xa[2], dequant8(c.z, a, lvl), acc);
-    acc = mfma16x16x32(xa[3], dequant8(c.w, a, lvl), acc);
+    for (int i = 0; i < kDecBlocks / 4; ++i) {
+      const int ib = 4 * i < nblk ? 4 * i : (nblk - 1) & ~3;
+      qw[i] = *reinterpret_cast<const uint32_t*>(a.q + qrow + ib);
+      sc[i] = a.scale[(qrow + ib) / kDqBlock];   // a word never crosses a 256-group
+    }
+  }
+  // all of this lane's codes: block i, bytes 8 g .. 8 g + 7
+  uint2 c[kDecBlocks];
+#pragma unroll
+  for (int i = 0; i < kDecBlocks; ++i)
+    c[i] = *reinterpret_cast<const uint2*>(crow + 32 * (i < nblk ? i : nblk - 1));
+  // X[m][64 kb0 .. 64 (kb0 + 16)) for LDS rows 0..M-1: 128 16-byte pieces
+  // per row (pieces past the range re-read the last valid one), at most 8 per
+  // thread, only as many rounds as the M rows need
+  const int64_t kx = 64 * kb0;
+  const int plim = 8 * nblk - 1;                 // last valid piece of a row
+  const int total = (int)a.M * 128;
+  const int rounds = (total + 255) >> 8;         // uniform
+  uint4 xv[8];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    if (it < rounds) {
+      int e = tid + 256 * it;
+      e = e < total ? e : total - 1;
+      const int m = e >> 7, q8 = e & 127;
+      xv[it] = *reinterpret_cast<const uint4*>(a.X + m * a.K + kx + 8 * (q8 < plim ? q8 : plim));
+    }
+  }
+  // keep every load above this point: the scheduler would otherwise sink each
+  // X load down to its LDS store and serialise their latencies
+  asm volatile("" ::: "memory");
+
+  // blocks past the range get a zero constant: they add exactly nothing, and
+  // the block loop below has no branch (so blocks interleave)
+  float ahat[kDecBlocks];
+  if (grouped) {
+#pragma unroll
+    for (int i = 0; i < kDecBlocks; ++i) {
+      const float v =
+          __builtin_fmaf((float)(int8_t)((qw[i / 4] >> (8 * (i & 3))) & 0xFFu), sc[i / 4], mu);
+      ahat[i] = i < nblk ? v : 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kDecBlocks; ++i) {
+      const float v = absmax_recon(a.q, a.scale, mu, qrow + (i < nblk ? i : nblk - 1));
+      ahat[i] = i < nblk ? v : 0.f;
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int e = tid + 256 * it;
+    if (it < rounds && e < total)
+      *reinterpret_cast<uint4*>(xs + (e >> 7) * kDecXStride + 8 * (e & 127)) = xv[it];
+  }
+  // row M stays zero: the padding token rows of the MFMA read it
+  for (int e = tid; e < kDecXStride / 8; e += 256)
+    *reinterpret_cast<uint4*>(xs + a.M * kDecXStride + 8 * e) = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+
+  const uint16_t* xrow = xs + (j16 < a.M ? j16 : a.M) * kDecXStride + 16 * g;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  // block i: lane group g holds inner indices 16 g .. 16 g + 15 (8 per MFMA)
+#pragma unroll
+  for (int i = 0; i < kDecBlocks; ++i) {
+    const uint4 x0 = *reinterpret_cast<const uint4*>(xrow + 64 * i);
+    const uint4 x1 = *reinterpret_cast<const uint4*>(xrow + 64 * i + 8);
+    f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+    t = mfma16x16x32(x0, levels8(c[i].x, pairs), t);
+    t = mfma16x16x32(x1, levels8(c[i].y, pairs), t);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(ahat[i], t[v], acc[v]);
   }
   // D[token 4g + v][row j16]
-  float* base = partial + (int64_t)split * M * N;
-  if (n < N) {
+  float* base = a.partial + (int64_t)split * a.M * a.N;
+  if (n < a.N) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int64_t m = 4 * g + v;
-      if (m < M) base[m * N + n] = acc[v];
+      if (m < a.M) base[m * a.N + n] = acc[v];
     }
   }
 }
 
-// Y[m][n] = bf16( sum_split partial + sum_j xas[m][j] * B[n][j] )
-__global__ __launch_bounds__(256) void k_gemv_finish(const float* __restrict__ partial,
-                                                     int splits, int64_t M, int64_t N,
-                                                     const uint16_t* __restrict__ xas, int r,
-                                                     int r32, const uint16_t* __restrict__ B,
-                                                     uint16_t* __restrict__ Y) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= M * N) return;
-  const int64_t m = idx / N, n = idx % N;
-  float s = 0.f;
-  for (int k = 0; k < splits; ++k) s += partial[(int64_t)k * M * N + idx];
-  float l = 0.f;
-  for (int j = 0; j < r; ++j) l = __builtin_fmaf(bf16_to_f32(xas[m * r32 + j]), bf16_to_f32(B[n * r + j]), l);
-  Y[idx] = (uint16_t)(pack_bf16x2(s + l, 0.f) & 0xFFFF);
+// LoRA down-projection slice `sl` (512 inner indices, one 128-wide step per
+// wave): partial[sl][m][j] = sum_k X[m][k] A[j][k], tokens as the 16 MFMA
+// rows.  One 16-column tile of A at a time keeps the registers of this
+// branch no higher than the streaming branch's.
+template <int RT>
+__device__ __forceinline__ void xa_slice(const DecodeArgs& a, int r, int64_t sl,
+                                         float (*red)[4][64]) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j16 = lane & 15, g = lane >> 4;
+  const int64_t K = a.K;
+  const int64_t k = sl * (kXaWaves * kSkStep) + (int64_t)wv * kSkStep;
+  const bool tok = j16 < a.M;
+  const uint32_t keep = tok ? 0xFFFFFFFFu : 0u;
+  const uint16_t* xrow = a.X + (int64_t)(tok ? j16 : 0) * K;
+  const uint16_t* A = a.xa.U;
+  f32x4_t acc[RT];
+#pragma unroll
+  for (int jt = 0; jt < RT; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (k < K) {
+    uint4 x[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      x[s] = keep_if(load8_bf16(xrow, k + 32 * s + 8 * g, K, true), keep);
+#pragma unroll
+    for (int jt = 0; jt < RT; ++jt) {
+      const int u = jt * 16 + j16;
+      uint4 bv[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        bv[s] = keep_if(load8_bf16(A + (int64_t)(u < r ? u : r - 1) * K, k + 32 * s + 8 * g, K, true),
+                        u < r ? 0xFFFFFFFFu : 0u);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc[jt] = mfma16x16x32(x[s], bv[s], acc[jt]);
+    }
+  }
+  // wave partials added in wave order, one 16-column tile at a time
+  float* part = a.xa.part + sl * a.M * (RT * 16);
+#pragma unroll
+  for (int jt = 0; jt < RT; ++jt) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wv][v][lane] = acc[jt][v];
+    __syncthreads();
+    if (wv == 0) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float sum = red[0][v][lane];
+#pragma unroll
+        for (int w = 1; w < kXaWaves; ++w) sum += red[w][v][lane];
+        const int64_t m = 4 * g + v;
+        if (m < a.M) part[m * (RT * 16) + jt * 16 + j16] = sum;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int RT>
+__global__ __launch_bounds__(256) void k_qlora_decode(DecodeArgs a, NF4Tables tab, int r) {
+  // one LDS arena (sized per launch) for either branch: [pairs 1 KB | X rows
+  // 0..M, row M zero] or the 4 KB of XA wave partials
+  extern __shared__ __attribute__((aligned(16))) uint8_t arena[];
+  const int64_t b = blockIdx.x;
+  if (b < a.xa_blocks) {
+    xa_slice<RT>(a, r, b, reinterpret_cast<float (*)[4][64]>(arena));
+  } else {
+    uint32_t* pairs = reinterpret_cast<uint32_t*>(arena);
+    uint16_t* xs = reinterpret_cast<uint16_t*>(arena + 256 * 4);
+    build_pairs(pairs, tab);
+    decode_rows(a, pairs, xs, b - a.xa_blocks);   // its barrier also covers the table
+  }
+}
+
+// Y[m][n] = bf16( sum_split partial + sum_j bf16(s XA[m][j]) B[n][j] ), with
+// XA the slice sum of the down-projection.  Workgroup (n block, token m):
+// first the r values of XA[m] (slices added in order, loads unrolled), then
+// one output per thread; the n block 0 workgroups also write bf16(XA).
+__global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__ partial,
+                                                       int splits, int64_t M, int64_t N,
+                                                       const float* __restrict__ xa_part,
+                                                       int ks, int rpad, int r, float scale,
+                                                       const uint16_t* __restrict__ B,
+                                                       uint16_t* __restrict__ Y,
+                                                       uint16_t* __restrict__ XA_out) {
+  __shared__ float xs[128];
+  const int64_t m = blockIdx.y;
+  const int t = threadIdx.x;
+  if (t < r) {
+    const float* src = xa_part + m * rpad + t;
+    const int64_t stride = M * rpad;
+    float v = src[0];
+    int k = 1;
+    for (; k + 8 <= ks; k += 8) {
+      float w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = src[(k + i) * stride];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v += w[i];
+    }
+    for (; k < ks; ++k) v += src[k * stride];
+    const uint32_t sb = pack_bf16x2(scale * v, 0.f) & 0xFFFFu;
+    xs[t] = __builtin_bit_cast(float, sb << 16);
+    if (blockIdx.x == 0 && XA_out) XA_out[m * r + t] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFF);
+  }
+  __syncthreads();
+  const int64_t n = (int64_t)blockIdx.x * 256 + t;
+  if (n >= N) return;
+  const float* src = partial + m * N + n;
+  const int64_t stride = M * N;
+  float y = src[0];
+  int k = 1;
+  for (; k + 8 <= splits; k += 8) {
+    float w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = src[(k + i) * stride];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y += w[i];
+  }
+  for (; k < splits; ++k) y += src[k * stride];
+  const uint16_t* brow = B + n * r;
+  if ((r & 7) == 0) {
+    // 16-byte loads of this row of B (rows are 16-byte aligned when r % 8 == 0)
+    for (int j0 = 0; j0 < r; j0 += 8) {
+      const uint4 bv = *reinterpret_cast<const uint4*>(brow + j0);
+      const uint32_t w[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        y = __builtin_fmaf(xs[j0 + e], bf16_to_f32((uint16_t)(w[e >> 1] >> (16 * (e & 1)))), y);
+    }
+  } else {
+    for (int j = 0; j < r; ++j) y = __builtin_fmaf(xs[j], bf16_to_f32(brow[j]), y);
+  }
+  Y[m * N + n] = (uint16_t)(pack_bf16x2(y, 0.f) & 0xFFFF);
+}
+
+template <int RT>
+hipError_t decode_rt(const DecodeArgs& a, int r, int64_t blocks, hipStream_t s) {
+  const size_t stream = 256 * 4 + (size_t)(a.M + 1) * kDecXStride * 2;
+  const size_t xa = (size_t)kXaWaves * 4 * 64 * 4;
+  return launch_kernel_lds(k_qlora_decode<RT>, dim3((unsigned)blocks), dim3(256),
+                           stream > xa ? stream : xa, s, a, host_tables(), r);
 }
 
 }  // namespace
 
 int gemv_splits(int64_t N, int64_t K) {
-  const int64_t groups = ceil_div(N, kRowsPerWg);
-  int64_t splits = ceil_div(1024, groups);
-  const int64_t maxs = K / 256 > 0 ? K / 256 : 1;
-  if (splits > maxs) splits = maxs;
-  if (splits < 1) splits = 1;
-  return (int)splits;
+  (void)N;
+  return (int)ceil_div(K / kBlock, kDecBlocks);   // 64-block ranges of kDecBlocks
 }
 
-hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, int64_t N,
-                       const float* ahat_t, int splits, float* partial, hipStream_t s) {
-  // split boundaries on 128 so each lane-group step stays inside one split
-  const int64_t kchunk = ceil_div(ceil_div(K, splits), kKStep) * kKStep;
-  return launch_kernel(k_qlora_gemv, dim3((unsigned)ceil_div(N, kRowsPerWg), (unsigned)splits),
-                       dim3(256), s, X, M, K, codes, N, ahat_t, host_tables(), kchunk, partial);
+int decode_xa_slices(int64_t K) {
+  // slices of 512 inner indices (one 128-wide step per wave)
+  return (int)ceil_div(K, (int64_t)kXaWaves * kSkStep);
 }
 
-hipError_t launch_gemv_finish(const float* partial, int splits, int64_t M, int64_t N,
-                              const uint16_t* xas, int r, int r32, const uint16_t* B, uint16_t* Y,
-                              hipStream_t s) {
-  hipLaunchKernelGGL(k_gemv_finish, dim3((unsigned)ceil_div(M * N, 256)), dim3(256), 0, s, partial,
-                     splits, M, N, xas, r, r32, B, Y);
+hipError_t launch_decode(const uint16_t* X, int64_t M, int64_t K, const NF4Ref& W, int64_t N,
+                         const uint16_t* A, const uint16_t* B, int r, float scale, int splits,
+                         float* partial, float* xa_part, uint16_t* Y, uint16_t* XA_out,
+                         hipStream_t s) {
+  const int64_t KB = K / kBlock;
+  DecodeArgs a{};
+  a.X = X; a.M = M; a.K = K; a.N = N;
+  a.codes = W.codes; a.q = W.q; a.scale = W.scale; a.mean = W.mean;
+  (void)KB;
+  a.splits = splits;
+  a.partial = partial;
+  const int rpad = skinny_rpad(r);
+  const int ks = decode_xa_slices(K);
+  a.xa_blocks = ks;                            // one row group of tokens (M <= 16)
+  a.xa = SkinnyJob{X, K, K, A, K, ks, (int64_t)kXaWaves * kSkStep, xa_part, scale,
+                   nullptr, nullptr, nullptr, 0, 1};
+  const int64_t blocks = ks + ceil_div(N, kDecRows) * splits;
+  hipError_t e;
+  switch (rpad) {
+    case 16: e = decode_rt<1>(a, r, blocks, s); break;
+    case 32: e = decode_rt<2>(a, r, blocks, s); break;
+    case 64: e = decode_rt<4>(a, r, blocks, s); break;
+    default: e = decode_rt<8>(a, r, blocks, s); break;
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_decode_finish, dim3((unsigned)ceil_div(N, 256), (unsigned)M), dim3(256), 0,
+                     s, partial, splits, M, N, xa_part, ks, rpad, r, scale, B, Y, XA_out);
   return hipGetLastError();
 }
 

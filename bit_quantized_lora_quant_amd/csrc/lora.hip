@@ -10,36 +10,16 @@
 // These steps stream one activation tensor each and are bound by HBM; they
 // are cut into enough workgroups to cover the chip, and independent small
 // steps share a launch.
-#include "nf4_common.h"
+#include "skinny.h"
 
 namespace qnf4 {
 namespace {
 
-constexpr int kSkStep = 128;    // inner indices per wave step (4 lane groups x 32)
 constexpr int kSkWaves = 8;     // waves per skinny workgroup at ranks above 16
 // rank <= 16 keeps few registers per lane: 16 waves (1024 threads) put twice
 // the loads in flight per CU
 template <int RT>
 constexpr int sk_waves() { return RT == 1 ? 16 : kSkWaves; }
-
-__device__ __forceinline__ uint4 load8_bf16(const uint16_t* __restrict__ p, int64_t idx,
-                                            int64_t limit, bool vec) {
-  // 8 consecutive bf16 at p[idx..idx+7]; entries at or past `limit` read 0
-  if (vec && idx + 8 <= limit) return *reinterpret_cast<const uint4*>(p + idx);
-  uint16_t e[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) e[q] = (idx + q < limit) ? p[idx + q] : (uint16_t)0;
-  uint4 v;
-  v.x = e[0] | ((uint32_t)e[1] << 16);
-  v.y = e[2] | ((uint32_t)e[3] << 16);
-  v.z = e[4] | ((uint32_t)e[5] << 16);
-  v.w = e[6] | ((uint32_t)e[7] << 16);
-  return v;
-}
-
-__device__ __forceinline__ uint16_t to_bf16(float v) {
-  return (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFF);
-}
 
 // One thread per element of [KB][N]: out[kb * N + n] = â(n * KB + kb).
 __device__ __forceinline__ void recon_elems(const ReconJob& J, int64_t b) {
@@ -49,135 +29,6 @@ __device__ __forceinline__ void recon_elems(const ReconJob& J, int64_t b) {
   J.out[e] = absmax_recon(J.q, J.scale, *J.mean, n * J.KB + kb);
 }
 
-
-// ------------------------------------------------------------ skinny NT
-// Workgroup (row group, slice): 16 rows of T, inner indices [kbeg, kend).
-// The 4 waves take interleaved 128-wide steps; lane (j16, g) reads the 32
-// contiguous inner indices 32g..32g+31 of a step from both operands (four
-// MFMA sub-steps).  Wave partials are added in wave order through LDS.
-template <int RT>
-__device__ __forceinline__ void skinny_slice(const SkinnyJob& J, int64_t M, int r, int r32,
-                                             int64_t b) {
-  constexpr int W = sk_waves<RT>();
-  __shared__ float red[W][RT][4][64];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int j16 = lane & 15, g = lane >> 4;
-  const int ks = (int)(b % J.ks);
-  const int64_t m0 = (b / J.ks) * 16;
-  int64_t mrow = m0 + j16;
-  mrow = mrow < M ? mrow : M - 1;
-  const int64_t kbeg = (int64_t)ks * J.kslice;
-  int64_t kend = kbeg + J.kslice;
-  kend = kend < J.kin ? kend : J.kin;
-  const bool tv = (J.ldt % 8) == 0;
-  const bool uv = (J.ldu % 8) == 0;
-  const uint16_t* trow = J.T + mrow * J.ldt;
-
-  f32x4_t acc[RT];
-#pragma unroll
-  for (int jt = 0; jt < RT; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // Operands of one step: sub-step s takes inner indices k + 32 s + 8 g ..
-  // + 7 from lane group g, so each load instruction reads 64 contiguous bytes
-  // per row.
-  auto load_step = [&](int64_t k, uint4 (&a)[4], uint4 (&bv)[RT][4]) {
-    if (tv && uv && k + kSkStep <= J.kin) {
-      // whole step in range (wave-uniform): plain vector loads; adapter rows
-      // past r are loaded clamped and zeroed by a select
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        a[s] = *reinterpret_cast<const uint4*>(trow + k + 32 * s + 8 * g);
-#pragma unroll
-      for (int jt = 0; jt < RT; ++jt) {
-        const int u = jt * 16 + j16;
-        const uint16_t* urow = J.U + (int64_t)(u < r ? u : r - 1) * J.ldu + k + 8 * g;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const uint4 v = *reinterpret_cast<const uint4*>(urow + 32 * s);
-          bv[jt][s] = u < r ? v : make_uint4(0u, 0u, 0u, 0u);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) a[s] = load8_bf16(trow, k + 32 * s + 8 * g, J.kin, tv);
-#pragma unroll
-      for (int jt = 0; jt < RT; ++jt) {
-        const int u = jt * 16 + j16;
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          bv[jt][s] = u < r ? load8_bf16(J.U + (int64_t)u * J.ldu, k + 32 * s + 8 * g, J.kin, uv)
-                            : make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-  };
-  constexpr int64_t stride = (int64_t)W * kSkStep;
-  int64_t k = kbeg + (int64_t)wv * kSkStep;
-  auto mfmas = [&](const uint4 (&a)[4], const uint4 (&bv)[RT][4]) {
-#pragma unroll
-    for (int jt = 0; jt < RT; ++jt)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) acc[jt] = mfma16x16x32(a[s], bv[jt][s], acc[jt]);
-  };
-  if constexpr (RT <= 4) {
-    // two steps in flight: the next step's loads are issued before this
-    // step's MFMAs
-    uint4 a0[4], b0[RT][4], a1[4], b1[RT][4];
-    if (k < kend) load_step(k, a0, b0);
-    while (k < kend) {
-      if (k + stride < kend) load_step(k + stride, a1, b1);
-      mfmas(a0, b0);
-      k += stride;
-      if (k >= kend) break;
-      if (k + stride < kend) load_step(k + stride, a0, b0);
-      mfmas(a1, b1);
-      k += stride;
-    }
-  } else {
-    for (; k < kend; k += stride) {   // r > 64: one step at a time
-      uint4 a0[4], b0[RT][4];
-      load_step(k, a0, b0);
-      mfmas(a0, b0);
-    }
-  }
-#pragma unroll
-  for (int jt = 0; jt < RT; ++jt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) red[wv][jt][v][lane] = acc[jt][v];
-  __syncthreads();
-  if (wv != 0) return;
-  // lane holds P[m0 + 4g + v][16 jt + j16]; a single slice writes the final
-  // outputs, several write float32 partials for the finish step
-  float* part = J.part + (int64_t)ks * M * (RT * 16);
-#pragma unroll
-  for (int jt = 0; jt < RT; ++jt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float sum = red[0][jt][v][lane];
-#pragma unroll
-      for (int w = 1; w < W; ++w) sum += red[w][jt][v][lane];
-      const int64_t m = m0 + 4 * g + v;
-      const int j = jt * 16 + j16;
-      if (J.ks > 1) {
-        if (m < M) part[m * (RT * 16) + j] = sum;
-        continue;
-      }
-      if (m < M) {
-        if (J.out_s && j < r32) J.out_s[m * r32 + j] = to_bf16(j < r ? J.scale * sum : 0.f);
-        if (J.out && j < r) J.out[m * r + j] = to_bf16(sum);
-      }
-      if (J.out_t && j < r && m < J.ldo_t)
-        J.out_t[(int64_t)j * J.ldo_t + m] = m < M ? to_bf16(sum) : 0;
-    }
-  if (J.ks == 1 && J.out_s) {   // padding columns of out_s past the computed tiles
-    for (int j = RT * 16 + j16; j < r32; j += 16)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t m = m0 + 4 * g + v;
-        if (m < M) J.out_s[m * r32 + j] = 0;
-      }
-  }
-}
 
 // Row groups of a job: past M only when out_t needs zero padding.
 __device__ __host__ __forceinline__ int64_t skinny_rows(const SkinnyJob& J, int64_t M) {
@@ -194,11 +45,11 @@ __global__ __launch_bounds__(sk_waves<RT>() * 64) void k_skinny_slices(SkinnyJob
                                                        int has_rc) {
   int64_t b = blockIdx.x;
   const int64_t b0 = skinny_blocks(j0, M);
-  if (b < b0) { skinny_slice<RT>(j0, M, r, r32, b); return; }
+  if (b < b0) { skinny_slice<RT, sk_waves<RT>()>(j0, M, r, r32, b); return; }
   b -= b0;
   if (nj > 1) {
     const int64_t b1 = skinny_blocks(j1, M);
-    if (b < b1) { skinny_slice<RT>(j1, M, r, r32, b); return; }
+    if (b < b1) { skinny_slice<RT, sk_waves<RT>()>(j1, M, r, r32, b); return; }
     b -= b1;
   }
   if (has_rc) recon_elems(rc, b);

@@ -20,17 +20,23 @@ struct PendingTiming {
 PendingTiming& pending_timing();
 
 template <typename... Params, typename... Args>
-inline hipError_t launch_kernel(void (*k)(Params...), dim3 grid, dim3 block, hipStream_t s,
-                                Args... args) {
+inline hipError_t launch_kernel_lds(void (*k)(Params...), dim3 grid, dim3 block, size_t lds,
+                                    hipStream_t s, Args... args) {
   PendingTiming& t = pending_timing();
   if (t.start) {
     const hipEvent_t a = t.start, b = t.stop;
     t.start = t.stop = nullptr;
-    hipExtLaunchKernelGGL(k, grid, block, 0, s, a, b, 0, static_cast<Params>(args)...);
+    hipExtLaunchKernelGGL(k, grid, block, (uint32_t)lds, s, a, b, 0, static_cast<Params>(args)...);
   } else {
-    hipLaunchKernelGGL(k, grid, block, 0, s, static_cast<Params>(args)...);
+    hipLaunchKernelGGL(k, grid, block, lds, s, static_cast<Params>(args)...);
   }
   return hipGetLastError();
+}
+
+template <typename... Params, typename... Args>
+inline hipError_t launch_kernel(void (*k)(Params...), dim3 grid, dim3 block, hipStream_t s,
+                                Args... args) {
+  return launch_kernel_lds(k, grid, block, 0, s, args...);
 }
 
 constexpr int kBlock = 64;     // weights per first-level absmax
@@ -148,6 +154,7 @@ struct SkinnyJob {
   uint16_t* out;
   uint16_t* out_t;
   int64_t ldo_t;
+  int part_only;   // write the slice partials even as a single slice
 };
 // Padded rank of the partial rows (16, 32, 64 or 128).
 int skinny_rpad(int r);
@@ -197,12 +204,21 @@ hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t N, const uint8_
 hipError_t launch_split_reduce(const float* part, int splits, int64_t count, uint16_t* out,
                                hipStream_t s);
 
-// decode path (M <= 16)
+// decode path (M <= 16): weight streaming with the block constants rebuilt
+// in registers, plus the LoRA down-projection slices, then one finish launch
+// (split sum + LoRA up-projection + bf16).  partial: [splits][M][N] floats;
+// xa_part: [decode_xa_slices(K)][M][skinny_rpad(r)] floats.
+struct NF4Ref {
+  const uint8_t* codes;
+  const int8_t* q;
+  const float* scale;
+  const float* mean;
+};
 int gemv_splits(int64_t N, int64_t K);
-hipError_t launch_gemv(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes, int64_t N,
-                       const float* ahat_t, int splits, float* partial, hipStream_t s);
-hipError_t launch_gemv_finish(const float* partial, int splits, int64_t M, int64_t N,
-                              const uint16_t* xas, int r, int r32, const uint16_t* B,
-                              uint16_t* Y, hipStream_t s);
+int decode_xa_slices(int64_t K);
+hipError_t launch_decode(const uint16_t* X, int64_t M, int64_t K, const NF4Ref& W, int64_t N,
+                         const uint16_t* A, const uint16_t* B, int r, float scale, int splits,
+                         float* partial, float* xa_part, uint16_t* Y, uint16_t* XA_out,
+                         hipStream_t s);
 
 }  // namespace qnf4

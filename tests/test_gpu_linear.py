@@ -86,11 +86,15 @@ def test_ragged_shapes(q, shape):
     _check_layer(q, w, x, a, b, dy, 2.0 * r, "ragged")
 
 
-@pytest.mark.parametrize("M", [1, 20, 300])
+@pytest.mark.parametrize("M", [1, 5, 16, 20, 300])
 def test_one_hot_rows_pick_bf16_weight_columns(q, M):
     """B = 0 and X = one-hot rows: Y[m, :] must equal bf16(W'[:, k_m]) exactly
     (pins layouts, nibble order and the dequant inside the GEMM); with one-hot
-    dY rows, dX[m, :] must equal bf16(W'[n_m, :]) exactly."""
+    dY rows, dX[m, :] must equal bf16(W'[n_m, :]) exactly.
+
+    The decode path (M <= 16) scales each block's dot products by the block
+    constant after the MFMA, so its weights enter as float32(a * bf16(level)):
+    there Y[m, n] must equal bf16(float32(a_(n, k_m) * bf16(level[code])))."""
     say("one-hot M=%d" % M)
     N, K, r = 320, 384, 8
     rng = np.random.default_rng(M)
@@ -109,10 +113,20 @@ def test_one_hot_rows_pick_bf16_weight_columns(q, M):
     Y = q.qlora_linear_fwd(qq, to_dev(x), to_dev(a), to_dev(b), 16.0)
     dX, _, _ = q.qlora_linear_bwd(qq, to_dev(x), to_dev(a), to_dev(b), 16.0, to_dev(dy))
     torch.cuda.synchronize()
-    _, wd = oracle_weight(w)
+    qt, wd = oracle_weight(w)
     wb = oracle.to_bf16_bits(wd).reshape(N, K)
     y = host(Y).view(torch.int16).numpy().view(np.uint16)
-    assert np.array_equal(y, wb.T[kk]), "Y rows are not the bf16 weight columns"
+    if M <= 16:
+        lv = np.asarray(oracle.codebook(), dtype=np.float32)
+        lvb = oracle.bf16_bits_to_f32(oracle.to_bf16_bits(lv)).astype(np.float32)
+        codes = oracle.unpack_codes(qt["codes"], N * K).reshape(N, K)
+        ahat = oracle.dequant_absmax(qt["absmax_q"], qt["absmax_scale"],
+                                     qt["absmax_mean"]).astype(np.float32).reshape(N, K // 64)
+        ycol = (ahat[:, kk // 64] * lvb[codes[:, kk]]).astype(np.float32)   # one fp32 rounding
+        want = oracle.to_bf16_bits(ycol).reshape(ycol.shape).T
+        assert np.array_equal(y, want), "Y rows are not a * bf16(level) of the weight columns"
+    else:
+        assert np.array_equal(y, wb.T[kk]), "Y rows are not the bf16 weight columns"
     dx = host(dX).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(dx, wb[nn]), "dX rows are not the bf16 weight rows"
 
