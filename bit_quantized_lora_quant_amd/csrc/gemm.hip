@@ -112,36 +112,56 @@ __device__ __forceinline__ void mfma_acc(f32x4_t& acc, const uint4& a, const u32
   const u32x4v_t av = {a.x, a.y, a.z, a.w};
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(av), "v"(b));
 }
+// Same, for callers whose B operands are assembled by the compiler right
+// before the call: a VALU write of a VGPR needs two wait states before an
+// MFMA reads it, and the hazard recognizer does not look inside inline asm.
+__device__ __forceinline__ void mfma_acc_vw(f32x4_t& acc, const uint4& a, const u32x4v_t& b) {
+  const u32x4v_t av = {a.x, a.y, a.z, a.w};
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(av), "v"(b));
+}
 __device__ __forceinline__ void mfma_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
+
+// One LDS-DMA load (global_load_lds_dwordx4): 16 bytes per lane from `g`
+// land at LDS address lds + 16 * lane.  Issued from inline asm so that the
+// wait-count pass does not track it: while a compiler-visible LDS DMA is in
+// flight that pass can no longer count LDS reads precisely and waits for all
+// of them (lgkmcnt(0)) at every use.  The callers wait for the DMA
+// themselves (vmcnt and a barrier) before the tile is read; the memory
+// clobber keeps LDS reads of a stage ahead of the DMA that refills it.  An
+// M0 write needs one wait state before the DMA reads it.
+__device__ __forceinline__ void dma16(const void* g, const void* lds) {
+  const uint32_t a = (uint32_t)(uintptr_t)(lds_void_t*)lds;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(a) : "m0", "memory");
+}
 
 // Global -> LDS copy of an activation tile [256 rows][64 cols] bf16 with the
 // LDS-DMA loads (global_load_lds_dwordx4: no VGPRs, no VALU).  Each load
 // instruction fills 1 KB = 8 rows; wave w issues loads q = 8w .. 8w+7 for
 // rows 8q .. 8q+7.  Lane t lands at row 8q + t/8, chunk position t%8, so it
 // fetches global chunk (t%8) ^ (t/8): the XOR swizzle lds_chunk reads back.
+template <int WAVES>
 struct TileDma {
-  uint32_t off[8];   // element offset of this lane's source chunk, per load
+  static constexpr int kLoads = 32 / WAVES;   // 8-row loads per wave
+  uint32_t off[kLoads];   // element offset of this lane's source chunk, per load
   __device__ __forceinline__ void init(int64_t ld, int64_t row0, int64_t rows_valid) {
     const int t = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int c = (t & 7) ^ (t >> 3);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int64_t row = row0 + 8 * (8 * wv + i) + (t >> 3);
+    for (int i = 0; i < kLoads; ++i) {
+      int64_t row = row0 + 8 * (kLoads * wv + i) + (t >> 3);
       row = row < rows_valid ? row : rows_valid - 1;
       off[i] = (uint32_t)(row * ld) + (uint32_t)(c * 8);
     }
   }
   __device__ __forceinline__ void issue(const uint16_t* __restrict__ src, uint32_t col0,
                                         uint16_t* lds_tile) const {
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(src + col0 + off[i]),
-                                       (lds_void_t*)(lds_tile + (8 * wv + i) * 512), 16, 0, 0);
+    for (int i = 0; i < kLoads; ++i) dma16(src + col0 + off[i], lds_tile + (kLoads * wv + i) * 512);
   }
 };
 
@@ -175,6 +195,29 @@ __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t& tm, int64_
 }
 
 // ------------------------------------------------------------------ forward
+// Every global read of the main loop is an LDS-DMA load, three stages deep:
+// at step kt the workgroup streams the X tile of step kt+2 and the code and
+// absmax tiles of step kt+3 (codes run one step ahead of X because a step
+// already rebuilds the next step's first sub-step).  Per stage:
+//   X      [256 rows][64]  bf16, 16-byte chunks XOR-swizzled by row  32 KB
+//   codes  [2 halves][256 rows][16 bytes]: half h = code bytes 16h..16h+15
+//          of the row's 32-byte step segment (sub-step h)              8 KB
+//   absmax [256 rows] fp32 (the block constant of the row at step kt)  1 KB
+// Each wave issues the same 11 DMA loads every step (8 X, 2 code, 1 absmax;
+// past the slice end they re-read its last step into a free stage), so the
+// end-of-step vmcnt(11) leaves exactly this step's loads in flight and the
+// previous step's have landed.
+constexpr int kStages = 3;
+constexpr int kDmaPerStep = 11;
+
+__device__ __forceinline__ void dma4(const void* g, const void* lds) {
+  const uint32_t a = (uint32_t)(uintptr_t)(lds_void_t*)lds;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(g), "s"(a) : "m0", "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14)); }
+
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1)))
 void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
@@ -183,12 +226,20 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                     const uint16_t* __restrict__ xas, const uint16_t* __restrict__ B, int r,
                     int r32, uint16_t* __restrict__ Y, int splits, int ksteps,
                     float* __restrict__ part) {
-  // two distinct LDS objects: the compiler can then prove that the buffer the
-  // DMA fills is not the one being read, and need not drain the DMA first
+  // distinct objects per stage, statically selected by the 3x unrolled loop
   __shared__ __attribute__((aligned(16))) uint16_t xs0[kTile * kStep];
   __shared__ __attribute__((aligned(16))) uint16_t xs1[kTile * kStep];
-  __shared__ float lvl[16];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ __attribute__((aligned(16))) uint16_t xs2[kTile * kStep];
+  __shared__ __attribute__((aligned(16))) uint32_t cs0[kTile * 8];
+  __shared__ __attribute__((aligned(16))) uint32_t cs1[kTile * 8];
+  __shared__ __attribute__((aligned(16))) uint32_t cs2[kTile * 8];
+  __shared__ __attribute__((aligned(16))) float as0[kTile];
+  __shared__ __attribute__((aligned(16))) float as1[kTile];
+  __shared__ __attribute__((aligned(16))) float as2[kTile];
+  // the level table first (largest alignment), at LDS address 0
+  __shared__ __attribute__((aligned(1024))) float lvl[16];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j16 = lane & 15, g = lane >> 4;
   int64_t tm, tn;
   int split;
@@ -196,20 +247,45 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
   const int64_t m0 = tm * kTile, n0 = tn * kTile;
   if (tid < 16) lvl[tid] = tab.level[tid];
 
-  // this lane's four W rows (clamped; columns past N are never stored)
-  int64_t nrow[4];
-  uint32_t coff[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int64_t n = n0 + 64 * wv + 16 * nt + j16;
-    nrow[nt] = n < N ? n : N - 1;
-    coff[nt] = (uint32_t)(nrow[nt] * (K / 2)) + (uint32_t)(g * 4);
-  }
   // this workgroup's steps [kt0, kt1) of the K loop (split-K slice)
   const uint32_t KTall = (uint32_t)(K / kStep);
   const uint32_t kt0 = (uint32_t)split * (uint32_t)ksteps;
   const uint32_t kt1 = kt0 + (uint32_t)ksteps < KTall ? kt0 + (uint32_t)ksteps : KTall;
   const uint32_t N32 = (uint32_t)N;
+
+  // DMA sources of this lane (rows clamped; results for them are never stored)
+  TileDma<4> dma;
+  dma.init(K, m0, M);
+  uint32_t cdma[2];   // code bytes: load i of wave wv fills LDS chunks 64(2wv+i)..+63
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int blk = 2 * wv + i;
+    int64_t n = n0 + (blk & 3) * 64 + lane;
+    n = n < N ? n : N - 1;
+    cdma[i] = (uint32_t)(n * (K / 2)) + (uint32_t)(16 * (blk >> 2));
+  }
+  uint32_t adma;      // absmax: row 64 wv + lane
+  {
+    int64_t n = n0 + 64 * wv + lane;
+    adma = (uint32_t)(n < N ? n : N - 1);
+  }
+  auto issue = [&](uint32_t tx, uint16_t* xd, uint32_t tc, uint32_t* cd, float* ad) {
+    tx = tx < kt1 ? tx : kt1 - 1;
+    tc = tc < kt1 ? tc : kt1 - 1;
+    dma.issue(X, tx * kStep, xd);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(codes + cdma[i] + tc * 32, cd + (2 * wv + i) * 256);
+    dma4(ahat_t + tc * N32 + adma, ad + 64 * wv);
+  };
+  // this lane's rows of the code / absmax stages
+  auto read_codes = [&](const uint32_t* cs, const float* as, uint2* c, float* a) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int row = 64 * wv + 16 * nt + j16;
+      c[nt] = make_uint2(cs[row * 4 + g], cs[(256 + row) * 4 + g]);
+      a[nt] = as[row];
+    }
+  };
 
   f32x4_t acc[16][4];
 #pragma unroll
@@ -221,34 +297,23 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
     }
   mfma_settle();
 
-  // Software pipeline, one sub-step (32 inner indices) ahead: while the
-  // MFMAs of sub-step s read operand set bop[s], the VALU rebuilds the next
-  // sub-step's operands into bop[s ^ 1] (free since the previous sub-step),
-  // one 2-weight slice per group of 4 MFMAs.  A step is 32 such groups
-  // (2 sub-steps x 16 row tiles); each group prefetches the next group's A
-  // operand and level lookups, and a scheduling barrier keeps that order so
-  // only two A operands are ever live.  Codes arrive two steps ahead; the X
-  // tile of step kt+1 streams into the other LDS buffer by DMA.  One barrier
-  // per step.
-  // X tiles stream global -> LDS by DMA one step ahead
-  TileDma dma;
-  dma.init(K, m0, M);
-  dma.issue(X, kt0 * kStep, xs0);
-  uint32_t coff32[4], arow[4];
+  // prologue: X(kt0) and codes(kt0), codes(kt0+1) resident; then the loads
+  // the first step's end-of-step wait is for: X(kt0+1), codes(kt0+2)
+  issue(kt0, xs0, kt0, cs0, as0);
+  {
+    const uint32_t t1 = kt0 + 1 < kt1 ? kt0 + 1 : kt1 - 1;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) { coff32[nt] = coff[nt]; arow[nt] = (uint32_t)nrow[nt]; }
-  uint2 cc[4], cn[4], cnn[4];
-  float ac[4], an[4], ann[4];
-  const uint32_t k1 = kt0 + 1 < kt1 ? kt0 + 1 : kt0;
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    cc[nt] = load_codes2(codes + coff32[nt] + kt0 * 32);   // first step
-    ac[nt] = ahat_t[kt0 * N32 + arow[nt]];
-    cn[nt] = load_codes2(codes + coff32[nt] + k1 * 32);    // second step
-    an[nt] = ahat_t[k1 * N32 + arow[nt]];
+    for (int i = 0; i < 2; ++i) dma16(codes + cdma[i] + t1 * 32, cs1 + (2 * wv + i) * 256);
+    dma4(ahat_t + t1 * N32 + adma, as1 + 64 * wv);
   }
   wait_vmem_all();
-  __syncthreads();   // level table and X tile 0 visible
+  __syncthreads();
+  uint2 cc[4], cn[4];
+  float ac[4], an[4];
+  read_codes(cs0, as0, cc, ac);
+  read_codes(cs1, as1, cn, an);
+  issue(kt0 + 1, xs1, kt0 + 2, cs2, as2);
+
   uint32_t bop[2][4][4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt)
@@ -257,79 +322,112 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
       bop[0][nt][dw] = pack_bf16x2(lvl[(cc[nt].x >> (8 * dw)) & 15u] * ac[nt],
                                    lvl[(cc[nt].x >> (8 * dw + 4)) & 15u] * ac[nt]);
 
-  // slice j (0..31) of a step builds bop[(j >> 4) ^ 1][nt][dw] (nt = (j>>2)&3,
-  // dw = j&3) from code word (j < 16 ? this step's .y : next step's .x);
-  // slices 32.. are the next step's 0.. (word: next step's .y = cn.y).
-  // Group i's A operand and slice i's level lookups are fetched kD groups
-  // ahead into small rings, so LDS latency hides behind 4*kD MFMAs.
+  // Group i (0..31) of a step: sub-step s = i >> 4, row tile mt = i & 15, four
+  // MFMAs (nt).  Slice i (nt = (i >> 2) & 3, dw = i & 3) rebuilds
+  // bop[s ^ 1][nt][dw] from code word k = i >> 2 of the step's word sequence
+  // (this step's .y for k < 4, next step's .x for k < 8, next step's .y for
+  // the slices 32.. that are the next step's 0..).  The A operand of group i
+  // and the two level lookups of slice i are fetched 4 groups ahead.
+  //
+  // One wave per SIMD hides about two VALU instructions behind each MFMA, so
+  // a group places its work between its four MFMAs (scheduling barriers keep
+  // the order): lookup, lookup, two multiplies, convert + A read.  A lookup
+  // address is one byte extract: each code word is pre-spread once into
+  // 4 x (low nibble) and 4 x (high nibble) per byte, which with the level
+  // table at LDS address 0 is the byte offset of the level.
+  auto lvl_at = [&](uint32_t off) { return *reinterpret_cast<const float*>(
+                                        reinterpret_cast<const char*>(lvl) + off); };
+  auto word = [&](int k) -> uint32_t {   // code word k (0..9) of this step
+    const int nt = k & 3;
+    return k < 4 ? cc[nt].y : (k < 8 ? cn[nt].x : cn[nt].y);
+  };
+  uint32_t w4lo[2], w4hi[2];   // spread words, slot k & 1
+  auto spread = [&](int k) {
+    const uint32_t w = word(k);
+    w4lo[k & 1] = (w << 2) & 0x3C3C3C3Cu;
+    w4hi[k & 1] = (w >> 2) & 0x3C3C3C3Cu;
+    // opaque to the optimiser, which would otherwise fold the spread back
+    // into a shift and mask of w at every lookup (two instructions, not one)
+    asm volatile("" : "+v"(w4lo[k & 1]), "+v"(w4hi[k & 1]));
+  };
+  auto byte_of = [](uint32_t w, int b) -> uint32_t {
+    return b == 0 ? (w & 0xFFu) : (b == 3 ? (w >> 24) : ((w >> (8 * b)) & 0xFFu));
+  };
   constexpr int kD = 4;
   uint4 aq[kD];
-  float lq0[kD], lq1[kD];
+  float lqa[8], lqb[8];   // slice k's two levels at k % 8
+  spread(0);
+  spread(1);
 #pragma unroll
   for (int d = 0; d < kD; ++d) {
     aq[d] = lds_chunk(xs0, d * 16 + j16, g);
-    const int nt = (d >> 2) & 3, dw = d & 3;
-    lq0[d] = lvl[(cc[nt].y >> (8 * dw)) & 15u];
-    lq1[d] = lvl[(cc[nt].y >> (8 * dw + 4)) & 15u];
+    lqa[d] = lvl_at(byte_of(w4lo[0], d));
+    lqb[d] = lvl_at(byte_of(w4hi[0], d));
   }
 
-  // one step: MFMAs read X tile kt from `xb`, the DMA fills `xn` with tile kt+1
-  auto step = [&](uint32_t kt, const uint16_t* xb, uint16_t* xn) {
-    // Free in steady state (the previous step ended drained), but it tells
-    // the wait-count pass that the loop-carried code words have landed, so
-    // it does not drain the in-flight DMA in the middle of the step.
-    wait_vmem_all();
-    const uint32_t kn = kt + 1 < kt1 ? kt + 1 : kt;        // last step re-reads itself
-    const uint32_t kn2 = kt + 2 < kt1 ? kt + 2 : kt1 - 1;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      cnn[nt] = load_codes2(codes + coff32[nt] + kn2 * 32);
-      ann[nt] = ahat_t[kn2 * N32 + arow[nt]];
-    }
-    compiler_fence();
-    dma.issue(X, kn * kStep, xn);
-    compiler_fence();   // keep the loads here, ahead of the MFMAs
-    __builtin_amdgcn_sched_barrier(0);
+  // one step: MFMAs read X stage `xb`; DMA fills X stage `xd` (tile kt+2)
+  // and code stage `cd`/`ad` (tile kt+3), spread over the step; at the end
+  // the code stage of tile kt+2 (`cr`/`ar`) and X stage `xr` (tile kt+1)
+  // are read
+  auto step = [&](uint32_t kt, const uint16_t* xb, uint16_t* xd, uint32_t* cd, float* ad,
+                  const uint32_t* cr, const float* ar, const uint16_t* xr) {
+    const uint32_t tx = kt + 2 < kt1 ? kt + 2 : kt1 - 1;
+    const uint32_t tc = kt + 3 < kt1 ? kt + 3 : kt1 - 1;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       const int s = i >> 4, mt = i & 15, q = i % kD;
+      const int ia = i + kD, ka = ia >> 2;
+      mfma_acc(acc[mt][0], aq[q], u32x4v_t{bop[s][0][0], bop[s][0][1], bop[s][0][2], bop[s][0][3]});
+      __builtin_amdgcn_sched_barrier(0);
+      lqa[ia & 7] = lvl_at(byte_of(w4lo[ka & 1], ia & 3));
+      if ((i & 7) == 0) {   // X tile kt+2: two of this wave's eight loads
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        mfma_acc(acc[mt][nt], aq[q],
-                 u32x4v_t{bop[s][nt][0], bop[s][nt][1], bop[s][nt][2], bop[s][nt][3]});
-      // finish slice i (its lookups arrived kD groups ago)
-      {
-        const int nt = (i >> 2) & 3, dw = i & 3;
-        const float sc = s ? an[nt] : ac[nt];
-        bop[s ^ 1][nt][dw] = pack_bf16x2(lq0[q] * sc, lq1[q] * sc);
-      }
-      // fetch group i+kD's A operand (this step only) and slice i+kD's lookups
-      const int ia = i + kD;
-      if (ia < 32) aq[q] = lds_chunk(xb, (ia & 15) * 16 + j16, 4 * (ia >> 4) + g);
-      {
-        const int j = ia & 31, nt = (j >> 2) & 3, dw = j & 3;
-        const uint32_t c = (ia >= 32) ? cn[nt].y : (j < 16 ? cc[nt].y : cn[nt].x);
-        lq0[q] = lvl[(c >> (8 * dw)) & 15u];
-        lq1[q] = lvl[(c >> (8 * dw + 4)) & 15u];
+        for (int l = 2 * (i >> 3); l < 2 * (i >> 3) + 2; ++l)
+          dma16(X + tx * kStep + dma.off[l], xd + (8 * wv + l) * 512);
       }
       __builtin_amdgcn_sched_barrier(0);
-    }
+      mfma_acc(acc[mt][1], aq[q], u32x4v_t{bop[s][1][0], bop[s][1][1], bop[s][1][2], bop[s][1][3]});
+      __builtin_amdgcn_sched_barrier(0);
+      lqb[ia & 7] = lvl_at(byte_of(w4hi[ka & 1], ia & 3));
+      if ((i & 3) == 0) spread((i >> 2) + 2);
+      if (i == 4) {         // code and absmax tiles of kt+3
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      cc[nt] = cn[nt]; ac[nt] = an[nt];
-      cn[nt] = cnn[nt]; an[nt] = ann[nt];
+        for (int l = 0; l < 2; ++l) dma16(codes + cdma[l] + tc * 32, cd + (2 * wv + l) * 256);
+        dma4(ahat_t + tc * N32 + adma, ad + 64 * wv);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_acc(acc[mt][2], aq[q], u32x4v_t{bop[s][2][0], bop[s][2][1], bop[s][2][2], bop[s][2][3]});
+      __builtin_amdgcn_sched_barrier(0);
+      const int nt = (i >> 2) & 3, dw = i & 3;
+      const float sc = s ? an[nt] : ac[nt];
+      const float v0 = lqa[i & 7] * sc, v1 = lqb[i & 7] * sc;
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_acc(acc[mt][3], aq[q], u32x4v_t{bop[s][3][0], bop[s][3][1], bop[s][3][2], bop[s][3][3]});
+      __builtin_amdgcn_sched_barrier(0);
+      bop[s ^ 1][nt][dw] = pack_bf16x2(v0, v1);
+      // group i+kD's A operand (this step only); its MFMAs have read aq[q]
+      if (ia < 32) aq[q] = lds_chunk(xb, (ia & 15) * 16 + j16, 4 * (ia >> 4) + g);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    wait_vmem_all();   // the DMA of tile kt+1 has landed
+    // X(kt+1) and codes(kt+2) have landed once only this step's loads remain
+    wait_vmem<kDmaPerStep>();
     __syncthreads();
 #pragma unroll
-    for (int d = 0; d < kD; ++d) aq[d] = lds_chunk(xn, d * 16 + j16, g);
+    for (int nt = 0; nt < 4; ++nt) { cc[nt] = cn[nt]; ac[nt] = an[nt]; }
+    read_codes(cr, ar, cn, an);
+#pragma unroll
+    for (int d = 0; d < kD; ++d) aq[d] = lds_chunk(xr, d * 16 + j16, g);
   };
+  // tile t lives in X stage t % 3 (relative to kt0) and code stage t % 3
   uint32_t kt = kt0;
-  for (; kt + 1 < kt1; kt += 2) {
-    step(kt, xs0, xs1);
-    step(kt + 1, xs1, xs0);
+  for (; kt + 2 < kt1; kt += 3) {
+    step(kt, xs0, xs2, cs0, as0, cs2, as2, xs1);
+    step(kt + 1, xs1, xs0, cs1, as1, cs0, as0, xs2);
+    step(kt + 2, xs2, xs1, cs2, as2, cs1, as1, xs0);
   }
-  if (kt < kt1) step(kt, xs0, xs1);
+  if (kt < kt1) step(kt, xs0, xs2, cs0, as0, cs2, as2, xs1);
+  if (kt + 1 < kt1) step(kt + 1, xs1, xs0, cs1, as1, cs0, as0, xs2);
+  wait_vmem_all();   // nothing left in flight into LDS at exit
   mfma_settle();
 
   // LoRA up-projection as r32 extra inner columns: A operand s.XA (bf16,
@@ -341,7 +439,9 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
     uint4 bb[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const uint16_t* p = B + nrow[nt] * r + j0;
+      int64_t n = n0 + 64 * wv + 16 * nt + j16;
+      n = n < N ? n : N - 1;
+      const uint16_t* p = B + n * r + j0;
       if (bvec && j0 + 8 <= r) {
         bb[nt] = *reinterpret_cast<const uint4*>(p);
       } else {
@@ -593,7 +693,7 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
     }
   };
 
-  TileDma dma;
+  TileDma<4> dma;
   dma.init(N, m0, M);
   dma.issue(dY, it0 * kStep, ys0);
   WStep wc, wn, wnn;
