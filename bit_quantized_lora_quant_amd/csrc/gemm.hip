@@ -632,10 +632,17 @@ void k_qlora_dx_nn(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
   }
 }
 
-// Fast dX path for N % 64 == 0 (every step full): the dY tile streams into
-// LDS by DMA, the W' operands of the next sub-step are rebuilt between the
-// MFMA groups of the current one (as in the forward kernel), accumulators are
-// pinned in AGPRs.
+// Fast dX path for N % 64 == 0 (every step full), built like the forward
+// kernel: the dY tile, the code tile and the absmax tile of a step stream into
+// three LDS stages by DMA (dY two steps ahead, codes and absmax three), and
+// the W' operands of the next sub-step are rebuilt between the MFMAs of the
+// current one.  Per stage:
+//   dY     [256 rows m][64 n] bf16, chunks XOR-swizzled by row        32 KB
+//   codes  8 blocks of 8 W rows x 128 bytes (the tile's 256 columns),
+//          block b at b * 1088 bytes (the 64-byte pad puts the four lane
+//          groups of a 16-bit code read on disjoint banks)           8.5 KB
+//   absmax [4 column blocks][64 rows] fp32                             1 KB
+constexpr int kCodeBlk = 1024 + 64;
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1)))
 void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
@@ -644,10 +651,18 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
                        const uint16_t* __restrict__ gs, const uint16_t* __restrict__ A, int r,
                        int r32, uint16_t* __restrict__ dX, int splits, int nsteps,
                        float* __restrict__ part) {
+  __shared__ __attribute__((aligned(1024))) float lvl[16];   // at LDS address 0
   __shared__ __attribute__((aligned(16))) uint16_t ys0[kTile * kStep];
   __shared__ __attribute__((aligned(16))) uint16_t ys1[kTile * kStep];
-  __shared__ float lvl[16];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ __attribute__((aligned(16))) uint16_t ys2[kTile * kStep];
+  __shared__ __attribute__((aligned(16))) uint8_t cs0[8 * kCodeBlk];
+  __shared__ __attribute__((aligned(16))) uint8_t cs1[8 * kCodeBlk];
+  __shared__ __attribute__((aligned(16))) uint8_t cs2[8 * kCodeBlk];
+  __shared__ __attribute__((aligned(16))) float as0[kTile];
+  __shared__ __attribute__((aligned(16))) float as1[kTile];
+  __shared__ __attribute__((aligned(16))) float as2[kTile];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j16 = lane & 15, g = lane >> 4;
   int64_t tm, tn;
   int split;
@@ -658,13 +673,54 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
   const int64_t kc = k0 + 64 * wv + 4 * j16;      // first of this lane's 4 columns
   const bool kvalid = kc < K;                       // K % 64 == 0: all 4 or none
   const int64_t kcl = kvalid ? kc : K - 4;
-  const uint32_t ldc = (uint32_t)(K / 2);
   // this workgroup's inner steps [it0, it1) (split over N)
   const uint32_t NTall = (uint32_t)(N / kStep);
   const uint32_t it0 = (uint32_t)split * (uint32_t)nsteps;
   const uint32_t it1 = it0 + (uint32_t)nsteps < NTall ? it0 + (uint32_t)nsteps : NTall;
-  const uint32_t ccol = (uint32_t)(kcl / 2);
-  const uint32_t abase = (uint32_t)(kcl / kBlock) * (uint32_t)N + 8 * g;
+  const uint32_t N32 = (uint32_t)N, ldc = (uint32_t)(K / 2);
+
+  // DMA sources of this lane: dY rows (clamped), code block rows (columns
+  // clamped into the row; such columns are never stored), absmax rows
+  TileDma<4> dma;
+  dma.init(N, m0, M);
+  uint32_t cdma[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int blk = 2 * wv + i;
+    int64_t cb = k0 / 2 + 16 * (lane & 7);
+    cb = cb < (int64_t)ldc - 16 ? cb : (int64_t)ldc - 16;
+    cdma[i] = (uint32_t)(8 * blk + (lane >> 3)) * ldc + (uint32_t)cb;
+  }
+  uint32_t adma;
+  {
+    int64_t kb = k0 / kBlock + wv;
+    kb = kb < K / kBlock ? kb : K / kBlock - 1;
+    adma = (uint32_t)kb * N32 + (uint32_t)lane;
+  }
+  auto issue_codes = [&](uint32_t tc, uint8_t* cd, float* ad) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      dma16(codes + cdma[i] + tc * kStep * ldc, cd + (2 * wv + i) * kCodeBlk);
+    dma4(ahat_t + adma + tc * kStep, ad + 64 * wv);
+  };
+  // this lane's W rows of a stage: pair-word 4s + q holds the 16-bit code
+  // group (columns kc..kc+3) of rows 32s + 8g + 2q (low half) and +1 (high);
+  // a[8s + e] is the block constant of row 32s + 8g + e
+  auto read_codes = [&](const uint8_t* cs, const float* as, uint32_t* c, float* a) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint8_t* p = cs + (4 * s2 + g) * kCodeBlk + (2 * q) * 128 + 32 * wv + 2 * j16;
+        c[4 * s2 + q] = (uint32_t)*reinterpret_cast<const uint16_t*>(p) |
+                        ((uint32_t)*reinterpret_cast<const uint16_t*>(p + 128) << 16);
+      }
+      const float4 lo = *reinterpret_cast<const float4*>(as + 64 * wv + 32 * s2 + 8 * g);
+      const float4 hi = *reinterpret_cast<const float4*>(as + 64 * wv + 32 * s2 + 8 * g + 4);
+      a[8 * s2 + 0] = lo.x; a[8 * s2 + 1] = lo.y; a[8 * s2 + 2] = lo.z; a[8 * s2 + 3] = lo.w;
+      a[8 * s2 + 4] = hi.x; a[8 * s2 + 5] = hi.y; a[8 * s2 + 6] = hi.z; a[8 * s2 + 7] = hi.w;
+    }
+  };
 
   f32x4_t acc[16][4];
 #pragma unroll
@@ -676,31 +732,20 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
     }
   mfma_settle();
 
-  // W rows of step n0: n0 + 32s + 8g + e (s = 0, 1; e = 0..7): 16 codes words
-  // (4 codes each, columns kc..kc+3) and their 16 block constants
-  struct WStep { uint32_t c[16]; float a[16]; };
-  auto load_w = [&](uint32_t n0, WStep& w) {
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        w.c[s2 * 8 + e] =
-            *reinterpret_cast<const uint16_t*>(codes + (n0 + 32 * s2 + 8 * g + e) * ldc + ccol);
-      const float4 lo = *reinterpret_cast<const float4*>(ahat_t + abase + n0 + 32 * s2);
-      const float4 hi = *reinterpret_cast<const float4*>(ahat_t + abase + n0 + 32 * s2 + 4);
-      w.a[s2 * 8 + 0] = lo.x; w.a[s2 * 8 + 1] = lo.y; w.a[s2 * 8 + 2] = lo.z; w.a[s2 * 8 + 3] = lo.w;
-      w.a[s2 * 8 + 4] = hi.x; w.a[s2 * 8 + 5] = hi.y; w.a[s2 * 8 + 6] = hi.z; w.a[s2 * 8 + 7] = hi.w;
-    }
-  };
-
-  TileDma<4> dma;
-  dma.init(N, m0, M);
+  // prologue: dY(it0) and codes(it0), codes(it0+1) resident; then the loads
+  // the first step's end-of-step wait is for: dY(it0+1), codes(it0+2)
+  const uint32_t itl = it1 - 1;
   dma.issue(dY, it0 * kStep, ys0);
-  WStep wc, wn, wnn;
-  load_w(it0 * kStep, wc);
-  load_w((it0 + 1 < it1 ? it0 + 1 : it0) * kStep, wn);
+  issue_codes(it0, cs0, as0);
+  issue_codes(it0 + 1 < it1 ? it0 + 1 : itl, cs1, as1);
   wait_vmem_all();
-  __syncthreads();   // level table and dY tile 0 visible
+  __syncthreads();
+  uint32_t cc[8], cn[8];
+  float ac[16], an[16];
+  read_codes(cs0, as0, cc, ac);
+  read_codes(cs1, as1, cn, an);
+  dma.issue(dY, (it0 + 1 < it1 ? it0 + 1 : itl) * kStep, ys1);
+  issue_codes(it0 + 2 < it1 ? it0 + 2 : itl, cs2, as2);
 
   // operand set of sub-step s: bop[s][t][q] = bf16 pair of W' rows (2q, 2q+1)
   // at column kc + t
@@ -709,72 +754,105 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      bop[0][t][q] = pack_bf16x2(lvl[(wc.c[2 * q] >> (4 * t)) & 15u] * wc.a[2 * q],
-                                 lvl[(wc.c[2 * q + 1] >> (4 * t)) & 15u] * wc.a[2 * q + 1]);
+      bop[0][t][q] = pack_bf16x2(lvl[(cc[q] >> (4 * t)) & 15u] * ac[2 * q],
+                                 lvl[(cc[q] >> (16 + 4 * t)) & 15u] * ac[2 * q + 1]);
 
-  // slice j (0..31): target bop[(j >> 4) ^ 1][t = (j >> 2) & 3][q = j & 3];
-  // rows: j < 16 -> this step's sub-step 1 (wc, words 8 + 2q, 9 + 2q);
-  // j >= 16 -> next step's sub-step 0 (wn, words 2q, 2q + 1); slices 32..
-  // are the next step's 0.. (wn, words 8 + 2q ..).
+  // Slice i (0..31) of a step builds bop[s ^ 1][t = i & 3][q = (i >> 2) & 3]
+  // from pair-word k = i >> 2 of the step's sequence: this step's sub-step 1
+  // (k < 4), the next step's sub-step 0 (k < 8), and for the lookahead the
+  // next step's sub-step 1 (k = 8, 9).  Group schedule and lookup addressing
+  // as in the forward kernel; a pair-word spreads into 4 x nibble bytes
+  // [row 2q: t0 t2, row 2q+1: t0 t2] and [.. t1 t3 ..].
+  auto lvl_at = [&](uint32_t off) { return *reinterpret_cast<const float*>(
+                                        reinterpret_cast<const char*>(lvl) + off); };
+  auto word = [&](int k) -> uint32_t {
+    const int q = k & 3;
+    return k < 4 ? cc[4 + q] : (k < 8 ? cn[q] : cn[4 + q]);
+  };
+  uint32_t w4lo[2], w4hi[2];
+  auto spread = [&](int k) {
+    const uint32_t w = word(k);
+    w4lo[k & 1] = (w << 2) & 0x3C3C3C3Cu;
+    w4hi[k & 1] = (w >> 2) & 0x3C3C3C3Cu;
+    asm volatile("" : "+v"(w4lo[k & 1]), "+v"(w4hi[k & 1]));
+  };
+  auto byte_of = [](uint32_t w, int b) -> uint32_t {
+    return b == 0 ? (w & 0xFFu) : (b == 3 ? (w >> 24) : ((w >> (8 * b)) & 0xFFu));
+  };
+  // row (hi) of column t in a spread pair-word
+  auto lookup = [&](int k, int t, int hi) {
+    const uint32_t w = (t & 1) ? w4hi[k & 1] : w4lo[k & 1];
+    return lvl_at(byte_of(w, 2 * hi + (t >> 1)));
+  };
   constexpr int kD = 4;
   uint4 aq[kD];
-  float lq0[kD], lq1[kD];
+  float lqa[8], lqb[8];
+  spread(0);
+  spread(1);
 #pragma unroll
   for (int d = 0; d < kD; ++d) {
     aq[d] = lds_chunk(ys0, d * 16 + j16, g);
-    const int t = (d >> 2) & 3, q = d & 3;
-    lq0[d] = lvl[(wc.c[8 + 2 * q] >> (4 * t)) & 15u];
-    lq1[d] = lvl[(wc.c[9 + 2 * q] >> (4 * t)) & 15u];
+    lqa[d] = lookup(0, d, 0);
+    lqb[d] = lookup(0, d, 1);
   }
 
-  auto step = [&](uint32_t it, const uint16_t* yb, uint16_t* yn) {
-    wait_vmem_all();   // see the forward kernel: keeps the wait pass from draining the DMA
-    const uint32_t nn = it + 1 < it1 ? it + 1 : it;       // last step re-reads itself
-    const uint32_t nn2 = it + 2 < it1 ? it + 2 : it1 - 1;
-    load_w(nn2 * kStep, wnn);
-    compiler_fence();
-    dma.issue(dY, nn * kStep, yn);
-    compiler_fence();
-    __builtin_amdgcn_sched_barrier(0);
+  auto step = [&](uint32_t it, const uint16_t* yb, uint16_t* yd, uint8_t* cd, float* ad,
+                  const uint8_t* cr, const float* ar, const uint16_t* yr) {
+    const uint32_t ty = it + 2 < it1 ? it + 2 : itl;
+    const uint32_t tc = it + 3 < it1 ? it + 3 : itl;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       const int s = i >> 4, mt = i & 15, qd = i % kD;
+      const int ia = i + kD, ka = ia >> 2;
+      mfma_acc(acc[mt][0], aq[qd], u32x4v_t{bop[s][0][0], bop[s][0][1], bop[s][0][2], bop[s][0][3]});
+      __builtin_amdgcn_sched_barrier(0);
+      lqa[ia & 7] = lookup(ka, ia & 3, 0);
+      if ((i & 7) == 0) {   // dY tile it+2: two of this wave's eight loads
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        mfma_acc(acc[mt][t], aq[qd],
-                 u32x4v_t{bop[s][t][0], bop[s][t][1], bop[s][t][2], bop[s][t][3]});
-      {
-        const int t = (i >> 2) & 3, q = i & 3;
-        const float a0 = s ? wn.a[2 * q] : wc.a[8 + 2 * q];
-        const float a1 = s ? wn.a[2 * q + 1] : wc.a[9 + 2 * q];
-        bop[s ^ 1][t][q] = pack_bf16x2(lq0[qd] * a0, lq1[qd] * a1);
-      }
-      const int ia = i + kD;
-      if (ia < 32) aq[qd] = lds_chunk(yb, (ia & 15) * 16 + j16, 4 * (ia >> 4) + g);
-      {
-        const int j = ia & 31, t = (j >> 2) & 3, q = j & 3;
-        uint32_t w0, w1;
-        if (ia >= 32) { w0 = wn.c[8 + 2 * q]; w1 = wn.c[9 + 2 * q]; }
-        else if (j < 16) { w0 = wc.c[8 + 2 * q]; w1 = wc.c[9 + 2 * q]; }
-        else { w0 = wn.c[2 * q]; w1 = wn.c[2 * q + 1]; }
-        lq0[qd] = lvl[(w0 >> (4 * t)) & 15u];
-        lq1[qd] = lvl[(w1 >> (4 * t)) & 15u];
+        for (int l = 2 * (i >> 3); l < 2 * (i >> 3) + 2; ++l)
+          dma16(dY + ty * kStep + dma.off[l], yd + (8 * wv + l) * 512);
       }
       __builtin_amdgcn_sched_barrier(0);
+      mfma_acc(acc[mt][1], aq[qd], u32x4v_t{bop[s][1][0], bop[s][1][1], bop[s][1][2], bop[s][1][3]});
+      __builtin_amdgcn_sched_barrier(0);
+      lqb[ia & 7] = lookup(ka, ia & 3, 1);
+      if ((i & 3) == 0) spread((i >> 2) + 2);
+      if (i == 4) issue_codes(tc, cd, ad);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_acc(acc[mt][2], aq[qd], u32x4v_t{bop[s][2][0], bop[s][2][1], bop[s][2][2], bop[s][2][3]});
+      __builtin_amdgcn_sched_barrier(0);
+      const int k = i >> 2, t = i & 3, q = k & 3;
+      const float a0 = k < 4 ? ac[8 + 2 * q] : an[2 * q];
+      const float a1 = k < 4 ? ac[9 + 2 * q] : an[2 * q + 1];
+      const float v0 = lqa[i & 7] * a0, v1 = lqb[i & 7] * a1;
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_acc(acc[mt][3], aq[qd], u32x4v_t{bop[s][3][0], bop[s][3][1], bop[s][3][2], bop[s][3][3]});
+      __builtin_amdgcn_sched_barrier(0);
+      bop[s ^ 1][t][q] = pack_bf16x2(v0, v1);
+      if (ia < 32) aq[qd] = lds_chunk(yb, (ia & 15) * 16 + j16, 4 * (ia >> 4) + g);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    wc = wn;
-    wn = wnn;
-    wait_vmem_all();   // the DMA of the next dY tile has landed
+    // dY(it+1) and codes(it+2) have landed once only this step's loads remain
+    wait_vmem<kDmaPerStep>();
     __syncthreads();
 #pragma unroll
-    for (int d = 0; d < kD; ++d) aq[d] = lds_chunk(yn, d * 16 + j16, g);
+    for (int e = 0; e < 8; ++e) cc[e] = cn[e];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ac[e] = an[e];
+    read_codes(cr, ar, cn, an);
+#pragma unroll
+    for (int d = 0; d < kD; ++d) aq[d] = lds_chunk(yr, d * 16 + j16, g);
   };
+  // step it lives in dY stage (it - it0) % 3 and code stage (it - it0) % 3
   uint32_t it = it0;
-  for (; it + 1 < it1; it += 2) {
-    step(it, ys0, ys1);
-    step(it + 1, ys1, ys0);
+  for (; it + 2 < it1; it += 3) {
+    step(it, ys0, ys2, cs0, as0, cs2, as2, ys1);
+    step(it + 1, ys1, ys0, cs1, as1, cs0, as0, ys2);
+    step(it + 2, ys2, ys1, cs2, as2, cs1, as1, ys0);
   }
-  if (it < it1) step(it, ys0, ys1);
+  if (it < it1) step(it, ys0, ys2, cs0, as0, cs2, as2, ys1);
+  if (it + 1 < it1) step(it + 1, ys1, ys0, cs1, as1, cs0, as0, ys2);
+  wait_vmem_all();   // nothing left in flight into LDS at exit
   mfma_settle();
 
   // LoRA: + (s.G) . A as r32 extra inner indices (last slice only)
