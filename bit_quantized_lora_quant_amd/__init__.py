@@ -24,7 +24,7 @@ EXPORTS = [
     "qlora_nf4_codebook", "qlora_status_string", "qlora_quantize_workspace_bytes",
     "qlora_quantize_nf4", "qlora_dequantize_nf4", "qlora_dequantize_absmax",
     "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
-    "qlora_trace_begin", "qlora_trace_end",
+    "qlora_trace_begin", "qlora_trace_pause", "qlora_trace_end",
 ]
 KERNELS = {"fwd_gemm": 0, "dx_gemm": 1, "quantize": 2, "dequant": 3, "gemv": 4,
            "split_reduce": 5}
@@ -71,10 +71,11 @@ def lib():
         L.qlora_linear_fwd.argtypes = [D, P, I64, P, P, I32, F, P, P, P, SZ, P]
         L.qlora_linear_bwd.argtypes = [D, P, I64, P, P, I32, F, P, P, P, P, P, P, SZ, P]
         L.qlora_trace_begin.argtypes = [ctypes.c_uint32, I32]
+        L.qlora_trace_pause.argtypes = [I32]
         L.qlora_trace_end.argtypes = [P, P]
         for name in ("qlora_quantize_nf4", "qlora_dequantize_nf4", "qlora_dequantize_absmax",
                      "qlora_linear_fwd", "qlora_linear_bwd", "qlora_trace_begin",
-                     "qlora_trace_end"):
+                     "qlora_trace_pause", "qlora_trace_end"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -234,6 +235,11 @@ def qlora_trace_begin(kernels, capacity: int = 4096):
     for k in kernels:
         mask |= 1 << KERNELS[k]
     _check(lib().qlora_trace_begin(mask, capacity), "qlora_trace_begin")
+
+
+def qlora_trace_pause(paused: bool):
+    """Stop (True) or resume (False) recording between begin and end."""
+    _check(lib().qlora_trace_pause(1 if paused else 0), "qlora_trace_pause")
 
 
 def qlora_trace_end():

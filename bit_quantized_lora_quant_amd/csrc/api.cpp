@@ -100,6 +100,7 @@ T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws)
 // ------------------------------------------------------ timing instrumentation
 struct Trace {
   uint32_t mask = 0;
+  bool paused = false;
   int32_t capacity = 0;
   hipEvent_t* ev[QLORA_KERNEL_COUNT] = {};   // 2 * capacity events per kernel
   int32_t used[QLORA_KERNEL_COUNT] = {};
@@ -122,7 +123,8 @@ namespace {
 template <typename F>
 hipError_t traced(int k, hipStream_t s, F&& launch) {
   (void)s;
-  const bool on = (g_trace.mask >> k) & 1u && g_trace.used[k] < g_trace.capacity;
+  const bool on =
+      !g_trace.paused && ((g_trace.mask >> k) & 1u) && g_trace.used[k] < g_trace.capacity;
   if (on) {
     pending_timing().start = g_trace.ev[k][2 * g_trace.used[k]];
     pending_timing().stop = g_trace.ev[k][2 * g_trace.used[k] + 1];
@@ -144,6 +146,7 @@ void trace_release() {
     g_trace.used[k] = 0;
   }
   g_trace.mask = 0;
+  g_trace.paused = false;
   g_trace.capacity = 0;
 }
 
@@ -339,6 +342,11 @@ qlora_status qlora_trace_begin(uint32_t kernel_mask, int32_t capacity) {
   }
   g_trace.mask = kernel_mask;
   g_trace.capacity = capacity;
+  return QLORA_OK;
+}
+
+qlora_status qlora_trace_pause(int32_t paused) {
+  g_trace.paused = paused != 0;
   return QLORA_OK;
 }
 

@@ -163,7 +163,11 @@ qlora_status qlora_linear_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
  * bit is set in `kernel_mask` (1 << qlora_kernel) records its own start and end
  * into a pair of HIP events (hipExtLaunchKernel: the dispatch itself takes the
  * timestamps, so no extra packets sit between kernels), for at most `capacity`
- * launches per kernel.  qlora_trace_end waits for those events (host synchronisation on
+ * launches per kernel.  qlora_trace_pause(1) stops recording (the launches run
+ * untimed, with no event work) until qlora_trace_pause(0); qlora_trace_begin
+ * starts unpaused.  A timed dispatch leaves the GPU idle for a few
+ * microseconds around it, so a benchmark times a sample of its launches.
+ * qlora_trace_end waits for those events (host synchronisation on
  * them only), writes the number of timed launches and their summed duration in
  * milliseconds into launches[QLORA_KERNEL_COUNT] / total_ms[QLORA_KERNEL_COUNT],
  * and releases the events.  Process-global state: not for concurrent use from
@@ -180,6 +184,7 @@ typedef enum {
 } qlora_kernel;
 
 qlora_status qlora_trace_begin(uint32_t kernel_mask, int32_t capacity);
+qlora_status qlora_trace_pause(int32_t paused);
 qlora_status qlora_trace_end(int32_t* launches, double* total_ms);
 
 #ifdef __cplusplus
