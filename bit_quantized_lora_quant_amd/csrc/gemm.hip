@@ -203,11 +203,11 @@ __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t& tm, int64_
 //   codes  [2 halves][256 rows][16 bytes]: half h = code bytes 16h..16h+15
 //          of the row's 32-byte step segment (sub-step h)              8 KB
 //   absmax [256 rows] fp32 (the block constant of the row at step kt)  1 KB
-// Each wave issues the same 11 DMA loads every step (8 X, 2 code, 1 absmax;
-// past the slice end they re-read its last step into a free stage), so the
-// end-of-step vmcnt(11) leaves exactly this step's loads in flight and the
-// previous step's have landed.
-constexpr int kStages = 3;
+// Every wave issues the same DMA loads every step (past the slice end they
+// re-read its last step into a free stage), so an end-of-step vmcnt(n), n =
+// the loads of one step, leaves exactly this step's loads in flight and the
+// previous step's have landed.  dX (4 waves): 8 activation, 2 code and 1
+// absmax loads per wave; forward (8 waves): 4, 1 and (waves 0-3) 1.
 constexpr int kDmaPerStep = 11;
 
 __device__ __forceinline__ void dma4(const void* g, const void* lds) {
@@ -218,15 +218,28 @@ __device__ __forceinline__ void dma4(const void* g, const void* lds) {
 template <int N>
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14)); }
 
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(1, 1)))
+// Two waves per SIMD: 8 waves, each owning a 256 x 32 slab (16 x 2 MFMA
+// tiles, 128 accumulators), so that while one wave waits (for LDS data, the
+// end-of-step barrier, a busy MFMA pipe) the other wave on its SIMD issues.
+// (One wave per SIMD with a 256 x 64 slab runs 6-12% slower: its stalls go
+// uncovered, while here every wave reads all 256 activation rows, which
+// doubles the A-operand LDS reads.)
+// Each W element is still dequantised once per workgroup: a wave rebuilds
+// the operands of its own 32 columns.  Group i (0..31) of a step is row tile
+// mt = i & 15 of sub-step s = i >> 4: two MFMAs with half a slice of dequant
+// work between them (one lookup, one multiply, every other group the
+// convert).  A wave issues 4 X, 1 code and (waves 0-3) 1 absmax DMA load
+// per step.
+constexpr int kThreadsW8 = 512;
+
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreadsW8, kThreadsW8),
+                          amdgpu_waves_per_eu(2, 2)))
 void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                     const uint8_t* __restrict__ codes, int64_t N,
                     const float* __restrict__ ahat_t, NF4Tables tab,
                     const uint16_t* __restrict__ xas, const uint16_t* __restrict__ B, int r,
                     int r32, uint16_t* __restrict__ Y, int splits, int ksteps,
                     float* __restrict__ part) {
-  // distinct objects per stage, statically selected by the 3x unrolled loop
   __shared__ __attribute__((aligned(16))) uint16_t xs0[kTile * kStep];
   __shared__ __attribute__((aligned(16))) uint16_t xs1[kTile * kStep];
   __shared__ __attribute__((aligned(16))) uint16_t xs2[kTile * kStep];
@@ -236,10 +249,9 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
   __shared__ __attribute__((aligned(16))) float as0[kTile];
   __shared__ __attribute__((aligned(16))) float as1[kTile];
   __shared__ __attribute__((aligned(16))) float as2[kTile];
-  // the level table first (largest alignment), at LDS address 0
-  __shared__ __attribute__((aligned(1024))) float lvl[16];
+  __shared__ __attribute__((aligned(1024))) float lvl[16];   // at LDS address 0
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0..7
   const int j16 = lane & 15, g = lane >> 4;
   int64_t tm, tn;
   int split;
@@ -247,178 +259,144 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
   const int64_t m0 = tm * kTile, n0 = tn * kTile;
   if (tid < 16) lvl[tid] = tab.level[tid];
 
-  // this workgroup's steps [kt0, kt1) of the K loop (split-K slice)
   const uint32_t KTall = (uint32_t)(K / kStep);
   const uint32_t kt0 = (uint32_t)split * (uint32_t)ksteps;
   const uint32_t kt1 = kt0 + (uint32_t)ksteps < KTall ? kt0 + (uint32_t)ksteps : KTall;
   const uint32_t N32 = (uint32_t)N;
 
-  // DMA sources of this lane (rows clamped; results for them are never stored)
-  TileDma<4> dma;
+  TileDma<8> dma;   // 4 X loads per wave
   dma.init(K, m0, M);
-  uint32_t cdma[2];   // code bytes: load i of wave wv fills LDS chunks 64(2wv+i)..+63
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int blk = 2 * wv + i;
-    int64_t n = n0 + (blk & 3) * 64 + lane;
-    n = n < N ? n : N - 1;
-    cdma[i] = (uint32_t)(n * (K / 2)) + (uint32_t)(16 * (blk >> 2));
-  }
-  uint32_t adma;      // absmax: row 64 wv + lane
+  uint32_t cdma;    // code chunks 64 wv .. 64 wv + 63 of the stage
   {
-    int64_t n = n0 + 64 * wv + lane;
+    int64_t n = n0 + (wv & 3) * 64 + lane;
+    n = n < N ? n : N - 1;
+    cdma = (uint32_t)(n * (K / 2)) + (uint32_t)(16 * (wv >> 2));
+  }
+  uint32_t adma;    // absmax rows 64 wv + lane (waves 0-3)
+  {
+    int64_t n = n0 + 64 * (wv & 3) + lane;
     adma = (uint32_t)(n < N ? n : N - 1);
   }
-  auto issue = [&](uint32_t tx, uint16_t* xd, uint32_t tc, uint32_t* cd, float* ad) {
-    tx = tx < kt1 ? tx : kt1 - 1;
-    tc = tc < kt1 ? tc : kt1 - 1;
-    dma.issue(X, tx * kStep, xd);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(codes + cdma[i] + tc * 32, cd + (2 * wv + i) * 256);
-    dma4(ahat_t + tc * N32 + adma, ad + 64 * wv);
+  auto issue_codes = [&](uint32_t tc, uint32_t* cd, float* ad) {
+    dma16(codes + cdma + tc * 32, cd + wv * 256);
+    if (wv < 4) dma4(ahat_t + tc * N32 + adma, ad + 64 * wv);
   };
-  // this lane's rows of the code / absmax stages
+  // this lane's two W rows 32 wv + 16 nt + j16
   auto read_codes = [&](const uint32_t* cs, const float* as, uint2* c, float* a) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int row = 64 * wv + 16 * nt + j16;
+    for (int nt = 0; nt < 2; ++nt) {
+      const int row = 32 * wv + 16 * nt + j16;
       c[nt] = make_uint2(cs[row * 4 + g], cs[(256 + row) * 4 + g]);
       a[nt] = as[row];
     }
   };
 
-  f32x4_t acc[16][4];
+  f32x4_t acc[16][2];
 #pragma unroll
   for (int mt = 0; mt < 16; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < 2; ++nt) {
       acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      asm volatile("" : "+a"(acc[mt][nt]));   // materialise in AGPRs, in order
+      asm volatile("" : "+a"(acc[mt][nt]));
     }
   mfma_settle();
 
-  // prologue: X(kt0) and codes(kt0), codes(kt0+1) resident; then the loads
-  // the first step's end-of-step wait is for: X(kt0+1), codes(kt0+2)
-  issue(kt0, xs0, kt0, cs0, as0);
-  {
-    const uint32_t t1 = kt0 + 1 < kt1 ? kt0 + 1 : kt1 - 1;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(codes + cdma[i] + t1 * 32, cs1 + (2 * wv + i) * 256);
-    dma4(ahat_t + t1 * N32 + adma, as1 + 64 * wv);
-  }
+  const uint32_t tl = kt1 - 1;
+  dma.issue(X, kt0 * kStep, xs0);
+  issue_codes(kt0, cs0, as0);
+  issue_codes(kt0 + 1 < kt1 ? kt0 + 1 : tl, cs1, as1);
   wait_vmem_all();
   __syncthreads();
-  uint2 cc[4], cn[4];
-  float ac[4], an[4];
+  uint2 cc[2], cn[2];
+  float ac[2], an[2];
   read_codes(cs0, as0, cc, ac);
   read_codes(cs1, as1, cn, an);
-  issue(kt0 + 1, xs1, kt0 + 2, cs2, as2);
+  dma.issue(X, (kt0 + 1 < kt1 ? kt0 + 1 : tl) * kStep, xs1);
+  issue_codes(kt0 + 2 < kt1 ? kt0 + 2 : tl, cs2, as2);
 
-  uint32_t bop[2][4][4];
+  uint32_t bop[2][2][4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
+  for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
     for (int dw = 0; dw < 4; ++dw)
       bop[0][nt][dw] = pack_bf16x2(lvl[(cc[nt].x >> (8 * dw)) & 15u] * ac[nt],
                                    lvl[(cc[nt].x >> (8 * dw + 4)) & 15u] * ac[nt]);
 
-  // Group i (0..31) of a step: sub-step s = i >> 4, row tile mt = i & 15, four
-  // MFMAs (nt).  Slice i (nt = (i >> 2) & 3, dw = i & 3) rebuilds
-  // bop[s ^ 1][nt][dw] from code word k = i >> 2 of the step's word sequence
-  // (this step's .y for k < 4, next step's .x for k < 8, next step's .y for
-  // the slices 32.. that are the next step's 0..).  The A operand of group i
-  // and the two level lookups of slice i are fetched 4 groups ahead.
-  //
-  // One wave per SIMD hides about two VALU instructions behind each MFMA, so
-  // a group places its work between its four MFMAs (scheduling barriers keep
-  // the order): lookup, lookup, two multiplies, convert + A read.  A lookup
-  // address is one byte extract: each code word is pre-spread once into
-  // 4 x (low nibble) and 4 x (high nibble) per byte, which with the level
-  // table at LDS address 0 is the byte offset of the level.
+  // Slice j (0..15) of a step rebuilds bop[s ^ 1][nt = (j >> 2) & 1][dw = j & 3]
+  // during groups 2j, 2j + 1 (s = j >> 3) from code word k = j >> 2: this
+  // step's .y (k < 2), the next step's .x (k < 4), and for the lookahead the
+  // next step's .y (k = 4, 5).  Its two level lookups happen four groups
+  // earlier (half-slice h = 2j + half in group h - 4).
   auto lvl_at = [&](uint32_t off) { return *reinterpret_cast<const float*>(
                                         reinterpret_cast<const char*>(lvl) + off); };
-  auto word = [&](int k) -> uint32_t {   // code word k (0..9) of this step
-    const int nt = k & 3;
-    return k < 4 ? cc[nt].y : (k < 8 ? cn[nt].x : cn[nt].y);
+  auto word = [&](int k) -> uint32_t {
+    const int nt = k & 1;
+    return k < 2 ? cc[nt].y : (k < 4 ? cn[nt].x : cn[nt].y);
   };
-  uint32_t w4lo[2], w4hi[2];   // spread words, slot k & 1
+  uint32_t w4lo[2], w4hi[2];
   auto spread = [&](int k) {
     const uint32_t w = word(k);
     w4lo[k & 1] = (w << 2) & 0x3C3C3C3Cu;
     w4hi[k & 1] = (w >> 2) & 0x3C3C3C3Cu;
-    // opaque to the optimiser, which would otherwise fold the spread back
-    // into a shift and mask of w at every lookup (two instructions, not one)
     asm volatile("" : "+v"(w4lo[k & 1]), "+v"(w4hi[k & 1]));
   };
   auto byte_of = [](uint32_t w, int b) -> uint32_t {
     return b == 0 ? (w & 0xFFu) : (b == 3 ? (w >> 24) : ((w >> (8 * b)) & 0xFFu));
   };
+  auto lookup = [&](int h) {   // level of half-slice h
+    const int js = h >> 1, k = js >> 2;
+    return lvl_at(byte_of((h & 1) ? w4hi[k & 1] : w4lo[k & 1], js & 3));
+  };
   constexpr int kD = 4;
   uint4 aq[kD];
-  float lqa[8], lqb[8];   // slice k's two levels at k % 8
+  float lq[2][4];   // slice j's levels at [half][j & 3]
+  float v0 = 0.f;
   spread(0);
-  spread(1);
 #pragma unroll
   for (int d = 0; d < kD; ++d) {
     aq[d] = lds_chunk(xs0, d * 16 + j16, g);
-    lqa[d] = lvl_at(byte_of(w4lo[0], d));
-    lqb[d] = lvl_at(byte_of(w4hi[0], d));
+    lq[d & 1][(d >> 1) & 3] = lookup(d);
   }
 
-  // one step: MFMAs read X stage `xb`; DMA fills X stage `xd` (tile kt+2)
-  // and code stage `cd`/`ad` (tile kt+3), spread over the step; at the end
-  // the code stage of tile kt+2 (`cr`/`ar`) and X stage `xr` (tile kt+1)
-  // are read
   auto step = [&](uint32_t kt, const uint16_t* xb, uint16_t* xd, uint32_t* cd, float* ad,
                   const uint32_t* cr, const float* ar, const uint16_t* xr) {
-    const uint32_t tx = kt + 2 < kt1 ? kt + 2 : kt1 - 1;
-    const uint32_t tc = kt + 3 < kt1 ? kt + 3 : kt1 - 1;
+    const uint32_t tx = kt + 2 < kt1 ? kt + 2 : tl;
+    const uint32_t tc = kt + 3 < kt1 ? kt + 3 : tl;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       const int s = i >> 4, mt = i & 15, q = i % kD;
-      const int ia = i + kD, ka = ia >> 2;
+      const int h = i + kD;
       mfma_acc(acc[mt][0], aq[q], u32x4v_t{bop[s][0][0], bop[s][0][1], bop[s][0][2], bop[s][0][3]});
       __builtin_amdgcn_sched_barrier(0);
-      lqa[ia & 7] = lvl_at(byte_of(w4lo[ka & 1], ia & 3));
-      if ((i & 7) == 0) {   // X tile kt+2: two of this wave's eight loads
-#pragma unroll
-        for (int l = 2 * (i >> 3); l < 2 * (i >> 3) + 2; ++l)
-          dma16(X + tx * kStep + dma.off[l], xd + (8 * wv + l) * 512);
-      }
+      lq[h & 1][(h >> 1) & 3] = lookup(h);
+      if ((i & 7) == 0) dma16(X + tx * kStep + dma.off[i >> 3], xd + (4 * wv + (i >> 3)) * 512);
+      if (i == 4) issue_codes(tc, cd, ad);
+      if ((i & 7) == 0) spread((i >> 3) + 1);
       __builtin_amdgcn_sched_barrier(0);
       mfma_acc(acc[mt][1], aq[q], u32x4v_t{bop[s][1][0], bop[s][1][1], bop[s][1][2], bop[s][1][3]});
       __builtin_amdgcn_sched_barrier(0);
-      lqb[ia & 7] = lvl_at(byte_of(w4hi[ka & 1], ia & 3));
-      if ((i & 3) == 0) spread((i >> 2) + 2);
-      if (i == 4) {         // code and absmax tiles of kt+3
-#pragma unroll
-        for (int l = 0; l < 2; ++l) dma16(codes + cdma[l] + tc * 32, cd + (2 * wv + l) * 256);
-        dma4(ahat_t + tc * N32 + adma, ad + 64 * wv);
+      {
+        const int j = i >> 1, nt = (j >> 2) & 1, dw = j & 3;
+        const float sc = s ? an[nt] : ac[nt];
+        if ((i & 1) == 0) {
+          v0 = lq[0][j & 3] * sc;
+        } else {
+          bop[s ^ 1][nt][dw] = pack_bf16x2(v0, lq[1][j & 3] * sc);
+        }
       }
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_acc(acc[mt][2], aq[q], u32x4v_t{bop[s][2][0], bop[s][2][1], bop[s][2][2], bop[s][2][3]});
-      __builtin_amdgcn_sched_barrier(0);
-      const int nt = (i >> 2) & 3, dw = i & 3;
-      const float sc = s ? an[nt] : ac[nt];
-      const float v0 = lqa[i & 7] * sc, v1 = lqb[i & 7] * sc;
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_acc(acc[mt][3], aq[q], u32x4v_t{bop[s][3][0], bop[s][3][1], bop[s][3][2], bop[s][3][3]});
-      __builtin_amdgcn_sched_barrier(0);
-      bop[s ^ 1][nt][dw] = pack_bf16x2(v0, v1);
-      // group i+kD's A operand (this step only); its MFMAs have read aq[q]
-      if (ia < 32) aq[q] = lds_chunk(xb, (ia & 15) * 16 + j16, 4 * (ia >> 4) + g);
+      if (h < 32) aq[q] = lds_chunk(xb, (h & 15) * 16 + j16, 4 * (h >> 4) + g);
       __builtin_amdgcn_sched_barrier(0);
     }
     // X(kt+1) and codes(kt+2) have landed once only this step's loads remain
-    wait_vmem<kDmaPerStep>();
+    if (wv < 4) wait_vmem<6>();
+    else wait_vmem<5>();
     __syncthreads();
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) { cc[nt] = cn[nt]; ac[nt] = an[nt]; }
+    for (int nt = 0; nt < 2; ++nt) { cc[nt] = cn[nt]; ac[nt] = an[nt]; }
     read_codes(cr, ar, cn, an);
 #pragma unroll
     for (int d = 0; d < kD; ++d) aq[d] = lds_chunk(xr, d * 16 + j16, g);
   };
-  // tile t lives in X stage t % 3 (relative to kt0) and code stage t % 3
   uint32_t kt = kt0;
   for (; kt + 2 < kt1; kt += 3) {
     step(kt, xs0, xs2, cs0, as0, cs2, as2, xs1);
@@ -427,19 +405,18 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
   }
   if (kt < kt1) step(kt, xs0, xs2, cs0, as0, cs2, as2, xs1);
   if (kt + 1 < kt1) step(kt + 1, xs1, xs0, cs1, as1, cs0, as0, xs2);
-  wait_vmem_all();   // nothing left in flight into LDS at exit
+  wait_vmem_all();
   mfma_settle();
 
-  // LoRA up-projection as r32 extra inner columns: A operand s.XA (bf16,
-  // [M, r32], zero padded), B operand rows of B [N, r]; last K slice only
+  // LoRA up-projection as r32 extra inner columns (last K slice only)
   const bool bvec = (r % 8) == 0;
   const int tail = split == splits - 1 ? r32 / 32 : 0;
   for (int ts = 0; ts < tail; ++ts) {
     const int j0 = ts * 32 + g * 8;
-    uint4 bb[4];
+    uint4 bb[2];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      int64_t n = n0 + 64 * wv + 16 * nt + j16;
+    for (int nt = 0; nt < 2; ++nt) {
+      int64_t n = n0 + 32 * wv + 16 * nt + j16;
       n = n < N ? n : N - 1;
       const uint16_t* p = B + n * r + j0;
       if (bvec && j0 + 8 <= r) {
@@ -459,19 +436,16 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
       m = m < M ? m : M - 1;
       const uint4 a = *reinterpret_cast<const uint4*>(xas + m * r32 + j0);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma16x16x32(a, bb[nt], acc[mt][nt]);
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma16x16x32(a, bb[nt], acc[mt][nt]);
     }
   }
 
-  // epilogue: C[row 4g + v][col j16] of each 16x16 tile, one row tile at a
-  // time so only 16 accumulators are in flight.  Split-K slices write float32
-  // partials [split][M][N] that a second kernel adds in split order.
   float* pbase = part + (int64_t)split * M * N;
 #pragma unroll
   for (int mt = 0; mt < 16; ++mt) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int64_t n = n0 + 64 * wv + 16 * nt + j16;
+    for (int nt = 0; nt < 2; ++nt) {
+      const int64_t n = n0 + 32 * wv + 16 * nt + j16;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int64_t m = m0 + mt * 16 + 4 * g + v;
@@ -963,7 +937,7 @@ hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_
                            int r, int r32, uint16_t* Y, int splits, float* part, hipStream_t s) {
   const int ksteps = (int)ceil_div(K / kStep, splits);
   const int64_t grid = ceil_div(M, kTile) * ceil_div(N, kTile) * splits;
-  return launch_kernel(k_qlora_fwd_nt, dim3((unsigned)grid), dim3(kThreads), s, X, M, K, codes, N,
+  return launch_kernel(k_qlora_fwd_nt, dim3((unsigned)grid), dim3(kThreadsW8), s, X, M, K, codes, N,
                        ahat_t, host_tables(), xas, B, r, r32, Y, splits, ksteps, part);
 }
 
