@@ -20,6 +20,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
           "-Wall", "-Wno-unused-function"]
 DEVICE = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# per-source device flags: the decode kernel keeps its MFMA results in VGPRs
+# (with AGPR results it holds 16 blocks' results live and fits one wave fewer
+# per SIMD); the GEMMs pin their accumulators in AGPRs themselves
+EXTRA = {"gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
 def _compile(src: str) -> str:
@@ -27,7 +31,7 @@ def _compile(src: str) -> str:
     obj = os.path.join(OBJ_DIR, src + ".o")
     cmd = [HIPCC] + COMMON
     if src.endswith(".hip"):
-        cmd += DEVICE + ["-x", "hip"]
+        cmd += DEVICE + EXTRA.get(src, []) + ["-x", "hip"]
     cmd += ["-c", path, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:

@@ -122,21 +122,6 @@ __device__ __forceinline__ void mfma_acc_vw(f32x4_t& acc, const uint4& a, const 
 __device__ __forceinline__ void mfma_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// One LDS-DMA load (global_load_lds_dwordx4): 16 bytes per lane from `g`
-// land at LDS address lds + 16 * lane.  Issued from inline asm so that the
-// wait-count pass does not track it: while a compiler-visible LDS DMA is in
-// flight that pass can no longer count LDS reads precisely and waits for all
-// of them (lgkmcnt(0)) at every use.  The callers wait for the DMA
-// themselves (vmcnt and a barrier) before the tile is read; the memory
-// clobber keeps LDS reads of a stage ahead of the DMA that refills it.  An
-// M0 write needs one wait state before the DMA reads it.
-__device__ __forceinline__ void dma16(const void* g, const void* lds) {
-  const uint32_t a = (uint32_t)(uintptr_t)(lds_void_t*)lds;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(a) : "m0", "memory");
-}
 
 // Global -> LDS copy of an activation tile [256 rows][64 cols] bf16 with the
 // LDS-DMA loads (global_load_lds_dwordx4: no VGPRs, no VALU).  Each load
@@ -210,11 +195,6 @@ __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t& tm, int64_
 // absmax loads per wave; forward (8 waves): 4, 1 and (waves 0-3) 1.
 constexpr int kDmaPerStep = 11;
 
-__device__ __forceinline__ void dma4(const void* g, const void* lds) {
-  const uint32_t a = (uint32_t)(uintptr_t)(lds_void_t*)lds;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(g), "s"(a) : "m0", "memory");
-}
 template <int N>
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14)); }
 

@@ -5,11 +5,13 @@
 //  * LoRA down-projection slices: X . A^T over inner-index slices (first in
 //    the grid, so they start early and leave no tail);
 //  * weight streamers: 64 rows of W by at most 16 64-blocks (1024 inner
-//    indices).  A streamer issues all its code loads at once, stages its
-//    slice of X in LDS meanwhile, then per 64-block turns each lane's 16
-//    codes into bf16 levels through a 256-entry LDS table of level pairs
-//    (one lookup per code byte, no multiply); two MFMAs (tokens padded to
-//    16) give the block's dot products, and the block constant -- rebuilt in
+//    indices).  A streamer stages its code tile and its slice of X in LDS
+//    by DMA (2 rows x 512 contiguous bytes per load), then per 64-block turns each lane's
+//    16 codes into bf16 levels through a 16-entry LDS table at address 0
+//    (one conflict-free 16-bit lookup per code, no multiply: a 256-entry
+//    table of level pairs halves the lookups but its random rows collide in
+//    the LDS banks, which cost more); two MFMAs (tokens padded to 16) give
+//    the block's dot products, and the block constant -- rebuilt in
 //    registers from its int8 code, the scale and the mean -- scales them as
 //    they are accumulated.  No dequantised weight and no constant table is
 //    written.
@@ -42,26 +44,33 @@ struct DecodeArgs {
   SkinnyJob xa;                 // X . A^T slices (partials only)
 };
 
-__device__ __forceinline__ void build_pairs(uint32_t* pairs, const NF4Tables& tab) {
-  // entry v: bf16(level[v & 15]) | bf16(level[v >> 4]) << 16 (256 threads)
-  const int v = threadIdx.x;
-  float lo = 0.f, hi = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    lo = (v & 15) == i ? tab.level[i] : lo;
-    hi = (v >> 4) == i ? tab.level[i] : hi;
-  }
-  pairs[v] = pack_bf16x2(lo, hi);
+// The LDS arena of a streaming workgroup starts with the 16 bf16 levels.
+constexpr int kDecTab = 64;   // bytes reserved for the table (keeps the rest 16-byte aligned)
+constexpr int kDecCodes = kDecRows * kDecBlocks * 32;   // the code tile, 32 KB
+
+__device__ __forceinline__ void build_levels(uint16_t* tab16, const NF4Tables& tab) {
+  if (threadIdx.x < 16) tab16[threadIdx.x] = (uint16_t)(pack_bf16x2(tab.level[threadIdx.x], 0.f) & 0xFFFF);
 }
 
-// 8 codes (one 32-bit word) -> 8 bf16 levels as an MFMA operand
-__device__ __forceinline__ uint4 levels8(uint32_t c, const uint32_t* pairs) {
-  uint4 r;
-  r.x = pairs[c & 0xFFu];
-  r.y = pairs[(c >> 8) & 0xFFu];
-  r.z = pairs[(c >> 16) & 0xFFu];
-  r.w = pairs[c >> 24];
-  return r;
+// 8 codes (one 32-bit word, code 2j in the low nibble of byte j) -> 8 bf16
+// levels as an MFMA operand.  The word is spread into 2 x nibble per byte, the
+// byte offset of the level in the table at LDS address 0.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 levels8(uint32_t c, const uint16_t* tab16) {
+  uint32_t lo = (c << 1) & 0x1E1E1E1Eu, hi = (c >> 3) & 0x1E1E1E1Eu;
+  asm volatile("" : "+v"(lo), "+v"(hi));   // keep the spread: one extract per lookup
+  const char* t = reinterpret_cast<const char*>(tab16);
+  uint32_t r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t bl = j == 0 ? (lo & 0xFFu) : (j == 3 ? (lo >> 24) : ((lo >> (8 * j)) & 0xFFu));
+    const uint32_t bh = j == 0 ? (hi & 0xFFu) : (j == 3 ? (hi >> 24) : ((hi >> (8 * j)) & 0xFFu));
+    u16x2_t v;
+    v.x = *reinterpret_cast<const uint16_t*>(t + bl);
+    v.y = *reinterpret_cast<const uint16_t*>(t + bh);
+    r[j] = __builtin_bit_cast(uint32_t, v);
+  }
+  return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
 // v if keep (an all-ones mask), else 0: a value select the compiler cannot
@@ -70,8 +79,8 @@ __device__ __forceinline__ uint4 keep_if(uint4 v, uint32_t keep) {
   return make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
 }
 
-__device__ __forceinline__ void decode_rows(const DecodeArgs& a, const uint32_t* pairs,
-                                            uint16_t* xs, int64_t b) {
+__device__ __forceinline__ void decode_rows(const DecodeArgs& a, const uint16_t* tab16,
+                                            uint8_t* cs, uint16_t* xs, int64_t b) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j16 = lane & 15, g = lane >> 4;
@@ -81,7 +90,6 @@ __device__ __forceinline__ void decode_rows(const DecodeArgs& a, const uint32_t*
   const int64_t KB = a.K / kBlock;
   const int64_t kb0 = (int64_t)split * kDecBlocks;
   const int nblk = (int)(KB - kb0 < kDecBlocks ? KB - kb0 : kDecBlocks);   // >= 1
-  const uint8_t* crow = a.codes + nl * (a.K / 2) + 32 * kb0 + 8 * g;
   const int64_t qrow = nl * KB + kb0;
   const float mu = *a.mean;
   // Loads: constants, codes, then X, with no per-lane branch around them
@@ -97,72 +105,78 @@ __device__ __forceinline__ void decode_rows(const DecodeArgs& a, const uint32_t*
       sc[i] = a.scale[(qrow + ib) / kDqBlock];   // a word never crosses a 256-group
     }
   }
-  // all of this lane's codes: block i, bytes 8 g .. 8 g + 7
-  uint2 c[kDecBlocks];
+  // The code tile (64 rows x 16 blocks x 32 bytes) into LDS by DMA, each load
+  // two rows x 512 contiguous bytes.  Read back per lane (row, block i, bytes
+  // 8 g ..), a row's 16-byte chunks would all sit on the same banks; chunk q
+  // of row R is stored at position q ^ (R & 15) instead.  Chunks past the
+  // range re-read the last valid one (their blocks meet zero constants).
+  {
+    const int64_t n0 = (b / a.splits) * kDecRows;
 #pragma unroll
-  for (int i = 0; i < kDecBlocks; ++i)
-    c[i] = *reinterpret_cast<const uint2*>(crow + 32 * (i < nblk ? i : nblk - 1));
-  // X[m][64 kb0 .. 64 (kb0 + 16)) for LDS rows 0..M-1: 128 16-byte pieces
-  // per row (pieces past the range re-read the last valid one), at most 8 per
-  // thread, only as many rounds as the M rows need
-  const int64_t kx = 64 * kb0;
-  const int plim = 8 * nblk - 1;                 // last valid piece of a row
-  const int total = (int)a.M * 128;
-  const int rounds = (total + 255) >> 8;         // uniform
-  uint4 xv[8];
-#pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    if (it < rounds) {
-      int e = tid + 256 * it;
-      e = e < total ? e : total - 1;
-      const int m = e >> 7, q8 = e & 127;
-      xv[it] = *reinterpret_cast<const uint4*>(a.X + m * a.K + kx + 8 * (q8 < plim ? q8 : plim));
+    for (int i = 0; i < 8; ++i) {
+      const int jj = 8 * wv + i, r = 2 * jj + (lane >> 5);
+      int64_t nr = n0 + r;
+      nr = nr < a.N ? nr : a.N - 1;
+      int q = (lane & 31) ^ (r & 15);
+      q = q < 2 * nblk ? q : 2 * nblk - 1;
+      dma16(a.codes + nr * (a.K / 2) + 32 * kb0 + 16 * q, cs + jj * 1024);
     }
   }
-  // keep every load above this point: the scheduler would otherwise sink each
-  // X load down to its LDS store and serialise their latencies
-  asm volatile("" ::: "memory");
+  // X[m][64 kb0 .. 64 (kb0 + 16)) into LDS rows 0..M-1 by DMA: two 1 KB
+  // pieces per row, spread over the waves (chunks past the range re-read the
+  // last valid one; they meet zero constants)
+  const int64_t kx = 64 * kb0;
+  const int clim = 64 * nblk - 8;                 // last valid 8-element chunk
+#pragma unroll 1
+  for (int j = wv; j < 2 * (int)a.M; j += 4) {
+    const int m = j >> 1, col = 512 * (j & 1) + 8 * lane;
+    dma16(a.X + m * a.K + kx + (col < clim ? col : clim), xs + m * kDecXStride + 512 * (j & 1));
+  }
 
-  // blocks past the range get a zero constant: they add exactly nothing, and
-  // the block loop below has no branch (so blocks interleave)
-  float ahat[kDecBlocks];
-  if (grouped) {
-#pragma unroll
-    for (int i = 0; i < kDecBlocks; ++i) {
-      const float v =
-          __builtin_fmaf((float)(int8_t)((qw[i / 4] >> (8 * (i & 3))) & 0xFFu), sc[i / 4], mu);
-      ahat[i] = i < nblk ? v : 0.f;
-    }
-  } else {
+  // Blocks past the range get a zero constant: they add exactly nothing, and
+  // the block loop below has no branch.  Four-to-a-word constants are
+  // rebuilt where they are used (fewer live registers).
+  float ahat_u[kDecBlocks];
+  if (!grouped) {
 #pragma unroll
     for (int i = 0; i < kDecBlocks; ++i) {
       const float v = absmax_recon(a.q, a.scale, mu, qrow + (i < nblk ? i : nblk - 1));
-      ahat[i] = i < nblk ? v : 0.f;
+      ahat_u[i] = i < nblk ? v : 0.f;
     }
   }
-#pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int e = tid + 256 * it;
-    if (it < rounds && e < total)
-      *reinterpret_cast<uint4*>(xs + (e >> 7) * kDecXStride + 8 * (e & 127)) = xv[it];
-  }
+  auto ahat = [&](int i) {
+    if (!grouped) return ahat_u[i];
+    const float v =
+        __builtin_fmaf((float)(int8_t)((qw[i / 4] >> (8 * (i & 3))) & 0xFFu), sc[i / 4], mu);
+    return i < nblk ? v : 0.f;
+  };
   // row M stays zero: the padding token rows of the MFMA read it
   for (int e = tid; e < kDecXStride / 8; e += 256)
     *reinterpret_cast<uint4*>(xs + a.M * kDecXStride + 8 * e) = make_uint4(0u, 0u, 0u, 0u);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA pieces have landed
   __syncthreads();
 
   const uint16_t* xrow = xs + (j16 < a.M ? j16 : a.M) * kDecXStride + 16 * g;
+  const uint8_t* crow = cs + (16 * wv + j16) * 512 + 8 * (g & 1);
+  auto codes_of = [&](int i) {   // this lane's 8 code bytes of block i
+    return *reinterpret_cast<const uint2*>(crow + 16 * ((2 * i + (g >> 1)) ^ j16));
+  };
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  // block i: lane group g holds inner indices 16 g .. 16 g + 15 (8 per MFMA)
+  // block i: lane group g holds inner indices 16 g .. 16 g + 15 (8 per MFMA).
+  // Four blocks at a time (a scheduling barrier between the groups), so that
+  // only four MFMA results are live.
 #pragma unroll
   for (int i = 0; i < kDecBlocks; ++i) {
     const uint4 x0 = *reinterpret_cast<const uint4*>(xrow + 64 * i);
     const uint4 x1 = *reinterpret_cast<const uint4*>(xrow + 64 * i + 8);
     f32x4_t t = {0.f, 0.f, 0.f, 0.f};
-    t = mfma16x16x32(x0, levels8(c[i].x, pairs), t);
-    t = mfma16x16x32(x1, levels8(c[i].y, pairs), t);
+    const uint2 ci = codes_of(i);
+    t = mfma16x16x32(x0, levels8(ci.x, tab16), t);
+    t = mfma16x16x32(x1, levels8(ci.y, tab16), t);
+    const float ah = ahat(i);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(ahat[i], t[v], acc[v]);
+    for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(ah, t[v], acc[v]);
+    if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
   }
   // D[token 4g + v][row j16]
   float* base = a.partial + (int64_t)split * a.M * a.N;
@@ -234,17 +248,18 @@ __device__ __forceinline__ void xa_slice(const DecodeArgs& a, int r, int64_t sl,
 
 template <int RT>
 __global__ __launch_bounds__(256) void k_qlora_decode(DecodeArgs a, NF4Tables tab, int r) {
-  // one LDS arena (sized per launch) for either branch: [pairs 1 KB | X rows
-  // 0..M, row M zero] or the 4 KB of XA wave partials
+  // one LDS arena (sized per launch) for either branch: [16 bf16 levels |
+  // code tile | X rows 0..M, row M zero] or the 4 KB of XA wave partials
   extern __shared__ __attribute__((aligned(16))) uint8_t arena[];
   const int64_t b = blockIdx.x;
   if (b < a.xa_blocks) {
     xa_slice<RT>(a, r, b, reinterpret_cast<float (*)[4][64]>(arena));
   } else {
-    uint32_t* pairs = reinterpret_cast<uint32_t*>(arena);
-    uint16_t* xs = reinterpret_cast<uint16_t*>(arena + 256 * 4);
-    build_pairs(pairs, tab);
-    decode_rows(a, pairs, xs, b - a.xa_blocks);   // its barrier also covers the table
+    uint16_t* tab16 = reinterpret_cast<uint16_t*>(arena);
+    uint8_t* cs = arena + kDecTab;
+    uint16_t* xs = reinterpret_cast<uint16_t*>(arena + kDecTab + kDecCodes);
+    build_levels(tab16, tab);
+    decode_rows(a, tab16, cs, xs, b - a.xa_blocks);   // its barrier also covers the table
   }
 }
 
@@ -312,7 +327,7 @@ __global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__
 
 template <int RT>
 hipError_t decode_rt(const DecodeArgs& a, int r, int64_t blocks, hipStream_t s) {
-  const size_t stream = 256 * 4 + (size_t)(a.M + 1) * kDecXStride * 2;
+  const size_t stream = kDecTab + kDecCodes + (size_t)(a.M + 1) * kDecXStride * 2;
   const size_t xa = (size_t)kXaWaves * 4 * 64 * 4;
   return launch_kernel_lds(k_qlora_decode<RT>, dim3((unsigned)blocks), dim3(256),
                            stream > xa ? stream : xa, s, a, host_tables(), r);

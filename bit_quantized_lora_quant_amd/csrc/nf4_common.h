@@ -96,6 +96,30 @@ __device__ __forceinline__ float group8_max(float v) {
 
 __host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One LDS-DMA load (global_load_lds_dwordx4): 16 bytes per lane from `g`
+// land at LDS address lds + 16 * lane.  Issued from inline asm so that the
+// wait-count pass does not track it: while a compiler-visible LDS DMA is in
+// flight that pass can no longer count LDS reads precisely and waits for all
+// of them (lgkmcnt(0)) at every use.  The callers wait for the DMA
+// themselves (vmcnt and a barrier) before the tile is read; the memory
+// clobber keeps LDS reads of a stage ahead of the DMA that refills it.  An
+// M0 write needs one wait state before the DMA reads it.
+__device__ __forceinline__ void dma16(const void* g, const void* lds) {
+  const uint32_t a = (uint32_t)(uintptr_t)(lds_void_t*)lds;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(a) : "m0", "memory");
+}
+
+// Same, 4 bytes per lane (global_load_lds_dword).
+__device__ __forceinline__ void dma4(const void* g, const void* lds) {
+  const uint32_t a = (uint32_t)(uintptr_t)(lds_void_t*)lds;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(g), "s"(a) : "m0", "memory");
+}
+
+
 // Reconstructed block constant b: one fused multiply-add, q * S + mean.
 __device__ __forceinline__ float absmax_recon(const int8_t* q, const float* scale, float mu,
                                               int64_t b) {
