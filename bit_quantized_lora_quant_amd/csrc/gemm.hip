@@ -410,14 +410,19 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
         bb[nt].w = e[6] | ((uint32_t)e[7] << 16);
       }
     }
+    uint4 a[16];   // all 16 row tiles' loads in flight at once
 #pragma unroll
     for (int mt = 0; mt < 16; ++mt) {
       int64_t m = m0 + mt * 16 + j16;
       m = m < M ? m : M - 1;
-      const uint4 a = *reinterpret_cast<const uint4*>(xas + m * r32 + j0);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma16x16x32(a, bb[nt], acc[mt][nt]);
+      a[mt] = *reinterpret_cast<const uint4*>(xas + m * r32 + j0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma16x16x32(a[mt], bb[nt], acc[mt][nt]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   float* pbase = part + (int64_t)split * M * N;
@@ -558,14 +563,18 @@ void k_qlora_dx_nn(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
       bb[t].z = h[4] | (h[5] << 16);
       bb[t].w = h[6] | (h[7] << 16);
     }
+    uint4 a[16];   // all 16 row tiles' loads in flight at once
 #pragma unroll
     for (int mt = 0; mt < 16; ++mt) {
       int64_t m = m0 + mt * 16 + j16;
       m = m < M ? m : M - 1;
-      const uint4 a = *reinterpret_cast<const uint4*>(gs + m * r32 + j0);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc[mt][t] = mfma16x16x32(a, bb[t], acc[mt][t]);
+      a[mt] = *reinterpret_cast<const uint4*>(gs + m * r32 + j0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[mt][t] = mfma16x16x32(a[mt], bb[t], acc[mt][t]);
   }
 
   // epilogue: lane holds columns kc..kc+3 of rows 4g + v -> one 8-byte store
@@ -834,14 +843,18 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
       bb[t].z = h[4] | (h[5] << 16);
       bb[t].w = h[6] | (h[7] << 16);
     }
+    uint4 a[16];   // all 16 row tiles' loads in flight at once
 #pragma unroll
     for (int mt = 0; mt < 16; ++mt) {
       int64_t m = m0 + mt * 16 + j16;
       m = m < M ? m : M - 1;
-      const uint4 a = *reinterpret_cast<const uint4*>(gs + m * r32 + j0);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc[mt][t] = mfma16x16x32(a, bb[t], acc[mt][t]);
+      a[mt] = *reinterpret_cast<const uint4*>(gs + m * r32 + j0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[mt][t] = mfma16x16x32(a[mt], bb[t], acc[mt][t]);
   }
 
   // epilogue: lane holds columns kc..kc+3 of rows 4g + v -> one 8-byte
