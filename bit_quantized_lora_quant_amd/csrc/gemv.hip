@@ -73,12 +73,6 @@ __device__ __forceinline__ uint4 levels8(uint32_t c, const uint16_t* tab16) {
   return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
-// v if keep (an all-ones mask), else 0: a value select the compiler cannot
-// turn into a select of load addresses
-__device__ __forceinline__ uint4 keep_if(uint4 v, uint32_t keep) {
-  return make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
-}
-
 __device__ __forceinline__ void decode_rows(const DecodeArgs& a, const uint16_t* tab16,
                                             uint8_t* cs, uint16_t* xs, int64_t b) {
   const int tid = threadIdx.x, lane = tid & 63;

@@ -143,29 +143,39 @@ __device__ __forceinline__ void grad_slice(const GradJob& J, int64_t M, int r, i
     for (int jt = 0; jt < RT; ++jt) acc[t][jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const bool fast = pv && p0 + 128 <= J.P;   // workgroup-uniform
-  auto load_step = [&](int64_t mb, uint4 (&rows)[8], uint4 (&bu)[RT]) {
-    if (fast) {
+  // this lane's rows of U, clamped: a row past r feeds only output column
+  // j >= r, which is never stored (no branch or select around the loads, which
+  // would cost the two-steps-in-flight schedule)
+  const uint16_t* urow[RT];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        int64_t m = mb + 8 * g + e;
-        m = m < M ? m : M - 1;              // U is zero there
-        rows[e] = *reinterpret_cast<const uint4*>(J.T + m * J.P + pc);
-      }
-    } else {
+  for (int jt = 0; jt < RT; ++jt) {
+    const int u = jt * 16 + i16;
+    urow[jt] = J.U + (int64_t)(u < r ? u : r - 1) * J.ldu;
+  }
+  // step mb: rows mb + 8g + e of T (clamped below M; U is zero there) and
+  // columns mb + 8g .. + 7 of U (within ldu, a multiple of 32)
+  auto load_u = [&](int64_t mb, uint4 (&bu)[RT]) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        int64_t m = mb + 8 * g + e;
-        m = m < M ? m : M - 1;
-        rows[e] = load8_bf16(J.T + m * J.P, pc, J.P, pv);
-      }
+    for (int jt = 0; jt < RT; ++jt)
+      bu[jt] = *reinterpret_cast<const uint4*>(urow[jt] + mb + 8 * g);
+  };
+  auto load_step = [&](int64_t mb, uint4 (&rows)[8], uint4 (&bu)[RT]) {   // 128 columns in range
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int64_t m = mb + 8 * g + e;
+      m = m < M ? m : M - 1;
+      rows[e] = *reinterpret_cast<const uint4*>(J.T + m * J.P + pc);
     }
+    load_u(mb, bu);
+  };
+  auto load_step_ragged = [&](int64_t mb, uint4 (&rows)[8], uint4 (&bu)[RT]) {
 #pragma unroll
-    for (int jt = 0; jt < RT; ++jt) {
-      const int u = jt * 16 + i16;
-      const uint4 v =
-          *reinterpret_cast<const uint4*>(J.U + (int64_t)(u < r ? u : r - 1) * J.ldu + mb + 8 * g);
-      bu[jt] = u < r ? v : make_uint4(0u, 0u, 0u, 0u);
+    for (int e = 0; e < 8; ++e) {
+      int64_t m = mb + 8 * g + e;
+      m = m < M ? m : M - 1;
+      rows[e] = load8_bf16(J.T + m * J.P, pc, J.P, pv);
     }
+    load_u(mb, bu);
   };
   auto mfmas = [&](const uint4 (&rows)[8], const uint4 (&bu)[RT]) {
 #pragma unroll
@@ -185,28 +195,62 @@ __device__ __forceinline__ void grad_slice(const GradJob& J, int64_t M, int r, i
       for (int jt = 0; jt < RT; ++jt) acc[t][jt] = mfma16x16x32(a, bu[jt], acc[t][jt]);
     }
   };
-  constexpr int64_t stride = 4 * 32;
-  int64_t mb = mbeg + 32 * wv;
-  if constexpr (RT <= 2) {
-    // two steps in flight, as in the skinny product
+  // this wave's steps: mb = first + 128 i, i < cnt
+  const int64_t first = mbeg + 32 * wv;
+  const int64_t cnt = first < mend ? (mend - first + 127) / 128 : 0;
+  // Steps of 32 whole rows with 128 columns in range, at rank <= 32, read
+  // through buffer views (fixed byte offsets per lane, the step's base as the
+  // uniform offset), two steps in flight: the next step's loads are issued
+  // before this step's MFMAs.
+  const int64_t tbytes = M * J.P * 2, ubytes = (int64_t)r * J.ldu * 2;
+  const bool bufs = fast && RT <= 2 && tbytes <= kBufferMax && ubytes <= kBufferMax;
+  const int64_t cnt_fast = bufs && first + 32 <= mend ? (mend - first - 32) / 128 + 1 : 0;
+  if (cnt_fast > 0) {
+    const __amdgpu_buffer_rsrc_t tview = buffer_view(J.T, tbytes);
+    const __amdgpu_buffer_rsrc_t uview = buffer_view(J.U, ubytes);
+    uint32_t roff[8], uoff[RT];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) roff[e] = (uint32_t)((8 * g + e) * J.P + pc) * 2;
+#pragma unroll
+    for (int jt = 0; jt < RT; ++jt) uoff[jt] = (uint32_t)((urow[jt] - J.U) + 8 * g) * 2;
+    auto load_fast = [&](int64_t i, uint4 (&rows)[8], uint4 (&bu)[RT]) {
+      const int64_t mb = first + 128 * i;
+      const uint32_t tb = (uint32_t)(mb * J.P) * 2, ub = (uint32_t)mb * 2;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rows[e] = buffer_load16(tview, roff[e], tb);
+#pragma unroll
+      for (int jt = 0; jt < RT; ++jt) bu[jt] = buffer_load16(uview, uoff[jt], ub);
+    };
     uint4 r0[8], u0[RT], r1[8], u1[RT];
-    if (mb < mend) load_step(mb, r0, u0);
-    while (mb < mend) {
-      if (mb + stride < mend) load_step(mb + stride, r1, u1);
+    load_fast(0, r0, u0);
+    int64_t i = 0;
+    for (; i + 2 < cnt_fast; i += 2) {
+      load_fast(i + 1, r1, u1);
+      __builtin_amdgcn_sched_barrier(0);
       mfmas(r0, u0);
-      mb += stride;
-      if (mb >= mend) break;
-      if (mb + stride < mend) load_step(mb + stride, r0, u0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_fast(i + 2, r0, u0);
+      __builtin_amdgcn_sched_barrier(0);
       mfmas(r1, u1);
-      mb += stride;
+      __builtin_amdgcn_sched_barrier(0);
     }
-  } else {
-    // wide ranks: the accumulators fill the register file, one step at a time
-    for (; mb < mend; mb += stride) {
-      uint4 r0[8], u0[RT];
-      load_step(mb, r0, u0);
+    if (i + 1 < cnt_fast) {   // the last one or two steps, peeled
+      load_fast(i + 1, r1, u1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(r0, u0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(r1, u1);
+    } else {
       mfmas(r0, u0);
     }
+  }
+  // the rest (a last step of fewer rows, ragged columns, or wide ranks whose
+  // accumulators fill the register file): one step at a time, rows clamped
+  for (int64_t i = cnt_fast; i < cnt; ++i) {
+    uint4 r0[8], u0[RT];
+    if (fast) load_step(first + 128 * i, r0, u0);
+    else load_step_ragged(first + 128 * i, r0, u0);
+    mfmas(r0, u0);
   }
   // D[i = 4g + v][j16] of MFMA (t, jt): p = p0 + 8 (4g + v) + t, j = 16 jt + j16
   float* base = J.partial + (int64_t)split * J.P * r;
@@ -294,7 +338,9 @@ int skinny_slices(int64_t M, int64_t kin) {
   // finish step then); else about 256 workgroups, at least one 128-wide
   // step per wave
   const int64_t groups = ceil_div(M, 16);
-  if (groups >= 64) return 1;
+  // a long inner dimension over fewer row groups than CUs: two slices, so
+  // the launch covers the chip (the finish step costs less than the idle half)
+  if (groups >= 64) return groups < 256 && kin >= 8192 ? 2 : 1;
   int64_t ks = ceil_div(256, groups);
   const int64_t maxs = ceil_div(kin, (int64_t)kSkWaves * kSkStep);
   if (ks > maxs) ks = maxs;

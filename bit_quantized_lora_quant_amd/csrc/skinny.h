@@ -23,6 +23,29 @@ __device__ __forceinline__ uint4 load8_bf16(const uint16_t* __restrict__ p, int6
   return v;
 }
 
+// Raw buffer view of `bytes` bytes at p (reads past the end return zero).
+// Buffer loads take a wave-uniform byte offset in a scalar register on top
+// of a fixed per-lane offset, so a streaming loop that moves its base per
+// step does no vector address arithmetic (which, between a step's loads and
+// the previous step's MFMAs, makes the compiler drain the loads in flight).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void* p, int64_t bytes) {
+  const int n = bytes < 0x7FFFFFFF ? (int)bytes : 0x7FFFFFFF;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t v, uint32_t lane_off,
+                                               uint32_t uniform_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       v, (int)lane_off, (int)uniform_off, 0));
+}
+// byte offsets of a buffer view are 32-bit
+constexpr int64_t kBufferMax = 0x7FFFFFFF;
+
+// v if keep (an all-ones mask), else 0: a value select the compiler cannot
+// turn into a branch around the load
+__device__ __forceinline__ uint4 keep_if(uint4 v, uint32_t keep) {
+  return make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+}
+
 __device__ __forceinline__ uint16_t to_bf16(float v) {
   return (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFF);
 }
@@ -53,68 +76,95 @@ __device__ __forceinline__ void skinny_slice(const SkinnyJob& J, int64_t M, int 
   f32x4_t acc[RT];
 #pragma unroll
   for (int jt = 0; jt < RT; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // Operands of one step: sub-step s takes inner indices k + 32 s + 8 g ..
-  // + 7 from lane group g, so each load instruction reads 64 contiguous bytes
-  // per row.
-  auto load_step = [&](int64_t k, uint4 (&a)[4], uint4 (&bv)[RT][4]) {
-    if (tv && uv && k + kSkStep <= J.kin) {
-      // whole step in range (wave-uniform): plain vector loads; adapter rows
-      // past r are loaded clamped and zeroed by a select
+  // this lane's adapter rows, clamped: a row past r feeds only output column
+  // u >= r, which is never stored
+  const uint16_t* urow[RT];
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        a[s] = *reinterpret_cast<const uint4*>(trow + k + 32 * s + 8 * g);
+  for (int jt = 0; jt < RT; ++jt) {
+    const int u = jt * 16 + j16;
+    urow[jt] = J.U + (int64_t)(u < r ? u : r - 1) * J.ldu;
+  }
+  // the fast path reads both operands through buffer views: fixed byte
+  // offsets per lane, 2 k per step as the uniform offset
+  const int64_t tbytes = (M > 0 ? (M - 1) * J.ldt + J.kin : 0) * 2;
+  const int64_t ubytes = ((int64_t)(r - 1) * J.ldu + J.kin) * 2;
+  const __amdgpu_buffer_rsrc_t tview = buffer_view(J.T, tbytes);
+  const __amdgpu_buffer_rsrc_t uview = buffer_view(J.U, ubytes);
+  const uint32_t toff = (uint32_t)(mrow * J.ldt + 8 * g) * 2;
+  uint32_t uoff[RT];
 #pragma unroll
-      for (int jt = 0; jt < RT; ++jt) {
-        const int u = jt * 16 + j16;
-        const uint16_t* urow = J.U + (int64_t)(u < r ? u : r - 1) * J.ldu + k + 8 * g;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const uint4 v = *reinterpret_cast<const uint4*>(urow + 32 * s);
-          bv[jt][s] = u < r ? v : make_uint4(0u, 0u, 0u, 0u);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) a[s] = load8_bf16(trow, k + 32 * s + 8 * g, J.kin, tv);
-#pragma unroll
-      for (int jt = 0; jt < RT; ++jt) {
-        const int u = jt * 16 + j16;
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          bv[jt][s] = u < r ? load8_bf16(J.U + (int64_t)u * J.ldu, k + 32 * s + 8 * g, J.kin, uv)
-                            : make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-  };
-  constexpr int64_t stride = (int64_t)W * kSkStep;
-  int64_t k = kbeg + (int64_t)wv * kSkStep;
+  for (int jt = 0; jt < RT; ++jt) uoff[jt] = (uint32_t)((urow[jt] - J.U) + 8 * g) * 2;
   auto mfmas = [&](const uint4 (&a)[4], const uint4 (&bv)[RT][4]) {
 #pragma unroll
     for (int jt = 0; jt < RT; ++jt)
 #pragma unroll
       for (int s = 0; s < 4; ++s) acc[jt] = mfma16x16x32(a[s], bv[jt][s], acc[jt]);
   };
-  if constexpr (RT <= 4) {
-    // two steps in flight: the next step's loads are issued before this
-    // step's MFMAs
-    uint4 a0[4], b0[RT][4], a1[4], b1[RT][4];
-    if (k < kend) load_step(k, a0, b0);
-    while (k < kend) {
-      if (k + stride < kend) load_step(k + stride, a1, b1);
-      mfmas(a0, b0);
-      k += stride;
-      if (k >= kend) break;
-      if (k + stride < kend) load_step(k + stride, a0, b0);
-      mfmas(a1, b1);
-      k += stride;
+  // Operands of one step: sub-step s takes inner indices k + 32 s + 8 g ..
+  // + 7 from lane group g, so each load instruction reads 64 contiguous bytes
+  // per row.  Whole steps of a slice whose rows are 16-byte aligned run on
+  // plain vector loads with no branch and no per-lane select between them,
+  // two steps in flight: the next step's loads are issued before this
+  // step's MFMAs.
+  const bool vec = tv && uv && tbytes <= kBufferMax && ubytes <= kBufferMax;
+  const int64_t nfull = vec ? (kend - kbeg) / kSkStep : 0;        // whole steps
+  const int64_t cnt = nfull > wv ? (nfull - wv + W - 1) / W : 0;   // this wave's
+  auto kat = [&](int64_t i) { return kbeg + (wv + i * W) * (int64_t)kSkStep; };
+  auto load_fast = [&](int64_t k, uint4 (&a)[4], uint4 (&bv)[RT][4]) {
+    const uint32_t kb = (uint32_t)k * 2;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[s] = buffer_load16(tview, toff + 64 * s, kb);
+#pragma unroll
+    for (int jt = 0; jt < RT; ++jt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) bv[jt][s] = buffer_load16(uview, uoff[jt] + 64 * s, kb);
+  };
+  if (cnt > 0) {
+    if constexpr (RT <= 4) {
+      uint4 a0[4], b0[RT][4], a1[4], b1[RT][4];
+      load_fast(kat(0), a0, b0);
+      // (scheduling barriers keep the compiler from sinking the loads next
+      // to their MFMAs; the last one or two steps are peeled)
+      int64_t i = 0;
+      for (; i + 2 < cnt; i += 2) {
+        load_fast(kat(i + 1), a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_fast(kat(i + 2), a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (i + 1 < cnt) {
+        load_fast(kat(i + 1), a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(a1, b1);
+      } else {
+        mfmas(a0, b0);
+      }
+    } else {
+      for (int64_t i = 0; i < cnt; ++i) {   // r > 64: one step at a time
+        uint4 a0[4], b0[RT][4];
+        load_fast(kat(i), a0, b0);
+        mfmas(a0, b0);
+      }
     }
-  } else {
-    for (; k < kend; k += stride) {   // r > 64: one step at a time
-      uint4 a0[4], b0[RT][4];
-      load_step(k, a0, b0);
-      mfmas(a0, b0);
-    }
+  }
+  // the remaining steps (a partial last step, or every step of unaligned
+  // rows): element-wise loads with bounds
+  for (int64_t k = kat(cnt); k < kend; k += (int64_t)W * kSkStep) {
+    uint4 a0[4], b0[RT][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a0[s] = load8_bf16(trow, k + 32 * s + 8 * g, J.kin, tv);
+#pragma unroll
+    for (int jt = 0; jt < RT; ++jt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        b0[jt][s] = load8_bf16(urow[jt], k + 32 * s + 8 * g, J.kin, uv);
+    mfmas(a0, b0);
   }
 #pragma unroll
   for (int jt = 0; jt < RT; ++jt)
