@@ -63,7 +63,26 @@ def phi_inv(p: float) -> float:
     return float(_load().oracle_phi_inv(float(p)))
 
 
-def codebook() -> np.ndarray:
+QUANT_TYPES = ("nf4", "int4")
+
+
+def int4_codebook() -> np.ndarray:
+    """The uniform 4-bit table the NF4 type is set against ("QLoRA: Fine-Tuning
+    a 70B on One GPU", section "NF4 Quantization: Beyond Standard INT4": 16
+    integer levels at uniform intervals).  Reading: the sixteen 4-bit
+    two's-complement integers k = -8 .. 7 over the block absmax scaled to 7,
+    i.e. level k / 7 (computed in double, rounded once to float32).  Level -8/7
+    lies below -1, so for |x| <= 1 it is never the nearest: 15 levels are used,
+    with an exact zero (code 8) and the ends -1 (code 1) and +1 (code 15)."""
+    return (np.arange(-8, 8, dtype=np.float64) / 7.0).astype(np.float32)
+
+
+def codebook(kind: str = "nf4") -> np.ndarray:
+    """The 16 levels of a 4-bit type, ascending (code k holds level k)."""
+    if kind == "int4":
+        return int4_codebook()
+    if kind != "nf4":
+        raise ValueError("unknown 4-bit type %r" % (kind,))
     out = np.zeros(16, dtype=np.float32)
     _load().oracle_codebook(_ptr(out))
     return out
@@ -77,26 +96,31 @@ def num_dq_blocks(n: int) -> int:
     return (num_blocks(n) + DQ_BLOCK - 1) // DQ_BLOCK
 
 
-def quantize(w: np.ndarray) -> dict:
-    """Blockwise NF4 quantisation followed by double quantisation.
+def quantize(w: np.ndarray, kind: str = "nf4", dq: bool = True) -> dict:
+    """Blockwise 4-bit quantisation (the NF4 table, or the INT4 table it is set
+    against), followed by double quantisation of the constants unless dq is
+    False (the double-quant switch of the pages' configuration,
+    "Practical Implementation" section).
 
-    Returns codes (packed, uint8[ceil(n/2)]), the exact first-level absmax
-    (float32[nb]) and the stored constants absmax_q (int8[nb]),
-    absmax_scale (float32[nd]) and absmax_mean (float32 scalar)."""
+    Returns codes (packed, uint8[ceil(n/2)]) and the exact first-level absmax
+    (float32[nb]), which without double quantisation is the stored constant;
+    with it, the stored constants absmax_q (int8[nb]), absmax_scale
+    (float32[nd]) and absmax_mean (float32 scalar)."""
     w = np.ascontiguousarray(w, dtype=np.float32).reshape(-1)
     n = w.size
     if n == 0:
         raise ValueError("empty tensor")
     nb = num_blocks(n)
-    nd = num_dq_blocks(n)
-    cb = codebook()
+    cb = codebook(kind)
     codes = np.zeros((n + 1) // 2, dtype=np.uint8)
     absmax = np.zeros(nb, dtype=np.float32)
     lib = _load()
     lib.oracle_quantize(_ptr(w), n, _ptr(cb), _ptr(codes), _ptr(absmax))
-    q, scale, mean = double_quant(absmax)
-    return {"n": n, "codes": codes, "absmax": absmax, "absmax_q": q,
-            "absmax_scale": scale, "absmax_mean": mean}
+    out = {"n": n, "codes": codes, "absmax": absmax, "kind": kind, "dq": dq}
+    if dq:
+        q, scale, mean = double_quant(absmax)
+        out.update({"absmax_q": q, "absmax_scale": scale, "absmax_mean": mean})
+    return out
 
 
 def double_quant(absmax: np.ndarray):
@@ -124,12 +148,20 @@ def dequant_absmax(absmax_q: np.ndarray, absmax_scale: np.ndarray, absmax_mean) 
     return out
 
 
+def block_constants(qt: dict) -> np.ndarray:
+    """The constant each 64-block dequantises with: the reconstruction from
+    the 8-bit state, or the stored float32 absmax without double quantisation."""
+    if qt.get("dq", True):
+        return dequant_absmax(qt["absmax_q"], qt["absmax_scale"], qt["absmax_mean"])
+    return np.ascontiguousarray(qt["absmax"], dtype=np.float32)
+
+
 def dequantize(qt: dict) -> np.ndarray:
     """float32 dequantised weights (flat), from the stored state only."""
-    ahat = dequant_absmax(qt["absmax_q"], qt["absmax_scale"], qt["absmax_mean"])
+    ahat = block_constants(qt)
     n = qt["n"]
     out = np.zeros(n, dtype=np.float32)
-    cb = codebook()
+    cb = codebook(qt.get("kind", "nf4"))
     _load().oracle_dequant(_ptr(np.ascontiguousarray(qt["codes"])), _ptr(ahat), n,
                            _ptr(cb), _ptr(out))
     return out
