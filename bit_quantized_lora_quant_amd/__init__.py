@@ -16,12 +16,14 @@ LIB_PATH = os.path.join(_HERE, "libqlora_nf4.so")
 
 QLORA_OK, QLORA_ERR_INVALID_ARG, QLORA_ERR_UNSUPPORTED, QLORA_ERR_WORKSPACE, QLORA_ERR_HIP = range(5)
 QLORA_F32, QLORA_BF16 = 0, 1
+QUANT_TYPES = {"nf4": 0, "int4": 1}   # QLORA_QUANT_NF4, QLORA_QUANT_INT4
 NF4_BLOCK = 64
 DQ_BLOCK = 256
 MAX_RANK = 128
 
 EXPORTS = [
-    "qlora_nf4_codebook", "qlora_status_string", "qlora_quantize_workspace_bytes",
+    "qlora_nf4_codebook", "qlora_codebook", "qlora_status_string",
+    "qlora_quantize_workspace_bytes",
     "qlora_quantize_nf4", "qlora_dequantize_nf4", "qlora_dequantize_absmax",
     "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_trace_begin", "qlora_trace_pause", "qlora_trace_end",
@@ -40,7 +42,9 @@ class NF4Descriptor(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
                 ("block", ctypes.c_int32), ("dq_block", ctypes.c_int32),
                 ("codes", ctypes.c_void_p), ("absmax_q", ctypes.c_void_p),
-                ("absmax_scale", ctypes.c_void_p), ("absmax_mean", ctypes.c_void_p)]
+                ("absmax_scale", ctypes.c_void_p), ("absmax_mean", ctypes.c_void_p),
+                ("absmax", ctypes.c_void_p), ("quant_type", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -59,6 +63,8 @@ def lib():
         D = ctypes.POINTER(NF4Descriptor)
         L.qlora_nf4_codebook.argtypes = [P]
         L.qlora_nf4_codebook.restype = None
+        L.qlora_codebook.argtypes = [I32, P]
+        L.qlora_codebook.restype = ctypes.c_int
         L.qlora_status_string.argtypes = [ctypes.c_int]
         L.qlora_status_string.restype = ctypes.c_char_p
         L.qlora_quantize_workspace_bytes.argtypes = [I64, I64]
@@ -105,31 +111,51 @@ def qlora_nf4_codebook():
     return [float(v) for v in buf]
 
 
-class NF4Tensor:
-    """Quantised frozen weight: device buffers owned by torch."""
+def qlora_codebook(quant_type: str = "nf4"):
+    """The 16 levels of a 4-bit type ("nf4" or "int4") as a list of floats."""
+    buf = (ctypes.c_float * 16)()
+    _check(lib().qlora_codebook(QUANT_TYPES[quant_type], buf), "qlora_codebook")
+    return [float(v) for v in buf]
 
-    def __init__(self, rows: int, cols: int, device):
+
+class NF4Tensor:
+    """Quantised frozen weight: device buffers owned by torch.  quant_type
+    "nf4" or "int4"; double_quant False keeps float32 block constants."""
+
+    def __init__(self, rows: int, cols: int, device, quant_type: str = "nf4",
+                 double_quant: bool = True):
         n = rows * cols
         nb = (n + NF4_BLOCK - 1) // NF4_BLOCK
         nd = (nb + DQ_BLOCK - 1) // DQ_BLOCK
         self.rows, self.cols = rows, cols
+        self.quant_type, self.double_quant = quant_type, double_quant
         self.codes = torch.empty((n + 1) // 2, dtype=torch.uint8, device=device)
-        self.absmax_q = torch.empty(nb, dtype=torch.int8, device=device)
-        self.absmax_scale = torch.empty(nd, dtype=torch.float32, device=device)
-        self.absmax_mean = torch.empty(1, dtype=torch.float32, device=device)
+        self.absmax_q = self.absmax_scale = self.absmax_mean = self.absmax = None
+        if double_quant:
+            self.absmax_q = torch.empty(nb, dtype=torch.int8, device=device)
+            self.absmax_scale = torch.empty(nd, dtype=torch.float32, device=device)
+            self.absmax_mean = torch.empty(1, dtype=torch.float32, device=device)
+        else:
+            self.absmax = torch.empty(nb, dtype=torch.float32, device=device)
 
     @property
     def numel(self):
         return self.rows * self.cols
 
+    @property
+    def num_blocks(self):
+        return (self.numel + NF4_BLOCK - 1) // NF4_BLOCK
+
     def descriptor(self) -> NF4Descriptor:
-        return NF4Descriptor(self.rows, self.cols, NF4_BLOCK, DQ_BLOCK,
-                             self.codes.data_ptr(), self.absmax_q.data_ptr(),
-                             self.absmax_scale.data_ptr(), self.absmax_mean.data_ptr())
+        p = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
+        return NF4Descriptor(self.rows, self.cols, NF4_BLOCK, DQ_BLOCK if self.double_quant else 0,
+                             p(self.codes), p(self.absmax_q), p(self.absmax_scale),
+                             p(self.absmax_mean), p(self.absmax), QUANT_TYPES[self.quant_type], 0)
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size()
-                   for t in (self.codes, self.absmax_q, self.absmax_scale, self.absmax_mean))
+                   for t in (self.codes, self.absmax_q, self.absmax_scale, self.absmax_mean,
+                             self.absmax) if t is not None)
 
 
 def qlora_quantize_workspace_bytes(rows: int, cols: int) -> int:
@@ -144,13 +170,15 @@ def workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
-def qlora_quantize_nf4(W: torch.Tensor, q: NF4Tensor = None, ws: torch.Tensor = None):
+def qlora_quantize_nf4(W: torch.Tensor, q: NF4Tensor = None, ws: torch.Tensor = None,
+                       quant_type: str = "nf4", double_quant: bool = True):
     """Quantise a float32 [rows, cols] device tensor; returns (NF4Tensor,
-    workspace).  The workspace's first nb floats hold the exact block absmax."""
+    workspace).  With double quantisation the workspace's first nb floats hold
+    the exact block absmax; without it the tensor's absmax holds them."""
     assert W.dtype == torch.float32 and W.is_contiguous() and W.dim() == 2
     rows, cols = W.shape
     if q is None:
-        q = NF4Tensor(rows, cols, W.device)
+        q = NF4Tensor(rows, cols, W.device, quant_type, double_quant)
     need = qlora_quantize_workspace_bytes(rows, cols)
     if ws is None:
         ws = workspace(need, W.device)
@@ -173,7 +201,7 @@ def qlora_dequantize_nf4(q: NF4Tensor, dtype=torch.bfloat16, out: torch.Tensor =
 
 def qlora_dequantize_absmax(q: NF4Tensor, out: torch.Tensor = None):
     if out is None:
-        out = torch.empty(q.absmax_q.numel(), dtype=torch.float32, device=q.codes.device)
+        out = torch.empty(q.num_blocks, dtype=torch.float32, device=q.codes.device)
     d = q.descriptor()
     _check(lib().qlora_dequantize_absmax(ctypes.byref(d), _ptr(out), _stream()),
            "qlora_dequantize_absmax")

@@ -23,14 +23,24 @@ int64_t nblocks(int64_t n) { return ceil_div(n, kBlock); }
 
 bool valid_tensor(const qlora_nf4_tensor* q) {
   if (!q || q->rows < 1 || q->cols < 1) return false;
-  if (q->block != QLORA_NF4_BLOCK || q->dq_block != QLORA_DQ_BLOCK) return false;
-  if (!q->codes || !q->absmax_q || !q->absmax_scale || !q->absmax_mean) return false;
-  if (!aligned(q->codes, 4) || !aligned(q->absmax_q, 4) || !aligned(q->absmax_scale, 4) ||
-      !aligned(q->absmax_mean, 4))
+  if (q->block != QLORA_NF4_BLOCK) return false;
+  if (q->quant_type != QLORA_QUANT_NF4 && q->quant_type != QLORA_QUANT_INT4) return false;
+  if (q->reserved != 0 || !q->codes || !aligned(q->codes, 4)) return false;
+  if (q->dq_block == QLORA_DQ_BLOCK) {
+    if (!q->absmax_q || !q->absmax_scale || !q->absmax_mean) return false;
+    if (!aligned(q->absmax_q, 4) || !aligned(q->absmax_scale, 4) || !aligned(q->absmax_mean, 4))
+      return false;
+  } else if (q->dq_block == 0) {
+    if (!q->absmax || !aligned(q->absmax, 4)) return false;
+  } else {
     return false;
+  }
   if (q->rows > INT64_MAX / q->cols) return false;
   return true;
 }
+
+// float32 block constants of a tensor quantised without double quantisation
+const float* f32_consts(const qlora_nf4_tensor* q) { return q->dq_block == 0 ? q->absmax : nullptr; }
 
 qlora_status hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP; }
 
@@ -168,6 +178,13 @@ void qlora_nf4_codebook(float out[16]) {
   if (out) std::memcpy(out, host_tables().level, sizeof(float) * 16);
 }
 
+qlora_status qlora_codebook(int32_t quant_type, float out[16]) {
+  if (!out || (quant_type != QLORA_QUANT_NF4 && quant_type != QLORA_QUANT_INT4))
+    return QLORA_ERR_INVALID_ARG;
+  std::memcpy(out, host_tables(quant_type).level, sizeof(float) * 16);
+  return QLORA_OK;
+}
+
 const char* qlora_status_string(qlora_status s) {
   switch (s) {
     case QLORA_OK: return "ok";
@@ -191,10 +208,12 @@ qlora_status qlora_quantize_nf4(const float* W, const qlora_nf4_tensor* q, void*
   const QuantWs L = quant_layout(n);
   if (!ws || ws_bytes < L.total || !aligned(ws, kAlign)) return QLORA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* absmax = at<float>(ws, L.absmax);
-  hipError_t e = traced(QLORA_KERNEL_QUANTIZE, s,
-                        [&] { return launch_quant_absmax(W, n, q->codes, absmax, s); });
-  if (e != hipSuccess) return QLORA_ERR_HIP;
+  // without double quantisation the exact absmax is the stored constant
+  float* absmax = q->dq_block == 0 ? q->absmax : at<float>(ws, L.absmax);
+  hipError_t e = traced(QLORA_KERNEL_QUANTIZE, s, [&] {
+    return launch_quant_absmax(W, n, q->codes, absmax, q->quant_type, s);
+  });
+  if (e != hipSuccess || q->dq_block == 0) return hip_status(e);
   e = launch_dq(absmax, nblocks(n), q->absmax_q, q->absmax_scale, q->absmax_mean,
                 at<double>(ws, L.pa), at<double>(ws, L.pb), s);
   return hip_status(e);
@@ -206,15 +225,15 @@ qlora_status qlora_dequantize_nf4(const qlora_nf4_tensor* q, qlora_dtype out_dty
   if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16) return QLORA_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(traced(QLORA_KERNEL_DEQUANT, s, [&] {
-    return launch_dequant(q->codes, q->absmax_q, q->absmax_scale, q->absmax_mean,
-                          q->rows * q->cols, out_dtype == QLORA_BF16, out, s);
+    return launch_dequant(q->codes, q->absmax_q, q->absmax_scale, q->absmax_mean, f32_consts(q),
+                          q->rows * q->cols, out_dtype == QLORA_BF16, out, q->quant_type, s);
   }));
 }
 
 qlora_status qlora_dequantize_absmax(const qlora_nf4_tensor* q, float* out, void* stream) {
   if (!valid_tensor(q) || !out) return QLORA_ERR_INVALID_ARG;
   return hip_status(launch_absmax_recon(q->absmax_q, q->absmax_scale, q->absmax_mean,
-                                        nblocks(q->rows * q->cols), out,
+                                        f32_consts(q), nblocks(q->rows * q->cols), out,
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -237,7 +256,8 @@ qlora_status qlora_linear_fwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
   const float scale = alpha / (float)r;
   hipError_t e;
   if (M <= 16) {
-    const NF4Ref w{W->codes, W->absmax_q, W->absmax_scale, W->absmax_mean};
+    const NF4Ref w{W->codes, W->absmax_q, W->absmax_scale, W->absmax_mean, f32_consts(W),
+                   W->quant_type};
     float* part = at<float>(ws, L.gemv_part);
     float* xa_part = at<float>(ws, L.dec_xa);
     e = traced(QLORA_KERNEL_GEMV, s, [&] {
@@ -252,12 +272,14 @@ qlora_status qlora_linear_fwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
   // with the block constants reconstructed in the same launch
   SkinnyJob xa{X, K, K, A, K, 0, 0, at<float>(ws, L.sk_k), scale, xas, XA_out, nullptr, 0};
   skinny_plan(&xa, M);
-  const ReconJob rc{W->absmax_q, W->absmax_scale, W->absmax_mean, N, K / kBlock, ahat_t};
+  const ReconJob rc{W->absmax_q, W->absmax_scale, W->absmax_mean, N, K / kBlock, ahat_t,
+                    f32_consts(W)};
   e = launch_skinny(&xa, 1, M, r, L.r32, &rc, s);
   if (e != hipSuccess) return QLORA_ERR_HIP;
   float* part = at<float>(ws, L.gemm_part);
   e = traced(QLORA_KERNEL_FWD_GEMM, s, [&] {
-    return launch_fwd_gemm(X, M, K, W->codes, N, ahat_t, xas, B, r, L.r32, Y, L.sf, part, s);
+    return launch_fwd_gemm(X, M, K, W->codes, N, ahat_t, xas, B, r, L.r32, Y, L.sf, part,
+                           W->quant_type, s);
   });
   if (e == hipSuccess && L.sf > 1)
     e = traced(QLORA_KERNEL_SPLIT_REDUCE, s,
@@ -291,7 +313,8 @@ qlora_status qlora_linear_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
   int nt = 0;
   tj[nt++] = TransposeJob{B, N, r, bt, L.np};
   if (XA_in) tj[nt++] = TransposeJob{XA_in, M, r, xat, L.mp};
-  const ReconJob rc{W->absmax_q, W->absmax_scale, W->absmax_mean, N, K / kBlock, ahat_t};
+  const ReconJob rc{W->absmax_q, W->absmax_scale, W->absmax_mean, N, K / kBlock, ahat_t,
+                    f32_consts(W)};
   QL_TRY(launch_prep(tj, nt, dX ? &rc : nullptr, s));
   // G = dY.B as bf16(s.G) [M, r32] (dX tail) and bf16(G)^T [r, M32] (dA);
   // without the forward's XA, X.A^T is recomputed beside it
@@ -307,7 +330,8 @@ qlora_status qlora_linear_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
   if (dX) {
     float* part = at<float>(ws, L.gemm_part);
     QL_TRY(traced(QLORA_KERNEL_DX_GEMM, s, [&] {
-      return launch_dx_gemm(dY, M, N, W->codes, K, ahat_t, gs, A, r, L.r32, dX, L.sx, part, s);
+      return launch_dx_gemm(dY, M, N, W->codes, K, ahat_t, gs, A, r, L.r32, dX, L.sx, part,
+                            W->quant_type, s);
     }));
     if (L.sx > 1)
       QL_TRY(traced(QLORA_KERNEL_SPLIT_REDUCE, s,

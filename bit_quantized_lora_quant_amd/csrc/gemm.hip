@@ -927,29 +927,31 @@ int dx_splits(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes,
                            int64_t N, const float* ahat_t, const uint16_t* xas, const uint16_t* B,
-                           int r, int r32, uint16_t* Y, int splits, float* part, hipStream_t s) {
+                           int r, int r32, uint16_t* Y, int splits, float* part, int kind,
+                           hipStream_t s) {
   const int ksteps = (int)ceil_div(K / kStep, splits);
   const int64_t grid = ceil_div(M, kTile) * ceil_div(N, kTile) * splits;
   return launch_kernel(k_qlora_fwd_nt, dim3((unsigned)grid), dim3(kThreadsW8), s, X, M, K, codes, N,
-                       ahat_t, host_tables(), xas, B, r, r32, Y, splits, ksteps, part);
+                       ahat_t, host_tables(kind), xas, B, r, r32, Y, splits, ksteps, part);
 }
 
 hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes,
                           int64_t K, const float* ahat_t, const uint16_t* gs, const uint16_t* A,
-                          int r, int r32, uint16_t* dX, int splits, float* part, hipStream_t s) {
+                          int r, int r32, uint16_t* dX, int splits, float* part, int kind,
+                          hipStream_t s) {
   const int64_t grid1 = ceil_div(M, kTile) * ceil_div(K, kTile);
   if (N % kStep == 0) {
     const int nsteps = (int)ceil_div(N / kStep, splits);
     launch_kernel(k_qlora_dx_nn_dma, dim3((unsigned)(grid1 * splits)), dim3(kThreads), s, dY, M, N,
-                  codes, K, ahat_t, host_tables(), gs, A, r, r32, dX, splits, nsteps, part);
+                  codes, K, ahat_t, host_tables(kind), gs, A, r, r32, dX, splits, nsteps, part);
   } else if (splits != 1) {
     return hipErrorInvalidValue;
   } else if (N % 8 == 0) {
     launch_kernel(k_qlora_dx_nn<1>, dim3((unsigned)grid1), dim3(kThreads), s, dY, M, N, codes, K,
-                  ahat_t, host_tables(), gs, A, r, r32, dX);
+                  ahat_t, host_tables(kind), gs, A, r, r32, dX);
   } else {
     launch_kernel(k_qlora_dx_nn<2>, dim3((unsigned)grid1), dim3(kThreads), s, dY, M, N, codes, K,
-                  ahat_t, host_tables(), gs, A, r, r32, dX);
+                  ahat_t, host_tables(kind), gs, A, r, r32, dX);
   }
   return hipGetLastError();
 }

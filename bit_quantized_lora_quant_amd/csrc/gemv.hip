@@ -46,6 +46,7 @@ struct DecodeArgs {
   const int8_t* q;
   const float* scale;
   const float* mean;
+  const float* f32;             // float32 block constants in place of q/scale/mean
   int splits;                   // 64-block ranges of kDecBlocks
   float* partial;               // [splits][M][N]
   int64_t xa_blocks;            // workgroups of X . A^T slices (first in the grid)
@@ -93,10 +94,10 @@ __device__ __forceinline__ void decode_rows(const DecodeArgs& a, const uint16_t*
   const int64_t kb0 = (int64_t)split * kDecBlocks;
   const int nblk = (int)(KB - kb0 < kDecBlocks ? KB - kb0 : kDecBlocks);   // >= 1
   const int64_t qrow = nl * KB + kb0;
-  const float mu = *a.mean;
+  const float mu = a.f32 ? 0.0f : *a.mean;
   // Loads: constants, codes, then X, with no per-lane branch around them
   // (indices past the range are clamped and the values ignored).
-  const bool grouped = (KB & 3) == 0;   // int8 constants four to a word
+  const bool grouped = !a.f32 && (KB & 3) == 0;   // int8 constants four to a word
   uint32_t qw[kDecBlocks / 4];
   float sc[kDecBlocks / 4];
   if (grouped) {
@@ -143,7 +144,8 @@ __device__ __forceinline__ void decode_rows(const DecodeArgs& a, const uint16_t*
   if (!grouped) {
 #pragma unroll
     for (int i = 0; i < kDecBlocks; ++i) {
-      const float v = absmax_recon(a.q, a.scale, mu, qrow + (i < nblk ? i : nblk - 1));
+      const int64_t bi = qrow + (i < nblk ? i : nblk - 1);
+      const float v = a.f32 ? a.f32[bi] : absmax_recon(a.q, a.scale, mu, bi);
       ahat_u[i] = i < nblk ? v : 0.f;
     }
   }
@@ -329,11 +331,11 @@ __global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__
 }
 
 template <int RT>
-hipError_t decode_rt(const DecodeArgs& a, int r, int64_t blocks, hipStream_t s) {
+hipError_t decode_rt(const DecodeArgs& a, int r, int64_t blocks, int kind, hipStream_t s) {
   const size_t stream = kDecTab + kDecCodes + (size_t)(a.M + 1) * kDecXStride * 2;
   const size_t xa = (size_t)kXaWaves * 4 * 64 * 4;
   return launch_kernel_lds(k_qlora_decode<RT>, dim3((unsigned)blocks), dim3(256),
-                           stream > xa ? stream : xa, s, a, host_tables(), r);
+                           stream > xa ? stream : xa, s, a, host_tables(kind), r);
 }
 
 }  // namespace
@@ -355,7 +357,7 @@ hipError_t launch_decode(const uint16_t* X, int64_t M, int64_t K, const NF4Ref& 
   const int64_t KB = K / kBlock;
   DecodeArgs a{};
   a.X = X; a.M = M; a.K = K; a.N = N;
-  a.codes = W.codes; a.q = W.q; a.scale = W.scale; a.mean = W.mean;
+  a.codes = W.codes; a.q = W.q; a.scale = W.scale; a.mean = W.mean; a.f32 = W.f32;
   (void)KB;
   a.splits = splits;
   a.partial = partial;
@@ -367,10 +369,10 @@ hipError_t launch_decode(const uint16_t* X, int64_t M, int64_t K, const NF4Ref& 
   const int64_t blocks = ks + ceil_div(N, kDecRows) * splits;
   hipError_t e;
   switch (rpad) {
-    case 16: e = decode_rt<1>(a, r, blocks, s); break;
-    case 32: e = decode_rt<2>(a, r, blocks, s); break;
-    case 64: e = decode_rt<4>(a, r, blocks, s); break;
-    default: e = decode_rt<8>(a, r, blocks, s); break;
+    case 16: e = decode_rt<1>(a, r, blocks, W.kind, s); break;
+    case 32: e = decode_rt<2>(a, r, blocks, W.kind, s); break;
+    case 64: e = decode_rt<4>(a, r, blocks, W.kind, s); break;
+    default: e = decode_rt<8>(a, r, blocks, W.kind, s); break;
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_decode_finish, dim3((unsigned)ceil_div(N, 256), (unsigned)M), dim3(256), 0,

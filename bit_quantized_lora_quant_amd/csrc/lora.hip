@@ -26,7 +26,7 @@ __device__ __forceinline__ void recon_elems(const ReconJob& J, int64_t b) {
   const int64_t e = b * blockDim.x + threadIdx.x;
   if (e >= J.N * J.KB) return;
   const int64_t kb = e / J.N, n = e - kb * J.N;
-  J.out[e] = absmax_recon(J.q, J.scale, *J.mean, n * J.KB + kb);
+  J.out[e] = J.f32 ? J.f32[n * J.KB + kb] : absmax_recon(J.q, J.scale, *J.mean, n * J.KB + kb);
 }
 
 

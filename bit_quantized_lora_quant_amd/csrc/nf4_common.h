@@ -56,8 +56,12 @@ struct NF4Tables {
   int bucket_ok;   // the thresholds suit the quantiser's 256-bucket search
 };
 
-// Host-side tables, built once from the normal quantile function.
-const NF4Tables& host_tables();
+// 4-bit types: the normal-quantile table and the uniform INT4 table.
+constexpr int kQuantNf4 = 0;
+constexpr int kQuantInt4 = 1;
+// Host-side tables of a type, built once (NF4 from the normal quantile
+// function, INT4 as k / 7).
+const NF4Tables& host_tables(int kind = kQuantNf4);
 
 // ---------------------------------------------------------------- helpers
 
@@ -129,27 +133,32 @@ __device__ __forceinline__ float absmax_recon(const int8_t* q, const float* scal
 // ---------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  All pointers are device.
 
+// kind: kQuantNf4 or kQuantInt4.  f32 (nullable): float32 block constants in
+// place of the double-quantised state (q, scale and mean then unused).
 hipError_t launch_quant_absmax(const float* w, int64_t n, uint8_t* codes, float* absmax,
-                               hipStream_t s);
+                               int kind, hipStream_t s);
 hipError_t launch_dq(const float* absmax, int64_t nb, int8_t* q, float* scale, float* mean,
                      double* partial_a, double* partial_b, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* codes, const int8_t* q, const float* scale,
-                          const float* mean, int64_t n, int out_bf16, void* out, hipStream_t s);
-hipError_t launch_absmax_recon(const int8_t* q, const float* scale, const float* mean, int64_t nb,
-                               float* out, hipStream_t s);
+                          const float* mean, const float* f32, int64_t n, int out_bf16,
+                          void* out, int kind, hipStream_t s);
+hipError_t launch_absmax_recon(const int8_t* q, const float* scale, const float* mean,
+                               const float* f32, int64_t nb, float* out, hipStream_t s);
 
 // ------------------------------------------------ side-path job launches
 // Several small independent steps share one launch (each is a few
 // microseconds of work; separate launches would cost more than the work).
 
 // Reconstructed constants laid out [K/64][N]: out[kb * N + n] = â of block
-// (n, kb).
+// (n, kb), from the double-quantised state or (f32 non-null) the float32
+// constants.
 struct ReconJob {
   const int8_t* q;
   const float* scale;
   const float* mean;
   int64_t N, KB;
   float* out;
+  const float* f32;
 };
 // bf16 transpose [rows, cols] -> [cols, ldo], zero for i in [rows, ldo)
 struct TransposeJob {
@@ -221,10 +230,12 @@ int fwd_splits(int64_t M, int64_t N, int64_t K);
 int dx_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes,
                            int64_t N, const float* ahat_t, const uint16_t* xas, const uint16_t* B,
-                           int r, int r32, uint16_t* Y, int splits, float* part, hipStream_t s);
+                           int r, int r32, uint16_t* Y, int splits, float* part, int kind,
+                           hipStream_t s);
 hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes,
                           int64_t K, const float* ahat_t, const uint16_t* gs, const uint16_t* A,
-                          int r, int r32, uint16_t* dX, int splits, float* part, hipStream_t s);
+                          int r, int r32, uint16_t* dX, int splits, float* part, int kind,
+                          hipStream_t s);
 hipError_t launch_split_reduce(const float* part, int splits, int64_t count, uint16_t* out,
                                hipStream_t s);
 
@@ -237,6 +248,8 @@ struct NF4Ref {
   const int8_t* q;
   const float* scale;
   const float* mean;
+  const float* f32;   // float32 block constants in place of q/scale/mean
+  int kind;           // kQuantNf4 or kQuantInt4
 };
 int gemv_splits(int64_t N, int64_t K);
 int decode_xa_slices(int64_t K);

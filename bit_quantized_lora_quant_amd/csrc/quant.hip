@@ -219,6 +219,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_nf4(const uint8_t* __restr
                                                           const int8_t* __restrict__ q,
                                                           const float* __restrict__ scale,
                                                           const float* __restrict__ mean,
+                                                          const float* __restrict__ f32,
                                                           int64_t n, NF4Tables tab,
                                                           void* __restrict__ out) {
   __shared__ float lvl[16];
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_nf4(const uint8_t* __restr
   const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
   const int64_t nchunks = ceil_div(n, kDqChunk);
-  const float mu = *mean;
+  const float mu = f32 ? 0.0f : *mean;
   for (int64_t c = wave; c < nchunks; c += nwaves) {
     const int64_t base = c * kDqChunk;
     const bool full = base + kDqChunk <= n;
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_nf4(const uint8_t* __restr
           if (e0 + 2 * k < n) cw[i] |= (uint32_t)codes[(e0 >> 1) + k] << (8 * k);
       }
       const int64_t b = (e0 < n ? e0 : n - 1) / kBlock;
-      a[i] = absmax_recon(q, scale, mu, b);
+      a[i] = f32 ? f32[b] : absmax_recon(q, scale, mu, b);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -282,9 +283,10 @@ __global__ __launch_bounds__(kThreads) void k_dequant_nf4(const uint8_t* __restr
 __global__ __launch_bounds__(kThreads) void k_absmax_recon(const int8_t* __restrict__ q,
                                                            const float* __restrict__ scale,
                                                            const float* __restrict__ mean,
+                                                           const float* __restrict__ f32,
                                                            int64_t nb, float* __restrict__ out) {
   const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (b < nb) out[b] = absmax_recon(q, scale, *mean, b);
+  if (b < nb) out[b] = f32 ? f32[b] : absmax_recon(q, scale, *mean, b);
 }
 
 // Constants rebuilt into [K/64][N]: out[kb * N + n] is the constant of row n,
@@ -300,10 +302,11 @@ static int64_t stream_grid(int64_t chunks) {
 }
 
 hipError_t launch_quant_absmax(const float* w, int64_t n, uint8_t* codes, float* absmax,
-                               hipStream_t s) {
-  if (!host_tables().bucket_ok) return hipErrorInvalidValue;
+                               int kind, hipStream_t s) {
+  const NF4Tables& tab = host_tables(kind);
+  if (!tab.bucket_ok) return hipErrorInvalidValue;
   return launch_kernel(k_quant_absmax_nf4, dim3((unsigned)stream_grid(ceil_div(n, kQChunk))),
-                       dim3(kThreads), s, w, n, host_tables(), codes, absmax);
+                       dim3(kThreads), s, w, n, tab, codes, absmax);
 }
 
 hipError_t launch_dq(const float* absmax, int64_t nb, int8_t* q, float* scale, float* mean,
@@ -328,19 +331,20 @@ hipError_t launch_dq(const float* absmax, int64_t nb, int8_t* q, float* scale, f
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const int8_t* q, const float* scale,
-                          const float* mean, int64_t n, int out_bf16, void* out, hipStream_t s) {
+                          const float* mean, const float* f32, int64_t n, int out_bf16,
+                          void* out, int kind, hipStream_t s) {
   const dim3 grid((unsigned)stream_grid(ceil_div(n, kDqChunk)));
   if (out_bf16)
-    return launch_kernel(k_dequant_nf4<true>, grid, dim3(kThreads), s, codes, q, scale, mean, n,
-                         host_tables(), out);
-  return launch_kernel(k_dequant_nf4<false>, grid, dim3(kThreads), s, codes, q, scale, mean, n,
-                       host_tables(), out);
+    return launch_kernel(k_dequant_nf4<true>, grid, dim3(kThreads), s, codes, q, scale, mean, f32,
+                         n, host_tables(kind), out);
+  return launch_kernel(k_dequant_nf4<false>, grid, dim3(kThreads), s, codes, q, scale, mean, f32,
+                       n, host_tables(kind), out);
 }
 
-hipError_t launch_absmax_recon(const int8_t* q, const float* scale, const float* mean, int64_t nb,
-                               float* out, hipStream_t s) {
+hipError_t launch_absmax_recon(const int8_t* q, const float* scale, const float* mean,
+                               const float* f32, int64_t nb, float* out, hipStream_t s) {
   hipLaunchKernelGGL(k_absmax_recon, dim3((unsigned)ceil_div(nb, kThreads)), dim3(kThreads), 0, s,
-                     q, scale, mean, nb, out);
+                     q, scale, mean, f32, nb, out);
   return hipGetLastError();
 }
 

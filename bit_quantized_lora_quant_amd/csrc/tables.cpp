@@ -1,4 +1,4 @@
-// Host construction of the NF4 levels and decision thresholds.
+// Host construction of the 4-bit levels and decision thresholds.
 //
 // Levels ("QLoRA: Fine-Tuning a 70B on One GPU", section "NF4 Quantization":
 // a 16-entry table built from the normal CDF; inquiringlines note on QLoRA,
@@ -34,18 +34,24 @@ double normal_quantile_upper(double p) {  // p in [1/2, 1)
   return x;
 }
 
-NF4Tables build() {
+NF4Tables build(int kind) {
   NF4Tables t;
-  const double P = 31.0 / 32.0;
-  const double z = normal_quantile_upper(P);
-  t.level[7] = 0.0f;
-  for (int j = 1; j <= 7; ++j) {
-    const double p = 0.5 + (P - 0.5) * j / 7.0;
-    t.level[7 - j] = (float)(-normal_quantile_upper(p) / z);
-  }
-  for (int j = 1; j <= 8; ++j) {
-    const double p = 0.5 + (P - 0.5) * j / 8.0;
-    t.level[7 + j] = (float)(normal_quantile_upper(p) / z);
+  if (kind == kQuantInt4) {
+    // the uniform table: k / 7 for the 4-bit integers k = -8..7 (section "NF4
+    // Quantization: Beyond Standard INT4": 16 integer levels at uniform steps)
+    for (int k = 0; k < 16; ++k) t.level[k] = (float)((double)(k - 8) / 7.0);
+  } else {
+    const double P = 31.0 / 32.0;
+    const double z = normal_quantile_upper(P);
+    t.level[7] = 0.0f;
+    for (int j = 1; j <= 7; ++j) {
+      const double p = 0.5 + (P - 0.5) * j / 7.0;
+      t.level[7 - j] = (float)(-normal_quantile_upper(p) / z);
+    }
+    for (int j = 1; j <= 8; ++j) {
+      const double p = 0.5 + (P - 0.5) * j / 8.0;
+      t.level[7 + j] = (float)(normal_quantile_upper(p) / z);
+    }
   }
   // thresholds: largest float <= exact midpoint (exact in double)
   for (int j = 0; j < 15; ++j) {
@@ -54,16 +60,22 @@ NF4Tables build() {
     if ((double)f > m) f = std::nextafterf(f, -INFINITY);
     t.thresh[j] = f;
   }
-  // The quantiser finds codes through 256 buckets of [-1, 1] (bucket
-  // floor(128 x + 128)); that is exact when no threshold lies near a bucket
-  // edge (the bucket index is off by at most 2^-16 there) and no bucket holds
-  // two thresholds.
+  // The quantiser finds codes through 256 buckets of [-1, 1]: bucket
+  // floor(fma(x, 128, 128)), holding the count of thresholds below it and
+  // the one threshold inside it.  Rounding is monotone, so a value can only
+  // land one bucket too high, and only then miscount, if some threshold at
+  // or above it sits below that bucket's edge: that needs a threshold t whose
+  // own fma(t, 128, 128) rounds up onto an edge.  Exact when no threshold
+  // does that and no bucket holds two thresholds.  (INT4 has one threshold
+  // exactly on an edge, at 1/2, and one a float below another, at -1/2:
+  // both exact.)
   t.bucket_ok = 1;
-  int prev = -1;
+  int prev = -1000;
   for (int j = 0; j < 15; ++j) {
-    const double u = 128.0 * (double)t.thresh[j] + 128.0;
-    if (std::fabs(u - std::nearbyint(u)) < 1.0 / 1024.0) t.bucket_ok = 0;
+    const double u = 128.0 * (double)t.thresh[j] + 128.0;   // exact
+    const float uf = std::fmaf(t.thresh[j], 128.0f, 128.0f);
     const int b = (int)std::floor(u);
+    if ((int)std::floor((double)uf) != b) t.bucket_ok = 0;
     if (b == prev) t.bucket_ok = 0;
     prev = b;
   }
@@ -72,11 +84,14 @@ NF4Tables build() {
 
 }  // namespace
 
-const NF4Tables& host_tables() {
-  static NF4Tables tables;
+const NF4Tables& host_tables(int kind) {
+  static NF4Tables tables[2];
   static std::once_flag once;
-  std::call_once(once, [] { tables = build(); });
-  return tables;
+  std::call_once(once, [] {
+    tables[kQuantNf4] = build(kQuantNf4);
+    tables[kQuantInt4] = build(kQuantInt4);
+  });
+  return tables[kind == kQuantInt4 ? kQuantInt4 : kQuantNf4];
 }
 
 }  // namespace qnf4

@@ -70,22 +70,36 @@ typedef uint16_t qlora_bf16;   /* raw bfloat16 bits */
 #define QLORA_DQ_BLOCK 256     /* first-level constants per second-level scale */
 #define QLORA_MAX_RANK 128
 
+/* 4-bit types (qlora_nf4_tensor.quant_type). */
+#define QLORA_QUANT_NF4 0      /* the normal-quantile table (default) */
+#define QLORA_QUANT_INT4 1     /* the uniform table NF4 is set against */
+
 /* Quantised-weight descriptor (host struct; buffers are device memory the
  * caller allocates).  With n = rows*cols, nb = ceil(n/64), nd = ceil(nb/256):
  *   codes        uint8[ceil(n/2)]  element 2i in the low nibble of byte i
+ * and, with double quantisation (dq_block = 256):
  *   absmax_q     int8[nb]          8-bit first-level constants
  *   absmax_scale float32[nd]       second-level scale of each 256 constants
  *   absmax_mean  float32[1]        per-tensor mean of the first-level constants
  * The reconstructed constant of block b is fma(absmax_q[b], absmax_scale[b/256],
- * absmax_mean[0]); weight i dequantises to level[code_i] * that constant. */
+ * absmax_mean[0]).  Without it (dq_block = 0; the double-quant switch of
+ * "QLoRA: Fine-Tuning a 70B on One GPU", section "Practical Implementation"):
+ *   absmax       float32[nb]       the block absmax itself
+ * and the three pointers above are unused.  Weight i dequantises to
+ * level[code_i] * the constant of its block, level from the table of
+ * quant_type.  Zero-initialise the struct: the fields after absmax_mean came
+ * later, and zero means NF4 with double quantisation. */
 typedef struct {
   int64_t rows, cols;
   int32_t block;      /* must be 64 */
-  int32_t dq_block;   /* must be 256 */
+  int32_t dq_block;   /* 256 (double quantisation) or 0 (float32 constants) */
   uint8_t* codes;
   int8_t* absmax_q;
   float* absmax_scale;
   float* absmax_mean;
+  float* absmax;      /* float32[nb] when dq_block == 0 */
+  int32_t quant_type; /* QLORA_QUANT_NF4 or QLORA_QUANT_INT4 */
+  int32_t reserved;   /* must be 0 */
 } qlora_nf4_tensor;
 
 /* Host copy of the 16 NF4 levels, ascending: 7 negative levels, an exact +0.0
@@ -95,18 +109,29 @@ typedef struct {
  * inquiringlines note: equal share of a zero-centred normal per bin). */
 void qlora_nf4_codebook(float out[16]);
 
+/* Host copy of the 16 levels of a 4-bit type, ascending.  QLORA_QUANT_NF4 is
+ * the table above.  QLORA_QUANT_INT4 is the uniform table the NF4 section
+ * ("NF4 Quantization: Beyond Standard INT4") sets NF4 against: the sixteen
+ * 4-bit integers k = -8..7 over the block absmax scaled to 7, level k/7 (in
+ * double, rounded once to float32); -8/7 lies below -1 and is never the
+ * nearest level.  Returns QLORA_ERR_INVALID_ARG for another type or a null
+ * out. */
+qlora_status qlora_codebook(int32_t quant_type, float out[16]);
+
 const char* qlora_status_string(qlora_status s);
 
 /* Bytes of workspace qlora_quantize_nf4 needs for a rows x cols tensor. */
 size_t qlora_quantize_workspace_bytes(int64_t rows, int64_t cols);
 
-/* Blockwise NF4 quantisation with double quantisation ("NF4 Quantization" and
- * "Double Quantization" sections).
+/* Blockwise 4-bit quantisation with double quantisation ("NF4 Quantization" and
+ * "Double Quantization" sections), to the table of q->quant_type, and without
+ * the second level when q->dq_block is 0.
  *   W   float32[rows*cols], device, read-only.
- *   q   descriptor whose four buffers receive the quantised state.
+ *   q   descriptor whose buffers receive the quantised state.
  *   ws  device workspace of at least qlora_quantize_workspace_bytes(); on
  *       return (once the stream passes) its first nb floats hold the exact
- *       first-level absmax of each 64-block.
+ *       first-level absmax of each 64-block (with double quantisation; without
+ *       it they go to q->absmax and the workspace is not written).
  * Steps: absmax of each block; x = w / absmax (IEEE float division; an all-zero
  * block gives x = 0); code = nearest level, ties to the lower; then the mean
  * of all absmax (exact binary tree of pairwise float64 sums, divided by nb and
@@ -122,7 +147,8 @@ qlora_status qlora_quantize_nf4(const float* W, const qlora_nf4_tensor* q, void*
 qlora_status qlora_dequantize_nf4(const qlora_nf4_tensor* q, qlora_dtype out_dtype, void* out,
                                   void* stream);
 
-/* Reconstructed first-level constants, float32[nb]. */
+/* The constant each 64-block dequantises with, float32[nb]: reconstructed from
+ * the 8-bit state, or a copy of q->absmax without double quantisation. */
 qlora_status qlora_dequantize_absmax(const qlora_nf4_tensor* q, float* out, void* stream);
 
 /* Bytes of workspace qlora_linear_fwd / qlora_linear_bwd need. */

@@ -51,6 +51,36 @@ def test_codebook_matches_oracle_bit_exact(q):
     assert np.array_equal(lib_cb.view(np.uint32), oracle.codebook().view(np.uint32))
 
 
+def test_int4_codebook_matches_oracle_bit_exact(q):
+    lib_cb = np.array(q.qlora_codebook("int4"), dtype=np.float32)
+    assert np.array_equal(lib_cb.view(np.uint32), oracle.codebook("int4").view(np.uint32))
+    nf4 = np.array(q.qlora_codebook("nf4"), dtype=np.float32)
+    assert np.array_equal(nf4.view(np.uint32), oracle.codebook().view(np.uint32))
+    buf = (ctypes.c_float * 16)()
+    assert q.lib().qlora_codebook(2, buf) == q.QLORA_ERR_INVALID_ARG
+    assert q.lib().qlora_codebook(0, None) == q.QLORA_ERR_INVALID_ARG
+
+
+def test_descriptor_type_and_constant_fields(q):
+    """dq_block 0 needs the float32 absmax buffer (and then not the 8-bit
+    state); the type must be NF4 or INT4 and the reserved field zero.  A
+    descriptor that passes validation gets as far as the workspace check."""
+    lib = q.lib()
+    P = ctypes.c_void_p
+    fake = 0x100000
+
+    def quant(d):
+        return lib.qlora_quantize_nf4(P(0x200000), ctypes.byref(d), P(0x300000), 16, None)
+
+    ok = q.NF4Descriptor(64, 64, 64, 0, fake, 0, 0, 0, fake, 1, 0)
+    assert quant(ok) == q.QLORA_ERR_WORKSPACE
+    for bad in (q.NF4Descriptor(64, 64, 64, 0, fake, fake, fake, fake, 0, 0, 0),
+                q.NF4Descriptor(64, 64, 64, 256, fake, fake, fake, fake, 0, 2, 0),
+                q.NF4Descriptor(64, 64, 64, 256, fake, fake, fake, fake, 0, 0, 1),
+                q.NF4Descriptor(64, 64, 64, 256, fake, 0, fake, fake, fake, 0, 0)):
+        assert quant(bad) == q.QLORA_ERR_INVALID_ARG
+
+
 def test_status_strings(q):
     for s in range(5):
         assert q.status_string(s)
