@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--legs", default="all",
-                    help="all, none, or a comma list of quant, decode, stack65b")
+                    help="all, none, or a comma list of quant, variants, decode, stack65b")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run 3 plain device-to-device copies of MIB MiB (the known-size "
@@ -299,6 +299,74 @@ def leg_quant_dequant(q, torch, workloads, passes=3):
     return res
 
 
+def leg_variants(q, torch, workloads, passes=3):
+    """The 4-bit type and constant variants on the same kernels, over the seven
+    weights of one Llama-3.1-8B layer: quantise and dequantise (bf16) GB/s and
+    bits/param for NF4 and INT4, with and without double quantisation; the
+    reconstruction error of each type on these N(0, 0.02) weights; and the
+    fused fwd+bwd of the gate projection at 2048 tokens for each variant."""
+    dev = "cuda:0"
+    wl = workloads.LLAMA8B_LAYER
+    Ws = [workloads.device_weight(5, 0, t, n, k) for t, (_, k, n) in enumerate(wl.linears)]
+    params = sum(W.numel() for W in Ws)
+    ws = q.workspace(max(q.qlora_quantize_workspace_bytes(*W.shape) for W in Ws), dev)
+    out = torch.empty(max(W.numel() for W in Ws), dtype=torch.bfloat16, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(6)
+    M, r, alpha = wl.m, wl.r, wl.alpha
+    _, Kg, Ng = wl.linears[4]   # gate projection
+    X = torch.randn((M, Kg), generator=g, device=dev).to(torch.bfloat16)
+    A = (torch.rand((r, Kg), generator=g, device=dev) * 2 - 1).mul_(Kg ** -0.5).to(torch.bfloat16)
+    B = (torch.randn((Ng, r), generator=g, device=dev) * 0.01).to(torch.bfloat16)
+    dY = torch.randn((M, Ng), generator=g, device=dev).to(torch.bfloat16)
+    lws = q.workspace(q.qlora_linear_workspace_bytes(M, Ng, Kg, r), dev)
+    res = {"tensors": "q/k/v/o/gate/up/down of one Llama-3.1-8B layer", "params": params}
+    for kind in ("nf4", "int4"):
+        for dq in (True, False):
+            Qs = [q.NF4Tensor(W.shape[0], W.shape[1], dev, kind, dq) for W in Ws]
+
+            def quant_pass():
+                for W, Q in zip(Ws, Qs):
+                    q.qlora_quantize_nf4(W, Q, ws)
+
+            def deq_pass():
+                for Q in Qs:
+                    q.qlora_dequantize_nf4(Q, out=out[: Q.numel].view(Q.rows, Q.cols))
+
+            quant_pass(); deq_pass()
+            gq, gd = graph_of(torch, quant_pass), graph_of(torch, deq_pass)
+            tq = timed(torch, gq.replay, passes)
+            td = timed(torch, gd.replay, passes)
+            del gq, gd
+            nbytes = sum(Q.nbytes() for Q in Qs)
+            sq = 0.0
+            for W, Q in zip(Ws, Qs):
+                back = q.qlora_dequantize_nf4(Q, torch.float32)
+                sq += float(((back.double() - W.double()) ** 2).sum().item())
+            Qg = Qs[4]
+            q.qlora_linear_fwd(Qg, X, A, B, alpha, ws=lws)
+            torch.cuda.synchronize()
+
+            def step():
+                Y = q.qlora_linear_fwd(Qg, X, A, B, alpha, ws=lws)
+                q.qlora_linear_bwd(Qg, X, A, B, alpha, dY, ws=lws)
+                return Y
+
+            tg = timed(torch, step, 5)
+            res["%s_%s" % (kind, "dq" if dq else "f32_constants")] = {
+                "bits_per_param": round(8.0 * nbytes / params, 5),
+                "quantize_GB/s": round((4 * params + nbytes) / tq / 1e9, 1),
+                "dequantize_bf16_GB/s": round((nbytes + 2 * params) / td / 1e9, 1),
+                "mse": float("%.5g" % (sq / params)),
+                "gate_fwd_bwd_ms": round(tg * 1e3, 3)}
+            del Qs
+    res["mse_ratio_nf4_over_int4"] = round(res["nf4_dq"]["mse"] / res["int4_dq"]["mse"], 4)
+    del Ws, ws, out, lws
+    torch.cuda.empty_cache()
+    log("variants leg: NF4 / INT4 error ratio %.3f" % res["mse_ratio_nf4_over_int4"])
+    return res
+
+
 def leg_decode(q, torch, workloads, steps=5):
     """Decode forward through 80 layers x 7 70B-shaped linears (distinct NF4
     weights, ~35 GB) at M = 1, 4, 16 tokens."""
@@ -439,10 +507,12 @@ def main():
     del layers, host_w
     torch.cuda.empty_cache()
     legs = {}
-    want = {"quant", "decode", "stack65b"} if args.legs == "all" else (
+    want = {"quant", "variants", "decode", "stack65b"} if args.legs == "all" else (
         set() if args.legs == "none" else set(args.legs.split(",")))
     if "quant" in want:
         legs["llama8b_weight_set_quant_dequant"] = leg_quant_dequant(q, torch, workloads)
+    if "variants" in want:
+        legs["nf4_int4_and_constant_variants"] = leg_variants(q, torch, workloads)
     if "decode" in want:
         legs["llama70b_decode_gemv"] = leg_decode(q, torch, workloads)
     if "stack65b" in want:
