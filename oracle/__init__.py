@@ -4,12 +4,14 @@ TEST INFRASTRUCTURE ONLY: the parity reference for the GPU library.  Only the
 tests, ``__graft_entry__.smoke()`` and the benchmark's ``cpu_baseline`` leg may
 import it.  It shares no code with the GPU library and never calls it.
 
-Two parts:
+Three parts:
   * ``nf4_oracle.c`` (wrapped here): codebook, blockwise absmax quantisation,
     double quantisation of the constants, dequantisation, bf16 rounding.
   * ``linear.py``: the forward and backward of
         Y = X . W'^T + (alpha / r) . (X . A^T) . B^T
-    written as their float64 definitions with numpy matmul as the only step.
+    written as their float64 definitions with numpy matmul as the only step,
+    optionally with dropout on the LoRA input.
+  * ``dropout.py``: the keep mask of that dropout (Philox4x32-10).
 
 Pins (tests/test_oracle_*.py) tie every function here to something other than
 itself: scipy's normal quantile, printed figures from the pages, closed forms,
@@ -22,6 +24,7 @@ import numpy as np
 
 from . import build as _build
 from .linear import linear_fwd, linear_bwd, lora_scale  # noqa: F401
+from . import dropout  # noqa: F401
 
 NF4_BLOCK = 64
 DQ_BLOCK = 256

@@ -34,22 +34,47 @@ def _f64(a):
     return np.asarray(a, dtype=np.float64)
 
 
-def linear_fwd(wd, x, a, b, alpha):
+def _dropout_scale(x, drop):
+    """keep / (1 - p) per element of x (all ones without dropout).  drop is
+    None or (p, seed, row0): row0 is the first row's index in the full X, for
+    a comparison on sampled rows."""
+    if drop is None or drop[0] == 0.0:
+        return None
+    from .dropout import keep_mask
+    p, seed = drop[0], drop[1]
+    row0 = drop[2] if len(drop) > 2 else 0
+    rows = np.asarray(row0).reshape(-1)
+    M, K = x.shape
+    if rows.size == 1:
+        keep = keep_mask(int(rows[0]) + M, K, p, seed)[int(rows[0]):]
+    else:   # explicit row indices
+        keep = keep_mask(int(rows.max()) + 1, K, p, seed)[rows]
+    return keep.astype(np.float64) / (1.0 - float(p))
+
+
+def linear_fwd(wd, x, a, b, alpha, drop=None):
     """Returns (Y, XA) in float64.  wd: [N, K] dequantised weight; x: [M, K];
-    a: [r, K]; b: [N, r]."""
+    a: [r, K]; b: [N, r].  With drop = (p, seed[, rows]) the down-projection
+    sees the dropped input D(X) (see dropout.py); the frozen path sees X."""
     wd, x, a, b = _f64(wd), _f64(x), _f64(a), _f64(b)
     s = lora_scale(alpha, a.shape[0])
-    xa = x @ a.T
+    d = _dropout_scale(x, drop)
+    xa = (x if d is None else x * d) @ a.T
     y = x @ wd.T + s * (xa @ b.T)
     return y, xa
 
 
-def linear_bwd(wd, x, a, b, alpha, dy):
-    """Returns (dX, dA, dB) in float64."""
+def linear_bwd(wd, x, a, b, alpha, dy, drop=None):
+    """Returns (dX, dA, dB) in float64.  With dropout, dA uses D(X), dB the
+    dropped forward's X . A^T, and the LoRA share of dX passes back through
+    the same keep / (1 - p) factors."""
     wd, x, a, b, dy = _f64(wd), _f64(x), _f64(a), _f64(b), _f64(dy)
     s = lora_scale(alpha, a.shape[0])
+    d = _dropout_scale(x, drop)
+    xd = x if d is None else x * d
     g = dy @ b
-    dx = dy @ wd + s * (g @ a)
-    da = s * (g.T @ x)
-    db = s * (dy.T @ (x @ a.T))
+    lora_dx = s * (g @ a)
+    dx = dy @ wd + (lora_dx if d is None else lora_dx * d)
+    da = s * (g.T @ xd)
+    db = s * (dy.T @ (xd @ a.T))
     return dx, da, db
