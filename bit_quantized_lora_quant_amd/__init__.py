@@ -26,6 +26,7 @@ EXPORTS = [
     "qlora_quantize_workspace_bytes",
     "qlora_quantize_nf4", "qlora_dequantize_nf4", "qlora_dequantize_absmax",
     "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
+    "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout", "qlora_dropout_mask",
     "qlora_trace_begin", "qlora_trace_pause", "qlora_trace_end",
 ]
 KERNELS = {"fwd_gemm": 0, "dx_gemm": 1, "quantize": 2, "dequant": 3, "gemv": 4,
@@ -45,6 +46,11 @@ class NF4Descriptor(ctypes.Structure):
                 ("absmax_scale", ctypes.c_void_p), ("absmax_mean", ctypes.c_void_p),
                 ("absmax", ctypes.c_void_p), ("quant_type", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
+
+
+class QloraDropout(ctypes.Structure):
+    """LoRA dropout of the adapter input: drop probability p, generator seed."""
+    _fields_ = [("p", ctypes.c_double), ("seed", ctypes.c_uint64)]
 
 
 _lib = None
@@ -76,6 +82,10 @@ def lib():
         L.qlora_linear_workspace_bytes.restype = SZ
         L.qlora_linear_fwd.argtypes = [D, P, I64, P, P, I32, F, P, P, P, SZ, P]
         L.qlora_linear_bwd.argtypes = [D, P, I64, P, P, I32, F, P, P, P, P, P, P, SZ, P]
+        L.qlora_linear_fwd_dropout.argtypes = [D, P, I64, P, P, I32, F, P, P, P, P, SZ, P]
+        L.qlora_linear_bwd_dropout.argtypes = [D, P, I64, P, P, I32, F, P, P, P, P, P, P, P,
+                                               SZ, P]
+        L.qlora_dropout_mask.argtypes = [I64, I64, P, P, P]
         L.qlora_trace_begin.argtypes = [ctypes.c_uint32, I32]
         L.qlora_trace_pause.argtypes = [I32]
         L.qlora_trace_end.argtypes = [P, P]
@@ -213,9 +223,29 @@ def _bf16(t):
     return t
 
 
+def _dropout(dropout):
+    """None, or a QloraDropout from (p, seed)."""
+    if dropout is None:
+        return None
+    p, seed = dropout
+    return QloraDropout(float(p), int(seed) & 0xFFFFFFFFFFFFFFFF)
+
+
+def qlora_dropout_mask(M: int, K: int, dropout, device, out=None):
+    """uint8 [M, K] keep flags of the dropout (p, seed) of an [M, K] input."""
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.uint8, device=device)
+    d = _dropout(dropout)
+    _check(lib().qlora_dropout_mask(M, K, ctypes.byref(d), _ptr(out) if out.numel() else None,
+                                    _stream()), "qlora_dropout_mask")
+    return out
+
+
 def qlora_linear_fwd(q: NF4Tensor, X, A, B, alpha: float, Y=None, XA_out=None, ws=None,
-                     return_xa: bool = False):
-    """Y = X W'^T + (alpha/r) (X A^T) B^T.  Returns Y, or (Y, XA) with return_xa."""
+                     return_xa: bool = False, dropout=None):
+    """Y = X W'^T + (alpha/r) (D(X) A^T) B^T.  Returns Y, or (Y, XA) with
+    return_xa.  dropout = (p, seed) drops adapter-input elements (D(X) = X
+    without it)."""
     M, K = X.shape
     r = A.shape[0]
     _bf16(X), _bf16(A), _bf16(B)
@@ -227,15 +257,23 @@ def qlora_linear_fwd(q: NF4Tensor, X, A, B, alpha: float, Y=None, XA_out=None, w
     if ws is None:
         ws = workspace(qlora_linear_workspace_bytes(M, q.rows, K, r), X.device)
     d = q.descriptor()
-    _check(lib().qlora_linear_fwd(ctypes.byref(d), _ptr(X), M, _ptr(A), _ptr(B), r,
-                                  ctypes.c_float(alpha), _ptr(Y), _ptr(XA_out), _ptr(ws),
-                                  ws.numel(), _stream()), "qlora_linear_fwd")
+    if dropout is None:
+        _check(lib().qlora_linear_fwd(ctypes.byref(d), _ptr(X), M, _ptr(A), _ptr(B), r,
+                                      ctypes.c_float(alpha), _ptr(Y), _ptr(XA_out), _ptr(ws),
+                                      ws.numel(), _stream()), "qlora_linear_fwd")
+    else:
+        dr = _dropout(dropout)
+        _check(lib().qlora_linear_fwd_dropout(ctypes.byref(d), _ptr(X), M, _ptr(A), _ptr(B), r,
+                                              ctypes.c_float(alpha), ctypes.byref(dr), _ptr(Y),
+                                              _ptr(XA_out), _ptr(ws), ws.numel(), _stream()),
+               "qlora_linear_fwd_dropout")
     return (Y, XA_out) if return_xa else Y
 
 
 def qlora_linear_bwd(q: NF4Tensor, X, A, B, alpha: float, dY, XA_in=None, need_dx: bool = True,
-                     dX=None, dA=None, dB=None, ws=None):
-    """Returns (dX or None, dA float32 [r, K], dB float32 [N, r])."""
+                     dX=None, dA=None, dB=None, ws=None, dropout=None):
+    """Returns (dX or None, dA float32 [r, K], dB float32 [N, r]).  dropout
+    must be the forward's (p, seed)."""
     M, K = X.shape
     r = A.shape[0]
     N = q.rows
@@ -250,10 +288,18 @@ def qlora_linear_bwd(q: NF4Tensor, X, A, B, alpha: float, dY, XA_in=None, need_d
     if ws is None:
         ws = workspace(qlora_linear_workspace_bytes(M, N, K, r), X.device)
     d = q.descriptor()
-    _check(lib().qlora_linear_bwd(ctypes.byref(d), _ptr(X), M, _ptr(A), _ptr(B), r,
-                                  ctypes.c_float(alpha), _ptr(dY), _ptr(XA_in),
-                                  _ptr(dX) if need_dx else None, _ptr(dA), _ptr(dB), _ptr(ws),
-                                  ws.numel(), _stream()), "qlora_linear_bwd")
+    if dropout is None:
+        _check(lib().qlora_linear_bwd(ctypes.byref(d), _ptr(X), M, _ptr(A), _ptr(B), r,
+                                      ctypes.c_float(alpha), _ptr(dY), _ptr(XA_in),
+                                      _ptr(dX) if need_dx else None, _ptr(dA), _ptr(dB),
+                                      _ptr(ws), ws.numel(), _stream()), "qlora_linear_bwd")
+    else:
+        dr = _dropout(dropout)
+        _check(lib().qlora_linear_bwd_dropout(ctypes.byref(d), _ptr(X), M, _ptr(A), _ptr(B), r,
+                                              ctypes.c_float(alpha), ctypes.byref(dr), _ptr(dY),
+                                              _ptr(XA_in), _ptr(dX) if need_dx else None,
+                                              _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(),
+                                              _stream()), "qlora_linear_bwd_dropout")
     return (dX if need_dx else None), dA, dB
 
 
@@ -282,16 +328,16 @@ class QLoRALinearFn(torch.autograd.Function):
     """autograd wrapper: frozen NF4 weight, trainable bf16 adapters A and B."""
 
     @staticmethod
-    def forward(ctx, X, A, B, q, alpha):
+    def forward(ctx, X, A, B, q, alpha, dropout=None):
         Y, XA = qlora_linear_fwd(q, X.contiguous(), A.contiguous(), B.contiguous(), alpha,
-                                 return_xa=True)
+                                 return_xa=True, dropout=dropout)
         ctx.save_for_backward(X, A, B, XA)
-        ctx.q, ctx.alpha = q, alpha
+        ctx.q, ctx.alpha, ctx.dropout = q, alpha, dropout
         return Y
 
     @staticmethod
     def backward(ctx, dY):
         X, A, B, XA = ctx.saved_tensors
         dX, dA, dB = qlora_linear_bwd(ctx.q, X, A, B, ctx.alpha, dY.contiguous(), XA_in=XA,
-                                      need_dx=ctx.needs_input_grad[0])
-        return dX, dA.to(A.dtype), dB.to(B.dtype), None, None
+                                      need_dx=ctx.needs_input_grad[0], dropout=ctx.dropout)
+        return dX, dA.to(A.dtype), dB.to(B.dtype), None, None, None

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <cmath>
 #include <cstring>
 
 #include "../../include/qlora_nf4.h"
@@ -170,6 +171,24 @@ qlora_status check_linear(const qlora_nf4_tensor* W, const void* X, int64_t M, c
   return QLORA_OK;
 }
 
+// Kernel parameters of a dropout of an input with rows of K elements: keep
+// when the element's generator word >= floor(p 2^32).  NULL, or a p whose
+// threshold is 0, is no dropout.  False for p outside [0, 1) or NaN.
+bool dropout_params(const qlora_dropout* d, int64_t K, DropoutParams* out) {
+  *out = DropoutParams{};
+  if (!d) return true;
+  if (!(d->p >= 0.0 && d->p < 1.0)) return false;
+  const double t = std::floor(d->p * 4294967296.0);
+  const uint32_t thr = t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
+  if (thr == 0) return true;
+  out->thr = thr;
+  out->inv = (float)(1.0 / (1.0 - d->p));
+  out->k0 = (uint32_t)(d->seed & 0xFFFFFFFFu);
+  out->k1 = (uint32_t)(d->seed >> 32);
+  out->cols = K;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -246,8 +265,19 @@ qlora_status qlora_linear_fwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
                               const qlora_bf16* A, const qlora_bf16* B, int32_t r, float alpha,
                               qlora_bf16* Y, qlora_bf16* XA_out, void* ws, size_t ws_bytes,
                               void* stream) {
+  return qlora_linear_fwd_dropout(W, X, M, A, B, r, alpha, nullptr, Y, XA_out, ws, ws_bytes,
+                                  stream);
+}
+
+qlora_status qlora_linear_fwd_dropout(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
+                                      const qlora_bf16* A, const qlora_bf16* B, int32_t r,
+                                      float alpha, const qlora_dropout* drop, qlora_bf16* Y,
+                                      qlora_bf16* XA_out, void* ws, size_t ws_bytes,
+                                      void* stream) {
   qlora_status st = check_linear(W, X, M, A, B, r, alpha);
   if (st != QLORA_OK) return st;
+  DropoutParams dp;
+  if (!dropout_params(drop, W->cols, &dp)) return QLORA_ERR_INVALID_ARG;
   if (!Y || !aligned(Y, 16)) return QLORA_ERR_INVALID_ARG;
   const int64_t N = W->rows, K = W->cols;
   const LinearWs L = linear_layout(M, N, K, r);
@@ -262,7 +292,7 @@ qlora_status qlora_linear_fwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
     float* xa_part = at<float>(ws, L.dec_xa);
     e = traced(QLORA_KERNEL_GEMV, s, [&] {
       return launch_decode(X, M, K, w, N, A, B, r, scale, L.gemv_splits, part, xa_part, Y,
-                           XA_out, s);
+                           XA_out, dp, s);
     });
     return hip_status(e);
   }
@@ -271,6 +301,7 @@ qlora_status qlora_linear_fwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
   // X.A^T -> bf16(s.XA) [M, r32] (GEMM tail) and bf16(XA) [M, r] (caller),
   // with the block constants reconstructed in the same launch
   SkinnyJob xa{X, K, K, A, K, 0, 0, at<float>(ws, L.sk_k), scale, xas, XA_out, nullptr, 0};
+  xa.drop = dp;
   skinny_plan(&xa, M);
   const ReconJob rc{W->absmax_q, W->absmax_scale, W->absmax_mean, N, K / kBlock, ahat_t,
                     f32_consts(W)};
@@ -291,8 +322,20 @@ qlora_status qlora_linear_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
                               const qlora_bf16* A, const qlora_bf16* B, int32_t r, float alpha,
                               const qlora_bf16* dY, const qlora_bf16* XA_in, qlora_bf16* dX,
                               float* dA, float* dB, void* ws, size_t ws_bytes, void* stream) {
+  return qlora_linear_bwd_dropout(W, X, M, A, B, r, alpha, nullptr, dY, XA_in, dX, dA, dB, ws,
+                                  ws_bytes, stream);
+}
+
+qlora_status qlora_linear_bwd_dropout(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
+                                      const qlora_bf16* A, const qlora_bf16* B, int32_t r,
+                                      float alpha, const qlora_dropout* drop,
+                                      const qlora_bf16* dY, const qlora_bf16* XA_in,
+                                      qlora_bf16* dX, float* dA, float* dB, void* ws,
+                                      size_t ws_bytes, void* stream) {
   qlora_status st = check_linear(W, X, M, A, B, r, alpha);
   if (st != QLORA_OK) return st;
+  DropoutParams dp;
+  if (!dropout_params(drop, W->cols, &dp)) return QLORA_ERR_INVALID_ARG;
   if (!dY || !dA || !dB || !aligned(dY, 16)) return QLORA_ERR_INVALID_ARG;
   if (dX && !aligned(dX, 16)) return QLORA_ERR_INVALID_ARG;
   const int64_t N = W->rows, K = W->cols;
@@ -322,28 +365,40 @@ qlora_status qlora_linear_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
   int nj = 0;
   sj[nj++] = SkinnyJob{dY, N, N, bt, L.np, 0, 0, at<float>(ws, L.sk_n), scale, gs, nullptr, gt,
                        L.mp};
-  if (!XA_in)
+  if (!XA_in) {
     sj[nj++] = SkinnyJob{X, K, K, A, K, 0, 0, at<float>(ws, L.sk_k), 1.0f, nullptr, nullptr, xat,
                          L.mp};
+    sj[nj - 1].drop = dp;
+  }
   for (int i = 0; i < nj; ++i) skinny_plan(&sj[i], M);
   QL_TRY(launch_skinny(sj, nj, M, r, L.r32, nullptr, s));
   if (dX) {
     float* part = at<float>(ws, L.gemm_part);
     QL_TRY(traced(QLORA_KERNEL_DX_GEMM, s, [&] {
       return launch_dx_gemm(dY, M, N, W->codes, K, ahat_t, gs, A, r, L.r32, dX, L.sx, part,
-                            W->quant_type, s);
+                            W->quant_type, &dp, s);
     }));
     if (L.sx > 1)
       QL_TRY(traced(QLORA_KERNEL_SPLIT_REDUCE, s,
                     [&] { return launch_split_reduce(part, L.sx, M * K, dX, s); }));
   }
   // dA = s . G^T X  (reduce over tokens into [r, K]);  dB = s . dY^T XA  ([N, r])
-  const GradJob gj[2] = {
+  GradJob gj[2] = {
       GradJob{X, K, gt, L.mp, L.sa, at<float>(ws, L.part_a), scale, 1, dA},
       GradJob{dY, N, xat, L.mp, L.sb, at<float>(ws, L.part_b), scale, 0, dB}};
+  gj[0].drop = dp;   // dA reads D(X)
   QL_TRY(launch_lora_grads(gj, 2, M, r, s));
 #undef QL_TRY
   return QLORA_OK;
+}
+
+qlora_status qlora_dropout_mask(int64_t M, int64_t K, const qlora_dropout* drop, uint8_t* out,
+                                void* stream) {
+  if (!drop || M < 0 || K < 0 || (M * K > 0 && !out)) return QLORA_ERR_INVALID_ARG;
+  if (K > 0 && M > INT64_MAX / K) return QLORA_ERR_INVALID_ARG;
+  DropoutParams dp;
+  if (!dropout_params(drop, K, &dp)) return QLORA_ERR_INVALID_ARG;
+  return hip_status(launch_dropout_mask(M, K, dp, out, static_cast<hipStream_t>(stream)));
 }
 
 qlora_status qlora_trace_begin(uint32_t kernel_mask, int32_t capacity) {

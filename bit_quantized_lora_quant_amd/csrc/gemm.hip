@@ -445,19 +445,97 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
 }
 
 // ----------------------------------------------------------------- backward
+// LoRA term of dX under dropout of X: the term passes back through the same
+// keep / (1 - p) factors as the forward's down-projection input, element by
+// element,
+//     acc[mt][t][v] = keep(m, kc + t) / (1 - p) * sum_j (s.G)[m][j] A[j][kc + t],
+//     m = m0 + 16 mt + 4 g + v,
+// so it is computed apart from the frozen product (four accumulators per row
+// tile, one row tile at a time) and becomes the starting value of the
+// accumulators, which the frozen product's MFMAs then add to (the tiles stay
+// in their registers; nothing is added to them by VALU afterwards).  The keep
+// words of columns kc .. kc + 3 (kc % 4 == 0) are the four words of one
+// generator block.  A's B operands are built once per 32 inner indices, as
+// in the unmasked tail.
+__device__ __forceinline__ void dropout_lora_init(f32x4_t (&acc)[16][4],
+                                                  const uint16_t* __restrict__ gs,
+                                                  const uint16_t* __restrict__ A, int r, int r32,
+                                                  int64_t M, int64_t K, int64_t m0, int64_t kcl,
+                                                  int j16, int g, const DropoutParams& d) {
+  const int nts = r32 / 32;   // 1 .. 4
+  uint4 bb[4][4];
+#pragma unroll
+  for (int ts = 0; ts < 4; ++ts) {
+    if (ts >= nts) break;
+    const int j0 = ts * 32 + g * 8;
+    uint2 rows[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = j0 + e;
+      rows[e] = (j < r) ? *reinterpret_cast<const uint2*>(A + (int64_t)j * K + kcl)
+                        : make_uint2(0u, 0u);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = (t < 2) ? rows[e].x : rows[e].y;
+        h[e] = (t & 1) ? (w >> 16) : (w & 0xFFFFu);
+      }
+      bb[ts][t].x = h[0] | (h[1] << 16);
+      bb[ts][t].y = h[2] | (h[3] << 16);
+      bb[ts][t].z = h[4] | (h[5] << 16);
+      bb[ts][t].w = h[6] | (h[7] << 16);
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < 16; ++mt) {
+    int64_t m = m0 + mt * 16 + j16;
+    m = m < M ? m : M - 1;
+    f32x4_t tl[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) tl[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ts = 0; ts < 4; ++ts) {
+      if (ts >= nts) break;
+      const uint4 a = *reinterpret_cast<const uint4*>(gs + m * r32 + ts * 32 + g * 8);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) tl[t] = mfma16x16x32(a, bb[ts][t], tl[t]);
+    }
+    uint4 wd[4];   // generator blocks of rows v = 0..3, columns kc .. kc + 3
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint64_t c =
+          ((uint64_t)(m0 + mt * 16 + 4 * g + v) * (uint64_t)K + (uint64_t)kcl) >> 2;
+      wd[v] = make_uint4((uint32_t)c, (uint32_t)(c >> 32), 0u, 0u);
+    }
+    philox4x32_10_rolled<4>(wd, d.k0, d.k1);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint4 w = wd[v];
+      acc[mt][0][v] = w.x >= d.thr ? d.inv * tl[0][v] : 0.f;
+      acc[mt][1][v] = w.y >= d.thr ? d.inv * tl[1][v] : 0.f;
+      acc[mt][2][v] = w.z >= d.thr ? d.inv * tl[2][v] : 0.f;
+      acc[mt][3][v] = w.w >= d.thr ? d.inv * tl[3][v] : 0.f;
+    }
+  }
+}
+
 // dX tile 256 (rows m) x 256 (cols k); inner loop over n in steps of 64.
 // Lane (j16, g) of wave w owns output columns kc = k0 + 64w + 4*j16 + t,
 // t = 0..3, one MFMA per t: so its B operand needs, for each t, 8 consecutive
 // W rows of one column -- exactly the 4 codes of a 16-bit load from each of 8
-// rows.  All four columns sit in one 64-block of each row.
-template <int MODE>
+// rows.  All four columns sit in one 64-block of each row.  DROP: the LoRA
+// term passes through the dropout of X (dropout_lora_init).
+template <int MODE, bool DROP>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1)))
 void k_qlora_dx_nn(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
                    const uint8_t* __restrict__ codes, int64_t K,
                    const float* __restrict__ ahat_t, NF4Tables tab,
                    const uint16_t* __restrict__ gs, const uint16_t* __restrict__ A, int r,
-                   int r32, uint16_t* __restrict__ dX) {
+                   int r32, uint16_t* __restrict__ dX, DropoutParams drop) {
   __shared__ __attribute__((aligned(16))) uint16_t ys[2][kTile * kStep];
   __shared__ float lvl[16];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -478,10 +556,19 @@ void k_qlora_dx_nn(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
   const uint32_t abase = kb * N32;
 
   f32x4_t acc[16][4];
+  if constexpr (DROP) {
+    dropout_lora_init(acc, gs, A, r, r32, M, K, m0, kcl, j16, g, drop);
 #pragma unroll
-  for (int mt = 0; mt < 16; ++mt)
+    for (int mt = 0; mt < 16; ++mt)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < 4; ++t) asm volatile("" : "+a"(acc[mt][t]));
+    mfma_settle();
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
   // 16 W rows per step (2 sub-steps x 8): rows n0 + 32s + 8g + e
   auto load_w = [&](uint32_t n0, uint32_t (&c)[16], float (&a)[16]) {
@@ -539,8 +626,9 @@ void k_qlora_dx_nn(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
     __syncthreads();
   }
 
-  // LoRA: + (s.G) . A as r32 extra inner indices
-  for (int ts = 0; ts < r32 / 32; ++ts) {
+  // LoRA: + (s.G) . A as r32 extra inner indices (under dropout it went in
+  // first, masked)
+  for (int ts = 0; ts < (DROP ? 0 : r32 / 32); ++ts) {
     const int j0 = ts * 32 + g * 8;
     uint2 rows[8];
 #pragma unroll
@@ -606,6 +694,7 @@ void k_qlora_dx_nn(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
 //          groups of a 16-bit code read on disjoint banks)           8.5 KB
 //   absmax [4 column blocks][64 rows] fp32                             1 KB
 constexpr int kCodeBlk = 1024 + 64;
+template <bool DROP>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1)))
 void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
@@ -613,7 +702,7 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
                        const float* __restrict__ ahat_t, NF4Tables tab,
                        const uint16_t* __restrict__ gs, const uint16_t* __restrict__ A, int r,
                        int r32, uint16_t* __restrict__ dX, int splits, int nsteps,
-                       float* __restrict__ part) {
+                       float* __restrict__ part, DropoutParams drop) {
   __shared__ __attribute__((aligned(1024))) float lvl[16];   // at LDS address 0
   __shared__ __attribute__((aligned(16))) uint16_t ys0[kTile * kStep];
   __shared__ __attribute__((aligned(16))) uint16_t ys1[kTile * kStep];
@@ -686,13 +775,19 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
   };
 
   f32x4_t acc[16][4];
+  // (under dropout, the last slice starts from the masked LoRA term)
+  if (DROP && split == splits - 1) {
+    dropout_lora_init(acc, gs, A, r, r32, M, K, m0, kcl, j16, g, drop);
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 #pragma unroll
   for (int mt = 0; mt < 16; ++mt)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      acc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      asm volatile("" : "+a"(acc[mt][t]));
-    }
+    for (int t = 0; t < 4; ++t) asm volatile("" : "+a"(acc[mt][t]));
   mfma_settle();
 
   // prologue: dY(it0) and codes(it0), codes(it0+1) resident; then the loads
@@ -818,8 +913,9 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
   wait_vmem_all();   // nothing left in flight into LDS at exit
   mfma_settle();
 
-  // LoRA: + (s.G) . A as r32 extra inner indices (last slice only)
-  const int tail = split == splits - 1 ? r32 / 32 : 0;
+  // LoRA: + (s.G) . A as r32 extra inner indices (last slice only; under
+  // dropout it went in first, masked)
+  const int tail = !DROP && split == splits - 1 ? r32 / 32 : 0;
   for (int ts = 0; ts < tail; ++ts) {
     const int j0 = ts * 32 + g * 8;
     uint2 rows[8];
@@ -883,6 +979,24 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
   }
 }
 
+// Keep flags (1 kept, 0 dropped) of elements 4c .. 4c + 3 of X, one
+// generator block per thread.
+__global__ __launch_bounds__(256) void k_dropout_mask(int64_t n, DropoutParams d,
+                                                      uint8_t* __restrict__ out) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t e = 4 * c;
+  if (e >= n) return;
+  const uint4 w = dropout_words((uint64_t)c, d);
+  const uint32_t f = (w.x >= d.thr ? 1u : 0u) | (w.y >= d.thr ? 0x100u : 0u) |
+                     (w.z >= d.thr ? 0x10000u : 0u) | (w.w >= d.thr ? 0x1000000u : 0u);
+  if (e + 4 <= n && (reinterpret_cast<uintptr_t>(out) & 3) == 0) {
+    *reinterpret_cast<uint32_t*>(out + e) = f;
+  } else {
+    const int64_t end = e + 4 < n ? e + 4 : n;
+    for (int64_t i = e; i < end; ++i) out[i] = (uint8_t)((f >> (8 * (i - e))) & 1u);
+  }
+}
+
 // out[i] = bf16(sum over s of part[s][i]), s in order; 4 elements per thread
 __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ part, int splits,
                                                       int64_t count,
@@ -938,21 +1052,36 @@ hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_
 hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes,
                           int64_t K, const float* ahat_t, const uint16_t* gs, const uint16_t* A,
                           int r, int r32, uint16_t* dX, int splits, float* part, int kind,
-                          hipStream_t s) {
+                          const DropoutParams* drop, hipStream_t s) {
   const int64_t grid1 = ceil_div(M, kTile) * ceil_div(K, kTile);
+  const bool dr = drop && drop->thr != 0 && r32 > 0;
+  const DropoutParams dp = dr ? *drop : DropoutParams{};
   if (N % kStep == 0) {
     const int nsteps = (int)ceil_div(N / kStep, splits);
-    launch_kernel(k_qlora_dx_nn_dma, dim3((unsigned)(grid1 * splits)), dim3(kThreads), s, dY, M, N,
-                  codes, K, ahat_t, host_tables(kind), gs, A, r, r32, dX, splits, nsteps, part);
+    launch_kernel(dr ? k_qlora_dx_nn_dma<true> : k_qlora_dx_nn_dma<false>,
+                  dim3((unsigned)(grid1 * splits)), dim3(kThreads), s, dY, M, N, codes, K, ahat_t,
+                  host_tables(kind), gs, A, r, r32, dX, splits, nsteps, part, dp);
   } else if (splits != 1) {
     return hipErrorInvalidValue;
   } else if (N % 8 == 0) {
-    launch_kernel(k_qlora_dx_nn<1>, dim3((unsigned)grid1), dim3(kThreads), s, dY, M, N, codes, K,
-                  ahat_t, host_tables(kind), gs, A, r, r32, dX);
+    launch_kernel(dr ? k_qlora_dx_nn<1, true> : k_qlora_dx_nn<1, false>, dim3((unsigned)grid1),
+                  dim3(kThreads), s, dY, M, N, codes, K, ahat_t, host_tables(kind), gs, A, r, r32,
+                  dX, dp);
   } else {
-    launch_kernel(k_qlora_dx_nn<2>, dim3((unsigned)grid1), dim3(kThreads), s, dY, M, N, codes, K,
-                  ahat_t, host_tables(kind), gs, A, r, r32, dX);
+    launch_kernel(dr ? k_qlora_dx_nn<2, true> : k_qlora_dx_nn<2, false>, dim3((unsigned)grid1),
+                  dim3(kThreads), s, dY, M, N, codes, K, ahat_t, host_tables(kind), gs, A, r, r32,
+                  dX, dp);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_dropout_mask(int64_t M, int64_t K, const DropoutParams& d, uint8_t* out,
+                               hipStream_t s) {
+  const int64_t n = M * K;
+  if (n == 0) return hipSuccess;
+  if (ceil_div(ceil_div(n, 4), 256) > 0x7FFFFFFF) return hipErrorInvalidValue;
+  launch_kernel(k_dropout_mask, dim3((unsigned)ceil_div(ceil_div(n, 4), 256)), dim3(256), s, n, d,
+                out);
   return hipGetLastError();
 }
 

@@ -218,6 +218,11 @@ __device__ __forceinline__ void xa_slice(const DecodeArgs& a, int r, int64_t sl,
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       x[s] = keep_if(load8_bf16(xrow, k + 32 * s + 8 * g, K, true), keep);
+    if (a.xa.drop.thr != 0) {   // LoRA dropout of X (element m K + k)
+      const uint64_t e = (uint64_t)(tok ? j16 : 0) * (uint64_t)K + k + 8 * g;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) x[s] = and4(x[s], dropout_keep8(e + 32 * s, a.xa.drop));
+    }
 #pragma unroll
     for (int jt = 0; jt < RT; ++jt) {
       const int u = jt * 16 + j16;
@@ -244,7 +249,8 @@ __device__ __forceinline__ void xa_slice(const DecodeArgs& a, int r, int64_t sl,
 #pragma unroll
         for (int w = 1; w < kXaWaves; ++w) sum += red[w][v][lane];
         const int64_t m = 4 * g + v;
-        if (m < a.M) part[m * (RT * 16) + jt * 16 + j16] = sum;
+        // (times 1 / (1 - p) under dropout; exactly 1 otherwise)
+        if (m < a.M) part[m * (RT * 16) + jt * 16 + j16] = sum * a.xa.drop.inv;
       }
     }
     __syncthreads();
@@ -353,7 +359,7 @@ int decode_xa_slices(int64_t K) {
 hipError_t launch_decode(const uint16_t* X, int64_t M, int64_t K, const NF4Ref& W, int64_t N,
                          const uint16_t* A, const uint16_t* B, int r, float scale, int splits,
                          float* partial, float* xa_part, uint16_t* Y, uint16_t* XA_out,
-                         hipStream_t s) {
+                         const DropoutParams& drop, hipStream_t s) {
   const int64_t KB = K / kBlock;
   DecodeArgs a{};
   a.X = X; a.M = M; a.K = K; a.N = N;
@@ -366,6 +372,7 @@ hipError_t launch_decode(const uint16_t* X, int64_t M, int64_t K, const NF4Ref& 
   a.xa_blocks = ks;                            // one row group of tokens (M <= 16)
   a.xa = SkinnyJob{X, K, K, A, K, ks, (int64_t)kXaWaves * kSkStep, xa_part, scale,
                    nullptr, nullptr, nullptr, 0, 1};
+  a.xa.drop = drop;
   const int64_t blocks = ks + ceil_div(N, kDecRows) * splits;
   hipError_t e;
   switch (rpad) {

@@ -39,17 +39,18 @@ __device__ __forceinline__ int64_t skinny_blocks(const SkinnyJob& J, int64_t M) 
   return ceil_div(skinny_rows(J, M), 16) * J.ks;
 }
 
-template <int RT>
+// DROP: some job reads X through the dropout mask
+template <int RT, bool DROP>
 __global__ __launch_bounds__(sk_waves<RT>() * 64) void k_skinny_slices(SkinnyJob j0, SkinnyJob j1, int nj,
                                                        int64_t M, int r, int r32, ReconJob rc,
                                                        int has_rc) {
   int64_t b = blockIdx.x;
   const int64_t b0 = skinny_blocks(j0, M);
-  if (b < b0) { skinny_slice<RT, sk_waves<RT>()>(j0, M, r, r32, b); return; }
+  if (b < b0) { skinny_slice<RT, sk_waves<RT>(), DROP>(j0, M, r, r32, b); return; }
   b -= b0;
   if (nj > 1) {
     const int64_t b1 = skinny_blocks(j1, M);
-    if (b < b1) { skinny_slice<RT, sk_waves<RT>()>(j1, M, r, r32, b); return; }
+    if (b < b1) { skinny_slice<RT, sk_waves<RT>(), DROP>(j1, M, r, r32, b); return; }
     b -= b1;
   }
   if (has_rc) recon_elems(rc, b);
@@ -120,8 +121,10 @@ __global__ __launch_bounds__(256) void k_prep(TransposeJob t0, TransposeJob t1, 
 // consecutive p (8 i16 .. 8 i16 + 7) of T and regroups them into the A
 // operands of 8 MFMAs: MFMA t handles p = p0 + 8 i + t, so the transpose of T
 // costs one 16-bit regroup per pair of rows, no LDS.  Wave partials are added
-// in wave order through LDS, one MFMA column t at a time.
-template <int RT>
+// in wave order through LDS, one MFMA column t at a time.  With DROP, a job
+// whose J.drop is set reads T = X through the dropout mask and scales its
+// partials by J.drop.inv.
+template <int RT, bool DROP>
 __device__ __forceinline__ void grad_slice(const GradJob& J, int64_t M, int r, int64_t b) {
   __shared__ float red[4][RT][4][64];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -195,6 +198,21 @@ __device__ __forceinline__ void grad_slice(const GradJob& J, int64_t M, int r, i
       for (int jt = 0; jt < RT; ++jt) acc[t][jt] = mfma16x16x32(a, bu[jt], acc[t][jt]);
     }
   };
+  // dropout of T's rows of step mb (wave-uniform switch); rows past M are
+  // clamped copies that meet zero columns of U
+  const bool dj = DROP && J.drop.thr != 0;
+  auto drop_t = [&](int64_t mb, uint4 (&rows)[8]) {
+    if constexpr (DROP) {
+      if (dj) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          int64_t m = mb + 8 * g + e;
+          m = m < M ? m : M - 1;
+          rows[e] = and4(rows[e], dropout_keep8((uint64_t)m * (uint64_t)J.drop.cols + pc, J.drop));
+        }
+      }
+    }
+  };
   // this wave's steps: mb = first + 128 i, i < cnt
   const int64_t first = mbeg + 32 * wv;
   const int64_t cnt = first < mend ? (mend - first + 127) / 128 : 0;
@@ -227,20 +245,25 @@ __device__ __forceinline__ void grad_slice(const GradJob& J, int64_t M, int r, i
     for (; i + 2 < cnt_fast; i += 2) {
       load_fast(i + 1, r1, u1);
       __builtin_amdgcn_sched_barrier(0);
+      drop_t(first + 128 * i, r0);
       mfmas(r0, u0);
       __builtin_amdgcn_sched_barrier(0);
       load_fast(i + 2, r0, u0);
       __builtin_amdgcn_sched_barrier(0);
+      drop_t(first + 128 * (i + 1), r1);
       mfmas(r1, u1);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (i + 1 < cnt_fast) {   // the last one or two steps, peeled
       load_fast(i + 1, r1, u1);
       __builtin_amdgcn_sched_barrier(0);
+      drop_t(first + 128 * i, r0);
       mfmas(r0, u0);
       __builtin_amdgcn_sched_barrier(0);
+      drop_t(first + 128 * (i + 1), r1);
       mfmas(r1, u1);
     } else {
+      drop_t(first + 128 * i, r0);
       mfmas(r0, u0);
     }
   }
@@ -250,6 +273,7 @@ __device__ __forceinline__ void grad_slice(const GradJob& J, int64_t M, int r, i
     uint4 r0[8], u0[RT];
     if (fast) load_step(first + 128 * i, r0, u0);
     else load_step_ragged(first + 128 * i, r0, u0);
+    drop_t(first + 128 * i, r0);
     mfmas(r0, u0);
   }
   // D[i = 4g + v][j16] of MFMA (t, jt): p = p0 + 8 (4g + v) + t, j = 16 jt + j16
@@ -269,6 +293,7 @@ __device__ __forceinline__ void grad_slice(const GradJob& J, int64_t M, int r, i
           float s = red[0][jt][v][lane];
 #pragma unroll
           for (int w = 1; w < 4; ++w) s += red[w][jt][v][lane];
+          if constexpr (DROP) s *= J.drop.inv;
           const int64_t p = p0 + 8 * (4 * g + v) + t;
           const int j = jt * 16 + i16;
           if (p < J.P && j < r) base[p * r + j] = s;
@@ -282,13 +307,13 @@ __device__ __forceinline__ int64_t grad_blocks(const GradJob& J) {
   return ceil_div(J.P, 128) * J.splits;
 }
 
-template <int RT>
+template <int RT, bool DROP>
 __global__ __launch_bounds__(256) void k_lora_grads(GradJob j0, GradJob j1, int nj, int64_t M,
                                                     int r) {
   int64_t b = blockIdx.x;
   const int64_t b0 = grad_blocks(j0);
-  if (b < b0) { grad_slice<RT>(j0, M, r, b); return; }
-  if (nj > 1) grad_slice<RT>(j1, M, r, b - b0);
+  if (b < b0) { grad_slice<RT, DROP>(j0, M, r, b); return; }
+  if (nj > 1) grad_slice<RT, DROP>(j1, M, r, b - b0);
 }
 
 __device__ __forceinline__ void grad_reduce_elem(const GradJob& J, int r, int64_t idx) {
@@ -314,7 +339,10 @@ hipError_t skinny_rt(const SkinnyJob* jobs, int nj, int64_t M, int r, int r32, c
   for (int i = 0; i < nj; ++i) blocks += ceil_div(skinny_rows(jobs[i], M), 16) * jobs[i].ks;
   blocks += rc ? ceil_div(rc->N * rc->KB, sk_waves<RT>() * 64) : 0;
   const ReconJob none{};
-  hipLaunchKernelGGL(k_skinny_slices<RT>, dim3((unsigned)blocks), dim3(sk_waves<RT>() * 64), 0, s,
+  bool drop = false;
+  for (int i = 0; i < nj; ++i) drop |= jobs[i].drop.thr != 0;
+  const auto kern = drop ? k_skinny_slices<RT, true> : k_skinny_slices<RT, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(sk_waves<RT>() * 64), 0, s,
                      jobs[0], nj > 1 ? jobs[1] : jobs[0], nj, M, r, r32, rc ? *rc : none,
                      rc ? 1 : 0);
   return hipGetLastError();
@@ -324,7 +352,10 @@ template <int RT>
 hipError_t grads_rt(const GradJob* jobs, int nj, int64_t M, int r, hipStream_t s) {
   int64_t blocks = 0;
   for (int i = 0; i < nj; ++i) blocks += ceil_div(jobs[i].P, 128) * jobs[i].splits;
-  hipLaunchKernelGGL(k_lora_grads<RT>, dim3((unsigned)blocks), dim3(256), 0, s, jobs[0],
+  bool drop = false;
+  for (int i = 0; i < nj; ++i) drop |= jobs[i].drop.thr != 0;
+  const auto kern = drop ? k_lora_grads<RT, true> : k_lora_grads<RT, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, jobs[0],
                      nj > 1 ? jobs[1] : jobs[0], nj, M, r);
   return hipGetLastError();
 }

@@ -8,6 +8,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "philox.h"
+
 namespace qnf4 {
 
 // Benchmark instrumentation: when an event pair is pending, the next launch
@@ -188,6 +190,9 @@ struct SkinnyJob {
   uint16_t* out_t;
   int64_t ldo_t;
   int part_only;   // write the slice partials even as a single slice
+  // dropout of T (T = X only): dropped elements read as zero, sums times
+  // drop.inv
+  DropoutParams drop{};
 };
 // Padded rank of the partial rows (16, 32, 64 or 128).
 int skinny_rpad(int r);
@@ -216,6 +221,7 @@ struct GradJob {
   float scale;
   int transposed;
   float* out;
+  DropoutParams drop{};   // dropout of T (T = X only), as in SkinnyJob
 };
 int lora_grad_splits(int64_t M, int64_t P);
 // Both jobs' partial launch, then both reductions.
@@ -232,10 +238,15 @@ hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_
                            int64_t N, const float* ahat_t, const uint16_t* xas, const uint16_t* B,
                            int r, int r32, uint16_t* Y, int splits, float* part, int kind,
                            hipStream_t s);
+// drop (nullable): the LoRA term of dX passes through the dropout of X,
+// dX = dY . W' + keep / (1 - p) * (s.G . A), element by element.
 hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes,
                           int64_t K, const float* ahat_t, const uint16_t* gs, const uint16_t* A,
                           int r, int r32, uint16_t* dX, int splits, float* part, int kind,
-                          hipStream_t s);
+                          const DropoutParams* drop, hipStream_t s);
+// keep flags (1 kept, 0 dropped) of the M x K elements of X
+hipError_t launch_dropout_mask(int64_t M, int64_t K, const DropoutParams& d, uint8_t* out,
+                               hipStream_t s);
 hipError_t launch_split_reduce(const float* part, int splits, int64_t count, uint16_t* out,
                                hipStream_t s);
 
@@ -256,6 +267,6 @@ int decode_xa_slices(int64_t K);
 hipError_t launch_decode(const uint16_t* X, int64_t M, int64_t K, const NF4Ref& W, int64_t N,
                          const uint16_t* A, const uint16_t* B, int r, float scale, int splits,
                          float* partial, float* xa_part, uint16_t* Y, uint16_t* XA_out,
-                         hipStream_t s);
+                         const DropoutParams& drop, hipStream_t s);
 
 }  // namespace qnf4

@@ -54,8 +54,10 @@ __device__ __forceinline__ uint16_t to_bf16(float v) {
 // Workgroup (row group, slice): 16 rows of T, inner indices [kbeg, kend).
 // The W waves take interleaved 128-wide steps; lane (j16, g) reads the 32
 // contiguous inner indices 32g..32g+31 of a step from both operands (four
-// MFMA sub-steps).  Wave partials are added in wave order through LDS.
-template <int RT, int W>
+// MFMA sub-steps).  Wave partials are added in wave order through LDS.  With
+// DROP, a job whose J.drop is set reads T through the dropout mask (T = X,
+// element e = m K + k) and scales its sums by J.drop.inv.
+template <int RT, int W, bool DROP = false>
 __device__ __forceinline__ void skinny_slice(const SkinnyJob& J, int64_t M, int r, int r32,
                                              int64_t b) {
   __shared__ float red[W][RT][4][64];
@@ -100,6 +102,17 @@ __device__ __forceinline__ void skinny_slice(const SkinnyJob& J, int64_t M, int 
 #pragma unroll
       for (int s = 0; s < 4; ++s) acc[jt] = mfma16x16x32(a[s], bv[jt][s], acc[jt]);
   };
+  // dropout of the T operand of the step at k (wave-uniform switch)
+  const bool dj = DROP && J.drop.thr != 0;
+  const uint64_t erow = (uint64_t)mrow * (uint64_t)J.drop.cols + 8 * g;
+  auto drop_t = [&](int64_t k, uint4 (&a)[4]) {
+    if constexpr (DROP) {
+      if (dj) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) a[s] = and4(a[s], dropout_keep8(erow + k + 32 * s, J.drop));
+      }
+    }
+  };
   // Operands of one step: sub-step s takes inner indices k + 32 s + 8 g ..
   // + 7 from lane group g, so each load instruction reads 64 contiguous bytes
   // per row.  Whole steps of a slice whose rows are 16-byte aligned run on
@@ -129,26 +142,32 @@ __device__ __forceinline__ void skinny_slice(const SkinnyJob& J, int64_t M, int 
       for (; i + 2 < cnt; i += 2) {
         load_fast(kat(i + 1), a1, b1);
         __builtin_amdgcn_sched_barrier(0);
+        drop_t(kat(i), a0);
         mfmas(a0, b0);
         __builtin_amdgcn_sched_barrier(0);
         load_fast(kat(i + 2), a0, b0);
         __builtin_amdgcn_sched_barrier(0);
+        drop_t(kat(i + 1), a1);
         mfmas(a1, b1);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (i + 1 < cnt) {
         load_fast(kat(i + 1), a1, b1);
         __builtin_amdgcn_sched_barrier(0);
+        drop_t(kat(i), a0);
         mfmas(a0, b0);
         __builtin_amdgcn_sched_barrier(0);
+        drop_t(kat(i + 1), a1);
         mfmas(a1, b1);
       } else {
+        drop_t(kat(i), a0);
         mfmas(a0, b0);
       }
     } else {
       for (int64_t i = 0; i < cnt; ++i) {   // r > 64: one step at a time
         uint4 a0[4], b0[RT][4];
         load_fast(kat(i), a0, b0);
+        drop_t(kat(i), a0);
         mfmas(a0, b0);
       }
     }
@@ -164,6 +183,7 @@ __device__ __forceinline__ void skinny_slice(const SkinnyJob& J, int64_t M, int 
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         b0[jt][s] = load8_bf16(urow[jt], k + 32 * s + 8 * g, J.kin, uv);
+    drop_t(k, a0);
     mfmas(a0, b0);
   }
 #pragma unroll
@@ -182,6 +202,7 @@ __device__ __forceinline__ void skinny_slice(const SkinnyJob& J, int64_t M, int 
       float sum = red[0][jt][v][lane];
 #pragma unroll
       for (int w = 1; w < W; ++w) sum += red[w][jt][v][lane];
+      if constexpr (DROP) sum *= J.drop.inv;
       const int64_t m = m0 + 4 * g + v;
       const int j = jt * 16 + j16;
       if (J.ks > 1 || J.part_only) {

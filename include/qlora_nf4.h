@@ -184,6 +184,53 @@ qlora_status qlora_linear_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
                               float* dA, float* dB, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * LoRA dropout ("QLoRA: Fine-Tuning a 70B on One GPU", section "Practical
+ * Implementation": the lora_dropout knob of the LoRA configuration).  Only the
+ * adapter path sees the dropped input:
+ *     Y = X . W'^T + s . (D(X) . A^T) . B^T,
+ *     D(X)[m][k] = keep(m, k) ? X[m][k] / (1 - p) : 0.
+ * keep comes from the counter-based generator Philox4x32-10 (Salmon, Moraes,
+ * Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011), so
+ * the backward regenerates the forward's mask instead of storing it: element
+ * e = m K + k of X takes output word e mod 4 of counter (e div 4 as a 64-bit
+ * value in words 0 and 1, words 2 and 3 zero) under key (seed & 0xFFFFFFFF,
+ * seed >> 32), and is kept when that word >= floor(p * 2^32).  The same
+ * (p, seed) must be passed to the forward and the backward of one step; a
+ * new seed per step and per layer draws a new mask. */
+typedef struct {
+  double p;        /* drop probability, 0 <= p < 1; 0 is no dropout */
+  uint64_t seed;
+} qlora_dropout;
+
+/* qlora_linear_fwd with dropout on the adapter input: XA_out receives
+ * bf16(D(X) . A^T).  drop NULL or drop->p == 0 is qlora_linear_fwd.  Same
+ * shapes, workspace and errors, plus QLORA_ERR_INVALID_ARG for p outside
+ * [0, 1) or not a number. */
+qlora_status qlora_linear_fwd_dropout(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
+                                      const qlora_bf16* A, const qlora_bf16* B, int32_t r,
+                                      float alpha, const qlora_dropout* drop, qlora_bf16* Y,
+                                      qlora_bf16* XA_out, void* ws, size_t ws_bytes,
+                                      void* stream);
+
+/* qlora_linear_bwd of the dropped layer (same drop as the forward):
+ *     dX = dY . W' + (s . G . A) * keep / (1 - p)   (element by element)
+ *     dA = s . G^T . D(X),   dB = s . dY^T . (D(X) . A^T)
+ * XA_in (nullable) must be the XA_out of qlora_linear_fwd_dropout with the
+ * same drop; when NULL, D(X) . A^T is recomputed with the regenerated mask. */
+qlora_status qlora_linear_bwd_dropout(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
+                                      const qlora_bf16* A, const qlora_bf16* B, int32_t r,
+                                      float alpha, const qlora_dropout* drop,
+                                      const qlora_bf16* dY, const qlora_bf16* XA_in,
+                                      qlora_bf16* dX, float* dA, float* dB, void* ws,
+                                      size_t ws_bytes, void* stream);
+
+/* The keep flags of an [M, K] input under drop: out[m * K + k] = 1 if the
+ * element is kept, else 0 (uint8, device memory, M * K bytes).  The mask the
+ * two calls above apply, for inspection and tests.  M, K >= 0. */
+qlora_status qlora_dropout_mask(int64_t M, int64_t K, const qlora_dropout* drop, uint8_t* out,
+                                void* stream);
+
+/* ------------------------------------------------------------------------
  * Kernel timing (benchmark instrumentation; not part of the method).
  * Between qlora_trace_begin and qlora_trace_end, every launch of a kernel whose
  * bit is set in `kernel_mask` (1 << qlora_kernel) records its own start and end

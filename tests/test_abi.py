@@ -145,3 +145,30 @@ def test_no_cpu_fallback(q, monkeypatch):
     monkeypatch.setattr(q, "LIB_PATH", "/nonexistent/libqlora_nf4.so")
     with pytest.raises(RuntimeError):
         q.lib()
+
+
+def test_dropout_argument_errors(q):
+    """Drop probabilities outside [0, 1) (and NaN) are rejected on the host
+    by all three dropout calls; an empty mask is a no-op."""
+    lib = q.lib()
+    P = ctypes.c_void_p
+    d = _desc(q)
+    X = P(0x400000)
+    for p in (1.0, -0.1, 2.0, float("nan")):
+        dr = q.QloraDropout(p, 7)
+        assert lib.qlora_linear_fwd_dropout(ctypes.byref(d), X, 4, X, X, 8, ctypes.c_float(1.0),
+                                            ctypes.byref(dr), X, None, X, 1 << 30, None) == \
+            q.QLORA_ERR_INVALID_ARG
+        assert lib.qlora_linear_bwd_dropout(ctypes.byref(d), X, 4, X, X, 8, ctypes.c_float(1.0),
+                                            ctypes.byref(dr), X, None, X, X, X, X, 1 << 30,
+                                            None) == q.QLORA_ERR_INVALID_ARG
+        assert lib.qlora_dropout_mask(4, 64, ctypes.byref(dr), X, None) == q.QLORA_ERR_INVALID_ARG
+    ok = q.QloraDropout(0.1, 7)
+    assert lib.qlora_dropout_mask(4, 64, None, X, None) == q.QLORA_ERR_INVALID_ARG
+    assert lib.qlora_dropout_mask(-1, 64, ctypes.byref(ok), X, None) == q.QLORA_ERR_INVALID_ARG
+    assert lib.qlora_dropout_mask(4, 64, ctypes.byref(ok), None, None) == q.QLORA_ERR_INVALID_ARG
+    assert lib.qlora_dropout_mask(0, 64, ctypes.byref(ok), None, None) == q.QLORA_OK
+    # the shape checks of the plain calls come first
+    assert lib.qlora_linear_fwd_dropout(ctypes.byref(d), X, 0, X, X, 8, ctypes.c_float(1.0),
+                                        ctypes.byref(ok), X, None, X, 1 << 30, None) == \
+        q.QLORA_ERR_INVALID_ARG
