@@ -8,8 +8,9 @@ quantisation.  ``value`` is tokens per second of that step with every input
 resident in HBM.  The JSON line also carries the dominant kernel's roofline
 (HIP-event durations measured on the library's stream during the timed
 region), the CPU oracle timed on a bounded sample, and the other legs of the
-path: quantise + dequantise of the full 8.03B-parameter weight set, the
-70B-shaped decode GEMV at 1 / 4 / 16 tokens, and the 80-layer LLaMA-65B stack.
+path: quantise + dequantise of the full 8.03B-parameter weight set, the NF4 /
+INT4 and constant variants, the layer step with LoRA dropout, the 70B-shaped
+decode GEMV at 1 / 4 / 16 tokens, and the 80-layer LLaMA-65B stack.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs all|none]
 """
@@ -38,7 +39,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--legs", default="all",
-                    help="all, none, or a comma list of quant, variants, decode, stack65b")
+                    help="all, none, or a comma list of quant, variants, dropout, decode, stack65b")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run 3 plain device-to-device copies of MIB MiB (the known-size "
@@ -299,6 +300,40 @@ def leg_quant_dequant(q, torch, workloads, passes=3):
     return res
 
 
+def leg_dropout(q, torch, layers, M, r, alpha, p=0.05, steps=10):
+    """The headline layer step with LoRA dropout p on every adapter input
+    (the Practical Implementation section's lora_dropout), against the same
+    step without: eager step time and the dX GEMM's average launch (which
+    starts its accumulators from the masked LoRA term), from HIP events."""
+
+    def step(drop):
+        for i, L in enumerate(layers):
+            d = None if drop is None else (drop, 1000 + i)
+            q.qlora_linear_fwd(L["q"], L["X"], L["A"], L["B"], alpha, Y=L["Y"], XA_out=L["XA"],
+                               ws=L["ws"], return_xa=True, dropout=d)
+        for i, L in reversed(list(enumerate(layers))):
+            d = None if drop is None else (drop, 1000 + i)
+            q.qlora_linear_bwd(L["q"], L["X"], L["A"], L["B"], alpha, L["dY"], XA_in=L["XA"],
+                               dX=L["dX"], dA=L["dA"], dB=L["dB"], ws=L["ws"], dropout=d)
+
+    res = {"p": p, "seeds": "1000 + linear index"}
+    for label, drop in (("no_dropout", None), ("dropout", p)):
+        step(drop)
+        sec = timed(torch, lambda: step(drop), steps)
+        q.qlora_trace_begin(["dx_gemm"], capacity=len(layers) + 1)
+        step(drop)
+        tr = q.qlora_trace_end()
+        n, ms = tr.get("dx_gemm", (0, 0.0))
+        res["step_ms_" + label] = round(sec * 1e3, 4)
+        res["dx_gemm_avg_us_" + label] = round(ms * 1e3 / max(n, 1), 2)
+    res["tokens_per_s_dropout"] = round(M / (res["step_ms_dropout"] * 1e-3), 1)
+    res["step_overhead_pct"] = round(
+        100.0 * (res["step_ms_dropout"] / res["step_ms_no_dropout"] - 1.0), 2)
+    log("dropout leg: %.3f ms/step with p=%.2f, %.3f without" %
+        (res["step_ms_dropout"], p, res["step_ms_no_dropout"]))
+    return res
+
+
 def leg_variants(q, torch, workloads, passes=3):
     """The 4-bit type and constant variants on the same kernels, over the seven
     weights of one Llama-3.1-8B layer: quantise and dequantise (bf16) GB/s and
@@ -504,11 +539,14 @@ def main():
     if args.cpu_baseline == "on":
         cpu = cpu_baseline(workloads, layers, host_w)
         log("cpu baseline: %s tokens/s on %d threads" % (cpu["value"], cpu["cores"]))
+    legs = {}
+    want = {"quant", "variants", "dropout", "decode", "stack65b"} if args.legs == "all" else (
+        set() if args.legs == "none" else set(args.legs.split(",")))
+    if "dropout" in want:
+        wl = workloads.LLAMA8B_LAYER
+        legs["llama8b_layer_lora_dropout"] = leg_dropout(q, torch, layers, wl.m, wl.r, wl.alpha)
     del layers, host_w
     torch.cuda.empty_cache()
-    legs = {}
-    want = {"quant", "variants", "decode", "stack65b"} if args.legs == "all" else (
-        set() if args.legs == "none" else set(args.legs.split(",")))
     if "quant" in want:
         legs["llama8b_weight_set_quant_dequant"] = leg_quant_dequant(q, torch, workloads)
     if "variants" in want:
