@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE ONLY: the parity reference for the GPU library.  Only the
 tests, ``__graft_entry__.smoke()`` and the benchmark's ``cpu_baseline`` leg may
 import it.  It shares no code with the GPU library and never calls it.
 
-Three parts:
+Four parts:
   * ``nf4_oracle.c`` (wrapped here): codebook, blockwise absmax quantisation,
     double quantisation of the constants, dequantisation, bf16 rounding.
   * ``linear.py``: the forward and backward of
@@ -12,6 +12,7 @@ Three parts:
     written as their float64 definitions with numpy matmul as the only step,
     optionally with dropout on the LoRA input.
   * ``dropout.py``: the keep mask of that dropout (Philox4x32-10).
+  * ``adamw.py``: the AdamW step on the adapters.
 
 Pins (tests/test_oracle_*.py) tie every function here to something other than
 itself: scipy's normal quantile, printed figures from the pages, closed forms,
@@ -25,6 +26,7 @@ import numpy as np
 from . import build as _build
 from .linear import linear_fwd, linear_bwd, lora_scale  # noqa: F401
 from . import dropout  # noqa: F401
+from . import adamw  # noqa: F401
 
 NF4_BLOCK = 64
 DQ_BLOCK = 256
