@@ -27,10 +27,11 @@ EXPORTS = [
     "qlora_quantize_nf4", "qlora_dequantize_nf4", "qlora_dequantize_absmax",
     "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout", "qlora_dropout_mask",
+    "qlora_adamw_step", "qlora_host_state_alloc", "qlora_host_state_free",
     "qlora_trace_begin", "qlora_trace_pause", "qlora_trace_end",
 ]
 KERNELS = {"fwd_gemm": 0, "dx_gemm": 1, "quantize": 2, "dequant": 3, "gemv": 4,
-           "split_reduce": 5}
+           "split_reduce": 5, "adamw": 6}
 
 
 class QloraError(RuntimeError):
@@ -51,6 +52,17 @@ class NF4Descriptor(ctypes.Structure):
 class QloraDropout(ctypes.Structure):
     """LoRA dropout of the adapter input: drop probability p, generator seed."""
     _fields_ = [("p", ctypes.c_double), ("seed", ctypes.c_uint64)]
+
+
+class AdamWTensor(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p),
+                ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p),
+                ("param_bf16", ctypes.c_void_p), ("numel", ctypes.c_int64)]
+
+
+class AdamWHparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double)]
 
 
 _lib = None
@@ -86,6 +98,9 @@ def lib():
         L.qlora_linear_bwd_dropout.argtypes = [D, P, I64, P, P, I32, F, P, P, P, P, P, P, P,
                                                SZ, P]
         L.qlora_dropout_mask.argtypes = [I64, I64, P, P, P]
+        L.qlora_adamw_step.argtypes = [P, I64, P, I32, P]
+        L.qlora_host_state_alloc.argtypes = [SZ, P]
+        L.qlora_host_state_free.argtypes = [P]
         L.qlora_trace_begin.argtypes = [ctypes.c_uint32, I32]
         L.qlora_trace_pause.argtypes = [I32]
         L.qlora_trace_end.argtypes = [P, P]
@@ -301,6 +316,55 @@ def qlora_linear_bwd(q: NF4Tensor, X, A, B, alpha: float, dY, XA_in=None, need_d
                                               _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(),
                                               _stream()), "qlora_linear_bwd_dropout")
     return (dX if need_dx else None), dA, dB
+
+
+def qlora_adamw_step(tensors, step: int, lr: float, beta1: float = 0.9, beta2: float = 0.999,
+                     eps: float = 1e-8, weight_decay: float = 0.0):
+    """One AdamW step.  tensors: list of (param, grad, exp_avg, exp_avg_sq,
+    param_bf16 or None); float32 contiguous tensors of one numel each (device
+    tensors, or host-state tensors from qlora_host_state_alloc for the two
+    statistics), param_bf16 bf16."""
+    arr = (AdamWTensor * max(len(tensors), 1))()
+    for i, (p, g, m, v, pb) in enumerate(tensors):
+        n = p.numel()
+        for t in (p, g, m, v):
+            assert t.dtype == torch.float32 and t.is_contiguous() and t.numel() == n
+        if pb is not None:
+            assert pb.dtype == torch.bfloat16 and pb.is_contiguous() and pb.numel() == n
+        arr[i] = AdamWTensor(_ptr(p), _ptr(g), _ptr(m), _ptr(v),
+                             _ptr(pb) if pb is not None else None, n)
+    h = AdamWHparams(lr, beta1, beta2, eps, weight_decay)
+    _check(lib().qlora_adamw_step(ctypes.byref(h), step, arr, len(tensors), _stream()),
+           "qlora_adamw_step")
+
+
+class HostState:
+    """Pinned, device-mapped host memory for optimiser statistics, viewed as a
+    float32 CPU tensor (``.tensor``).  Freed by ``free()`` or when collected."""
+
+    def __init__(self, numel: int):
+        ptr = ctypes.c_void_p()
+        _check(lib().qlora_host_state_alloc(4 * numel, ctypes.byref(ptr)),
+               "qlora_host_state_alloc")
+        self.ptr = ptr.value
+        buf = (ctypes.c_byte * (4 * numel)).from_address(self.ptr)
+        self.tensor = torch.frombuffer(buf, dtype=torch.float32, count=numel)
+
+    def free(self):
+        if self.ptr:
+            self.tensor = None
+            _check(lib().qlora_host_state_free(self.ptr), "qlora_host_state_free")
+            self.ptr = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def qlora_host_state_alloc(numel: int) -> HostState:
+    return HostState(numel)
 
 
 def qlora_trace_begin(kernels, capacity: int = 4096):

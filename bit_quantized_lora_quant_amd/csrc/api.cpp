@@ -401,6 +401,70 @@ qlora_status qlora_dropout_mask(int64_t M, int64_t K, const qlora_dropout* drop,
   return hip_status(launch_dropout_mask(M, K, dp, out, static_cast<hipStream_t>(stream)));
 }
 
+qlora_status qlora_adamw_step(const qlora_adamw_hparams* h, int64_t step,
+                              const qlora_adamw_tensor* tensors, int32_t count, void* stream) {
+  if (!h || step < 1 || count < 0 || (count > 0 && !tensors)) return QLORA_ERR_INVALID_ARG;
+  if (!(h->lr >= 0.0) || !(h->beta1 >= 0.0 && h->beta1 < 1.0) ||
+      !(h->beta2 >= 0.0 && h->beta2 < 1.0) || !(h->eps > 0.0) || !(h->weight_decay >= 0.0) ||
+      !std::isfinite(h->lr) || !std::isfinite(h->eps) || !std::isfinite(h->weight_decay))
+    return QLORA_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < count; ++i) {
+    const qlora_adamw_tensor& t = tensors[i];
+    if (t.numel < 0) return QLORA_ERR_INVALID_ARG;
+    if (t.numel == 0) continue;
+    if (!t.param || !t.grad || !t.exp_avg || !t.exp_avg_sq) return QLORA_ERR_INVALID_ARG;
+    if (!aligned(t.param, 4) || !aligned(t.grad, 4) || !aligned(t.exp_avg, 4) ||
+        !aligned(t.exp_avg_sq, 4) || (t.param_bf16 && !aligned(t.param_bf16, 2)))
+      return QLORA_ERR_INVALID_ARG;
+  }
+  const double lr = h->lr, b1 = h->beta1, b2 = h->beta2;
+  AdamHyper hp;
+  hp.decay = (float)(1.0 - lr * h->weight_decay);
+  hp.b1 = (float)b1;
+  hp.one_minus_b1 = (float)(1.0 - b1);
+  hp.b2 = (float)b2;
+  hp.one_minus_b2 = (float)(1.0 - b2);
+  hp.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(1.0 - std::pow(b2, (double)step)));
+  hp.eps = (float)h->eps;
+  hp.step_size = (float)(lr / (1.0 - std::pow(b1, (double)step)));
+  if (!(hp.eps > 0.f)) return QLORA_ERR_INVALID_ARG;   // eps below float's range
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t i0 = 0; i0 < count; i0 += kAdamBatch) {
+    AdamBatch bt{};
+    bt.count = std::min(count - i0, kAdamBatch);
+    bt.chunk_start[0] = 0;
+    for (int j = 0; j < bt.count; ++j) {
+      const qlora_adamw_tensor& t = tensors[i0 + j];
+      bt.t[j] = AdamTensor{t.param, t.grad, t.exp_avg, t.exp_avg_sq,
+                           reinterpret_cast<uint16_t*>(t.param_bf16), t.numel};
+      bt.chunk_start[j + 1] = bt.chunk_start[j] + adamw_chunks(t.numel);
+    }
+    const hipError_t e = traced(QLORA_KERNEL_ADAMW, s, [&] { return launch_adamw(bt, hp, s); });
+    if (e != hipSuccess) return QLORA_ERR_HIP;
+  }
+  return QLORA_OK;
+}
+
+qlora_status qlora_host_state_alloc(size_t bytes, void** ptr) {
+  if (!ptr || bytes == 0) return QLORA_ERR_INVALID_ARG;
+  *ptr = nullptr;
+  void* p = nullptr;
+  if (hipHostMalloc(&p, bytes, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess)
+    return QLORA_ERR_HIP;
+  void* d = nullptr;
+  if (hipHostGetDevicePointer(&d, p, 0) != hipSuccess || d != p) {
+    (void)hipHostFree(p);
+    return QLORA_ERR_UNSUPPORTED;
+  }
+  *ptr = p;
+  return QLORA_OK;
+}
+
+qlora_status qlora_host_state_free(void* ptr) {
+  if (!ptr) return QLORA_OK;
+  return hipHostFree(ptr) == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
+}
+
 qlora_status qlora_trace_begin(uint32_t kernel_mask, int32_t capacity) {
   if (kernel_mask == 0 || kernel_mask >= (1u << QLORA_KERNEL_COUNT) || capacity < 1 ||
       capacity > (1 << 20))

@@ -231,6 +231,62 @@ qlora_status qlora_dropout_mask(int64_t M, int64_t K, const qlora_dropout* drop,
                                 void* stream);
 
 /* ------------------------------------------------------------------------
+ * Adapter optimiser.  AdamW keeps a running mean m and a running mean v of
+ * the squared gradient for every trainable parameter ("QLoRA: Fine-Tuning a
+ * 70B on One GPU", section "Paged Optimizers"); the adapters train as float32
+ * master weights with float32 gradients and statistics ("Fine-Tuning Memory
+ * Requirements: Full Training vs LoRA vs QLoRA", sections "Where training
+ * memory goes" and "LoRA: freeze the base, train small adapters").  One call
+ * applies step t (1-based) of Adam with decoupled weight decay to every
+ * tensor, element by element in float32:
+ *     p <- p * (1 - lr * weight_decay)
+ *     m <- beta1 * m + (1 - beta1) * g
+ *     v <- beta2 * v + (1 - beta2) * g^2
+ *     p <- p - lr / (1 - beta1^t) * m / (sqrt(v) / sqrt(1 - beta2^t) + eps)
+ * and writes bf16(p) to param_bf16 when it is set (the adapter operand of
+ * qlora_linear_fwd / _bwd).  The kernel's float32 coefficients beta1,
+ * 1 - beta1, beta2, 1 - beta2, eps, 1 - lr * weight_decay, lr / (1 - beta1^t)
+ * and 1 / sqrt(1 - beta2^t) are each formed in double on the host from the
+ * double hyperparameters and rounded to float once. */
+typedef struct {
+  float* param;            /* float32 master weights [numel], updated in place */
+  const float* grad;       /* float32 gradient [numel] (dA or dB of the backward) */
+  float* exp_avg;          /* m [numel], updated in place */
+  float* exp_avg_sq;       /* v [numel], updated in place */
+  qlora_bf16* param_bf16;  /* nullable: receives bf16(param) after the update */
+  int64_t numel;           /* >= 0; 0 skips the tensor */
+} qlora_adamw_tensor;
+
+typedef struct {
+  double lr;            /* >= 0 */
+  double beta1, beta2;  /* in [0, 1) */
+  double eps;           /* > 0 */
+  double weight_decay;  /* >= 0 */
+} qlora_adamw_hparams;
+
+/* One AdamW step (number `step` >= 1) over `count` tensors, asynchronously on
+ * `stream` (up to 48 tensors per launch).  All pointers of a tensor with
+ * numel > 0 must be non-null and 4-byte aligned (param_bf16: 2-byte); 16-byte
+ * alignment takes the vector path.  The tensors must not overlap.  exp_avg
+ * and exp_avg_sq (and the others) may be device memory or host memory from
+ * qlora_host_state_alloc.  Returns QLORA_ERR_INVALID_ARG for bad
+ * hyperparameters, step, count or tensors (nothing launched). */
+qlora_status qlora_adamw_step(const qlora_adamw_hparams* h, int64_t step,
+                              const qlora_adamw_tensor* tensors, int32_t count, void* stream);
+
+/* Optimiser state kept in host memory ("QLoRA: Fine-Tuning a 70B on One
+ * GPU", section "Paged Optimizers": host RAM serves as an extension of device
+ * memory for the optimiser statistics).  Allocates `bytes` of pinned,
+ * coherent host memory mapped into the device address space at the same
+ * address, so qlora_adamw_step reads and writes it in place over the host
+ * link while the device memory holds only the weights and gradients.  The
+ * caller owns it and releases it with qlora_host_state_free; its contents
+ * start undefined.  QLORA_ERR_UNSUPPORTED if the mapping would need a
+ * different device address. */
+qlora_status qlora_host_state_alloc(size_t bytes, void** ptr);
+qlora_status qlora_host_state_free(void* ptr);
+
+/* ------------------------------------------------------------------------
  * Kernel timing (benchmark instrumentation; not part of the method).
  * Between qlora_trace_begin and qlora_trace_end, every launch of a kernel whose
  * bit is set in `kernel_mask` (1 << qlora_kernel) records its own start and end
@@ -253,7 +309,8 @@ typedef enum {
   QLORA_KERNEL_DEQUANT = 3,    /* dequantise to float32 / bf16 */
   QLORA_KERNEL_GEMV = 4,       /* decode forward (M <= 16), main kernel */
   QLORA_KERNEL_SPLIT_REDUCE = 5, /* sum of split-K GEMM partials -> bf16 */
-  QLORA_KERNEL_COUNT = 6
+  QLORA_KERNEL_ADAMW = 6,      /* optimiser step */
+  QLORA_KERNEL_COUNT = 7
 } qlora_kernel;
 
 qlora_status qlora_trace_begin(uint32_t kernel_mask, int32_t capacity);

@@ -172,3 +172,33 @@ def test_dropout_argument_errors(q):
     assert lib.qlora_linear_fwd_dropout(ctypes.byref(d), X, 0, X, X, 8, ctypes.c_float(1.0),
                                         ctypes.byref(ok), X, None, X, 1 << 30, None) == \
         q.QLORA_ERR_INVALID_ARG
+
+
+def test_adamw_argument_errors(q):
+    """Bad hyperparameters, step numbers and tensors come back as status
+    codes on the host; an empty tensor list is a no-op."""
+    lib = q.lib()
+    fake = 0x100000
+    arr = (q.AdamWTensor * 1)(q.AdamWTensor(fake, fake, fake, fake, None, 8))
+    ok = q.AdamWHparams(1e-3, 0.9, 0.999, 1e-8, 0.0)
+    for h in (q.AdamWHparams(-1.0, 0.9, 0.999, 1e-8, 0.0),
+              q.AdamWHparams(float("nan"), 0.9, 0.999, 1e-8, 0.0),
+              q.AdamWHparams(1e-3, 1.0, 0.999, 1e-8, 0.0),
+              q.AdamWHparams(1e-3, 0.9, -0.1, 1e-8, 0.0),
+              q.AdamWHparams(1e-3, 0.9, 0.999, 0.0, 0.0),
+              q.AdamWHparams(1e-3, 0.9, 0.999, 1e-8, -1.0)):
+        assert lib.qlora_adamw_step(ctypes.byref(h), 1, arr, 1, None) == q.QLORA_ERR_INVALID_ARG
+    assert lib.qlora_adamw_step(ctypes.byref(ok), 0, arr, 1, None) == q.QLORA_ERR_INVALID_ARG
+    assert lib.qlora_adamw_step(None, 1, arr, 1, None) == q.QLORA_ERR_INVALID_ARG
+    assert lib.qlora_adamw_step(ctypes.byref(ok), 1, None, 1, None) == q.QLORA_ERR_INVALID_ARG
+    for t in (q.AdamWTensor(fake + 2, fake, fake, fake, None, 8),
+              q.AdamWTensor(fake, 0, fake, fake, None, 8),
+              q.AdamWTensor(fake, fake, fake, fake, fake + 1, 8),
+              q.AdamWTensor(fake, fake, fake, fake, None, -1)):
+        one = (q.AdamWTensor * 1)(t)
+        assert lib.qlora_adamw_step(ctypes.byref(ok), 1, one, 1, None) == q.QLORA_ERR_INVALID_ARG
+    assert lib.qlora_adamw_step(ctypes.byref(ok), 1, arr, 0, None) == q.QLORA_OK
+    ptr = ctypes.c_void_p()
+    assert lib.qlora_host_state_alloc(0, ctypes.byref(ptr)) == q.QLORA_ERR_INVALID_ARG
+    assert lib.qlora_host_state_alloc(64, None) == q.QLORA_ERR_INVALID_ARG
+    assert lib.qlora_host_state_free(None) == q.QLORA_OK
