@@ -9,8 +9,9 @@ resident in HBM.  The JSON line also carries the dominant kernel's roofline
 (HIP-event durations measured on the library's stream during the timed
 region), the CPU oracle timed on a bounded sample, and the other legs of the
 path: quantise + dequantise of the full 8.03B-parameter weight set, the NF4 /
-INT4 and constant variants, the layer step with LoRA dropout, the 70B-shaped
-decode GEMV at 1 / 4 / 16 tokens, and the 80-layer LLaMA-65B stack.
+INT4 and constant variants, the layer step with LoRA dropout, the AdamW step
+over every 8B adapter, the 70B-shaped decode GEMV at 1 / 4 / 16 tokens, and the
+80-layer LLaMA-65B stack.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs all|none]
 """
@@ -39,7 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--legs", default="all",
-                    help="all, none, or a comma list of quant, variants, dropout, decode, stack65b")
+                    help="all, none, or a comma list of quant, variants, dropout, adamw, decode, "
+                         "stack65b")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run 3 plain device-to-device copies of MIB MiB (the known-size "
@@ -334,6 +336,78 @@ def leg_dropout(q, torch, layers, M, r, alpha, p=0.05, steps=10):
     return res
 
 
+def leg_adamw(q, torch, workloads, reps=10):
+    """The adapter optimiser step over every adapter of Llama-3.1-8B at r = 16
+    (32 layers x 7 projections x {A, B} = 448 tensors, 41.9M parameters):
+    float32 masters, gradients and statistics, bf16 copies written in the same
+    pass.  Algorithmic HBM bytes per parameter: 16 read + 14 written.  Then the
+    same step with both statistics in mapped host memory (16 bytes per
+    parameter cross the host link)."""
+    dev = "cuda:0"
+    wl = workloads.LLAMA8B_LAYER
+    r = wl.r
+    shapes = []
+    for _ in range(wl.layers):
+        for _, K, N in wl.linears:
+            shapes += [(r, K), (N, r)]
+    total = sum(a * b for a, b in shapes)
+    g = torch.Generator(device=dev)
+    g.manual_seed(8)
+    P = torch.randn(total, generator=g, device=dev) * 0.02
+    G = torch.randn(total, generator=g, device=dev) * 1e-3
+    M = torch.zeros(total, device=dev)
+    V = torch.zeros(total, device=dev)
+    PB = torch.empty(total, dtype=torch.bfloat16, device=dev)
+
+    def views(m_all, v_all):
+        out, off = [], 0
+        for a, b in shapes:
+            n = a * b
+            out.append((P[off:off + n], G[off:off + n], m_all[off:off + n], v_all[off:off + n],
+                        PB[off:off + n]))
+            off += n
+        return out
+
+    res = {"tensors": len(shapes), "params": total, "hparams": "lr 2e-4, betas (0.9, 0.999), "
+           "eps 1e-8, weight decay 0.01"}
+    hs = []
+    for label in ("device_statistics", "host_statistics"):
+        if label == "host_statistics":
+            hs = [q.qlora_host_state_alloc(total) for _ in range(2)]
+            hs[0].tensor.zero_()
+            hs[1].tensor.zero_()
+            ts = views(hs[0].tensor, hs[1].tensor)
+        else:
+            ts = views(M, V)
+
+        def step():
+            q.qlora_adamw_step(ts, 1, 2e-4, 0.9, 0.999, 1e-8, 0.01)
+
+        step()
+        gr = graph_of(torch, step)
+        sec = timed(torch, gr.replay, reps)
+        del gr
+        q.qlora_trace_begin(["adamw"], capacity=64)
+        step()
+        tr = q.qlora_trace_end()
+        n, ms = tr.get("adamw", (0, 0.0))
+        ent = {"step_ms": round(sec * 1e3, 4), "launches": n,
+               "kernel_ms": round(ms, 4)}
+        if label == "device_statistics":
+            gbs = 30.0 * total / sec / 1e9
+            ent.update({"hbm_GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
+        else:
+            ent["host_link_GB/s"] = round(16.0 * total / sec / 1e9, 2)
+        res[label] = ent
+    for h in hs:
+        h.free()
+    del P, G, M, V, PB
+    torch.cuda.empty_cache()
+    log("adamw leg: %.3f ms with device statistics, %.3f ms with host statistics" %
+        (res["device_statistics"]["step_ms"], res["host_statistics"]["step_ms"]))
+    return res
+
+
 def leg_variants(q, torch, workloads, passes=3):
     """The 4-bit type and constant variants on the same kernels, over the seven
     weights of one Llama-3.1-8B layer: quantise and dequantise (bf16) GB/s and
@@ -540,7 +614,7 @@ def main():
         cpu = cpu_baseline(workloads, layers, host_w)
         log("cpu baseline: %s tokens/s on %d threads" % (cpu["value"], cpu["cores"]))
     legs = {}
-    want = {"quant", "variants", "dropout", "decode", "stack65b"} if args.legs == "all" else (
+    want = {"quant", "variants", "dropout", "adamw", "decode", "stack65b"} if args.legs == "all" else (
         set() if args.legs == "none" else set(args.legs.split(",")))
     if "dropout" in want:
         wl = workloads.LLAMA8B_LAYER
@@ -551,6 +625,8 @@ def main():
         legs["llama8b_weight_set_quant_dequant"] = leg_quant_dequant(q, torch, workloads)
     if "variants" in want:
         legs["nf4_int4_and_constant_variants"] = leg_variants(q, torch, workloads)
+    if "adamw" in want:
+        legs["llama8b_adapters_adamw_step"] = leg_adamw(q, torch, workloads)
     if "decode" in want:
         legs["llama70b_decode_gemv"] = leg_decode(q, torch, workloads)
     if "stack65b" in want:
