@@ -28,6 +28,7 @@ EXPORTS = [
     "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout", "qlora_dropout_mask",
     "qlora_adamw_step", "qlora_host_state_alloc", "qlora_host_state_free",
+    "qlora_merge_workspace_bytes", "qlora_merge_requantize",
     "qlora_trace_begin", "qlora_trace_pause", "qlora_trace_end",
 ]
 KERNELS = {"fwd_gemm": 0, "dx_gemm": 1, "quantize": 2, "dequant": 3, "gemv": 4,
@@ -99,6 +100,9 @@ def lib():
                                                SZ, P]
         L.qlora_dropout_mask.argtypes = [I64, I64, P, P, P]
         L.qlora_adamw_step.argtypes = [P, I64, P, I32, P]
+        L.qlora_merge_workspace_bytes.restype = SZ
+        L.qlora_merge_workspace_bytes.argtypes = [I64, I64]
+        L.qlora_merge_requantize.argtypes = [D, P, P, I32, F, D, P, P, SZ, P]
         L.qlora_host_state_alloc.argtypes = [SZ, P]
         L.qlora_host_state_free.argtypes = [P]
         L.qlora_trace_begin.argtypes = [ctypes.c_uint32, I32]
@@ -316,6 +320,34 @@ def qlora_linear_bwd(q: NF4Tensor, X, A, B, alpha: float, dY, XA_in=None, need_d
                                               _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(),
                                               _stream()), "qlora_linear_bwd_dropout")
     return (dX if need_dx else None), dA, dB
+
+
+def qlora_merge_workspace_bytes(rows: int, cols: int) -> int:
+    return int(lib().qlora_merge_workspace_bytes(rows, cols))
+
+
+def qlora_merge_requantize(q: NF4Tensor, A, B, alpha: float, out: NF4Tensor = None,
+                           merged=None, ws=None, return_merged: bool = False):
+    """Folds the adapters into the weight (W' + (alpha/r) B A) and quantises the
+    result into `out` (a new tensor of q's type by default; q itself for an
+    in-place merge).  Returns out, or (out, merged float32 [N, K]) with
+    return_merged."""
+    _bf16(A), _bf16(B)
+    r = A.shape[0]
+    assert A.shape == (r, q.cols) and B.shape == (q.rows, r)
+    dev = A.device
+    if out is None:
+        out = NF4Tensor(q.rows, q.cols, dev, q.quant_type, q.double_quant)
+    if return_merged and merged is None:
+        merged = torch.empty((q.rows, q.cols), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(qlora_merge_workspace_bytes(q.rows, q.cols), dev)
+    d, do = q.descriptor(), out.descriptor()
+    _check(lib().qlora_merge_requantize(ctypes.byref(d), _ptr(A), _ptr(B), r,
+                                        ctypes.c_float(alpha), ctypes.byref(do), _ptr(merged),
+                                        _ptr(ws), ws.numel(), _stream()),
+           "qlora_merge_requantize")
+    return (out, merged) if return_merged else out
 
 
 def qlora_adamw_step(tensors, step: int, lr: float, beta1: float = 0.9, beta2: float = 0.999,

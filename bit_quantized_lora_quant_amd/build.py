@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC_DIR = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqlora_nf4.so")
-SOURCES = ["tables.cpp", "api.cpp", "quant.hip", "gemm.hip", "lora.hip", "gemv.hip", "adamw.hip"]
+SOURCES = ["tables.cpp", "api.cpp", "quant.hip", "gemm.hip", "lora.hip", "gemv.hip", "adamw.hip",
+           "merge.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

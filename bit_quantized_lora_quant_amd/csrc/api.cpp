@@ -401,6 +401,40 @@ qlora_status qlora_dropout_mask(int64_t M, int64_t K, const qlora_dropout* drop,
   return hip_status(launch_dropout_mask(M, K, dp, out, static_cast<hipStream_t>(stream)));
 }
 
+size_t qlora_merge_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 1 || rows > INT64_MAX / cols / 8) return 0;
+  const int64_t n = rows * cols;
+  return align_up((size_t)n * sizeof(float)) + quant_layout(n).total;
+}
+
+qlora_status qlora_merge_requantize(const qlora_nf4_tensor* W, const qlora_bf16* A,
+                                    const qlora_bf16* B, int32_t r, float alpha,
+                                    const qlora_nf4_tensor* out, float* merged, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  if (!valid_tensor(W) || !valid_tensor(out) || !A || !B) return QLORA_ERR_INVALID_ARG;
+  if (out->rows != W->rows || out->cols != W->cols) return QLORA_ERR_INVALID_ARG;
+  if (r < 1 || r > QLORA_MAX_RANK || !std::isfinite(alpha)) return QLORA_ERR_INVALID_ARG;
+  if (!aligned(A, 2) || !aligned(B, 2) || (merged && !aligned(merged, 16)))
+    return QLORA_ERR_INVALID_ARG;
+  const int64_t N = W->rows, K = W->cols, n = N * K;
+  const QuantWs Q = quant_layout(n);
+  const size_t moff = merged ? 0 : align_up((size_t)n * sizeof(float));
+  if (!ws || ws_bytes < moff + Q.total || !aligned(ws, kAlign)) return QLORA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* mbuf = merged ? merged : at<float>(ws, 0);
+  void* qws = at<uint8_t>(ws, moff);
+  hipError_t e = launch_dequant(W->codes, W->absmax_q, W->absmax_scale, W->absmax_mean,
+                                f32_consts(W), n, 0, mbuf, W->quant_type, s);
+  if (e == hipSuccess) e = launch_merge_lora_add(mbuf, N, K, A, B, r, alpha / (float)r, s);
+  if (e != hipSuccess) return QLORA_ERR_HIP;
+  float* absmax = out->dq_block == 0 ? out->absmax : at<float>(qws, Q.absmax);
+  e = launch_quant_absmax(mbuf, n, out->codes, absmax, out->quant_type, s);
+  if (e == hipSuccess && out->dq_block != 0)
+    e = launch_dq(absmax, nblocks(n), out->absmax_q, out->absmax_scale, out->absmax_mean,
+                  at<double>(qws, Q.pa), at<double>(qws, Q.pb), s);
+  return hip_status(e);
+}
+
 qlora_status qlora_adamw_step(const qlora_adamw_hparams* h, int64_t step,
                               const qlora_adamw_tensor* tensors, int32_t count, void* stream) {
   if (!h || step < 1 || count < 0 || (count > 0 && !tensors)) return QLORA_ERR_INVALID_ARG;

@@ -42,6 +42,7 @@ inline hipError_t launch_kernel(void (*k)(Params...), dim3 grid, dim3 block, hip
 }
 
 constexpr int kBlock = 64;     // weights per first-level absmax
+constexpr int kMaxRank = 128;  // largest adapter rank
 constexpr int kDqBlock = 256;  // first-level constants per second-level scale
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -293,6 +294,10 @@ struct AdamHyper {
   float decay, b1, one_minus_b1, b2, one_minus_b2, inv_sqrt_bc2, eps, step_size;
 };
 int64_t adamw_chunks(int64_t n);
+// merged[n][k] += s * sum_j B[n][j] A[j][k] (float32, j in order, fused
+// multiply-add per term), merged [N, K] float32, A [r, K], B [N, r] bf16
+hipError_t launch_merge_lora_add(float* merged, int64_t N, int64_t K, const uint16_t* A,
+                                 const uint16_t* B, int r, float scale, hipStream_t s);
 hipError_t launch_adamw(const AdamBatch& batch, const AdamHyper& h, hipStream_t s);
 
 }  // namespace qnf4

@@ -231,6 +231,34 @@ qlora_status qlora_dropout_mask(int64_t M, int64_t K, const qlora_dropout* drop,
                                 void* stream);
 
 /* ------------------------------------------------------------------------
+ * Adapter merge for deployment.  The adapter pair is a low-rank update of the
+ * frozen weight ("Fine-Tuning Memory Requirements: Full Training vs LoRA vs
+ * QLoRA", section "LoRA: freeze the base, train small adapters"), so it folds
+ * into it:
+ *     merged = W' + s . B . A,   s = alpha / r,
+ * elementwise merged[n][k] = fl32(W'[n][k] + fl32(s * p)), p the float32 sum
+ * of B[n][j] * A[j][k] over j = 0 .. r-1 in order, one fused multiply-add per
+ * term; W' is the dequantised weight (as qlora_dequantize_nf4 gives it).  The
+ * merged float32 weight is then quantised into `out` exactly as
+ * qlora_quantize_nf4 would quantise it (its table, its double-quantisation
+ * switch).  `out` may be W itself: W is read completely before any of out is
+ * written (stream order). */
+
+/* Bytes of workspace for qlora_merge_requantize with merged == NULL (room for
+ * the float32 merged weight plus the quantiser's scratch); with a caller
+ * buffer for merged, qlora_quantize_workspace_bytes(rows, cols) suffices. */
+size_t qlora_merge_workspace_bytes(int64_t rows, int64_t cols);
+
+/* W, out: valid 4-bit tensors of the same rows x cols.  A [r, K], B [N, r]
+ * bf16 (2-byte aligned), 1 <= r <= 128.  merged (nullable, 16-byte aligned):
+ * receives the float32 merged weight [N, K]; when NULL it lives in the
+ * workspace.  Errors as qlora_quantize_nf4. */
+qlora_status qlora_merge_requantize(const qlora_nf4_tensor* W, const qlora_bf16* A,
+                                    const qlora_bf16* B, int32_t r, float alpha,
+                                    const qlora_nf4_tensor* out, float* merged, void* ws,
+                                    size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Adapter optimiser.  AdamW keeps a running mean m and a running mean v of
  * the squared gradient for every trainable parameter ("QLoRA: Fine-Tuning a
  * 70B on One GPU", section "Paged Optimizers"); the adapters train as float32

@@ -10,7 +10,8 @@ Four parts:
   * ``linear.py``: the forward and backward of
         Y = X . W'^T + (alpha / r) . (X . A^T) . B^T
     written as their float64 definitions with numpy matmul as the only step,
-    optionally with dropout on the LoRA input.
+    optionally with dropout on the LoRA input, and the merged weight
+    W' + (alpha / r) . B . A.
   * ``dropout.py``: the keep mask of that dropout (Philox4x32-10).
   * ``adamw.py``: the AdamW step on the adapters.
 
@@ -24,7 +25,7 @@ import os
 import numpy as np
 
 from . import build as _build
-from .linear import linear_fwd, linear_bwd, lora_scale  # noqa: F401
+from .linear import linear_fwd, linear_bwd, lora_scale, merge_adapter  # noqa: F401
 from . import dropout  # noqa: F401
 from . import adamw  # noqa: F401
 

@@ -78,3 +78,12 @@ def linear_bwd(wd, x, a, b, alpha, dy, drop=None):
     da = s * (g.T @ xd)
     db = s * (dy.T @ (xd @ a.T))
     return dx, da, db
+
+
+def merge_adapter(wd, a, b, alpha):
+    """The merged weight of an adapted layer in float64: W' + s . B . A, whose
+    plain product X . W_merged^T is the adapted forward ("Fine-Tuning Memory
+    Requirements: Full Training vs LoRA vs QLoRA", section "LoRA: freeze the
+    base, train small adapters": the adapters are a low-rank update of W)."""
+    wd, a, b = _f64(wd), _f64(a), _f64(b)
+    return wd + lora_scale(alpha, a.shape[0]) * (b @ a)

@@ -108,3 +108,23 @@ def test_frozen_weight_has_no_gradient_output():
     out = oracle.linear_bwd(_rand(rng, 4, 64), _rand(rng, 2, 64), _rand(rng, 1, 64),
                             _rand(rng, 4, 1), 1.0, _rand(rng, 2, 4))
     assert len(out) == 3
+
+
+def test_merged_weight_reproduces_the_adapted_layer():
+    """The merged weight's plain product equals the adapted forward, and its
+    input gradient the adapted dX (float64 rounding only)."""
+    rng = np.random.default_rng(77)
+    N, K, M, r = 24, 128, 9, 5
+    wd = rng.standard_normal((N, K)) * 0.05
+    a = rng.standard_normal((r, K)) * 0.1
+    b = rng.standard_normal((N, r)) * 0.1
+    x = rng.standard_normal((M, K))
+    dy = rng.standard_normal((M, N))
+    wm = oracle.merge_adapter(wd, a, b, 10.0)
+    y, _ = oracle.linear_fwd(wd, x, a, b, 10.0)
+    assert np.allclose(x @ wm.T, y, rtol=1e-12, atol=1e-12)
+    dx, _, _ = oracle.linear_bwd(wd, x, a, b, 10.0, dy)
+    assert np.allclose(dy @ wm, dx, rtol=1e-12, atol=1e-12)
+    # rank one: the update is the outer product of B's and A's single vectors
+    w1 = oracle.merge_adapter(wd, a[:1], b[:, :1], 3.0)
+    assert np.allclose(w1 - wd, 3.0 * np.outer(b[:, 0], a[0]), rtol=1e-14, atol=1e-15)
