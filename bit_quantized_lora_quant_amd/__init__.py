@@ -29,6 +29,7 @@ EXPORTS = [
     "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout", "qlora_dropout_mask",
     "qlora_adamw_step", "qlora_host_state_alloc", "qlora_host_state_free",
     "qlora_merge_workspace_bytes", "qlora_merge_requantize",
+    "qlora_grouped_workspace_bytes", "qlora_grouped_fwd", "qlora_grouped_bwd",
     "qlora_trace_begin", "qlora_trace_pause", "qlora_trace_end",
 ]
 KERNELS = {"fwd_gemm": 0, "dx_gemm": 1, "quantize": 2, "dequant": 3, "gemv": 4,
@@ -100,6 +101,11 @@ def lib():
                                                SZ, P]
         L.qlora_dropout_mask.argtypes = [I64, I64, P, P, P]
         L.qlora_adamw_step.argtypes = [P, I64, P, I32, P]
+        L.qlora_grouped_workspace_bytes.restype = SZ
+        L.qlora_grouped_workspace_bytes.argtypes = [I64, I64, I64, I32, I32]
+        L.qlora_grouped_fwd.argtypes = [D, P, I64, P, P, I32, I32, P, F, P, P, P, SZ, P]
+        L.qlora_grouped_bwd.argtypes = [D, P, I64, P, P, I32, I32, P, F, P, P, P, P, P, P, SZ,
+                                        P]
         L.qlora_merge_workspace_bytes.restype = SZ
         L.qlora_merge_workspace_bytes.argtypes = [I64, I64]
         L.qlora_merge_requantize.argtypes = [D, P, P, I32, F, D, P, P, SZ, P]
@@ -319,6 +325,62 @@ def qlora_linear_bwd(q: NF4Tensor, X, A, B, alpha: float, dY, XA_in=None, need_d
                                               _ptr(XA_in), _ptr(dX) if need_dx else None,
                                               _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(),
                                               _stream()), "qlora_linear_bwd_dropout")
+    return (dX if need_dx else None), dA, dB
+
+
+def qlora_grouped_workspace_bytes(M: int, N: int, K: int, r: int, groups: int) -> int:
+    return int(lib().qlora_grouped_workspace_bytes(M, N, K, r, groups))
+
+
+def _rows_arg(group_rows):
+    arr = (ctypes.c_int64 * len(group_rows))(*[int(n) for n in group_rows])
+    return arr
+
+
+def qlora_grouped_fwd(q: NF4Tensor, X, A, B, r: int, group_rows, alpha: float, Y=None,
+                      XA_out=None, ws=None, return_xa: bool = False):
+    """Fused projections of one input: q holds the concatenated rows, A [G r, K]
+    the stacked A_g, B [N, G r] the block-diagonal B_g.  Returns Y [M, N] (or
+    (Y, XA [M, G r]))."""
+    M, K = X.shape
+    G = len(group_rows)
+    _bf16(X), _bf16(A), _bf16(B)
+    assert A.shape == (G * r, K) and B.shape == (q.rows, G * r) and K == q.cols
+    if Y is None:
+        Y = torch.empty((M, q.rows), dtype=torch.bfloat16, device=X.device)
+    if return_xa and XA_out is None:
+        XA_out = torch.empty((M, G * r), dtype=torch.bfloat16, device=X.device)
+    if ws is None:
+        ws = workspace(qlora_grouped_workspace_bytes(M, q.rows, K, r, G), X.device)
+    d = q.descriptor()
+    rows = _rows_arg(group_rows)
+    _check(lib().qlora_grouped_fwd(ctypes.byref(d), _ptr(X), M, _ptr(A), _ptr(B), r, G, rows,
+                                   ctypes.c_float(alpha), _ptr(Y), _ptr(XA_out), _ptr(ws),
+                                   ws.numel(), _stream()), "qlora_grouped_fwd")
+    return (Y, XA_out) if return_xa else Y
+
+
+def qlora_grouped_bwd(q: NF4Tensor, X, A, B, r: int, group_rows, alpha: float, dY, XA_in=None,
+                      need_dx: bool = True, dX=None, dA=None, dB=None, ws=None):
+    """Returns (dX or None, dA float32 [G r, K], dB float32 [N, G r] block-diagonal)."""
+    M, K = X.shape
+    G = len(group_rows)
+    N = q.rows
+    _bf16(X), _bf16(A), _bf16(B), _bf16(dY)
+    if need_dx and dX is None:
+        dX = torch.empty((M, K), dtype=torch.bfloat16, device=X.device)
+    if dA is None:
+        dA = torch.empty((G * r, K), dtype=torch.float32, device=X.device)
+    if dB is None:
+        dB = torch.empty((N, G * r), dtype=torch.float32, device=X.device)
+    if ws is None:
+        ws = workspace(qlora_grouped_workspace_bytes(M, N, K, r, G), X.device)
+    d = q.descriptor()
+    rows = _rows_arg(group_rows)
+    _check(lib().qlora_grouped_bwd(ctypes.byref(d), _ptr(X), M, _ptr(A), _ptr(B), r, G, rows,
+                                   ctypes.c_float(alpha), _ptr(dY), _ptr(XA_in),
+                                   _ptr(dX) if need_dx else None, _ptr(dA), _ptr(dB), _ptr(ws),
+                                   ws.numel(), _stream()), "qlora_grouped_bwd")
     return (dX if need_dx else None), dA, dB
 
 

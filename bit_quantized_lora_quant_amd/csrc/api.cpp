@@ -326,12 +326,13 @@ qlora_status qlora_linear_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
                                   ws_bytes, stream);
 }
 
-qlora_status qlora_linear_bwd_dropout(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
-                                      const qlora_bf16* A, const qlora_bf16* B, int32_t r,
-                                      float alpha, const qlora_dropout* drop,
-                                      const qlora_bf16* dY, const qlora_bf16* XA_in,
-                                      qlora_bf16* dX, float* dA, float* dB, void* ws,
-                                      size_t ws_bytes, void* stream) {
+// The backward; `grp` (nullable) makes dB block-diagonal (grouped linear).
+static qlora_status linear_bwd_impl(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
+                                    const qlora_bf16* A, const qlora_bf16* B, int32_t r,
+                                    float alpha, const qlora_dropout* drop,
+                                    const qlora_bf16* dY, const qlora_bf16* XA_in,
+                                    qlora_bf16* dX, float* dA, float* dB, void* ws,
+                                    size_t ws_bytes, void* stream, const GradJob* grp) {
   qlora_status st = check_linear(W, X, M, A, B, r, alpha);
   if (st != QLORA_OK) return st;
   DropoutParams dp;
@@ -387,9 +388,69 @@ qlora_status qlora_linear_bwd_dropout(const qlora_nf4_tensor* W, const qlora_bf1
       GradJob{X, K, gt, L.mp, L.sa, at<float>(ws, L.part_a), scale, 1, dA},
       GradJob{dY, N, xat, L.mp, L.sb, at<float>(ws, L.part_b), scale, 0, dB}};
   gj[0].drop = dp;   // dA reads D(X)
+  if (grp) {
+    gj[1].groups = grp->groups;
+    gj[1].gr = grp->gr;
+    for (int g = 0; g < kMaxGroups; ++g) gj[1].end[g] = grp->end[g];
+  }
   QL_TRY(launch_lora_grads(gj, 2, M, r, s));
 #undef QL_TRY
   return QLORA_OK;
+}
+
+qlora_status qlora_linear_bwd_dropout(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
+                                      const qlora_bf16* A, const qlora_bf16* B, int32_t r,
+                                      float alpha, const qlora_dropout* drop,
+                                      const qlora_bf16* dY, const qlora_bf16* XA_in,
+                                      qlora_bf16* dX, float* dA, float* dB, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  return linear_bwd_impl(W, X, M, A, B, r, alpha, drop, dY, XA_in, dX, dA, dB, ws, ws_bytes,
+                         stream, nullptr);
+}
+
+// Grouping of a fused weight: G segments of rows ending at the running sums
+// of group_rows, r adapter rows each.  False for a bad grouping.
+static bool grouping(const qlora_nf4_tensor* W, int32_t r, int32_t groups,
+                     const int64_t* group_rows, GradJob* g) {
+  if (!W || groups < 1 || groups > kMaxGroups || !group_rows || r < 1) return false;
+  if ((int64_t)groups * r > QLORA_MAX_RANK) return false;
+  g->groups = groups;
+  g->gr = r;
+  int64_t sum = 0;
+  for (int i = 0; i < groups; ++i) {
+    if (group_rows[i] < 1) return false;
+    sum += group_rows[i];
+    g->end[i] = sum;
+  }
+  return sum == W->rows;
+}
+
+size_t qlora_grouped_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, int32_t groups) {
+  if (groups < 1 || groups > kMaxGroups || (int64_t)groups * r > QLORA_MAX_RANK) return 0;
+  return qlora_linear_workspace_bytes(M, N, K, groups * r);
+}
+
+qlora_status qlora_grouped_fwd(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
+                               const qlora_bf16* A, const qlora_bf16* B, int32_t r,
+                               int32_t groups, const int64_t* group_rows, float alpha,
+                               qlora_bf16* Y, qlora_bf16* XA_out, void* ws, size_t ws_bytes,
+                               void* stream) {
+  GradJob g{};
+  if (!valid_tensor(W) || !grouping(W, r, groups, group_rows, &g)) return QLORA_ERR_INVALID_ARG;
+  // rank G r with alpha G keeps every group's scale at alpha / r
+  return qlora_linear_fwd_dropout(W, X, M, A, B, groups * r, alpha * (float)groups, nullptr, Y,
+                                  XA_out, ws, ws_bytes, stream);
+}
+
+qlora_status qlora_grouped_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
+                               const qlora_bf16* A, const qlora_bf16* B, int32_t r,
+                               int32_t groups, const int64_t* group_rows, float alpha,
+                               const qlora_bf16* dY, const qlora_bf16* XA_in, qlora_bf16* dX,
+                               float* dA, float* dB, void* ws, size_t ws_bytes, void* stream) {
+  GradJob g{};
+  if (!valid_tensor(W) || !grouping(W, r, groups, group_rows, &g)) return QLORA_ERR_INVALID_ARG;
+  return linear_bwd_impl(W, X, M, A, B, groups * r, alpha * (float)groups, nullptr, dY, XA_in,
+                         dX, dA, dB, ws, ws_bytes, stream, &g);
 }
 
 qlora_status qlora_dropout_mask(int64_t M, int64_t K, const qlora_dropout* drop, uint8_t* out,

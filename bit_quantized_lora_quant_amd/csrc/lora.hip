@@ -320,6 +320,11 @@ __device__ __forceinline__ void grad_reduce_elem(const GradJob& J, int r, int64_
   if (idx >= J.P * r) return;
   int64_t p, j;
   if (J.transposed) { j = idx / J.P; p = idx - j * J.P; } else { p = idx / r; j = idx - p * r; }
+  if (J.groups > 0) {   // off the diagonal blocks of a grouped linear: zero
+    int g = 0;
+    while (g + 1 < J.groups && p >= J.end[g]) ++g;
+    if (j / J.gr != g) { J.out[idx] = 0.f; return; }
+  }
   float s = J.partial[p * r + j];
   for (int k = 1; k < J.splits; ++k) s += J.partial[(int64_t)k * J.P * r + p * r + j];
   J.out[idx] = J.scale * s;

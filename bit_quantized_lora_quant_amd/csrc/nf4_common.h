@@ -43,6 +43,7 @@ inline hipError_t launch_kernel(void (*k)(Params...), dim3 grid, dim3 block, hip
 
 constexpr int kBlock = 64;     // weights per first-level absmax
 constexpr int kMaxRank = 128;  // largest adapter rank
+constexpr int kMaxGroups = 8;  // projections fused into one grouped linear
 constexpr int kDqBlock = 256;  // first-level constants per second-level scale
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -223,6 +224,12 @@ struct GradJob {
   int transposed;
   float* out;
   DropoutParams drop{};   // dropout of T (T = X only), as in SkinnyJob
+  // Block-diagonal output ([P][r] layout only): rows p of group g are
+  // [end[g-1], end[g]) and own columns [g gr, (g+1) gr); the reduction writes
+  // 0 everywhere else.  groups == 0: the whole output.
+  int groups = 0;
+  int gr = 0;
+  int64_t end[kMaxGroups] = {};
 };
 int lora_grad_splits(int64_t M, int64_t P);
 // Both jobs' partial launch, then both reductions.

@@ -231,6 +231,39 @@ qlora_status qlora_dropout_mask(int64_t M, int64_t K, const qlora_dropout* drop,
                                 void* stream);
 
 /* ------------------------------------------------------------------------
+ * Grouped linear: the projections of a layer that read the same input (the
+ * query, key and value projections; the gate and up projections) run as one
+ * fused weight, so one GEMM makes one pass over X for all of them.  LoRA puts
+ * an adapter pair at each of these projections ("Fine-Tuning Memory
+ * Requirements: Full Training vs LoRA vs QLoRA", section "LoRA: freeze the
+ * base, train small adapters": rank r on all seven linear projections), so
+ * group g (rows [e_(g-1), e_g) of W, e_g the running sum of group_rows) keeps
+ * its own A_g [r, K] and B_g [N_g, r]:
+ *     A [G r, K]   the A_g stacked;
+ *     B [N, G r]   block-diagonal: rows of group g hold B_g in columns
+ *                  [g r, (g+1) r) and zeros elsewhere (the caller keeps the
+ *                  zeros; the backward never moves them);
+ * and the call computes, for every group, Y_g = X . W_g'^T + (alpha/r)
+ * (X . A_g^T) . B_g^T (Y [M, N] holds the Y_g side by side; XA [M, G r] the
+ * X . A_g^T side by side).  The backward gives dX = sum_g of the groups'
+ * input gradients, dA [G r, K] stacked, and dB [N, G r] with the diagonal
+ * blocks' gradients and exact zeros elsewhere.  1 <= G <= 8, G r <= 128.
+ * Without dropout (each projection's dropout draws its own mask).  W is one
+ * 4-bit tensor of the concatenated rows (its double quantisation spans the
+ * groups).  Other requirements and errors as qlora_linear_fwd / _bwd. */
+size_t qlora_grouped_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, int32_t groups);
+qlora_status qlora_grouped_fwd(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
+                               const qlora_bf16* A, const qlora_bf16* B, int32_t r,
+                               int32_t groups, const int64_t* group_rows, float alpha,
+                               qlora_bf16* Y, qlora_bf16* XA_out, void* ws, size_t ws_bytes,
+                               void* stream);
+qlora_status qlora_grouped_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
+                               const qlora_bf16* A, const qlora_bf16* B, int32_t r,
+                               int32_t groups, const int64_t* group_rows, float alpha,
+                               const qlora_bf16* dY, const qlora_bf16* XA_in, qlora_bf16* dX,
+                               float* dA, float* dB, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Adapter merge for deployment.  The adapter pair is a low-rank update of the
  * frozen weight ("Fine-Tuning Memory Requirements: Full Training vs LoRA vs
  * QLoRA", section "LoRA: freeze the base, train small adapters"), so it folds

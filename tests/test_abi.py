@@ -202,3 +202,23 @@ def test_adamw_argument_errors(q):
     assert lib.qlora_host_state_alloc(0, ctypes.byref(ptr)) == q.QLORA_ERR_INVALID_ARG
     assert lib.qlora_host_state_alloc(64, None) == q.QLORA_ERR_INVALID_ARG
     assert lib.qlora_host_state_free(None) == q.QLORA_OK
+
+
+def test_grouped_argument_errors(q):
+    """Groupings that do not cover W's rows, more than 8 groups, an empty
+    group or a total rank above 128 are rejected on the host."""
+    lib = q.lib()
+    P = ctypes.c_void_p
+    d = _desc(q, rows=128, cols=128)
+    X = P(0x400000)
+    for rows, r in (((64, 63), 8), ((16,) * 9, 8), ((64, 0, 64), 8), ((64, 64), 65)):
+        arr = (ctypes.c_int64 * len(rows))(*rows)
+        assert lib.qlora_grouped_fwd(ctypes.byref(d), X, 32, X, X, r, len(rows), arr,
+                                     ctypes.c_float(16.0), X, None, X, 1 << 30, None) == \
+            q.QLORA_ERR_INVALID_ARG
+        assert lib.qlora_grouped_bwd(ctypes.byref(d), X, 32, X, X, r, len(rows), arr,
+                                     ctypes.c_float(16.0), X, None, X, X, X, X, 1 << 30,
+                                     None) == q.QLORA_ERR_INVALID_ARG
+    assert q.qlora_grouped_workspace_bytes(32, 128, 128, 65, 2) == 0
+    assert q.qlora_grouped_workspace_bytes(32, 128, 128, 16, 2) == \
+        q.qlora_linear_workspace_bytes(32, 128, 128, 32)
