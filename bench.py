@@ -4,12 +4,15 @@
 Headline step: forward then backward (reverse order) through the seven
 Llama-3.1-8B layer projections (q, k, v, o 4096-wide, k/v 1024, gate/up/down
 14336) at 2048 tokens, LoRA r = 16, alpha = 32, NF4 weights with double
-quantisation.  ``value`` is tokens per second of that step with every input
-resident in HBM.  The JSON line also carries the dominant kernel's roofline
-(HIP-event durations measured on the library's stream during the timed
-region), the CPU oracle timed on a bounded sample, and the other legs of the
-path: quantise + dequantise of the full 8.03B-parameter weight set, the NF4 /
-INT4 and constant variants, the layer step with LoRA dropout, the AdamW step
+quantisation, each projection with its own adapter pair.  The layer driver
+runs the projections that share an input as one grouped weight (q/k/v, and
+gate/up), so the step is 4 fused-GEMM pairs.  ``value`` is tokens per second
+of that step with every input resident in HBM.  The JSON line also carries the
+dominant kernel's roofline (HIP-event durations measured on the library's
+stream during the timed region), the CPU oracle timed on a bounded sample, and
+the other legs of the path: quantise + dequantise of the full 8.03B-parameter
+weight set, the NF4 / INT4 and constant variants, the layer step with LoRA
+dropout, the same step as 7 separate linears (layer driver leg), the AdamW step
 over every 8B adapter, the 70B-shaped decode GEMV at 1 / 4 / 16 tokens, and the
 80-layer LLaMA-65B stack.
 
@@ -40,8 +43,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--legs", default="all",
-                    help="all, none, or a comma list of quant, variants, dropout, adamw, decode, "
-                         "stack65b")
+                    help="all, none, or a comma list of quant, variants, dropout, driver, adamw, "
+                         "decode, stack65b")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run 3 plain device-to-device copies of MIB MiB (the known-size "
@@ -119,6 +122,68 @@ def linear_flops(M, N, K, r):
     return 4 * M * N * K + 6 * M * r * (K + N)
 
 
+# The layer driver: the projections that read one input run as one grouped
+# weight (q/k/v: N = 6144 with three adapter pairs; gate/up: N = 28672 with
+# two), o and down alone -- 4 fused-GEMM pairs per step instead of 7.
+GROUPS = [[0, 1, 2], [3], [4, 5], [6]]
+
+
+def build_units(q, torch, layers, host_w, M, r):
+    dev = "cuda:0"
+    units = []
+    for idx in GROUPS:
+        if len(idx) == 1:
+            units.append(dict(single=True, **layers[idx[0]]))
+            continue
+        Ls = [layers[i] for i in idx]
+        rows = [L["N"] for L in Ls]
+        N, K, G = sum(rows), Ls[0]["K"], len(Ls)
+        qq, _ = q.qlora_quantize_nf4(torch.cat([torch.from_numpy(host_w[i]) for i in idx], 0)
+                                     .to(dev))
+        A = torch.cat([L["A"] for L in Ls], 0).contiguous()
+        B = torch.zeros((N, G * r), dtype=torch.bfloat16, device=dev)
+        e = 0
+        for g, L in enumerate(Ls):
+            B[e:e + L["N"], g * r:(g + 1) * r] = L["B"]
+            e += L["N"]
+        dY = torch.cat([L["dY"] for L in Ls], 1).contiguous()
+        units.append(dict(single=False, rows=rows, N=N, K=K, G=G, q=qq, X=Ls[0]["X"], A=A, B=B,
+                          dY=dY, Y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                          XA=torch.empty((M, G * r), dtype=torch.bfloat16, device=dev),
+                          dX=torch.empty((M, K), dtype=torch.bfloat16, device=dev),
+                          dA=torch.empty((G * r, K), dtype=torch.float32, device=dev),
+                          dB=torch.empty((N, G * r), dtype=torch.float32, device=dev),
+                          ws=q.workspace(q.qlora_grouped_workspace_bytes(M, N, K, r, G), dev)))
+    return units
+
+
+def unit_step(q, units, r, alpha):
+    """Forward of every unit in layer order, then the backward in reverse."""
+    for u in units:
+        if u["single"]:
+            q.qlora_linear_fwd(u["q"], u["X"], u["A"], u["B"], alpha, Y=u["Y"], XA_out=u["XA"],
+                               ws=u["ws"], return_xa=True)
+        else:
+            q.qlora_grouped_fwd(u["q"], u["X"], u["A"], u["B"], r, u["rows"], alpha, Y=u["Y"],
+                                XA_out=u["XA"], ws=u["ws"], return_xa=True)
+    for u in reversed(units):
+        if u["single"]:
+            q.qlora_linear_bwd(u["q"], u["X"], u["A"], u["B"], alpha, u["dY"], XA_in=u["XA"],
+                               dX=u["dX"], dA=u["dA"], dB=u["dB"], ws=u["ws"])
+        else:
+            q.qlora_grouped_bwd(u["q"], u["X"], u["A"], u["B"], r, u["rows"], alpha, u["dY"],
+                                XA_in=u["XA"], dX=u["dX"], dA=u["dA"], dB=u["dB"], ws=u["ws"])
+
+
+def separate_step(q, layers, alpha):
+    for L in layers:
+        q.qlora_linear_fwd(L["q"], L["X"], L["A"], L["B"], alpha, Y=L["Y"], XA_out=L["XA"],
+                           ws=L["ws"], return_xa=True)
+    for L in reversed(layers):
+        q.qlora_linear_bwd(L["q"], L["X"], L["A"], L["B"], alpha, L["dY"], XA_in=L["XA"],
+                           dX=L["dX"], dA=L["dA"], dB=L["dB"], ws=L["ws"])
+
+
 def headline(args, q, torch, workloads):
     wl = workloads.LLAMA8B_LAYER
     dev = "cuda:0"
@@ -137,16 +202,12 @@ def headline(args, q, torch, workloads):
         L["dB"] = torch.empty((N, r), dtype=torch.float32, device=dev)
         L["ws"] = q.workspace(q.qlora_linear_workspace_bytes(M, N, K, r), dev)
         layers.append(L)
+    units = build_units(q, torch, layers, host_w, M, r)
     torch.cuda.synchronize()
-    log("headline inputs ready (%d linears)" % len(layers))
+    log("headline inputs ready (%d linears in %d units)" % (len(layers), len(units)))
 
     def step():
-        for L in layers:
-            q.qlora_linear_fwd(L["q"], L["X"], L["A"], L["B"], alpha, Y=L["Y"], XA_out=L["XA"],
-                               ws=L["ws"], return_xa=True)
-        for L in reversed(layers):
-            q.qlora_linear_bwd(L["q"], L["X"], L["A"], L["B"], alpha, L["dY"], XA_in=L["XA"],
-                               dX=L["dX"], dA=L["dA"], dB=L["dB"], ws=L["ws"])
+        unit_step(q, units, r, alpha)
 
     for _ in range(args.warmup):
         step()
@@ -157,7 +218,7 @@ def headline(args, q, torch, workloads):
     # at least one): the step time carries little of that cost.
     sampled = [i for i in range(args.steps) if i % 10 == 5] or [args.steps - 1]
     q.qlora_trace_begin(["fwd_gemm", "dx_gemm", "split_reduce"],
-                        capacity=4 * len(layers) * len(sampled) + 8)
+                        capacity=4 * len(units) * len(sampled) + 8)
     q.qlora_trace_pause(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -173,21 +234,22 @@ def headline(args, q, torch, workloads):
     tr = q.qlora_trace_end()
     sec = (t1 - t0) / args.steps
     flops = sum(linear_flops(M, L["N"], L["K"], r) for L in layers)
-    # per-kernel algorithmic flops: fwd GEMM 2MN(K + r), dX GEMM 2MK(N + r)
-    kflops = {"fwd_gemm": sum(2 * M * L["N"] * (L["K"] + r) for L in layers),
-              "dx_gemm": sum(2 * M * L["K"] * (L["N"] + r) for L in layers)}
+    # per-kernel algorithmic flops of a unit: fwd GEMM 2MN(K + r) (each row of
+    # W meets one adapter of rank r), dX GEMM 2MK(N + G r) (G adapters)
+    kflops = {"fwd_gemm": sum(2 * M * u["N"] * (u["K"] + r) for u in units),
+              "dx_gemm": sum(2 * M * u["K"] * (u["N"] + u.get("G", 1) * r) for u in units)}
     kern = {}
     for name, (n, ms) in tr.items():
         if name not in kflops:
             continue
         avg_ms = ms / n
-        per_launch = kflops[name] / len(layers)
+        per_launch = kflops[name] / len(units)
         kern[name] = {"launches": n, "avg_us": avg_ms * 1e3,
-                      "tflops": kflops[name] * (n / len(layers)) / (ms * 1e-3) / 1e12,
+                      "tflops": kflops[name] * (n / len(units)) / (ms * 1e-3) / 1e12,
                       "flops_per_launch": per_launch}
     dom = max(kern, key=lambda k: kern[k]["avg_us"] * kern[k]["launches"])
     d = kern[dom]
-    # the dX GEMM with N % 64 == 0 (all seven Llama linears) runs k_qlora_dx_nn_dma
+    # the dX GEMM with N % 64 == 0 (every unit of the Llama layer) runs k_qlora_dx_nn_dma
     roof = {"kernel": {"fwd_gemm": "k_qlora_fwd_nt", "dx_gemm": "k_qlora_dx_nn_dma"}[dom],
             "bound": "mfma", "achieved": round(d["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(d["tflops"] / PEAK_BF16_TFLOPS, 4),
@@ -204,7 +266,7 @@ def headline(args, q, torch, workloads):
     roof["timed_steps"] = sampled
     res = dict(sec=sec, tokens=M, flops=flops, roofline=roof, kernels=other)
     log("headline: %.3f ms/step, %.1f TFLOP/s" % (sec * 1e3, flops / sec / 1e12))
-    return res, layers, host_w
+    return res, layers, host_w, units
 
 
 # ---------------------------------------------------------- cpu baseline
@@ -333,6 +395,23 @@ def leg_dropout(q, torch, layers, M, r, alpha, p=0.05, steps=10):
         100.0 * (res["step_ms_dropout"] / res["step_ms_no_dropout"] - 1.0), 2)
     log("dropout leg: %.3f ms/step with p=%.2f, %.3f without" %
         (res["step_ms_dropout"], p, res["step_ms_no_dropout"]))
+    return res
+
+
+def leg_layer_driver(q, torch, layers, units, M, r, alpha, steps=10):
+    """The layer step as 7 separate linears against the grouped units of the
+    headline (q/k/v and gate/up each one grouped weight), both eager, on the
+    same inputs."""
+    res = {"units": "q/k/v grouped, o, gate/up grouped, down"}
+    for label, fn in (("separate_7", lambda: separate_step(q, layers, alpha)),
+                      ("grouped_4", lambda: unit_step(q, units, r, alpha))):
+        fn()
+        sec = timed(torch, fn, steps)
+        res["step_ms_" + label] = round(sec * 1e3, 4)
+        res["tokens_per_s_" + label] = round(M / sec, 1)
+    res["speedup"] = round(res["step_ms_separate_7"] / res["step_ms_grouped_4"], 4)
+    log("layer driver leg: %.3f ms grouped, %.3f ms separate" %
+        (res["step_ms_grouped_4"], res["step_ms_separate_7"]))
     return res
 
 
@@ -608,18 +687,23 @@ def main():
     q.lib()
     if args.calibrate_copy:
         calibrate_copy(torch, args.calibrate_copy)
-    head, layers, host_w = headline(args, q, torch, workloads)
+    head, layers, host_w, units = headline(args, q, torch, workloads)
     cpu = None
     if args.cpu_baseline == "on":
         cpu = cpu_baseline(workloads, layers, host_w)
         log("cpu baseline: %s tokens/s on %d threads" % (cpu["value"], cpu["cores"]))
     legs = {}
-    want = {"quant", "variants", "dropout", "adamw", "decode", "stack65b"} if args.legs == "all" else (
+    want = {"quant", "variants", "dropout", "driver", "adamw", "decode", "stack65b"} \
+        if args.legs == "all" else (
         set() if args.legs == "none" else set(args.legs.split(",")))
     if "dropout" in want:
         wl = workloads.LLAMA8B_LAYER
         legs["llama8b_layer_lora_dropout"] = leg_dropout(q, torch, layers, wl.m, wl.r, wl.alpha)
-    del layers, host_w
+    if "driver" in want:
+        wl = workloads.LLAMA8B_LAYER
+        legs["llama8b_layer_driver_grouped"] = leg_layer_driver(q, torch, layers, units, wl.m,
+                                                                wl.r, wl.alpha)
+    del layers, host_w, units
     torch.cuda.empty_cache()
     if "quant" in want:
         legs["llama8b_weight_set_quant_dequant"] = leg_quant_dequant(q, torch, workloads)
@@ -648,7 +732,9 @@ def main():
         "data": "synthetic (seeded; random NF4-quantised weights, no checkpoint)",
         "config": {"workload": "Llama-3.1-8B layer linears q/k/v/o/gate/up/down, 2048 tokens, "
                                "LoRA r=16 alpha=32, NF4 + double quant, fwd+bwd",
-                   "tokens": 2048, "rank": 16, "linears": 7},
+                   "tokens": 2048, "rank": 16, "linears": 7,
+                   "driver": "q/k/v and gate/up each one grouped weight over their shared "
+                             "input, o and down alone (4 fused-GEMM pairs)"},
         "tflops": round(tflops, 2),
         "frac_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": head["roofline"],

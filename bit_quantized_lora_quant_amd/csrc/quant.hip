@@ -214,7 +214,10 @@ __global__ __launch_bounds__(kThreads) void k_dq_blocks(const float* __restrict_
 // all four code loads of a chunk in flight together.
 constexpr int kDqChunk = 2048;
 
-template <bool BF16>
+// F32: float32 block constants (no double quantisation); a template switch,
+// since a per-load choice between the two constant sources makes the
+// compiler wait for each chunk's loads before the next chunk's.
+template <bool BF16, bool F32>
 __global__ __launch_bounds__(kThreads) void k_dequant_nf4(const uint8_t* __restrict__ codes,
                                                           const int8_t* __restrict__ q,
                                                           const float* __restrict__ scale,
@@ -229,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_nf4(const uint8_t* __restr
   const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
   const int64_t nchunks = ceil_div(n, kDqChunk);
-  const float mu = f32 ? 0.0f : *mean;
+  const float mu = F32 ? 0.0f : *mean;
   for (int64_t c = wave; c < nchunks; c += nwaves) {
     const int64_t base = c * kDqChunk;
     const bool full = base + kDqChunk <= n;
@@ -246,7 +249,8 @@ __global__ __launch_bounds__(kThreads) void k_dequant_nf4(const uint8_t* __restr
           if (e0 + 2 * k < n) cw[i] |= (uint32_t)codes[(e0 >> 1) + k] << (8 * k);
       }
       const int64_t b = (e0 < n ? e0 : n - 1) / kBlock;
-      a[i] = f32 ? f32[b] : absmax_recon(q, scale, mu, b);
+      if constexpr (F32) a[i] = f32[b];
+      else a[i] = absmax_recon(q, scale, mu, b);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -334,11 +338,10 @@ hipError_t launch_dequant(const uint8_t* codes, const int8_t* q, const float* sc
                           const float* mean, const float* f32, int64_t n, int out_bf16,
                           void* out, int kind, hipStream_t s) {
   const dim3 grid((unsigned)stream_grid(ceil_div(n, kDqChunk)));
-  if (out_bf16)
-    return launch_kernel(k_dequant_nf4<true>, grid, dim3(kThreads), s, codes, q, scale, mean, f32,
-                         n, host_tables(kind), out);
-  return launch_kernel(k_dequant_nf4<false>, grid, dim3(kThreads), s, codes, q, scale, mean, f32,
-                       n, host_tables(kind), out);
+  const auto k = out_bf16 ? (f32 ? k_dequant_nf4<true, true> : k_dequant_nf4<true, false>)
+                          : (f32 ? k_dequant_nf4<false, true> : k_dequant_nf4<false, false>);
+  return launch_kernel(k, grid, dim3(kThreads), s, codes, q, scale, mean, f32, n,
+                       host_tables(kind), out);
 }
 
 hipError_t launch_absmax_recon(const int8_t* q, const float* scale, const float* mean,
