@@ -370,22 +370,29 @@ def leg_dropout(q, torch, layers, M, r, alpha, p=0.05, steps=10):
     step without: eager step time and the dX GEMM's average launch (which
     starts its accumulators from the masked LoRA term), from HIP events."""
 
-    def step(drop):
+    bits = [q.keep_bits_buffer(M, L["K"], "cuda:0") for L in layers]
+
+    def step(drop, keep):
         for i, L in enumerate(layers):
             d = None if drop is None else (drop, 1000 + i)
             q.qlora_linear_fwd(L["q"], L["X"], L["A"], L["B"], alpha, Y=L["Y"], XA_out=L["XA"],
-                               ws=L["ws"], return_xa=True, dropout=d)
+                               ws=L["ws"], return_xa=True, dropout=d,
+                               keep_bits=bits[i] if keep else None)
         for i, L in reversed(list(enumerate(layers))):
             d = None if drop is None else (drop, 1000 + i)
             q.qlora_linear_bwd(L["q"], L["X"], L["A"], L["B"], alpha, L["dY"], XA_in=L["XA"],
-                               dX=L["dX"], dA=L["dA"], dB=L["dB"], ws=L["ws"], dropout=d)
+                               dX=L["dX"], dA=L["dA"], dB=L["dB"], ws=L["ws"], dropout=d,
+                               keep_bits=bits[i] if keep else None)
 
-    res = {"p": p, "seeds": "1000 + linear index"}
-    for label, drop in (("no_dropout", None), ("dropout", p)):
-        step(drop)
-        sec = timed(torch, lambda: step(drop), steps)
+    res = {"p": p, "seeds": "1000 + linear index",
+           "dropout": "the forward stores the keep bits, the backward reads them",
+           "dropout_regenerate": "the backward runs the generator again"}
+    for label, drop, keep in (("no_dropout", None, False), ("dropout", p, True),
+                              ("dropout_regenerate", p, False)):
+        step(drop, keep)
+        sec = timed(torch, lambda: step(drop, keep), steps)
         q.qlora_trace_begin(["dx_gemm"], capacity=len(layers) + 1)
-        step(drop)
+        step(drop, keep)
         tr = q.qlora_trace_end()
         n, ms = tr.get("dx_gemm", (0, 0.0))
         res["step_ms_" + label] = round(sec * 1e3, 4)

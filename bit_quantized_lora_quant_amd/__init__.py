@@ -96,8 +96,8 @@ def lib():
         L.qlora_linear_workspace_bytes.restype = SZ
         L.qlora_linear_fwd.argtypes = [D, P, I64, P, P, I32, F, P, P, P, SZ, P]
         L.qlora_linear_bwd.argtypes = [D, P, I64, P, P, I32, F, P, P, P, P, P, P, SZ, P]
-        L.qlora_linear_fwd_dropout.argtypes = [D, P, I64, P, P, I32, F, P, P, P, P, SZ, P]
-        L.qlora_linear_bwd_dropout.argtypes = [D, P, I64, P, P, I32, F, P, P, P, P, P, P, P,
+        L.qlora_linear_fwd_dropout.argtypes = [D, P, I64, P, P, I32, F, P, P, P, P, P, SZ, P]
+        L.qlora_linear_bwd_dropout.argtypes = [D, P, I64, P, P, I32, F, P, P, P, P, P, P, P, P,
                                                SZ, P]
         L.qlora_dropout_mask.argtypes = [I64, I64, P, P, P]
         L.qlora_adamw_step.argtypes = [P, I64, P, I32, P]
@@ -266,11 +266,16 @@ def qlora_dropout_mask(M: int, K: int, dropout, device, out=None):
     return out
 
 
+def keep_bits_buffer(M: int, K: int, device):
+    """uint8 [M * K / 8] for the forward's dropout keep bits."""
+    return torch.empty((M * K + 7) // 8, dtype=torch.uint8, device=device)
+
+
 def qlora_linear_fwd(q: NF4Tensor, X, A, B, alpha: float, Y=None, XA_out=None, ws=None,
-                     return_xa: bool = False, dropout=None):
+                     return_xa: bool = False, dropout=None, keep_bits=None):
     """Y = X W'^T + (alpha/r) (D(X) A^T) B^T.  Returns Y, or (Y, XA) with
     return_xa.  dropout = (p, seed) drops adapter-input elements (D(X) = X
-    without it)."""
+    without it); keep_bits (from keep_bits_buffer) receives the mask."""
     M, K = X.shape
     r = A.shape[0]
     _bf16(X), _bf16(A), _bf16(B)
@@ -289,16 +294,17 @@ def qlora_linear_fwd(q: NF4Tensor, X, A, B, alpha: float, Y=None, XA_out=None, w
     else:
         dr = _dropout(dropout)
         _check(lib().qlora_linear_fwd_dropout(ctypes.byref(d), _ptr(X), M, _ptr(A), _ptr(B), r,
-                                              ctypes.c_float(alpha), ctypes.byref(dr), _ptr(Y),
-                                              _ptr(XA_out), _ptr(ws), ws.numel(), _stream()),
+                                              ctypes.c_float(alpha), ctypes.byref(dr),
+                                              _ptr(keep_bits), _ptr(Y), _ptr(XA_out), _ptr(ws),
+                                              ws.numel(), _stream()),
                "qlora_linear_fwd_dropout")
     return (Y, XA_out) if return_xa else Y
 
 
 def qlora_linear_bwd(q: NF4Tensor, X, A, B, alpha: float, dY, XA_in=None, need_dx: bool = True,
-                     dX=None, dA=None, dB=None, ws=None, dropout=None):
+                     dX=None, dA=None, dB=None, ws=None, dropout=None, keep_bits=None):
     """Returns (dX or None, dA float32 [r, K], dB float32 [N, r]).  dropout
-    must be the forward's (p, seed)."""
+    must be the forward's (p, seed); keep_bits (optional) its stored mask."""
     M, K = X.shape
     r = A.shape[0]
     N = q.rows
@@ -321,7 +327,8 @@ def qlora_linear_bwd(q: NF4Tensor, X, A, B, alpha: float, dY, XA_in=None, need_d
     else:
         dr = _dropout(dropout)
         _check(lib().qlora_linear_bwd_dropout(ctypes.byref(d), _ptr(X), M, _ptr(A), _ptr(B), r,
-                                              ctypes.c_float(alpha), ctypes.byref(dr), _ptr(dY),
+                                              ctypes.c_float(alpha), ctypes.byref(dr),
+                                              _ptr(keep_bits), _ptr(dY),
                                               _ptr(XA_in), _ptr(dX) if need_dx else None,
                                               _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(),
                                               _stream()), "qlora_linear_bwd_dropout")
@@ -487,15 +494,17 @@ class QLoRALinearFn(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, X, A, B, q, alpha, dropout=None):
+        bits = keep_bits_buffer(X.shape[0], X.shape[1], X.device) if dropout else None
         Y, XA = qlora_linear_fwd(q, X.contiguous(), A.contiguous(), B.contiguous(), alpha,
-                                 return_xa=True, dropout=dropout)
+                                 return_xa=True, dropout=dropout, keep_bits=bits)
         ctx.save_for_backward(X, A, B, XA)
-        ctx.q, ctx.alpha, ctx.dropout = q, alpha, dropout
+        ctx.q, ctx.alpha, ctx.dropout, ctx.bits = q, alpha, dropout, bits
         return Y
 
     @staticmethod
     def backward(ctx, dY):
         X, A, B, XA = ctx.saved_tensors
         dX, dA, dB = qlora_linear_bwd(ctx.q, X, A, B, ctx.alpha, dY.contiguous(), XA_in=XA,
-                                      need_dx=ctx.needs_input_grad[0], dropout=ctx.dropout)
+                                      need_dx=ctx.needs_input_grad[0], dropout=ctx.dropout,
+                                      keep_bits=ctx.bits)
         return dX, dA.to(A.dtype), dB.to(B.dtype), None, None, None

@@ -265,19 +265,20 @@ qlora_status qlora_linear_fwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
                               const qlora_bf16* A, const qlora_bf16* B, int32_t r, float alpha,
                               qlora_bf16* Y, qlora_bf16* XA_out, void* ws, size_t ws_bytes,
                               void* stream) {
-  return qlora_linear_fwd_dropout(W, X, M, A, B, r, alpha, nullptr, Y, XA_out, ws, ws_bytes,
-                                  stream);
+  return qlora_linear_fwd_dropout(W, X, M, A, B, r, alpha, nullptr, nullptr, Y, XA_out, ws,
+                                  ws_bytes, stream);
 }
 
 qlora_status qlora_linear_fwd_dropout(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
                                       const qlora_bf16* A, const qlora_bf16* B, int32_t r,
-                                      float alpha, const qlora_dropout* drop, qlora_bf16* Y,
-                                      qlora_bf16* XA_out, void* ws, size_t ws_bytes,
-                                      void* stream) {
+                                      float alpha, const qlora_dropout* drop,
+                                      uint8_t* keep_bits_out, qlora_bf16* Y, qlora_bf16* XA_out,
+                                      void* ws, size_t ws_bytes, void* stream) {
   qlora_status st = check_linear(W, X, M, A, B, r, alpha);
   if (st != QLORA_OK) return st;
   DropoutParams dp;
   if (!dropout_params(drop, W->cols, &dp)) return QLORA_ERR_INVALID_ARG;
+  if (dp.thr != 0) dp.bits_out = keep_bits_out;
   if (!Y || !aligned(Y, 16)) return QLORA_ERR_INVALID_ARG;
   const int64_t N = W->rows, K = W->cols;
   const LinearWs L = linear_layout(M, N, K, r);
@@ -322,7 +323,8 @@ qlora_status qlora_linear_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
                               const qlora_bf16* A, const qlora_bf16* B, int32_t r, float alpha,
                               const qlora_bf16* dY, const qlora_bf16* XA_in, qlora_bf16* dX,
                               float* dA, float* dB, void* ws, size_t ws_bytes, void* stream) {
-  return qlora_linear_bwd_dropout(W, X, M, A, B, r, alpha, nullptr, dY, XA_in, dX, dA, dB, ws,
+  return qlora_linear_bwd_dropout(W, X, M, A, B, r, alpha, nullptr, nullptr, dY, XA_in, dX, dA,
+                                  dB, ws,
                                   ws_bytes, stream);
 }
 
@@ -330,13 +332,15 @@ qlora_status qlora_linear_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
 static qlora_status linear_bwd_impl(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
                                     const qlora_bf16* A, const qlora_bf16* B, int32_t r,
                                     float alpha, const qlora_dropout* drop,
-                                    const qlora_bf16* dY, const qlora_bf16* XA_in,
-                                    qlora_bf16* dX, float* dA, float* dB, void* ws,
-                                    size_t ws_bytes, void* stream, const GradJob* grp) {
+                                    const uint8_t* keep_bits_in, const qlora_bf16* dY,
+                                    const qlora_bf16* XA_in, qlora_bf16* dX, float* dA,
+                                    float* dB, void* ws, size_t ws_bytes, void* stream,
+                                    const GradJob* grp) {
   qlora_status st = check_linear(W, X, M, A, B, r, alpha);
   if (st != QLORA_OK) return st;
   DropoutParams dp;
   if (!dropout_params(drop, W->cols, &dp)) return QLORA_ERR_INVALID_ARG;
+  if (dp.thr != 0) dp.bits = keep_bits_in;
   if (!dY || !dA || !dB || !aligned(dY, 16)) return QLORA_ERR_INVALID_ARG;
   if (dX && !aligned(dX, 16)) return QLORA_ERR_INVALID_ARG;
   const int64_t N = W->rows, K = W->cols;
@@ -401,10 +405,11 @@ static qlora_status linear_bwd_impl(const qlora_nf4_tensor* W, const qlora_bf16*
 qlora_status qlora_linear_bwd_dropout(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
                                       const qlora_bf16* A, const qlora_bf16* B, int32_t r,
                                       float alpha, const qlora_dropout* drop,
-                                      const qlora_bf16* dY, const qlora_bf16* XA_in,
-                                      qlora_bf16* dX, float* dA, float* dB, void* ws,
-                                      size_t ws_bytes, void* stream) {
-  return linear_bwd_impl(W, X, M, A, B, r, alpha, drop, dY, XA_in, dX, dA, dB, ws, ws_bytes,
+                                      const uint8_t* keep_bits_in, const qlora_bf16* dY,
+                                      const qlora_bf16* XA_in, qlora_bf16* dX, float* dA,
+                                      float* dB, void* ws, size_t ws_bytes, void* stream) {
+  return linear_bwd_impl(W, X, M, A, B, r, alpha, drop, keep_bits_in, dY, XA_in, dX, dA, dB, ws,
+                         ws_bytes,
                          stream, nullptr);
 }
 
@@ -438,8 +443,8 @@ qlora_status qlora_grouped_fwd(const qlora_nf4_tensor* W, const qlora_bf16* X, i
   GradJob g{};
   if (!valid_tensor(W) || !grouping(W, r, groups, group_rows, &g)) return QLORA_ERR_INVALID_ARG;
   // rank G r with alpha G keeps every group's scale at alpha / r
-  return qlora_linear_fwd_dropout(W, X, M, A, B, groups * r, alpha * (float)groups, nullptr, Y,
-                                  XA_out, ws, ws_bytes, stream);
+  return qlora_linear_fwd_dropout(W, X, M, A, B, groups * r, alpha * (float)groups, nullptr,
+                                  nullptr, Y, XA_out, ws, ws_bytes, stream);
 }
 
 qlora_status qlora_grouped_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
@@ -449,7 +454,8 @@ qlora_status qlora_grouped_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, i
                                float* dA, float* dB, void* ws, size_t ws_bytes, void* stream) {
   GradJob g{};
   if (!valid_tensor(W) || !grouping(W, r, groups, group_rows, &g)) return QLORA_ERR_INVALID_ARG;
-  return linear_bwd_impl(W, X, M, A, B, groups * r, alpha * (float)groups, nullptr, dY, XA_in,
+  return linear_bwd_impl(W, X, M, A, B, groups * r, alpha * (float)groups, nullptr, nullptr, dY,
+                         XA_in,
                          dX, dA, dB, ws, ws_bytes, stream, &g);
 }
 

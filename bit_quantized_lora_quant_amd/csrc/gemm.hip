@@ -450,23 +450,26 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
 // element,
 //     acc[mt][t][v] = keep(m, kc + t) / (1 - p) * sum_j (s.G)[m][j] A[j][kc + t],
 //     m = m0 + 16 mt + 4 g + v,
-// so it is computed apart from the frozen product (four accumulators per row
-// tile, one row tile at a time) and becomes the starting value of the
-// accumulators, which the frozen product's MFMAs then add to (the tiles stay
-// in their registers; nothing is added to them by VALU afterwards).  The keep
-// words of columns kc .. kc + 3 (kc % 4 == 0) are the four words of one
-// generator block.  A's B operands are built once per 32 inner indices, as
-// in the unmasked tail.
+// so it is computed first, apart from the frozen product, masked, and becomes
+// the starting value of the accumulators that the frozen product's MFMAs then
+// add to (nothing is added to them by VALU afterwards).  The product runs as
+// the unmasked tail does: per 32 adapter indices, A's B operands once and all
+// 16 row tiles' (s.G) loads in flight together.  The keep bits come from the
+// generator, one block per row and 4 consecutive columns, with the round loop
+// rolled over 4 blocks at a time (fully unrolled, the 16 row tiles exceed the
+// unroller's budget and the accumulators fall into scratch).  The generator
+// is used even where the forward stored the mask: 64 scattered byte loads
+// per lane measured slower here than the 64 generator blocks.
 __device__ __forceinline__ void dropout_lora_init(f32x4_t (&acc)[16][4],
                                                   const uint16_t* __restrict__ gs,
                                                   const uint16_t* __restrict__ A, int r, int r32,
                                                   int64_t M, int64_t K, int64_t m0, int64_t kcl,
                                                   int j16, int g, const DropoutParams& d) {
-  const int nts = r32 / 32;   // 1 .. 4
-  uint4 bb[4][4];
 #pragma unroll
-  for (int ts = 0; ts < 4; ++ts) {
-    if (ts >= nts) break;
+  for (int mt = 0; mt < 16; ++mt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int ts = 0; ts < r32 / 32; ++ts) {
     const int j0 = ts * 32 + g * 8;
     uint2 rows[8];
 #pragma unroll
@@ -475,6 +478,7 @@ __device__ __forceinline__ void dropout_lora_init(f32x4_t (&acc)[16][4],
       rows[e] = (j < r) ? *reinterpret_cast<const uint2*>(A + (int64_t)j * K + kcl)
                         : make_uint2(0u, 0u);
     }
+    uint4 bb[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       uint32_t h[8];
@@ -483,27 +487,28 @@ __device__ __forceinline__ void dropout_lora_init(f32x4_t (&acc)[16][4],
         const uint32_t w = (t < 2) ? rows[e].x : rows[e].y;
         h[e] = (t & 1) ? (w >> 16) : (w & 0xFFFFu);
       }
-      bb[ts][t].x = h[0] | (h[1] << 16);
-      bb[ts][t].y = h[2] | (h[3] << 16);
-      bb[ts][t].z = h[4] | (h[5] << 16);
-      bb[ts][t].w = h[6] | (h[7] << 16);
+      bb[t].x = h[0] | (h[1] << 16);
+      bb[t].y = h[2] | (h[3] << 16);
+      bb[t].z = h[4] | (h[5] << 16);
+      bb[t].w = h[6] | (h[7] << 16);
     }
+    uint4 a[16];
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt) {
+      int64_t m = m0 + mt * 16 + j16;
+      m = m < M ? m : M - 1;
+      a[mt] = *reinterpret_cast<const uint4*>(gs + m * r32 + j0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[mt][t] = mfma16x16x32(a[mt], bb[t], acc[mt][t]);
   }
 #pragma unroll
   for (int mt = 0; mt < 16; ++mt) {
-    int64_t m = m0 + mt * 16 + j16;
-    m = m < M ? m : M - 1;
-    f32x4_t tl[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) tl[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ts = 0; ts < 4; ++ts) {
-      if (ts >= nts) break;
-      const uint4 a = *reinterpret_cast<const uint4*>(gs + m * r32 + ts * 32 + g * 8);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) tl[t] = mfma16x16x32(a, bb[ts][t], tl[t]);
-    }
-    uint4 wd[4];   // generator blocks of rows v = 0..3, columns kc .. kc + 3
+    uint32_t kn[4];   // keep bits of rows v = 0..3, columns kc .. kc + 3
+    uint4 wd[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const uint64_t c =
@@ -512,13 +517,12 @@ __device__ __forceinline__ void dropout_lora_init(f32x4_t (&acc)[16][4],
     }
     philox4x32_10_rolled<4>(wd, d.k0, d.k1);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const uint4 w = wd[v];
-      acc[mt][0][v] = w.x >= d.thr ? d.inv * tl[0][v] : 0.f;
-      acc[mt][1][v] = w.y >= d.thr ? d.inv * tl[1][v] : 0.f;
-      acc[mt][2][v] = w.z >= d.thr ? d.inv * tl[2][v] : 0.f;
-      acc[mt][3][v] = w.w >= d.thr ? d.inv * tl[3][v] : 0.f;
-    }
+    for (int v = 0; v < 4; ++v) kn[v] = keep_nibble(wd[v], d.thr);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        acc[mt][t][v] = ((kn[v] >> t) & 1u) ? d.inv * acc[mt][t][v] : 0.f;
   }
 }
 

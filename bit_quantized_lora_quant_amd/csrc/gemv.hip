@@ -221,7 +221,12 @@ __device__ __forceinline__ void xa_slice(const DecodeArgs& a, int r, int64_t sl,
     if (a.xa.drop.thr != 0) {   // LoRA dropout of X (element m K + k)
       const uint64_t e = (uint64_t)(tok ? j16 : 0) * (uint64_t)K + k + 8 * g;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) x[s] = and4(x[s], dropout_keep8(e + 32 * s, a.xa.drop));
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t kb = dropout_byte(e + 32 * s, a.xa.drop);
+        x[s] = and4(x[s], byte_mask8(kb));
+        if (tok && a.xa.drop.bits_out && k + 32 * s + 8 * g < K)
+          a.xa.drop.bits_out[(e + 32 * s) >> 3] = (uint8_t)kb;
+      }
     }
 #pragma unroll
     for (int jt = 0; jt < RT; ++jt) {

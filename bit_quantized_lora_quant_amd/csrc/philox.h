@@ -17,6 +17,10 @@
 // at least thr = floor(p 2^32).  The kernels apply the mask as a bit mask on
 // the bf16 operand (dropped elements become +0) and the 1 / (1 - p) factor
 // on the float32 sums.
+//
+// The forward can also leave the mask behind as bits (bit e % 8 of byte
+// e / 8 is element e's keep decision, 1/16 of X's bytes), so that the
+// backward reads it instead of running the generator again.
 #pragma once
 
 #include <cstdint>
@@ -28,6 +32,8 @@ struct DropoutParams {
   float inv = 1.f;        // 1 / (1 - p); 1 without dropout
   uint32_t k0 = 0, k1 = 0;  // key: seed low and high words
   int64_t cols = 0;       // K, the row length of X
+  const uint8_t* bits = nullptr;  // keep bits to read instead of the generator
+  uint8_t* bits_out = nullptr;    // where a forward writes the keep bits
 };
 
 __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
@@ -70,20 +76,32 @@ __device__ __forceinline__ uint4 dropout_words(uint64_t c, const DropoutParams& 
   return philox4x32_10(make_uint4((uint32_t)c, (uint32_t)(c >> 32), 0u, 0u), d.k0, d.k1);
 }
 
-// 0xFFFF for a kept element, 0 for a dropped one, placed at bit `shift`.
-__device__ __forceinline__ uint32_t keep_bits(uint32_t word, uint32_t thr, int shift) {
-  return word >= thr ? (0xFFFFu << shift) : 0u;
+// Keep bits of the 4 elements of block c (bit i: element 4c + i).
+__device__ __forceinline__ uint32_t keep_nibble(const uint4 w, uint32_t thr) {
+  return (w.x >= thr ? 1u : 0u) | (w.y >= thr ? 2u : 0u) | (w.z >= thr ? 4u : 0u) |
+         (w.w >= thr ? 8u : 0u);
 }
 
-// And-masks for the 8 bf16 of elements e .. e + 7 of X (e % 4 == 0), packed
-// as a uint4 load holds them (element 2i in the low half of word i).
+// Keep bits of elements e .. e + 7 of X (e % 8 == 0; bit i: element e + i):
+// the forward's stored bits when there are any, else the generator.
+__device__ __forceinline__ uint32_t dropout_byte(uint64_t e, const DropoutParams& d) {
+  if (d.bits) return d.bits[e >> 3];
+  return keep_nibble(dropout_words(e >> 2, d), d.thr) |
+         (keep_nibble(dropout_words((e >> 2) + 1, d), d.thr) << 4);
+}
+
+// And-masks for 8 bf16 from their keep bits, packed as a uint4 load holds
+// them (element 2i in the low half of word i).
+__device__ __forceinline__ uint4 byte_mask8(uint32_t b) {
+  return make_uint4(((b & 1u) ? 0xFFFFu : 0u) | ((b & 2u) ? 0xFFFF0000u : 0u),
+                    ((b & 4u) ? 0xFFFFu : 0u) | ((b & 8u) ? 0xFFFF0000u : 0u),
+                    ((b & 16u) ? 0xFFFFu : 0u) | ((b & 32u) ? 0xFFFF0000u : 0u),
+                    ((b & 64u) ? 0xFFFFu : 0u) | ((b & 128u) ? 0xFFFF0000u : 0u));
+}
+
+// And-masks for the 8 bf16 of elements e .. e + 7 of X (e % 8 == 0).
 __device__ __forceinline__ uint4 dropout_keep8(uint64_t e, const DropoutParams& d) {
-  const uint4 w0 = dropout_words(e >> 2, d);
-  const uint4 w1 = dropout_words((e >> 2) + 1, d);
-  return make_uint4(keep_bits(w0.x, d.thr, 0) | keep_bits(w0.y, d.thr, 16),
-                    keep_bits(w0.z, d.thr, 0) | keep_bits(w0.w, d.thr, 16),
-                    keep_bits(w1.x, d.thr, 0) | keep_bits(w1.y, d.thr, 16),
-                    keep_bits(w1.z, d.thr, 0) | keep_bits(w1.w, d.thr, 16));
+  return byte_mask8(dropout_byte(e, d));
 }
 
 __device__ __forceinline__ uint4 and4(uint4 v, uint4 m) {

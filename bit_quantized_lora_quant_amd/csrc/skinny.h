@@ -102,14 +102,21 @@ __device__ __forceinline__ void skinny_slice(const SkinnyJob& J, int64_t M, int 
 #pragma unroll
       for (int s = 0; s < 4; ++s) acc[jt] = mfma16x16x32(a[s], bv[jt][s], acc[jt]);
   };
-  // dropout of the T operand of the step at k (wave-uniform switch)
+  // dropout of the T operand of the step at k (wave-uniform switch); a lane
+  // of a real row also stores the keep bits when the forward keeps them
   const bool dj = DROP && J.drop.thr != 0;
   const uint64_t erow = (uint64_t)mrow * (uint64_t)J.drop.cols + 8 * g;
+  const bool wbits = DROP && J.drop.bits_out && m0 + j16 < M;
   auto drop_t = [&](int64_t k, uint4 (&a)[4]) {
     if constexpr (DROP) {
       if (dj) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) a[s] = and4(a[s], dropout_keep8(erow + k + 32 * s, J.drop));
+        for (int s = 0; s < 4; ++s) {
+          const uint64_t e = erow + k + 32 * s;
+          const uint32_t kb = dropout_byte(e, J.drop);
+          a[s] = and4(a[s], byte_mask8(kb));
+          if (wbits && k + 32 * s + 8 * g < J.kin) J.drop.bits_out[e >> 3] = (uint8_t)kb;
+        }
       }
     }
   };

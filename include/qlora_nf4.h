@@ -203,26 +203,30 @@ typedef struct {
 } qlora_dropout;
 
 /* qlora_linear_fwd with dropout on the adapter input: XA_out receives
- * bf16(D(X) . A^T).  drop NULL or drop->p == 0 is qlora_linear_fwd.  Same
- * shapes, workspace and errors, plus QLORA_ERR_INVALID_ARG for p outside
- * [0, 1) or not a number. */
+ * bf16(D(X) . A^T).  keep_bits_out (nullable, device, M * K / 8 bytes)
+ * receives the mask as bits: bit e % 8 of byte e / 8 is 1 if element
+ * e = m K + k is kept.  drop NULL or drop->p == 0 is qlora_linear_fwd (the
+ * bits are then not written).  Same shapes, workspace and errors, plus
+ * QLORA_ERR_INVALID_ARG for p outside [0, 1) or not a number. */
 qlora_status qlora_linear_fwd_dropout(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
                                       const qlora_bf16* A, const qlora_bf16* B, int32_t r,
-                                      float alpha, const qlora_dropout* drop, qlora_bf16* Y,
-                                      qlora_bf16* XA_out, void* ws, size_t ws_bytes,
-                                      void* stream);
+                                      float alpha, const qlora_dropout* drop,
+                                      uint8_t* keep_bits_out, qlora_bf16* Y, qlora_bf16* XA_out,
+                                      void* ws, size_t ws_bytes, void* stream);
 
 /* qlora_linear_bwd of the dropped layer (same drop as the forward):
  *     dX = dY . W' + (s . G . A) * keep / (1 - p)   (element by element)
  *     dA = s . G^T . D(X),   dB = s . dY^T . (D(X) . A^T)
  * XA_in (nullable) must be the XA_out of qlora_linear_fwd_dropout with the
- * same drop; when NULL, D(X) . A^T is recomputed with the regenerated mask. */
+ * same drop; when NULL, D(X) . A^T is recomputed.  keep_bits_in (nullable)
+ * must be the forward's keep_bits_out for the same drop: the backward then
+ * reads the mask instead of regenerating it (same result, less work). */
 qlora_status qlora_linear_bwd_dropout(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
                                       const qlora_bf16* A, const qlora_bf16* B, int32_t r,
                                       float alpha, const qlora_dropout* drop,
-                                      const qlora_bf16* dY, const qlora_bf16* XA_in,
-                                      qlora_bf16* dX, float* dA, float* dB, void* ws,
-                                      size_t ws_bytes, void* stream);
+                                      const uint8_t* keep_bits_in, const qlora_bf16* dY,
+                                      const qlora_bf16* XA_in, qlora_bf16* dX, float* dA,
+                                      float* dB, void* ws, size_t ws_bytes, void* stream);
 
 /* The keep flags of an [M, K] input under drop: out[m * K + k] = 1 if the
  * element is kept, else 0 (uint8, device memory, M * K bytes).  The mask the

@@ -157,10 +157,10 @@ def test_dropout_argument_errors(q):
     for p in (1.0, -0.1, 2.0, float("nan")):
         dr = q.QloraDropout(p, 7)
         assert lib.qlora_linear_fwd_dropout(ctypes.byref(d), X, 4, X, X, 8, ctypes.c_float(1.0),
-                                            ctypes.byref(dr), X, None, X, 1 << 30, None) == \
-            q.QLORA_ERR_INVALID_ARG
+                                            ctypes.byref(dr), None, X, None, X, 1 << 30,
+                                            None) == q.QLORA_ERR_INVALID_ARG
         assert lib.qlora_linear_bwd_dropout(ctypes.byref(d), X, 4, X, X, 8, ctypes.c_float(1.0),
-                                            ctypes.byref(dr), X, None, X, X, X, X, 1 << 30,
+                                            ctypes.byref(dr), None, X, None, X, X, X, X, 1 << 30,
                                             None) == q.QLORA_ERR_INVALID_ARG
         assert lib.qlora_dropout_mask(4, 64, ctypes.byref(dr), X, None) == q.QLORA_ERR_INVALID_ARG
     ok = q.QloraDropout(0.1, 7)
@@ -170,7 +170,7 @@ def test_dropout_argument_errors(q):
     assert lib.qlora_dropout_mask(0, 64, ctypes.byref(ok), None, None) == q.QLORA_OK
     # the shape checks of the plain calls come first
     assert lib.qlora_linear_fwd_dropout(ctypes.byref(d), X, 0, X, X, 8, ctypes.c_float(1.0),
-                                        ctypes.byref(ok), X, None, X, 1 << 30, None) == \
+                                        ctypes.byref(ok), None, X, None, X, 1 << 30, None) == \
         q.QLORA_ERR_INVALID_ARG
 
 

@@ -78,11 +78,22 @@ def test_linear_fwd_bwd_with_dropout(q, M, N, K, r, p):
     qq, _ = q.qlora_quantize_nf4(to_dev(w))
     X, A, B, dY = to_dev(x), to_dev(a), to_dev(b), to_dev(dy)
     drop = (p, seed)
-    Y, XA = q.qlora_linear_fwd(qq, X, A, B, alpha, return_xa=True, dropout=drop)
+    bits = q.keep_bits_buffer(M, K, DEV)
+    Y, XA = q.qlora_linear_fwd(qq, X, A, B, alpha, return_xa=True, dropout=drop, keep_bits=bits)
     dX, dA, dB = q.qlora_linear_bwd(qq, X, A, B, alpha, dY, XA_in=XA, dropout=drop)
     # the backward without the forward's XA regenerates the mask for it
     dX2, dA2, dB2 = q.qlora_linear_bwd(qq, X, A, B, alpha, dY, XA_in=None, dropout=drop)
+    # reading the forward's stored bits instead gives the same bits
+    dX3, dA3, dB3 = q.qlora_linear_bwd(qq, X, A, B, alpha, dY, XA_in=XA, dropout=drop,
+                                       keep_bits=bits)
+    dX4, dA4, dB4 = q.qlora_linear_bwd(qq, X, A, B, alpha, dY, XA_in=None, dropout=drop,
+                                       keep_bits=bits)
     torch.cuda.synchronize()
+    assert np.array_equal(host(bits).numpy(),
+                          np.packbits(odrop.keep_mask(M, K, p, seed).reshape(-1),
+                                      bitorder="little")), "stored keep bits"
+    for u, v in ((dX, dX3), (dA, dA3), (dB, dB3), (dX2, dX4), (dA2, dA4), (dB2, dB4)):
+        assert torch.equal(host(u), host(v))
     _, wd = oracle_weight(w)
     xf, af, bfl, dyf = bf16_np(x), bf16_np(a), bf16_np(b), bf16_np(dy)
     y_ref, xa_ref = oracle.linear_fwd(wd, xf, af, bfl, alpha, drop=drop)
@@ -109,9 +120,13 @@ def test_decode_with_dropout(q, M):
     say("dropout decode M=%d" % M)
     w, x, a, b, _ = _inputs(M, M, N, K, r)
     qq, _ = q.qlora_quantize_nf4(to_dev(w))
+    bits = q.keep_bits_buffer(M, K, DEV)
     Y, XA = q.qlora_linear_fwd(qq, to_dev(x), to_dev(a), to_dev(b), 16.0, return_xa=True,
-                               dropout=(p, seed))
+                               dropout=(p, seed), keep_bits=bits)
     torch.cuda.synchronize()
+    assert np.array_equal(host(bits).numpy(),
+                          np.packbits(odrop.keep_mask(M, K, p, seed).reshape(-1),
+                                      bitorder="little")), "stored keep bits (decode)"
     _, wd = oracle_weight(w)
     y_ref, xa_ref = oracle.linear_fwd(wd, bf16_np(x), bf16_np(a), bf16_np(b), 16.0,
                                       drop=(p, seed))
