@@ -250,7 +250,7 @@ def headline(args, q, torch, workloads):
     dom = max(kern, key=lambda k: kern[k]["avg_us"] * kern[k]["launches"])
     d = kern[dom]
     # the dX GEMM with N % 64 == 0 (every unit of the Llama layer) runs k_qlora_dx_nn_dma
-    roof = {"kernel": {"fwd_gemm": "k_qlora_fwd_nt", "dx_gemm": "k_qlora_dx_nn_dma"}[dom],
+    roof = {"kernel": {"fwd_gemm": "k_qlora_fwd_nt", "dx_gemm": "k_qlora_dx_nn_dma<false>"}[dom],
             "bound": "mfma", "achieved": round(d["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(d["tflops"] / PEAK_BF16_TFLOPS, 4),
             "traffic": None,
