@@ -387,10 +387,15 @@ def leg_dropout(q, torch, layers, M, r, alpha, p=0.05, steps=10):
     res = {"p": p, "seeds": "1000 + linear index",
            "dropout": "the forward stores the keep bits, the backward reads them",
            "dropout_regenerate": "the backward runs the generator again"}
-    for label, drop, keep in (("no_dropout", None, False), ("dropout", p, True),
-                              ("dropout_regenerate", p, False)):
-        step(drop, keep)
-        sec = timed(torch, lambda: step(drop, keep), steps)
+    cfgs = (("no_dropout", None, False), ("dropout", p, True), ("dropout_regenerate", p, False))
+    best = {}
+    for _ in range(3):   # alternate the configurations; keep each one's best
+        for label, drop, keep in cfgs:
+            step(drop, keep)
+            sec = timed(torch, lambda: step(drop, keep), steps)
+            best[label] = min(best.get(label, sec), sec)
+    for label, drop, keep in cfgs:
+        sec = best[label]
         q.qlora_trace_begin(["dx_gemm"], capacity=len(layers) + 1)
         step(drop, keep)
         tr = q.qlora_trace_end()
@@ -410,10 +415,14 @@ def leg_layer_driver(q, torch, layers, units, M, r, alpha, steps=10):
     headline (q/k/v and gate/up each one grouped weight), both eager, on the
     same inputs."""
     res = {"units": "q/k/v grouped, o, gate/up grouped, down"}
-    for label, fn in (("separate_7", lambda: separate_step(q, layers, alpha)),
-                      ("grouped_4", lambda: unit_step(q, units, r, alpha))):
-        fn()
-        sec = timed(torch, fn, steps)
+    best = {}
+    for _ in range(3):   # alternate the two; keep each one's best
+        for label, fn in (("separate_7", lambda: separate_step(q, layers, alpha)),
+                          ("grouped_4", lambda: unit_step(q, units, r, alpha))):
+            fn()
+            sec = timed(torch, fn, steps)
+            best[label] = min(best.get(label, sec), sec)
+    for label, sec in best.items():
         res["step_ms_" + label] = round(sec * 1e3, 4)
         res["tokens_per_s_" + label] = round(M / sec, 1)
     res["speedup"] = round(res["step_ms_separate_7"] / res["step_ms_grouped_4"], 4)
