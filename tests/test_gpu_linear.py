@@ -205,3 +205,27 @@ def test_autograd_wrapper(q):
     assert_close("dX", bf16_np(X.grad), dx_ref)
     assert_close("dA", bf16_np(A.grad), da_ref)
     assert_close("dB", bf16_np(B.grad), db_ref)
+
+
+def test_autograd_wrapper_with_dropout(q):
+    """The autograd wrapper with dropout: the forward stores the keep bits and
+    the backward reads them; gradients equal the oracle's under that mask."""
+    say("autograd dropout")
+    M, N, K, r = 96, 256, 512, 8
+    w, x, a, b, dy = _inputs(12, M, N, K, r)
+    qq, _ = q.qlora_quantize_nf4(to_dev(w))
+    X = to_dev(x).requires_grad_(True)
+    A = to_dev(a).requires_grad_(True)
+    B = to_dev(b).requires_grad_(True)
+    drop = (0.2, 31337)
+    Y = q.QLoRALinearFn.apply(X, A, B, qq, 16.0, drop)
+    Y.backward(to_dev(dy))
+    torch.cuda.synchronize()
+    _, wd = oracle_weight(w)
+    y_ref, _ = oracle.linear_fwd(wd, bf16_np(x), bf16_np(a), bf16_np(b), 16.0, drop=drop)
+    dx_ref, da_ref, db_ref = oracle.linear_bwd(wd, bf16_np(x), bf16_np(a), bf16_np(b), 16.0,
+                                               bf16_np(dy), drop=drop)
+    assert_close("Y", bf16_np(Y), y_ref)
+    assert_close("dX", bf16_np(X.grad), dx_ref)
+    assert_close("dA", bf16_np(A.grad), da_ref)
+    assert_close("dB", bf16_np(B.grad), db_ref)
