@@ -464,14 +464,17 @@ def leg_adamw(q, torch, workloads, reps=10):
         return out
 
     res = {"tensors": len(shapes), "params": total, "hparams": "lr 2e-4, betas (0.9, 0.999), "
-           "eps 1e-8, weight decay 0.01"}
+           "eps 1e-8, weight decay 0.01",
+           "flat": "device_statistics_flat: the same parameters as one flat tensor"}
     hs = []
-    for label in ("device_statistics", "host_statistics"):
+    for label in ("device_statistics", "device_statistics_flat", "host_statistics"):
         if label == "host_statistics":
             hs = [q.qlora_host_state_alloc(total) for _ in range(2)]
             hs[0].tensor.zero_()
             hs[1].tensor.zero_()
             ts = views(hs[0].tensor, hs[1].tensor)
+        elif label == "device_statistics_flat":
+            ts = [(P, G, M, V, PB)]
         else:
             ts = views(M, V)
 
@@ -488,7 +491,7 @@ def leg_adamw(q, torch, workloads, reps=10):
         n, ms = tr.get("adamw", (0, 0.0))
         ent = {"step_ms": round(sec * 1e3, 4), "launches": n,
                "kernel_ms": round(ms, 4)}
-        if label == "device_statistics":
+        if label != "host_statistics":
             gbs = 30.0 * total / sec / 1e9
             ent.update({"hbm_GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
         else:
