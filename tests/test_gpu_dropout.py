@@ -66,6 +66,7 @@ LINEAR = [  # M, N, K, r, p
     (130, 1003, 192, 8, 0.5),      # N odd: element-wise dY tiles
     (600, 264, 64, 128, 0.2),      # widest rank
     (40, 4096, 256, 64, 0.1),      # few rows, many columns
+    (8, 512, 1024, 16, 0.2),       # decode-path forward (keep bits from its slices), GEMM backward
 ]
 
 
