@@ -441,7 +441,9 @@ def qlora_adamw_step(tensors, step: int, lr: float, beta1: float = 0.9, beta2: f
 
 class HostState:
     """Pinned, device-mapped host memory for optimiser statistics, viewed as a
-    float32 CPU tensor (``.tensor``).  Freed by ``free()`` or when collected."""
+    float32 CPU tensor (``.tensor``).  Freed by ``free()`` or when collected;
+    views taken of ``.tensor`` must not outlive it, and no queued GPU work may
+    still use the memory when it is freed (synchronise first)."""
 
     def __init__(self, numel: int):
         ptr = ctypes.c_void_p()
