@@ -127,29 +127,30 @@ def test_full_weight_set_tensors(q, which):
 
 
 @pytest.mark.timeout(600)
-def test_every_float_in_the_unit_interval(q):
+@pytest.mark.parametrize("kind", ["nf4", "int4"])
+def test_every_float_in_the_unit_interval(q, kind):
     """Exhaustive: every float32 in [-1, 1] (all 2 x 1,065,353,217 bit patterns
     from +-0 to +-1) quantised on the device inside blocks whose absmax is
-    exactly 1, so the quantiser's input is the value itself; the NF4 codes
-    equal the oracle's nearest-level codes (ties to the lower level) for
-    every one of them."""
+    exactly 1, so the quantiser's input is the value itself; the codes (NF4
+    and INT4 tables) equal the oracle's nearest-level codes (ties to the lower
+    level) for every one of them."""
     total = 0x3F800001                      # patterns 0x00000000 .. 0x3F800000
     per_block = 63                          # the 64th element of a block is 1.0
     nb = 1 << 22                            # blocks per chunk (264M values)
     chunk = per_block * nb
-    Q = q.NF4Tensor(nb, 64, DEV, "nf4", False)
+    Q = q.NF4Tensor(nb, 64, DEV, kind, False)
     ws = q.workspace(q.qlora_quantize_workspace_bytes(nb, 64), DEV)
     host_w = np.ones((nb, 64), dtype=np.float32)
     for sign in (0, 0x80000000):
         for start in range(0, total, chunk):
             n = min(chunk, total - start)
-            say("exhaustive sign=%x start=%d n=%d" % (sign, start, n))
+            say("exhaustive %s sign=%x start=%d n=%d" % (kind, sign, start, n))
             buf = np.zeros(chunk, dtype=np.uint32)
             buf[:n] = np.arange(start, start + n, dtype=np.uint32) | np.uint32(sign)
             host_w[:, :per_block] = buf.view(np.float32).reshape(nb, per_block)
             W = torch.from_numpy(host_w).to(DEV)
             q.qlora_quantize_nf4(W, Q, ws)
             codes = host(Q.codes).numpy()
-            ref = oracle.quantize(host_w.reshape(-1), kind="nf4", dq=False)["codes"]
+            ref = oracle.quantize(host_w.reshape(-1), kind=kind, dq=False)["codes"]
             assert np.array_equal(codes, ref), "codes differ in chunk at %d (sign %x)" % (start, sign)
             del W
