@@ -177,3 +177,23 @@ def test_argument_errors(q):
     bad = (q.AdamWTensor * 1)(q.AdamWTensor(P.data_ptr() + 2, P.data_ptr(), P.data_ptr(),
                                             P.data_ptr(), None, 4))
     assert lib.qlora_adamw_step(ctypes.byref(ok), 1, bad, 1, None) == q.QLORA_ERR_INVALID_ARG
+
+
+def test_zero_learning_rate_keeps_the_weights(q):
+    """lr = 0: the weights (and their bf16 copy) stay bit for bit while both
+    statistics move as the oracle's."""
+    say("adamw lr=0")
+    rng = np.random.default_rng(21)
+    n = 9000
+    p = (rng.standard_normal(n) * 0.05).astype(np.float32)
+    g = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+    P, G = torch.from_numpy(p).to(DEV), torch.from_numpy(g).to(DEV)
+    M, V = torch.zeros(n, device=DEV), torch.zeros(n, device=DEV)
+    PB = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    q.qlora_adamw_step([(P, G, M, V, PB)], 1, 0.0, weight_decay=0.1)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(P).numpy().view(np.int32), p.view(np.int32))
+    assert torch.equal(host(PB), torch.from_numpy(p).to(torch.bfloat16))
+    _, m_ref, v_ref = adamw_step(p, g, np.zeros(n), np.zeros(n), 1, 0.0, 0.9, 0.999, 1e-8, 0.1)
+    _close("m", host(M).numpy(), m_ref)
+    _close("v", host(V).numpy(), v_ref)

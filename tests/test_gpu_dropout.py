@@ -178,3 +178,20 @@ def test_zero_probability_is_the_plain_layer(q, M):
     torch.cuda.synchronize()
     for u, v in zip(plain, dropped):
         assert torch.equal(host(u), host(v))
+
+
+def test_probability_below_the_generator_resolution_is_no_dropout(q):
+    """p below 2^-32 gives threshold 0 (every word keeps): the plain layer bit
+    for bit."""
+    M, N, K, r = 64, 256, 512, 8
+    say("dropout p=1e-12")
+    w, x, a, b, dy = _inputs(3, M, N, K, r)
+    qq, _ = q.qlora_quantize_nf4(to_dev(w))
+    X, A, B, dY = to_dev(x), to_dev(a), to_dev(b), to_dev(dy)
+    plain = list(q.qlora_linear_fwd(qq, X, A, B, 16.0, return_xa=True))
+    plain += list(q.qlora_linear_bwd(qq, X, A, B, 16.0, dY))
+    tiny = list(q.qlora_linear_fwd(qq, X, A, B, 16.0, return_xa=True, dropout=(1e-12, 5)))
+    tiny += list(q.qlora_linear_bwd(qq, X, A, B, 16.0, dY, dropout=(1e-12, 5)))
+    torch.cuda.synchronize()
+    for u, v in zip(plain, tiny):
+        assert torch.equal(host(u), host(v))
