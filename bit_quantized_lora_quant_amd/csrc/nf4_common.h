@@ -291,7 +291,7 @@ struct AdamTensor {
   uint16_t* pb;   // nullable bf16 copy of p
   int64_t n;
 };
-constexpr int kAdamBatch = 48;
+constexpr int kAdamBatch = 64;   // 3.6 KB of kernel arguments
 struct AdamBatch {
   int count;
   int64_t chunk_start[kAdamBatch + 1];

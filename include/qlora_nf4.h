@@ -330,7 +330,7 @@ typedef struct {
 } qlora_adamw_hparams;
 
 /* One AdamW step (number `step` >= 1) over `count` tensors, asynchronously on
- * `stream` (up to 48 tensors per launch).  All pointers of a tensor with
+ * `stream` (up to 64 tensors per launch).  All pointers of a tensor with
  * numel > 0 must be non-null and 4-byte aligned (param_bf16: 2-byte); 16-byte
  * alignment takes the vector path.  The tensors must not overlap.  exp_avg
  * and exp_avg_sq (and the others) may be device memory or host memory from

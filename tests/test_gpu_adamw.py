@@ -4,7 +4,7 @@ master weights and both statistics within a float32 bound over three steps
 against float64), the bf16 copy bit for bit against the device's own float32
 result, and exact agreements between the kernel's own paths: unaligned
 tensors (element-wise) against aligned ones (vector), several launches
-(more than 48 tensors), and statistics in mapped host memory against
+(more than 64 tensors), and statistics in mapped host memory against
 statistics in device memory."""
 import numpy as np
 import pytest
