@@ -25,7 +25,8 @@ import os
 import numpy as np
 
 from . import build as _build
-from .linear import linear_fwd, linear_bwd, lora_scale, merge_adapter  # noqa: F401
+from .linear import (linear_fwd, linear_bwd, adapter_grads, lora_scale,  # noqa: F401
+                     merge_adapter)
 from . import dropout  # noqa: F401
 from . import adamw  # noqa: F401
 

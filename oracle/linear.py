@@ -64,6 +64,21 @@ def linear_fwd(wd, x, a, b, alpha, drop=None):
     return y, xa
 
 
+def adapter_grads(x, a, b, alpha, dy, drop=None):
+    """(dA, dB) in float64, the adapter gradients alone (they reduce over all
+    tokens, so they need every row of X and dY; the frozen W plays no part):
+        dA = s . (dY . B)^T . D(X),   dB = s . dY^T . (D(X) . A^T)
+    with D(X) = X without dropout."""
+    x, a, b, dy = _f64(x), _f64(a), _f64(b), _f64(dy)
+    s = lora_scale(alpha, a.shape[0])
+    d = _dropout_scale(x, drop)
+    xd = x if d is None else x * d
+    g = dy @ b
+    da = s * (g.T @ xd)
+    db = s * (dy.T @ (xd @ a.T))
+    return da, db
+
+
 def linear_bwd(wd, x, a, b, alpha, dy, drop=None):
     """Returns (dX, dA, dB) in float64.  With dropout, dA uses D(X), dB the
     dropped forward's X . A^T, and the LoRA share of dX passes back through
@@ -71,12 +86,10 @@ def linear_bwd(wd, x, a, b, alpha, dy, drop=None):
     wd, x, a, b, dy = _f64(wd), _f64(x), _f64(a), _f64(b), _f64(dy)
     s = lora_scale(alpha, a.shape[0])
     d = _dropout_scale(x, drop)
-    xd = x if d is None else x * d
     g = dy @ b
     lora_dx = s * (g @ a)
     dx = dy @ wd + (lora_dx if d is None else lora_dx * d)
-    da = s * (g.T @ xd)
-    db = s * (dy.T @ (xd @ a.T))
+    da, db = adapter_grads(x, a, b, alpha, dy, drop)
     return dx, da, db
 
 

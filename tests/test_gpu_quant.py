@@ -88,6 +88,38 @@ def test_heavy_tailed_and_wide_range(q):
     _roundtrip(q, w)
 
 
+@pytest.mark.parametrize("consts,mean", [
+    ([4.0, 2.0 ** -22, 2.0 ** -51, 2.0 ** -51], 1.0 + 2.0 ** -23),   # tree != left to right
+    ([4.0, 2.0 ** -51, 2.0 ** -22, 2.0 ** -51], 1.0),                # tree != exact mean
+    ([5.0, 5.0 * 2.0 ** -24, 2.0 ** -51, 2.0 ** -51, 0.0], 1.0 + 2.0 ** -23),   # padded tree
+], ids=["left-to-right", "exact", "padded"])
+def test_mean_tree_order_constants(q, consts, mean):
+    """Blocks whose absmax are constants at which the adjacent-pair float64
+    tree, a left-to-right sum and the exact mean round to different float32
+    means (worked out by hand in the oracle's pins): the device's mean is
+    the tree's, and the whole state matches the oracle."""
+    say("quant tree-order constants %s" % (consts,))
+    w = np.zeros((len(consts), 64), dtype=np.float32)
+    w[:, 0] = consts
+    w[:, 1] = -np.float32(0.5) * np.asarray(consts, dtype=np.float32)
+    _roundtrip(q, w)
+    assert oracle.quantize(w)["absmax_mean"] == np.float32(mean)
+
+
+def test_blocks_dequantise_with_the_rebuilt_constant(q):
+    """The oracle pin's double-quantisation block on the device: absmax 1 +-
+    2^-9 rebuild to exactly 1, so those blocks dequantise to the bare levels."""
+    say("quant rebuilt-constant blocks")
+    cb = oracle.codebook()
+    a = np.ones(256, dtype=np.float64)
+    a[0], a[1], a[2], a[3] = 1 + 127 / 128, 1 / 128, 1 + 2.0 ** -9, 1 - 2.0 ** -9
+    idx = np.tile(np.arange(16), 4)
+    w = np.stack([(cb[idx].astype(np.float64) * a_b).astype(np.float32) for a_b in a])
+    qq = _roundtrip(q, w)
+    back = host(q.qlora_dequantize_nf4(qq, torch.float32)).numpy().reshape(256, 64)
+    assert np.array_equal(back[2], cb[idx]) and np.array_equal(back[3], cb[idx])
+
+
 def test_deterministic_repeat(q):
     say("quant determinism")
     w = to_dev((np.random.default_rng(3).standard_normal((512, 2048)) * 0.02).astype(np.float32))

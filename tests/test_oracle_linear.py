@@ -90,6 +90,9 @@ def test_backward_central_differences(alpha):
             t[idx] = old
             num[idx] = (lp - lm) / (2 * h)
         assert np.allclose(num, g, rtol=1e-7, atol=1e-8), name
+    # the gradients-only entry is the same dA, dB, and needs no weight
+    da2, db2 = oracle.adapter_grads(x, a, b, alpha, dy)
+    assert np.array_equal(da2, da) and np.array_equal(db2, db)
 
 
 def test_backward_adjoint_identity():
