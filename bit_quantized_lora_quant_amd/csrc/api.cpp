@@ -22,6 +22,20 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int64_t nblocks(int64_t n) { return ceil_div(n, kBlock); }
 
+// Largest sizes the kernels address.  The GEMM tile loaders take 32-bit
+// element offsets into X / dX [M, K], Y / dY [M, N], the codes (N K / 2
+// bytes) and the constant table [K/64][N]; one-dimensional launches over the
+// block constants or the dropout elements must stay under 2^32 threads.
+constexpr int64_t kOff32 = (int64_t)1 << 32;
+constexpr int64_t kMaxWeights = (int64_t)1 << 37;   // nb = n / 64 <= 2^31
+
+// a * b < lim for a, b >= 1, without forming the product
+bool below(int64_t a, int64_t b, int64_t lim) { return a <= (lim - 1) / b; }
+
+bool linear_fits(int64_t M, int64_t N, int64_t K) {
+  return below(M, K, kOff32) && below(M, N, kOff32) && below(N, K / 2 > 0 ? K / 2 : 1, kOff32);
+}
+
 bool valid_tensor(const qlora_nf4_tensor* q) {
   if (!q || q->rows < 1 || q->cols < 1) return false;
   if (q->block != QLORA_NF4_BLOCK) return false;
@@ -39,6 +53,9 @@ bool valid_tensor(const qlora_nf4_tensor* q) {
   if (q->rows > INT64_MAX / q->cols) return false;
   return true;
 }
+
+// the quantise / dequantise launches handle at most kMaxWeights weights
+bool tensor_fits(const qlora_nf4_tensor* q) { return below(q->rows, q->cols, kMaxWeights + 1); }
 
 // float32 block constants of a tensor quantised without double quantisation
 const float* f32_consts(const qlora_nf4_tensor* q) { return q->dq_block == 0 ? q->absmax : nullptr; }
@@ -167,6 +184,7 @@ qlora_status check_linear(const qlora_nf4_tensor* W, const void* X, int64_t M, c
   if (M < 1 || r < 1 || r > QLORA_MAX_RANK) return QLORA_ERR_INVALID_ARG;
   if (!(alpha == alpha)) return QLORA_ERR_INVALID_ARG;
   if (W->cols % QLORA_NF4_BLOCK != 0) return QLORA_ERR_UNSUPPORTED;
+  if (!linear_fits(M, W->rows, W->cols)) return QLORA_ERR_UNSUPPORTED;
   if (!aligned(X, 16) || !aligned(A, 16) || !aligned(B, 16)) return QLORA_ERR_INVALID_ARG;
   return QLORA_OK;
 }
@@ -216,13 +234,14 @@ const char* qlora_status_string(qlora_status s) {
 }
 
 size_t qlora_quantize_workspace_bytes(int64_t rows, int64_t cols) {
-  if (rows < 1 || cols < 1 || rows > INT64_MAX / cols) return 0;
+  if (rows < 1 || cols < 1 || !below(rows, cols, kMaxWeights + 1)) return 0;
   return quant_layout(rows * cols).total;
 }
 
 qlora_status qlora_quantize_nf4(const float* W, const qlora_nf4_tensor* q, void* ws,
                                 size_t ws_bytes, void* stream) {
   if (!W || !valid_tensor(q) || !aligned(W, 16)) return QLORA_ERR_INVALID_ARG;
+  if (!tensor_fits(q)) return QLORA_ERR_UNSUPPORTED;
   const int64_t n = q->rows * q->cols;
   const QuantWs L = quant_layout(n);
   if (!ws || ws_bytes < L.total || !aligned(ws, kAlign)) return QLORA_ERR_WORKSPACE;
@@ -242,6 +261,7 @@ qlora_status qlora_dequantize_nf4(const qlora_nf4_tensor* q, qlora_dtype out_dty
                                   void* stream) {
   if (!valid_tensor(q) || !out || !aligned(out, 16)) return QLORA_ERR_INVALID_ARG;
   if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16) return QLORA_ERR_INVALID_ARG;
+  if (!tensor_fits(q)) return QLORA_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(traced(QLORA_KERNEL_DEQUANT, s, [&] {
     return launch_dequant(q->codes, q->absmax_q, q->absmax_scale, q->absmax_mean, f32_consts(q),
@@ -251,6 +271,7 @@ qlora_status qlora_dequantize_nf4(const qlora_nf4_tensor* q, qlora_dtype out_dty
 
 qlora_status qlora_dequantize_absmax(const qlora_nf4_tensor* q, float* out, void* stream) {
   if (!valid_tensor(q) || !out) return QLORA_ERR_INVALID_ARG;
+  if (!tensor_fits(q)) return QLORA_ERR_UNSUPPORTED;
   return hip_status(launch_absmax_recon(q->absmax_q, q->absmax_scale, q->absmax_mean,
                                         f32_consts(q), nblocks(q->rows * q->cols), out,
                                         static_cast<hipStream_t>(stream)));
@@ -258,6 +279,7 @@ qlora_status qlora_dequantize_absmax(const qlora_nf4_tensor* q, float* out, void
 
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
   if (M < 1 || N < 1 || K < 1 || r < 1 || r > QLORA_MAX_RANK) return 0;
+  if (!linear_fits(M, N, K)) return 0;
   return linear_layout(M, N, K, r).total;
 }
 
@@ -461,15 +483,19 @@ qlora_status qlora_grouped_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, i
 
 qlora_status qlora_dropout_mask(int64_t M, int64_t K, const qlora_dropout* drop, uint8_t* out,
                                 void* stream) {
-  if (!drop || M < 0 || K < 0 || (M * K > 0 && !out)) return QLORA_ERR_INVALID_ARG;
+  if (!drop || M < 0 || K < 0) return QLORA_ERR_INVALID_ARG;
   if (K > 0 && M > INT64_MAX / K) return QLORA_ERR_INVALID_ARG;
+  if (M * K > 0 && !out) return QLORA_ERR_INVALID_ARG;
+  // one thread per 4 elements, in one grid dimension
+  if (M * K >= 4 * (kOff32 - 256)) return QLORA_ERR_UNSUPPORTED;
   DropoutParams dp;
   if (!dropout_params(drop, K, &dp)) return QLORA_ERR_INVALID_ARG;
   return hip_status(launch_dropout_mask(M, K, dp, out, static_cast<hipStream_t>(stream)));
 }
 
 size_t qlora_merge_workspace_bytes(int64_t rows, int64_t cols) {
-  if (rows < 1 || cols < 1 || rows > INT64_MAX / cols / 8) return 0;
+  if (rows < 1 || cols < 1 || !below(rows, cols, kMaxWeights + 1)) return 0;
+  if (!merge_fits(rows, cols)) return 0;
   const int64_t n = rows * cols;
   return align_up((size_t)n * sizeof(float)) + quant_layout(n).total;
 }
@@ -480,6 +506,7 @@ qlora_status qlora_merge_requantize(const qlora_nf4_tensor* W, const qlora_bf16*
                                     size_t ws_bytes, void* stream) {
   if (!valid_tensor(W) || !valid_tensor(out) || !A || !B) return QLORA_ERR_INVALID_ARG;
   if (out->rows != W->rows || out->cols != W->cols) return QLORA_ERR_INVALID_ARG;
+  if (!tensor_fits(W) || !merge_fits(W->rows, W->cols)) return QLORA_ERR_UNSUPPORTED;
   if (r < 1 || r > QLORA_MAX_RANK || !std::isfinite(alpha)) return QLORA_ERR_INVALID_ARG;
   if (!aligned(A, 2) || !aligned(B, 2) || (merged && !aligned(merged, 16)))
     return QLORA_ERR_INVALID_ARG;

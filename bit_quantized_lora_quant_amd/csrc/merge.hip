@@ -64,10 +64,16 @@ __global__ __launch_bounds__(kMergeCols) void k_merge_lora_add(
 
 }  // namespace
 
+bool merge_fits(int64_t N, int64_t K) {
+  // one grid dimension: fewer than 2^32 threads
+  const int64_t rows = ceil_div(N, kMergeRows), cols = ceil_div(K, kMergeCols);
+  return rows <= (((int64_t)1 << 32) / kMergeCols - 1) / cols;
+}
+
 hipError_t launch_merge_lora_add(float* merged, int64_t N, int64_t K, const uint16_t* A,
                                  const uint16_t* B, int r, float scale, hipStream_t s) {
   const int64_t blocks = ceil_div(N, kMergeRows) * ceil_div(K, kMergeCols);
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (!merge_fits(N, K)) return hipErrorInvalidValue;
   if (r < 1 || r > kMaxRank) return hipErrorInvalidValue;
   launch_kernel(k_merge_lora_add, dim3((unsigned)blocks), dim3(kMergeCols), s, merged, N, K, A,
                 B, r, scale);

@@ -305,6 +305,8 @@ int64_t adamw_chunks(int64_t n);
 // multiply-add per term), merged [N, K] float32, A [r, K], B [N, r] bf16
 hipError_t launch_merge_lora_add(float* merged, int64_t N, int64_t K, const uint16_t* A,
                                  const uint16_t* B, int r, float scale, hipStream_t s);
+// whether the merge launch's grid can cover an N x K weight
+bool merge_fits(int64_t N, int64_t K);
 hipError_t launch_adamw(const AdamBatch& batch, const AdamHyper& h, hipStream_t s);
 
 }  // namespace qnf4

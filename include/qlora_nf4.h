@@ -137,7 +137,8 @@ size_t qlora_quantize_workspace_bytes(int64_t rows, int64_t cols);
  * of all absmax (exact binary tree of pairwise float64 sums, divided by nb and
  * rounded to float32), deviations d = absmax - mean, per 256 constants
  * scale = max|d| / 127 and q = clamp(rint(d / scale), -127, 127) (0 when the
- * scale is 0).  Any rows*cols >= 1 is accepted. */
+ * scale is 0).  Any 1 <= rows*cols <= 2^37 is accepted; a larger tensor
+ * returns QLORA_ERR_UNSUPPORTED (as do the dequantise calls). */
 qlora_status qlora_quantize_nf4(const float* W, const qlora_nf4_tensor* q, void* ws,
                                 size_t ws_bytes, void* stream);
 
@@ -162,8 +163,10 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
  *   X [M, K], A [r, K], B [N, r], Y [M, N] (bf16).  XA_out (nullable) receives
  *   bf16(X . A^T) [M, r] for reuse by the backward.
  * Requires K % 64 == 0, M >= 1, 1 <= r <= 128; X, A, B, Y, dY, dX 16-byte
- * aligned.  M <= 16 takes the
- * bandwidth-bound decode path (same result definition). */
+ * aligned.  The kernels address X, Y, dY and dX and the codes with 32-bit
+ * offsets: M*K, M*N and N*K/2 must each be below 2^32, else
+ * QLORA_ERR_UNSUPPORTED (and the workspace query returns 0).  M <= 16 takes
+ * the bandwidth-bound decode path (same result definition). */
 qlora_status qlora_linear_fwd(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
                               const qlora_bf16* A, const qlora_bf16* B, int32_t r, float alpha,
                               qlora_bf16* Y, qlora_bf16* XA_out, void* ws, size_t ws_bytes,
@@ -230,7 +233,8 @@ qlora_status qlora_linear_bwd_dropout(const qlora_nf4_tensor* W, const qlora_bf1
 
 /* The keep flags of an [M, K] input under drop: out[m * K + k] = 1 if the
  * element is kept, else 0 (uint8, device memory, M * K bytes).  The mask the
- * two calls above apply, for inspection and tests.  M, K >= 0. */
+ * two calls above apply, for inspection and tests.  M, K >= 0;
+ * QLORA_ERR_UNSUPPORTED from 2^34 - 1024 elements on. */
 qlora_status qlora_dropout_mask(int64_t M, int64_t K, const qlora_dropout* drop, uint8_t* out,
                                 void* stream);
 
@@ -289,7 +293,8 @@ size_t qlora_merge_workspace_bytes(int64_t rows, int64_t cols);
 /* W, out: valid 4-bit tensors of the same rows x cols.  A [r, K], B [N, r]
  * bf16 (2-byte aligned), 1 <= r <= 128.  merged (nullable, 16-byte aligned):
  * receives the float32 merged weight [N, K]; when NULL it lives in the
- * workspace.  Errors as qlora_quantize_nf4. */
+ * workspace.  Errors as qlora_quantize_nf4, plus QLORA_ERR_UNSUPPORTED when
+ * rows * cols reaches about 2^36 (the merge launch's grid). */
 qlora_status qlora_merge_requantize(const qlora_nf4_tensor* W, const qlora_bf16* A,
                                     const qlora_bf16* B, int32_t r, float alpha,
                                     const qlora_nf4_tensor* out, float* merged, void* ws,

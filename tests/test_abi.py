@@ -222,3 +222,60 @@ def test_grouped_argument_errors(q):
     assert q.qlora_grouped_workspace_bytes(32, 128, 128, 65, 2) == 0
     assert q.qlora_grouped_workspace_bytes(32, 128, 128, 16, 2) == \
         q.qlora_linear_workspace_bytes(32, 128, 128, 32)
+
+
+def test_shapes_past_32_bit_offsets_are_unsupported(q):
+    """The GEMMs address X, Y, dY, dX and the codes with 32-bit offsets, so
+    M*K, M*N or N*K/2 at 2^32 must be refused before anything launches (the
+    buffers are never touched: the shape check comes before the workspace
+    check), and the workspace query returns 0 for them."""
+    lib = q.lib()
+    P = ctypes.c_void_p
+    fake = P(0x100000)
+    cases = [  # (M, N, K): refused
+        (1 << 20, 64, 1 << 12),        # M*K = 2^32
+        (1 << 20, 1 << 12, 64),        # M*N = 2^32
+        (32, 1 << 20, 1 << 13),        # N*K/2 = 2^32
+    ]
+    for M, N, K in cases:
+        d = _desc(q, rows=N, cols=K)
+        assert q.qlora_linear_workspace_bytes(M, N, K, 8) == 0, (M, N, K)
+        st = lib.qlora_linear_fwd(ctypes.byref(d), fake, M, fake, fake, 8,
+                                  ctypes.c_float(16.0), fake, None, None, 0, None)
+        assert st == q.QLORA_ERR_UNSUPPORTED, (M, N, K, st)
+        st = lib.qlora_linear_bwd(ctypes.byref(d), fake, M, fake, fake, 8,
+                                  ctypes.c_float(16.0), fake, None, fake, fake, fake, None, 0,
+                                  None)
+        assert st == q.QLORA_ERR_UNSUPPORTED, (M, N, K, st)
+    # just below every limit: the shape passes and the missing workspace is
+    # what is reported
+    M, N, K = (1 << 20) - 1, 64, 1 << 12
+    d = _desc(q, rows=N, cols=K)
+    assert lib.qlora_linear_fwd(ctypes.byref(d), fake, M, fake, fake, 8, ctypes.c_float(16.0),
+                                fake, None, None, 0, None) == q.QLORA_ERR_WORKSPACE
+    M, N, K = 32, (1 << 19), (1 << 14) - 64
+    d = _desc(q, rows=N, cols=K)
+    assert q.qlora_linear_workspace_bytes(M, N, K, 8) > 0
+    assert lib.qlora_linear_fwd(ctypes.byref(d), fake, M, fake, fake, 8, ctypes.c_float(16.0),
+                                fake, None, None, 0, None) == q.QLORA_ERR_WORKSPACE
+
+
+def test_oversized_tensors_and_masks_are_unsupported(q):
+    lib = q.lib()
+    P = ctypes.c_void_p
+    fake = P(0x100000)
+    big = _desc(q, rows=1 << 20, cols=(1 << 17) + 64)      # just over 2^37 weights
+    assert q.qlora_quantize_workspace_bytes(1 << 20, (1 << 17) + 64) == 0
+    assert lib.qlora_quantize_nf4(fake, ctypes.byref(big), fake, 1 << 30, None) == \
+        q.QLORA_ERR_UNSUPPORTED
+    assert lib.qlora_dequantize_nf4(ctypes.byref(big), q.QLORA_BF16, fake, None) == \
+        q.QLORA_ERR_UNSUPPORTED
+    assert lib.qlora_dequantize_absmax(ctypes.byref(big), fake, None) == q.QLORA_ERR_UNSUPPORTED
+    assert q.qlora_merge_workspace_bytes(1 << 20, (1 << 17) + 64) == 0
+    drop = q.QloraDropout(0.1, 5)
+    # M * K would overflow int64: invalid, checked before the product is formed
+    assert lib.qlora_dropout_mask(ctypes.c_int64((1 << 62)), 8, ctypes.byref(drop), fake,
+                                  None) == q.QLORA_ERR_INVALID_ARG
+    # 2^35 elements: more threads than one grid dimension holds
+    assert lib.qlora_dropout_mask(ctypes.c_int64(1 << 23), 1 << 12, ctypes.byref(drop), fake,
+                                  None) == q.QLORA_ERR_UNSUPPORTED
