@@ -1,22 +1,23 @@
 #!/usr/bin/env python
 """Benchmark of the frozen-NF4 LoRA linear on one MI355X.
 
-Headline step: forward then backward (reverse order) through the seven
-Llama-3.1-8B layer projections (q, k, v, o 4096-wide, k/v 1024, gate/up/down
-14336) at 2048 tokens, LoRA r = 16, alpha = 32, NF4 weights with double
-quantisation, each projection with its own adapter pair.  The layer driver
-runs the projections that share an input as one grouped weight (q/k/v, and
-gate/up), so the step is 4 fused-GEMM pairs.  ``value`` is tokens per second
-of that step with every input resident in HBM.  The JSON line also carries the
-dominant kernel's roofline (HIP-event durations measured on the library's
-stream during the timed region), the CPU oracle timed on a bounded sample, and
-the other legs of the path: quantise + dequantise of the full 8.03B-parameter
-weight set, the NF4 / INT4 and constant variants, the layer step with LoRA
-dropout, the same step as 7 separate linears (layer driver leg), the AdamW step
-over every 8B adapter, the 70B-shaped decode GEMV at 1 / 4 / 16 tokens, and the
-80-layer LLaMA-65B stack.
+Headline step: forward then backward (reverse order) through 80 LLaMA-65B
+layers, each with its own NF4 weights (double quantisation) for the seven
+projections (q, k, v, o 8192 -> 8192, gate/up 8192 -> 22016, down 22016 ->
+8192, about 33 GB of quantised state resident in HBM), 4 x 1024 = 4096 tokens,
+LoRA r = 64, alpha = 16, each projection with its own adapter pair.  ``value``
+is tokens per second of that step with every input resident in HBM.  The JSON
+line also carries the dominant kernel's roofline (HIP-event durations measured
+on the library's stream during the timed region, algorithmic flops per launch,
+HBM bytes per launch from the committed rocprofv3 counter summary), the CPU
+oracle timed on a bounded sample of the same step, and the other legs of the
+path: the Llama-3.1-8B layer step (2048 tokens, r = 16, layer driver), that
+step with LoRA dropout and as 7 separate linears, quantise + dequantise of the
+full 8.03B-parameter weight set, the NF4 / INT4 and constant variants, the
+AdamW step over every 8B adapter, and the 70B-shaped decode GEMV at 1 / 4 / 16
+tokens.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs all|none]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs all|none|...]
 """
 import argparse
 import hashlib
@@ -41,10 +42,10 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--legs", default="all",
-                    help="all, none, or a comma list of quant, variants, dropout, driver, adamw, "
-                         "decode, stack65b")
+                    help="all, none, or a comma list of layer8b, quant, variants, dropout, driver, "
+                         "adamw, decode")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run 3 plain device-to-device copies of MIB MiB (the known-size "
@@ -184,7 +185,133 @@ def separate_step(q, layers, alpha):
                            dX=L["dX"], dA=L["dA"], dB=L["dB"], ws=L["ws"])
 
 
+def kernel_table(tr, kflops, launches_per_step, sampled):
+    """Per-kernel averages from the traced launches: `kflops[name]` is the
+    algorithmic flops of one step's launches of that kernel."""
+    kern = {}
+    for name, (n, ms) in tr.items():
+        if not n:
+            continue
+        ent = {"launches": n, "avg_launch_us": round(ms * 1e3 / n, 2),
+               "us_per_step": round(ms * 1e3 / len(sampled), 2)}
+        if name in kflops:
+            per_launch = kflops[name] / launches_per_step[name]
+            tf = per_launch * n / (ms * 1e-3) / 1e12
+            ent.update({"flops_per_launch": per_launch, "tflops": round(tf, 2),
+                        "frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+        kern[name] = ent
+    return kern
+
+
+KERNEL_SYMBOL = {"fwd_gemm": "k_qlora_fwd_nt", "dx_gemm": "k_qlora_dx_nn_dma<false>"}
+
+
+def roofline_of(kern):
+    """The roofline object of whichever GEMM takes more time per step."""
+    dom = max((k for k in kern if "tflops" in kern[k]), key=lambda k: kern[k]["us_per_step"])
+    d = kern[dom]
+    roof = {"kernel": KERNEL_SYMBOL[dom], "bound": "mfma", "achieved": d["tflops"],
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": d["frac"], "traffic": None,
+            "avg_launch_us": d["avg_launch_us"], "flops_per_launch": d["flops_per_launch"]}
+    roof["traffic"] = traffic_for(roof["kernel"])
+    return roof
+
+
+def timed_steps(args, q, torch, step, traced, capacity):
+    """W untimed steps, then K timed steps between two synchronisations.  The
+    kernels in `traced` record their own start and end on a sample of the
+    timed steps (every tenth, at least one): a self-timed dispatch idles the
+    GPU for a few microseconds around it, so the step time carries little of
+    that cost."""
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    sampled = [i for i in range(args.steps) if i % 10 == 5] or [args.steps - 1]
+    q.qlora_trace_begin(traced, capacity=capacity * len(sampled) + 8)
+    q.qlora_trace_pause(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if i in sampled:
+            q.qlora_trace_pause(False)
+            step()
+            q.qlora_trace_pause(True)
+        else:
+            step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    tr = q.qlora_trace_end()
+    return (t1 - t0) / args.steps, tr, sampled
+
+
 def headline(args, q, torch, workloads):
+    """fwd + bwd through 80 LLaMA-65B layers (7 linears each, distinct NF4
+    weights), 4096 tokens, r = 64, alpha = 16.  The layers' weights are drawn
+    and quantised on the device; the activations, adapters and output buffers
+    of one shape are shared by the layers (they are a few hundred MB, the
+    weights 33 GB)."""
+    dev = "cuda:0"
+    wl = workloads.LLAMA65B_LAYER
+    M, r, alpha = wl.m, wl.r, wl.alpha
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    qws = q.workspace(max(q.qlora_quantize_workspace_bytes(n, k) for _, k, n in wl.linears), dev)
+    lin = []
+    for layer in range(wl.layers):
+        for t, (name, K, N) in enumerate(wl.linears):
+            W = workloads.device_weight(3, layer, t, N, K)
+            Q, _ = q.qlora_quantize_nf4(W, ws=qws)
+            del W
+            lin.append((Q, K, N))
+        if layer % 20 == 19:
+            torch.cuda.synchronize()
+            log("headline: %d/%d layers quantised" % (layer + 1, wl.layers))
+    del qws
+    torch.cuda.empty_cache()
+    shp = {(K, N) for _, K, N in wl.linears}
+    X = {K: torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16) for K, _ in shp}
+    dY = {N: torch.randn((M, N), generator=g, device=dev).to(torch.bfloat16) for _, N in shp}
+    A = {K: ((torch.rand((r, K), generator=g, device=dev) * 2 - 1) * K ** -0.5).to(torch.bfloat16)
+         for K, _ in shp}
+    B = {N: (torch.randn((N, r), generator=g, device=dev) * 0.01).to(torch.bfloat16) for _, N in shp}
+    Y = {N: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _, N in shp}
+    dX = {K: torch.empty((M, K), dtype=torch.bfloat16, device=dev) for K, _ in shp}
+    dA = {K: torch.empty((r, K), dtype=torch.float32, device=dev) for K, _ in shp}
+    dB = {N: torch.empty((N, r), dtype=torch.float32, device=dev) for _, N in shp}
+    XA = {K: torch.empty((M, r), dtype=torch.bfloat16, device=dev) for K, _ in shp}
+    ws = q.workspace(max(q.qlora_linear_workspace_bytes(M, N, K, r) for K, N in shp), dev)
+    torch.cuda.synchronize()
+    log("headline inputs ready (%d linears, %.1f GB of quantised weights)"
+        % (len(lin), sum(Q.nbytes() for Q, _, _ in lin) / 1e9))
+
+    def step():
+        for Q, K, N in lin:
+            q.qlora_linear_fwd(Q, X[K], A[K], B[N], alpha, Y=Y[N], XA_out=XA[K], ws=ws,
+                               return_xa=True)
+        for Q, K, N in reversed(lin):
+            q.qlora_linear_bwd(Q, X[K], A[K], B[N], alpha, dY[N], XA_in=XA[K], dX=dX[K],
+                               dA=dA[K], dB=dB[N], ws=ws)
+
+    sec, tr, sampled = timed_steps(args, q, torch, step, ["fwd_gemm", "dx_gemm", "split_reduce"],
+                                   capacity=2 * len(lin) + 8)
+    flops = sum(linear_flops(M, N, K, r) for _, K, N in lin)
+    # per-kernel algorithmic flops: fwd GEMM 2MN(K + r), dX GEMM 2MK(N + r)
+    kflops = {"fwd_gemm": sum(2 * M * N * (K + r) for _, K, N in lin),
+              "dx_gemm": sum(2 * M * K * (N + r) for _, K, N in lin)}
+    kern = kernel_table(tr, kflops, {"fwd_gemm": len(lin), "dx_gemm": len(lin)}, sampled)
+    roof = roofline_of(kern)
+    roof["timed_steps"] = sampled
+    log("headline: %.4f s/step, %.1f TFLOP/s" % (sec, flops / sec / 1e12))
+    res = dict(sec=sec, tokens=M, flops=flops, roofline=roof, kernels=kern)
+    del lin, X, dY, A, B, Y, dX, dA, dB, XA, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def leg_layer8b(args, q, torch, workloads):
+    """fwd + bwd through the seven Llama-3.1-8B layer projections at 2048
+    tokens, r = 16, alpha = 32, run by the layer driver (q/k/v and gate/up as
+    grouped weights: 4 fused-GEMM pairs)."""
     wl = workloads.LLAMA8B_LAYER
     dev = "cuda:0"
     M, r, alpha = wl.m, wl.r, wl.alpha
@@ -204,105 +331,74 @@ def headline(args, q, torch, workloads):
         layers.append(L)
     units = build_units(q, torch, layers, host_w, M, r)
     torch.cuda.synchronize()
-    log("headline inputs ready (%d linears in %d units)" % (len(layers), len(units)))
+    log("8B layer leg: inputs ready (%d linears in %d units)" % (len(layers), len(units)))
 
     def step():
         unit_step(q, units, r, alpha)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # Kernel durations come from HIP events that the timed dispatches record
-    # themselves.  A timed dispatch idles the GPU for a few microseconds around
-    # it, so only a sample of the timed steps records them (every tenth step,
-    # at least one): the step time carries little of that cost.
-    sampled = [i for i in range(args.steps) if i % 10 == 5] or [args.steps - 1]
-    q.qlora_trace_begin(["fwd_gemm", "dx_gemm", "split_reduce"],
-                        capacity=4 * len(units) * len(sampled) + 8)
-    q.qlora_trace_pause(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if i in sampled:
-            q.qlora_trace_pause(False)
-            step()
-            q.qlora_trace_pause(True)
-        else:
-            step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    tr = q.qlora_trace_end()
-    sec = (t1 - t0) / args.steps
+    sec, tr, sampled = timed_steps(args, q, torch, step, ["fwd_gemm", "dx_gemm", "split_reduce"],
+                                   capacity=4 * len(units) + 8)
     flops = sum(linear_flops(M, L["N"], L["K"], r) for L in layers)
-    # per-kernel algorithmic flops of a unit: fwd GEMM 2MN(K + r) (each row of
-    # W meets one adapter of rank r), dX GEMM 2MK(N + G r) (G adapters)
+    # fwd GEMM 2MN(K + r) (each row of W meets one adapter of rank r), dX
+    # GEMM 2MK(N + G r) (G adapters of a grouped unit)
     kflops = {"fwd_gemm": sum(2 * M * u["N"] * (u["K"] + r) for u in units),
               "dx_gemm": sum(2 * M * u["K"] * (u["N"] + u.get("G", 1) * r) for u in units)}
-    kern = {}
-    for name, (n, ms) in tr.items():
-        if name not in kflops:
-            continue
-        avg_ms = ms / n
-        per_launch = kflops[name] / len(units)
-        kern[name] = {"launches": n, "avg_us": avg_ms * 1e3,
-                      "tflops": kflops[name] * (n / len(units)) / (ms * 1e-3) / 1e12,
-                      "flops_per_launch": per_launch}
-    dom = max(kern, key=lambda k: kern[k]["avg_us"] * kern[k]["launches"])
-    d = kern[dom]
-    # the dX GEMM with N % 64 == 0 (every unit of the Llama layer) runs k_qlora_dx_nn_dma
-    roof = {"kernel": {"fwd_gemm": "k_qlora_fwd_nt", "dx_gemm": "k_qlora_dx_nn_dma<false>"}[dom],
-            "bound": "mfma", "achieved": round(d["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(d["tflops"] / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
-            "avg_launch_us": round(d["avg_us"], 2),
-            "flops_per_launch": d["flops_per_launch"]}
-    roof["traffic"] = traffic_for(roof["kernel"])
-    other = {k: {"avg_launch_us": round(v["avg_us"], 2), "tflops": round(v["tflops"], 2),
-                 "frac": round(v["tflops"] / PEAK_BF16_TFLOPS, 4)} for k, v in kern.items()}
-    for k, (n, ms) in tr.items():   # per-step time of every timed kernel
-        if n:
-            other.setdefault(k, {})["us_per_step"] = round(ms * 1e3 / len(sampled), 2)
-            other[k].setdefault("avg_launch_us", round(ms * 1e3 / n, 2))
-    roof["timed_steps"] = sampled
-    res = dict(sec=sec, tokens=M, flops=flops, roofline=roof, kernels=other)
-    log("headline: %.3f ms/step, %.1f TFLOP/s" % (sec * 1e3, flops / sec / 1e12))
-    return res, layers, host_w, units
+    kern = kernel_table(tr, kflops, {"fwd_gemm": len(units), "dx_gemm": len(units)}, sampled)
+    res = {"workload": "Llama-3.1-8B layer linears q/k/v/o/gate/up/down, 2048 tokens, LoRA r=16 "
+                       "alpha=32, NF4 + double quant, fwd+bwd, layer driver (q/k/v and gate/up "
+                       "grouped: 4 fused-GEMM pairs)",
+           "ms_per_step": round(sec * 1e3, 4), "tokens/s": round(M / sec, 1),
+           "TFLOP/s": round(flops / sec / 1e12, 2),
+           "frac_mfma": round(flops / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "kernels": kern, "timed_steps": sampled}
+    log("8B layer leg: %.3f ms/step, %.1f TFLOP/s" % (sec * 1e3, flops / sec / 1e12))
+    return res, layers, units
 
 
 # ---------------------------------------------------------- cpu baseline
-def cpu_baseline(workloads, layers, host_w, sample_tokens=256):
-    """The oracle as it stands, on a bounded sample of the headline step: the
-    float32 dequantisation of all seven weights (once per step, as the GPU
-    path rebuilds them every step) plus the float64 fwd+bwd of `sample_tokens`
-    tokens; extrapolated to the step's 2048 tokens."""
+def cpu_baseline(workloads, sample_tokens=256):
+    """The oracle as it stands, on a bounded sample of the headline step: for
+    layer 0 of the 65B stack, the float32 dequantisation of its seven weights
+    (once per step, as the GPU path rebuilds them every step) plus the
+    float64 fwd+bwd of `sample_tokens` of the 4096 tokens; the linear part is
+    scaled to 4096 tokens and the layer to 80 layers."""
     import numpy as np
     import oracle
     try:
         import threadpoolctl
         blas = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
     except Exception:
-        blas = os.cpu_count() or 1
-    wl = workloads.LLAMA8B_LAYER
-    qts = [oracle.quantize(w) for w in host_w]           # load-time, untimed
-    t0 = time.perf_counter()
-    wds = [oracle.dequantize(qt).reshape(w.shape) for qt, w in zip(qts, host_w)]
-    t_deq = time.perf_counter() - t0
-    t_lin = 0.0
-    for t, L in enumerate(layers):
-        _, x, a, b, dy = workloads.linear_inputs(wl, 0, t)
-        xs = workloads.bf16_to_f64(x[:sample_tokens])
-        dys = workloads.bf16_to_f64(dy[:sample_tokens])
+        blas = 1
+    wl = workloads.LLAMA65B_LAYER
+    t_deq = t_lin = 0.0
+    for t, (name, K, N) in enumerate(wl.linears):
+        w = workloads.weight(wl.key, 0, t, N, K)
+        qt = oracle.quantize(w)                            # load-time, untimed
+        del w
+        x = workloads.activations(wl.key, 0, t, sample_tokens, K)
+        dy = workloads.activations(wl.key, 0, t, sample_tokens, N, workloads.ROLE_DY)
+        a = workloads.lora_a(wl.key, 0, t, wl.r, K)
+        b = workloads.lora_b(wl.key, 0, t, N, wl.r)
+        xs, dys = workloads.bf16_to_f64(x), workloads.bf16_to_f64(dy)
         af, bfl = workloads.bf16_to_f64(a), workloads.bf16_to_f64(b)
+        t0 = time.perf_counter()
+        wd = oracle.dequantize(qt).reshape(N, K)
         t1 = time.perf_counter()
-        oracle.linear_fwd(wds[t], xs, af, bfl, wl.alpha)
-        oracle.linear_bwd(wds[t], xs, af, bfl, wl.alpha, dys)
-        t_lin += time.perf_counter() - t1
-    step = t_deq + t_lin * (wl.m / sample_tokens)
-    return {"value": round(wl.m / step, 2), "unit": "tokens/s",
-            "cores": int(max(blas, oracle.threads())), "kind": "oracle",
-            "sample": ("dequantise the 7 Llama-3.1-8B weights (%.2f s) + float64 fwd+bwd of %d of "
-                       "the 2048 tokens (%.2f s), linear part scaled x%d"
-                       % (t_deq, sample_tokens, t_lin, wl.m // sample_tokens))}
+        oracle.linear_fwd(wd, xs, af, bfl, wl.alpha)
+        oracle.linear_bwd(wd, xs, af, bfl, wl.alpha, dys)
+        t2 = time.perf_counter()
+        t_deq += t1 - t0
+        t_lin += t2 - t1
+        del qt, wd
+    layer = t_deq + t_lin * (wl.m / sample_tokens)
+    step = wl.layers * layer
+    return {"value": round(wl.m / step, 3), "unit": "tokens/s",
+            "cores": int(max(blas, oracle.threads())), "nproc": os.cpu_count(),
+            "kind": "oracle",
+            "sample": ("layer 0 of the 65B stack: dequantise its 7 weights (%.2f s) + float64 "
+                       "fwd+bwd of %d of the 4096 tokens (%.2f s); linear part scaled x%d, "
+                       "layer x%d" % (t_deq, sample_tokens, t_lin, wl.m // sample_tokens,
+                                      wl.layers))}
 
 
 # -------------------------------------------------------------------- legs
@@ -634,62 +730,6 @@ def leg_decode(q, torch, workloads, steps=5):
     return out
 
 
-def leg_65b_stack(q, torch, workloads, steps=2):
-    """fwd + bwd through 80 LLaMA-65B layers (7 linears each, distinct NF4
-    weights ~33 GB), 4096 tokens, r = 64, alpha = 16."""
-    dev = "cuda:0"
-    wl = workloads.LLAMA65B_LAYER
-    M, r, alpha = wl.m, wl.r, wl.alpha
-    g = torch.Generator(device=dev)
-    g.manual_seed(3)
-    qws = q.workspace(max(q.qlora_quantize_workspace_bytes(n, k) for _, k, n in wl.linears), dev)
-    lin = []
-    for layer in range(wl.layers):
-        for t, (name, K, N) in enumerate(wl.linears):
-            W = workloads.device_weight(3, layer, t, N, K)
-            Q, _ = q.qlora_quantize_nf4(W, ws=qws)
-            del W
-            lin.append((Q, K, N))
-        if layer % 20 == 19:
-            torch.cuda.synchronize()
-            log("65B leg: %d/%d layers quantised" % (layer + 1, wl.layers))
-    del qws
-    shp = {(K, N) for _, K, N in wl.linears}
-    X = {K: torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16) for K, _ in shp}
-    dY = {N: torch.randn((M, N), generator=g, device=dev).to(torch.bfloat16) for _, N in shp}
-    A = {K: ((torch.rand((r, K), generator=g, device=dev) * 2 - 1) * K ** -0.5).to(torch.bfloat16)
-         for K, _ in shp}
-    B = {N: (torch.randn((N, r), generator=g, device=dev) * 0.01).to(torch.bfloat16) for _, N in shp}
-    Y = {N: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _, N in shp}
-    dX = {K: torch.empty((M, K), dtype=torch.bfloat16, device=dev) for K, _ in shp}
-    dA = {K: torch.empty((r, K), dtype=torch.float32, device=dev) for K, _ in shp}
-    dB = {N: torch.empty((N, r), dtype=torch.float32, device=dev) for _, N in shp}
-    XA = {K: torch.empty((M, r), dtype=torch.bfloat16, device=dev) for K, _ in shp}
-    ws = q.workspace(max(q.qlora_linear_workspace_bytes(M, N, K, r) for K, N in shp), dev)
-
-    def step():
-        for Q, K, N in lin:
-            q.qlora_linear_fwd(Q, X[K], A[K], B[N], alpha, Y=Y[N], XA_out=XA[K], ws=ws, return_xa=True)
-        for Q, K, N in reversed(lin):
-            q.qlora_linear_bwd(Q, X[K], A[K], B[N], alpha, dY[N], XA_in=XA[K], dX=dX[K], dA=dA[K],
-                               dB=dB[N], ws=ws)
-
-    step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    sec = (time.perf_counter() - t0) / steps
-    flops = sum(linear_flops(M, N, K, r) for _, K, N in lin)
-    del lin
-    torch.cuda.empty_cache()
-    log("65B leg: %.3f s per 80-layer step" % sec)
-    return {"s_per_step": round(sec, 4), "tokens/s": round(M / sec, 1),
-            "TFLOP/s": round(flops / sec / 1e12, 1),
-            "frac_mfma": round(flops / sec / 1e12 / PEAK_BF16_TFLOPS, 4)}
-
-
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -706,24 +746,26 @@ def main():
     q.lib()
     if args.calibrate_copy:
         calibrate_copy(torch, args.calibrate_copy)
-    head, layers, host_w, units = headline(args, q, torch, workloads)
+    head = headline(args, q, torch, workloads)
     cpu = None
     if args.cpu_baseline == "on":
-        cpu = cpu_baseline(workloads, layers, host_w)
+        cpu = cpu_baseline(workloads)
         log("cpu baseline: %s tokens/s on %d threads" % (cpu["value"], cpu["cores"]))
     legs = {}
-    want = {"quant", "variants", "dropout", "driver", "adamw", "decode", "stack65b"} \
+    want = {"layer8b", "quant", "variants", "dropout", "driver", "adamw", "decode"} \
         if args.legs == "all" else (
         set() if args.legs == "none" else set(args.legs.split(",")))
-    if "dropout" in want:
+    if want & {"layer8b", "dropout", "driver"}:
         wl = workloads.LLAMA8B_LAYER
-        legs["llama8b_layer_lora_dropout"] = leg_dropout(q, torch, layers, wl.m, wl.r, wl.alpha)
-    if "driver" in want:
-        wl = workloads.LLAMA8B_LAYER
-        legs["llama8b_layer_driver_grouped"] = leg_layer_driver(q, torch, layers, units, wl.m,
-                                                                wl.r, wl.alpha)
-    del layers, host_w, units
-    torch.cuda.empty_cache()
+        legs["llama8b_layer_step"], layers, units = leg_layer8b(args, q, torch, workloads)
+        if "dropout" in want:
+            legs["llama8b_layer_lora_dropout"] = leg_dropout(q, torch, layers, wl.m, wl.r,
+                                                             wl.alpha)
+        if "driver" in want:
+            legs["llama8b_layer_driver_grouped"] = leg_layer_driver(q, torch, layers, units,
+                                                                    wl.m, wl.r, wl.alpha)
+        del layers, units
+        torch.cuda.empty_cache()
     if "quant" in want:
         legs["llama8b_weight_set_quant_dequant"] = leg_quant_dequant(q, torch, workloads)
     if "variants" in want:
@@ -732,28 +774,26 @@ def main():
         legs["llama8b_adapters_adamw_step"] = leg_adamw(q, torch, workloads)
     if "decode" in want:
         legs["llama70b_decode_gemv"] = leg_decode(q, torch, workloads)
-    if "stack65b" in want:
-        legs["llama65b_80_layer_stack"] = leg_65b_stack(q, torch, workloads)
     tokens_s = head["tokens"] / head["sec"]
     tflops = head["flops"] / head["sec"] / 1e12
     line = {
         "metric": "QLoRA linear fwd+bwd tokens/s (TFLOP/s, % MFMA peak); NF4 dequant/GEMV GB/s",
-        "value": round(tokens_s, 1),
+        "value": round(tokens_s, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(head["sec"] * 1e3, 4),
+        "ms_per_step": round(head["sec"] * 1e3, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; random NF4-quantised weights, no checkpoint)",
-        "config": {"workload": "Llama-3.1-8B layer linears q/k/v/o/gate/up/down, 2048 tokens, "
-                               "LoRA r=16 alpha=32, NF4 + double quant, fwd+bwd",
-                   "tokens": 2048, "rank": 16, "linears": 7,
-                   "driver": "q/k/v and gate/up each one grouped weight over their shared "
-                             "input, o and down alone (4 fused-GEMM pairs)"},
+        "config": {"workload": "LLaMA-65B layer linears q/k/v/o 8192->8192, gate/up "
+                               "8192->22016, down 22016->8192, repeated 80x (distinct NF4 + "
+                               "double-quant weights per layer), 4x1024 = 4096 tokens, LoRA "
+                               "r=64 alpha=16 on all seven, fwd+bwd",
+                   "tokens": 4096, "rank": 64, "layers": 80, "linears_per_layer": 7},
         "tflops": round(tflops, 2),
         "frac_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": head["roofline"],

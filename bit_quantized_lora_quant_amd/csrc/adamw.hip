@@ -21,7 +21,7 @@
 // The statistics may live in pinned host memory mapped into the device
 // address space (the paged placement): the same kernel then streams them
 // over the host link.
-#include "nf4_common.h"
+#include "optim.h"
 
 namespace qnf4 {
 namespace {

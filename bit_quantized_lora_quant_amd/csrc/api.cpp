@@ -9,7 +9,8 @@
 #include <cstring>
 
 #include "../../include/qlora_nf4.h"
-#include "nf4_common.h"
+#include "launch.h"
+#include "optim.h"
 
 using namespace qnf4;
 

@@ -23,7 +23,7 @@
 // (l % 16) of B and 8 consecutive inner indices of group (l / 16).  Which
 // actual inner indices a group stands for is free as long as A and B agree;
 // the kernels use that freedom to give each lane a contiguous run of codes.
-#include "nf4_common.h"
+#include "launch.h"
 
 namespace qnf4 {
 namespace {

@@ -13,7 +13,7 @@
 // (the bf16 products are exact in float32).  The r-wide inner products are
 // tiny next to the weight's traffic (2 N K r flop against 8 N K bytes), so
 // they run on the vector ALUs from LDS.
-#include "nf4_common.h"
+#include "launch.h"
 
 namespace qnf4 {
 namespace {

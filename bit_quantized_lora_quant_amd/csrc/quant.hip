@@ -9,7 +9,7 @@
 // Arithmetic that decides a code or a constant is IEEE float32 with round to
 // nearest even (this file is built with -ffp-contract=off); the one fused
 // operation is the explicit fmaf that rebuilds a constant.
-#include "nf4_common.h"
+#include "launch.h"
 
 namespace qnf4 {
 namespace {

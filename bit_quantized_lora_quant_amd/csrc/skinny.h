@@ -2,7 +2,7 @@
 // a workgroup: shared by the side-path launches and the decode kernel.
 #pragma once
 
-#include "nf4_common.h"
+#include "launch.h"
 
 namespace qnf4 {
 

@@ -15,7 +15,7 @@
 #include <cstring>
 #include <mutex>
 
-#include "nf4_common.h"
+#include "launch.h"
 
 namespace qnf4 {
 namespace {
