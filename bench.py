@@ -533,7 +533,8 @@ def leg_adamw(q, torch, workloads, reps=10):
     float32 masters, gradients and statistics, bf16 copies written in the same
     pass.  Algorithmic HBM bytes per parameter: 16 read + 14 written.  Then the
     same step with both statistics in mapped host memory (16 bytes per
-    parameter cross the host link)."""
+    parameter cross the host link), and both again with 8-bit statistics
+    (2 + 8/256 bytes of state per parameter)."""
     dev = "cuda:0"
     wl = workloads.LLAMA8B_LAYER
     r = wl.r
@@ -595,10 +596,56 @@ def leg_adamw(q, torch, workloads, reps=10):
         res[label] = ent
     for h in hs:
         h.free()
-    del P, G, M, V, PB
+    del M, V
+    # 8-bit statistics (blocks of 256, codes plus a float32 scale per block):
+    # every adapter size is a multiple of 256, so each tensor's state is a
+    # view of one flat state on block boundaries
+    for label, on_host in (("device_statistics_8bit", False), ("host_statistics_8bit", True)):
+        flat = q.AdamW8State(total, dev, host=on_host)
+        ts, off = [], 0
+        for a, b in shapes:
+            n = a * b
+            assert n % q.ADAMW8_BLOCK == 0
+            v = type("StateView", (), {})()
+            v.numel = n
+            v.m_q, v.v_q = flat.m_q[off:off + n], flat.v_q[off:off + n]
+            bo, bn = off // q.ADAMW8_BLOCK, n // q.ADAMW8_BLOCK
+            v.m_scale, v.v_scale = flat.m_scale[bo:bo + bn], flat.v_scale[bo:bo + bn]
+            ts.append((P[off:off + n], G[off:off + n], v, PB[off:off + n]))
+            off += n
+
+        def step8():
+            q.qlora_adamw8_step(ts, 1, 2e-4, 0.9, 0.999, 1e-8, 0.01)
+
+        step8()
+        gr = graph_of(torch, step8)
+        sec = timed(torch, gr.replay, reps)
+        del gr
+        q.qlora_trace_begin(["adamw8"], capacity=64)
+        step8()
+        tr = q.qlora_trace_end()
+        n, ms = tr.get("adamw8", (0, 0.0))
+        ent = {"step_ms": round(sec * 1e3, 4), "launches": n, "kernel_ms": round(ms, 4),
+               "state_bytes_per_param": round(flat.nbytes() / total, 4)}
+        # algorithmic bytes: p, g, 2 codes and 2/256 scales read; p, 2 codes,
+        # 2/256 scales and the bf16 copy written
+        if not on_host:
+            gbs = (18.0 + 16.0 / 256) * total / sec / 1e9
+            ent.update({"hbm_GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
+        else:
+            ent["host_link_GB/s"] = round((4.0 + 16.0 / 256) * total / sec / 1e9, 2)
+        res[label] = ent
+        torch.cuda.synchronize()
+        ts = None
+        flat.free()
+        del flat
+    del P, G, PB
     torch.cuda.empty_cache()
-    log("adamw leg: %.3f ms with device statistics, %.3f ms with host statistics" %
-        (res["device_statistics"]["step_ms"], res["host_statistics"]["step_ms"]))
+    log("adamw leg: %.3f / %.3f ms with float32 / 8-bit device statistics, %.3f / %.3f ms "
+        "with host statistics" % (res["device_statistics"]["step_ms"],
+                                  res["device_statistics_8bit"]["step_ms"],
+                                  res["host_statistics"]["step_ms"],
+                                  res["host_statistics_8bit"]["step_ms"]))
     return res
 
 

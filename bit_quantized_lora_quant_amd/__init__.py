@@ -27,13 +27,14 @@ EXPORTS = [
     "qlora_quantize_nf4", "qlora_dequantize_nf4", "qlora_dequantize_absmax",
     "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout", "qlora_dropout_mask",
-    "qlora_adamw_step", "qlora_host_state_alloc", "qlora_host_state_free",
+    "qlora_adamw_step", "qlora_adamw8_step", "qlora_host_state_alloc", "qlora_host_state_free",
     "qlora_merge_workspace_bytes", "qlora_merge_requantize",
     "qlora_grouped_workspace_bytes", "qlora_grouped_fwd", "qlora_grouped_bwd",
     "qlora_trace_begin", "qlora_trace_pause", "qlora_trace_end",
 ]
 KERNELS = {"fwd_gemm": 0, "dx_gemm": 1, "quantize": 2, "dequant": 3, "gemv": 4,
-           "split_reduce": 5, "adamw": 6}
+           "split_reduce": 5, "adamw": 6, "adamw8": 7}
+ADAMW8_BLOCK = 256
 
 
 class QloraError(RuntimeError):
@@ -59,6 +60,13 @@ class QloraDropout(ctypes.Structure):
 class AdamWTensor(ctypes.Structure):
     _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p),
                 ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p),
+                ("param_bf16", ctypes.c_void_p), ("numel", ctypes.c_int64)]
+
+
+class AdamW8Tensor(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p),
+                ("exp_avg_q", ctypes.c_void_p), ("exp_avg_scale", ctypes.c_void_p),
+                ("exp_avg_sq_q", ctypes.c_void_p), ("exp_avg_sq_scale", ctypes.c_void_p),
                 ("param_bf16", ctypes.c_void_p), ("numel", ctypes.c_int64)]
 
 
@@ -101,6 +109,7 @@ def lib():
                                                SZ, P]
         L.qlora_dropout_mask.argtypes = [I64, I64, P, P, P]
         L.qlora_adamw_step.argtypes = [P, I64, P, I32, P]
+        L.qlora_adamw8_step.argtypes = [P, I64, P, I32, P]
         L.qlora_grouped_workspace_bytes.restype = SZ
         L.qlora_grouped_workspace_bytes.argtypes = [I64, I64, I64, I32, I32]
         L.qlora_grouped_fwd.argtypes = [D, P, I64, P, P, I32, I32, P, F, P, P, P, SZ, P]
@@ -439,19 +448,40 @@ def qlora_adamw_step(tensors, step: int, lr: float, beta1: float = 0.9, beta2: f
            "qlora_adamw_step")
 
 
+def qlora_adamw8_step(tensors, step: int, lr: float, beta1: float = 0.9, beta2: float = 0.999,
+                      eps: float = 1e-8, weight_decay: float = 0.0):
+    """One AdamW step with 8-bit statistics.  tensors: list of (param, grad,
+    state, param_bf16 or None) with param and grad float32 contiguous tensors
+    of one numel and state an AdamW8State of that numel (device or host)."""
+    arr = (AdamW8Tensor * max(len(tensors), 1))()
+    for i, (p, g, st, pb) in enumerate(tensors):
+        n = p.numel()
+        for t in (p, g):
+            assert t.dtype == torch.float32 and t.is_contiguous() and t.numel() == n
+        assert st.numel == n
+        if pb is not None:
+            assert pb.dtype == torch.bfloat16 and pb.is_contiguous() and pb.numel() == n
+        arr[i] = AdamW8Tensor(_ptr(p), _ptr(g), _ptr(st.m_q), _ptr(st.m_scale), _ptr(st.v_q),
+                              _ptr(st.v_scale), _ptr(pb) if pb is not None else None, n)
+    h = AdamWHparams(lr, beta1, beta2, eps, weight_decay)
+    _check(lib().qlora_adamw8_step(ctypes.byref(h), step, arr, len(tensors), _stream()),
+           "qlora_adamw8_step")
+
+
 class HostState:
     """Pinned, device-mapped host memory for optimiser statistics, viewed as a
-    float32 CPU tensor (``.tensor``).  Freed by ``free()`` or when collected;
-    views taken of ``.tensor`` must not outlive it, and no queued GPU work may
-    still use the memory when it is freed (synchronise first)."""
+    CPU tensor of `dtype` (``.tensor``).  Freed by ``free()`` or when
+    collected; views taken of ``.tensor`` must not outlive it, and no queued
+    GPU work may still use the memory when it is freed (synchronise first)."""
 
-    def __init__(self, numel: int):
+    def __init__(self, numel: int, dtype=torch.float32):
+        size = torch.empty(0, dtype=dtype).element_size()
         ptr = ctypes.c_void_p()
-        _check(lib().qlora_host_state_alloc(4 * numel, ctypes.byref(ptr)),
+        _check(lib().qlora_host_state_alloc(max(size * numel, 1), ctypes.byref(ptr)),
                "qlora_host_state_alloc")
         self.ptr = ptr.value
-        buf = (ctypes.c_byte * (4 * numel)).from_address(self.ptr)
-        self.tensor = torch.frombuffer(buf, dtype=torch.float32, count=numel)
+        buf = (ctypes.c_byte * max(size * numel, 1)).from_address(self.ptr)
+        self.tensor = torch.frombuffer(buf, dtype=dtype, count=numel)
 
     def free(self):
         if self.ptr:
@@ -466,8 +496,43 @@ class HostState:
             pass
 
 
-def qlora_host_state_alloc(numel: int) -> HostState:
-    return HostState(numel)
+def qlora_host_state_alloc(numel: int, dtype=torch.float32) -> HostState:
+    return HostState(numel, dtype)
+
+
+class AdamW8State:
+    """The 8-bit statistics of one tensor of `numel` parameters, zero (the
+    state before step 1): int8 codes of m and uint8 codes of sqrt(v), one
+    float32 scale of each per 256 parameters.  host=True keeps them in
+    pinned, device-mapped host memory (the paged placement)."""
+
+    def __init__(self, numel: int, device, host: bool = False):
+        nb = (numel + ADAMW8_BLOCK - 1) // ADAMW8_BLOCK
+        self.numel = numel
+        self._host = []
+        if host:
+            bufs = [HostState(numel, torch.int8), HostState(nb, torch.float32),
+                    HostState(numel, torch.uint8), HostState(nb, torch.float32)]
+            self._host = bufs
+            for b in bufs:
+                b.tensor.zero_()
+            self.m_q, self.m_scale, self.v_q, self.v_scale = (b.tensor for b in bufs)
+        else:
+            self.m_q = torch.zeros(numel, dtype=torch.int8, device=device)
+            self.m_scale = torch.zeros(nb, dtype=torch.float32, device=device)
+            self.v_q = torch.zeros(numel, dtype=torch.uint8, device=device)
+            self.v_scale = torch.zeros(nb, dtype=torch.float32, device=device)
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.m_q, self.m_scale, self.v_q,
+                                                           self.v_scale))
+
+    def free(self):
+        """Release host buffers (synchronise first); device ones go with the object."""
+        self.m_q = self.m_scale = self.v_q = self.v_scale = None
+        for b in self._host:
+            b.free()
+        self._host = []
 
 
 def qlora_trace_begin(kernels, capacity: int = 4096):

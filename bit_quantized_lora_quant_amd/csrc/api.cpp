@@ -530,22 +530,15 @@ qlora_status qlora_merge_requantize(const qlora_nf4_tensor* W, const qlora_bf16*
   return hip_status(e);
 }
 
-qlora_status qlora_adamw_step(const qlora_adamw_hparams* h, int64_t step,
-                              const qlora_adamw_tensor* tensors, int32_t count, void* stream) {
-  if (!h || step < 1 || count < 0 || (count > 0 && !tensors)) return QLORA_ERR_INVALID_ARG;
+// Checks the hyperparameters and folds them into the float32 coefficients of
+// step `step`, each formed in double and rounded once.
+static qlora_status adam_hyper(const qlora_adamw_hparams* h, int64_t step, int32_t count,
+                               bool have_tensors, AdamHyper* out) {
+  if (!h || step < 1 || count < 0 || (count > 0 && !have_tensors)) return QLORA_ERR_INVALID_ARG;
   if (!(h->lr >= 0.0) || !(h->beta1 >= 0.0 && h->beta1 < 1.0) ||
       !(h->beta2 >= 0.0 && h->beta2 < 1.0) || !(h->eps > 0.0) || !(h->weight_decay >= 0.0) ||
       !std::isfinite(h->lr) || !std::isfinite(h->eps) || !std::isfinite(h->weight_decay))
     return QLORA_ERR_INVALID_ARG;
-  for (int32_t i = 0; i < count; ++i) {
-    const qlora_adamw_tensor& t = tensors[i];
-    if (t.numel < 0) return QLORA_ERR_INVALID_ARG;
-    if (t.numel == 0) continue;
-    if (!t.param || !t.grad || !t.exp_avg || !t.exp_avg_sq) return QLORA_ERR_INVALID_ARG;
-    if (!aligned(t.param, 4) || !aligned(t.grad, 4) || !aligned(t.exp_avg, 4) ||
-        !aligned(t.exp_avg_sq, 4) || (t.param_bf16 && !aligned(t.param_bf16, 2)))
-      return QLORA_ERR_INVALID_ARG;
-  }
   const double lr = h->lr, b1 = h->beta1, b2 = h->beta2;
   AdamHyper hp;
   hp.decay = (float)(1.0 - lr * h->weight_decay);
@@ -557,6 +550,24 @@ qlora_status qlora_adamw_step(const qlora_adamw_hparams* h, int64_t step,
   hp.eps = (float)h->eps;
   hp.step_size = (float)(lr / (1.0 - std::pow(b1, (double)step)));
   if (!(hp.eps > 0.f)) return QLORA_ERR_INVALID_ARG;   // eps below float's range
+  *out = hp;
+  return QLORA_OK;
+}
+
+qlora_status qlora_adamw_step(const qlora_adamw_hparams* h, int64_t step,
+                              const qlora_adamw_tensor* tensors, int32_t count, void* stream) {
+  AdamHyper hp;
+  const qlora_status st = adam_hyper(h, step, count, tensors != nullptr, &hp);
+  if (st != QLORA_OK) return st;
+  for (int32_t i = 0; i < count; ++i) {
+    const qlora_adamw_tensor& t = tensors[i];
+    if (t.numel < 0) return QLORA_ERR_INVALID_ARG;
+    if (t.numel == 0) continue;
+    if (!t.param || !t.grad || !t.exp_avg || !t.exp_avg_sq) return QLORA_ERR_INVALID_ARG;
+    if (!aligned(t.param, 4) || !aligned(t.grad, 4) || !aligned(t.exp_avg, 4) ||
+        !aligned(t.exp_avg_sq, 4) || (t.param_bf16 && !aligned(t.param_bf16, 2)))
+      return QLORA_ERR_INVALID_ARG;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int32_t i0 = 0; i0 < count; i0 += kAdamBatch) {
     AdamBatch bt{};
@@ -569,6 +580,40 @@ qlora_status qlora_adamw_step(const qlora_adamw_hparams* h, int64_t step,
       bt.chunk_start[j + 1] = bt.chunk_start[j] + adamw_chunks(t.numel);
     }
     const hipError_t e = traced(QLORA_KERNEL_ADAMW, s, [&] { return launch_adamw(bt, hp, s); });
+    if (e != hipSuccess) return QLORA_ERR_HIP;
+  }
+  return QLORA_OK;
+}
+
+qlora_status qlora_adamw8_step(const qlora_adamw_hparams* h, int64_t step,
+                               const qlora_adamw8_tensor* tensors, int32_t count, void* stream) {
+  AdamHyper hp;
+  const qlora_status st = adam_hyper(h, step, count, tensors != nullptr, &hp);
+  if (st != QLORA_OK) return st;
+  for (int32_t i = 0; i < count; ++i) {
+    const qlora_adamw8_tensor& t = tensors[i];
+    if (t.numel < 0) return QLORA_ERR_INVALID_ARG;
+    if (t.numel == 0) continue;
+    if (!t.param || !t.grad || !t.exp_avg_q || !t.exp_avg_scale || !t.exp_avg_sq_q ||
+        !t.exp_avg_sq_scale)
+      return QLORA_ERR_INVALID_ARG;
+    if (!aligned(t.param, 4) || !aligned(t.grad, 4) || !aligned(t.exp_avg_scale, 4) ||
+        !aligned(t.exp_avg_sq_scale, 4) || (t.param_bf16 && !aligned(t.param_bf16, 2)))
+      return QLORA_ERR_INVALID_ARG;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t i0 = 0; i0 < count; i0 += kAdam8Batch) {
+    Adam8Batch bt{};
+    bt.count = std::min(count - i0, kAdam8Batch);
+    bt.wg_start[0] = 0;
+    for (int j = 0; j < bt.count; ++j) {
+      const qlora_adamw8_tensor& t = tensors[i0 + j];
+      bt.t[j] = Adam8Tensor{t.param, t.grad, t.exp_avg_q, t.exp_avg_scale, t.exp_avg_sq_q,
+                            t.exp_avg_sq_scale, reinterpret_cast<uint16_t*>(t.param_bf16),
+                            t.numel};
+      bt.wg_start[j + 1] = bt.wg_start[j] + adamw8_workgroups(t.numel);
+    }
+    const hipError_t e = traced(QLORA_KERNEL_ADAMW8, s, [&] { return launch_adamw8(bt, hp, s); });
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
   return QLORA_OK;

@@ -344,6 +344,46 @@ typedef struct {
 qlora_status qlora_adamw_step(const qlora_adamw_hparams* h, int64_t step,
                               const qlora_adamw_tensor* tensors, int32_t count, void* stream);
 
+/* AdamW with 8-bit statistics (the 8-bit paged AdamW named in the training
+ * arguments of the addaly.com lesson "Fitting a fine-tune in 16 GB"; the
+ * pages fix no 8-bit format).  The statistics are kept blockwise in 8 bits,
+ * as the method keeps its block constants ("QLoRA: Fine-Tuning a 70B on One
+ * GPU", section "Double Quantization": 8-bit integers with a float32 scale):
+ * element e of a tensor lies in block e / 256, and
+ *     m      = exp_avg_q[e] * exp_avg_scale[e / 256]          (int8 codes)
+ *     sqrt(v) = exp_avg_sq_q[e] * exp_avg_sq_scale[e / 256]   (uint8 codes)
+ * One call applies step t of the float32 update of qlora_adamw_step to the
+ * dequantised statistics (the new sqrt(v), one correctly rounded square
+ * root, serves both the update and the new codes) and quantises them again
+ * per block:
+ *     exp_avg_scale    = max |m| / 127,   exp_avg_q    = clamp(rint(m / scale), -127, 127)
+ *     exp_avg_sq_scale = max sqrt(v) / 255, exp_avg_sq_q = clamp(rint(sqrt(v) / scale), 0, 255)
+ * with code 0 where a block's scale is 0 (rint: half to even; every
+ * operation one IEEE float32 rounding, no contraction).  All-zero codes and
+ * scales are the zero state of step 1.  2 + 8/256 bytes of state per
+ * parameter instead of 8.  The state may be device memory or host memory
+ * from qlora_host_state_alloc. */
+#define QLORA_ADAMW8_BLOCK 256
+typedef struct {
+  float* param;              /* float32 master weights [numel], updated in place */
+  const float* grad;         /* float32 gradient [numel] */
+  int8_t* exp_avg_q;         /* [numel], updated in place */
+  float* exp_avg_scale;      /* [ceil(numel / 256)], updated in place */
+  uint8_t* exp_avg_sq_q;     /* [numel], codes of sqrt(v), updated in place */
+  float* exp_avg_sq_scale;   /* [ceil(numel / 256)], updated in place */
+  qlora_bf16* param_bf16;    /* nullable: receives bf16(param) after the update */
+  int64_t numel;             /* >= 0; 0 skips the tensor */
+} qlora_adamw8_tensor;
+
+/* One AdamW step with 8-bit statistics over `count` tensors (up to 48 per
+ * launch), asynchronously on `stream`.  param, grad and the scales must be
+ * 4-byte aligned (param_bf16: 2-byte); 16-byte param and grad with 4-byte
+ * codes take the vector path.  Tensors must not overlap.  Returns
+ * QLORA_ERR_INVALID_ARG for bad hyperparameters, step, count or tensors
+ * (nothing launched). */
+qlora_status qlora_adamw8_step(const qlora_adamw_hparams* h, int64_t step,
+                               const qlora_adamw8_tensor* tensors, int32_t count, void* stream);
+
 /* Optimiser state kept in host memory ("QLoRA: Fine-Tuning a 70B on One
  * GPU", section "Paged Optimizers": host RAM serves as an extension of device
  * memory for the optimiser statistics).  Allocates `bytes` of pinned,
@@ -380,7 +420,8 @@ typedef enum {
   QLORA_KERNEL_GEMV = 4,       /* decode forward (M <= 16), main kernel */
   QLORA_KERNEL_SPLIT_REDUCE = 5, /* sum of split-K GEMM partials -> bf16 */
   QLORA_KERNEL_ADAMW = 6,      /* optimiser step */
-  QLORA_KERNEL_COUNT = 7
+  QLORA_KERNEL_ADAMW8 = 7,     /* optimiser step with 8-bit statistics */
+  QLORA_KERNEL_COUNT = 8
 } qlora_kernel;
 
 qlora_status qlora_trace_begin(uint32_t kernel_mask, int32_t capacity);
