@@ -24,7 +24,8 @@ MAX_RANK = 128
 EXPORTS = [
     "qlora_nf4_codebook", "qlora_codebook", "qlora_status_string",
     "qlora_quantize_workspace_bytes",
-    "qlora_quantize_nf4", "qlora_dequantize_nf4", "qlora_dequantize_absmax",
+    "qlora_quantize_nf4", "qlora_quantize_nf4_noalloc", "qlora_dequantize_nf4",
+    "qlora_dequantize_absmax",
     "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout", "qlora_dropout_mask",
     "qlora_adamw_step", "qlora_adamw8_step", "qlora_host_state_alloc", "qlora_host_state_free",
@@ -98,6 +99,7 @@ def lib():
         L.qlora_quantize_workspace_bytes.argtypes = [I64, I64]
         L.qlora_quantize_workspace_bytes.restype = SZ
         L.qlora_quantize_nf4.argtypes = [P, D, P, SZ, P]
+        L.qlora_quantize_nf4_noalloc.argtypes = [P, D, P]
         L.qlora_dequantize_nf4.argtypes = [D, ctypes.c_int, P, P]
         L.qlora_dequantize_absmax.argtypes = [D, P, P]
         L.qlora_linear_workspace_bytes.argtypes = [I64, I64, I64, I32]

@@ -239,6 +239,10 @@ size_t qlora_quantize_workspace_bytes(int64_t rows, int64_t cols) {
   return quant_layout(rows * cols).total;
 }
 
+// Launch sequence of the quantiser on a workspace the caller has checked.
+static qlora_status quantize_on(const float* W, const qlora_nf4_tensor* q, void* ws,
+                                const QuantWs& L, hipStream_t s);
+
 qlora_status qlora_quantize_nf4(const float* W, const qlora_nf4_tensor* q, void* ws,
                                 size_t ws_bytes, void* stream) {
   if (!W || !valid_tensor(q) || !aligned(W, 16)) return QLORA_ERR_INVALID_ARG;
@@ -246,7 +250,25 @@ qlora_status qlora_quantize_nf4(const float* W, const qlora_nf4_tensor* q, void*
   const int64_t n = q->rows * q->cols;
   const QuantWs L = quant_layout(n);
   if (!ws || ws_bytes < L.total || !aligned(ws, kAlign)) return QLORA_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  return quantize_on(W, q, ws, L, static_cast<hipStream_t>(stream));
+}
+
+qlora_status qlora_quantize_nf4_noalloc(const float* W, const qlora_nf4_tensor* q,
+                                        void* stream) {
+  if (!W || !valid_tensor(q) || !aligned(W, 16)) return QLORA_ERR_INVALID_ARG;
+  // at most 2^29 weights (the stated limit); the layout of that size fits the
+  // array, which the second check confirms
+  if (!below(q->rows, q->cols, ((int64_t)1 << 29) + 1)) return QLORA_ERR_UNSUPPORTED;
+  const QuantWs L = quant_layout(q->rows * q->cols);
+  if (L.total > quant_scratch_bytes()) return QLORA_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if (quant_scratch(&ws) != hipSuccess) return QLORA_ERR_HIP;
+  return quantize_on(W, q, ws, L, static_cast<hipStream_t>(stream));
+}
+
+static qlora_status quantize_on(const float* W, const qlora_nf4_tensor* q, void* ws,
+                                const QuantWs& L, hipStream_t s) {
+  const int64_t n = q->rows * q->cols;
   // without double quantisation the exact absmax is the stored constant
   float* absmax = q->dq_block == 0 ? q->absmax : at<float>(ws, L.absmax);
   hipError_t e = traced(QLORA_KERNEL_QUANTIZE, s, [&] {

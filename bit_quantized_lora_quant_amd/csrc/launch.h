@@ -19,6 +19,10 @@ hipError_t launch_dq(const float* absmax, int64_t nb, int8_t* q, float* scale, f
 hipError_t launch_dequant(const uint8_t* codes, const int8_t* q, const float* scale,
                           const float* mean, const float* f32, int64_t n, int out_bf16,
                           void* out, int kind, hipStream_t s);
+// The quantiser's allocation-free scratch on the current device: its size,
+// and its device address (looked up once per device).
+size_t quant_scratch_bytes();
+hipError_t quant_scratch(void** ptr);
 hipError_t launch_absmax_recon(const int8_t* q, const float* scale, const float* mean,
                                const float* f32, int64_t nb, float* out, hipStream_t s);
 

@@ -9,6 +9,8 @@
 // Arithmetic that decides a code or a constant is IEEE float32 with round to
 // nearest even (this file is built with -ffp-contract=off); the one fused
 // operation is the explicit fmaf that rebuilds a constant.
+#include <mutex>
+
 #include "launch.h"
 
 namespace qnf4 {
@@ -298,6 +300,38 @@ __global__ __launch_bounds__(kThreads) void k_absmax_recon(const int8_t* __restr
 // stores are contiguous.
 
 }  // namespace
+
+// ------------------------------------------------- allocation-free scratch
+// The quantiser's scratch (the exact block absmax and the mean tree's
+// float64 partials) for callers that cannot allocate: one file-scope device
+// array, which each GPU the library runs on holds until the process ends.
+// Host code uses only the device address hipGetSymbolAddress gives for the
+// current device (the array's name is a host-side stand-in).
+namespace {
+constexpr size_t kQuantScratchBytes = (32u << 20) + (64u << 10);
+__device__ __align__(256) uint8_t scratch[kQuantScratchBytes];
+}  // namespace
+
+size_t quant_scratch_bytes() { return kQuantScratchBytes; }
+
+hipError_t quant_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static void* addr[kMaxDevices] = {};
+  static std::mutex lock;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(lock);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 // Grid-stride launches: about 32 waves per CU, fewer for small tensors.
 static int64_t stream_grid(int64_t chunks) {

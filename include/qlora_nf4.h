@@ -142,6 +142,19 @@ size_t qlora_quantize_workspace_bytes(int64_t rows, int64_t cols);
 qlora_status qlora_quantize_nf4(const float* W, const qlora_nf4_tensor* q, void* ws,
                                 size_t ws_bytes, void* stream);
 
+/* qlora_quantize_nf4 for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops, harnesses that forbid hipMalloc):
+ * the same launches and results, with the scratch in a fixed array of
+ * 32 MiB + 64 KiB that the library keeps on each GPU it runs on until the
+ * process ends, so tensors of up to 2^29 weights (536,870,912) are
+ * accepted; a larger one returns QLORA_ERR_UNSUPPORTED with nothing
+ * launched.  Allocates nothing and needs no workspace.  All calls on one
+ * GPU share its array, which keeps the last call's contents: calls that
+ * overlap on one GPU (several streams or host threads) race and must be
+ * ordered by the caller.  The exact block absmax is not returned. */
+qlora_status qlora_quantize_nf4_noalloc(const float* W, const qlora_nf4_tensor* q,
+                                        void* stream);
+
 /* Dequantise to float32 or bf16 (round to nearest even) into out[rows*cols]
  * ("Double Quantization" section: NF4 weights converted back to the compute
  * dtype).  The float32 result is the single product level[code] * constant. */

@@ -279,3 +279,16 @@ def test_oversized_tensors_and_masks_are_unsupported(q):
     # 2^35 elements: more threads than one grid dimension holds
     assert lib.qlora_dropout_mask(ctypes.c_int64(1 << 23), 1 << 12, ctypes.byref(drop), fake,
                                   None) == q.QLORA_ERR_UNSUPPORTED
+
+
+def test_noalloc_quantise_refuses_past_its_fixed_scratch(q):
+    """The allocation-free quantiser takes at most 2^29 weights: one block
+    more is refused on the host before any device call (fake buffers)."""
+    lib = q.lib()
+    fake = 0x100000
+    for rows, cols in (((1 << 23) + 1, 64), (1 << 20, (1 << 9) + 64), (1 << 30, 64)):
+        d = q.NF4Descriptor(rows, cols, 64, 256, fake, fake, fake, fake, 0, 0, 0)
+        assert lib.qlora_quantize_nf4_noalloc(ctypes.c_void_p(fake), ctypes.byref(d), None) == \
+            q.QLORA_ERR_UNSUPPORTED, (rows, cols)
+    d = _desc(q)
+    assert lib.qlora_quantize_nf4_noalloc(None, ctypes.byref(d), None) == q.QLORA_ERR_INVALID_ARG
