@@ -348,7 +348,7 @@ qlora_status qlora_linear_fwd_dropout(const qlora_nf4_tensor* W, const qlora_bf1
   // with the block constants reconstructed in the same launch
   SkinnyJob xa{X, K, K, A, K, 0, 0, at<float>(ws, L.sk_k), scale, xas, XA_out, nullptr, 0};
   xa.drop = dp;
-  skinny_plan(&xa, M);
+  skinny_plan(&xa, M, r);
   const ReconJob rc{W->absmax_q, W->absmax_scale, W->absmax_mean, N, K / kBlock, ahat_t,
                     f32_consts(W)};
   e = launch_skinny(&xa, 1, M, r, L.r32, &rc, s);
@@ -420,7 +420,7 @@ static qlora_status linear_bwd_impl(const qlora_nf4_tensor* W, const qlora_bf16*
                          L.mp};
     sj[nj - 1].drop = dp;
   }
-  for (int i = 0; i < nj; ++i) skinny_plan(&sj[i], M);
+  for (int i = 0; i < nj; ++i) skinny_plan(&sj[i], M, r);
   QL_TRY(launch_skinny(sj, nj, M, r, L.r32, nullptr, s));
   if (dX) {
     float* part = at<float>(ws, L.gemm_part);

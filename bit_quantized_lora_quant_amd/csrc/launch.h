@@ -69,17 +69,18 @@ struct SkinnyJob {
   uint16_t* out_t;
   int64_t ldo_t;
   int part_only;   // write the slice partials even as a single slice
+  int staged = 0;  // set by skinny_plan: LDS-staged kernel (ranks 17..64)
   // dropout of T (T = X only): dropped elements read as zero, sums times
   // drop.inv
   DropoutParams drop{};
 };
 // Padded rank of the partial rows (16, 32, 64 or 128).
 int skinny_rpad(int r);
-int skinny_slices(int64_t M, int64_t kin);
+int skinny_slices(int64_t M, int64_t kin, int r);
 // Floats of `part` a job with these sizes needs.
 size_t skinny_part_floats(int64_t M, int64_t kin, int r);
 // Fills ks / kslice of each job from its kin.
-void skinny_plan(SkinnyJob* j, int64_t M);
+void skinny_plan(SkinnyJob* j, int64_t M, int r);
 // Slice launch (jobs + optional recon), then the finish launch.
 hipError_t launch_skinny(const SkinnyJob* jobs, int njobs, int64_t M, int r, int r32,
                          const ReconJob* recon, hipStream_t s);

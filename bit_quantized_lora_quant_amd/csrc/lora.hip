@@ -21,12 +21,35 @@ constexpr int kSkWaves = 8;     // waves per skinny workgroup at ranks above 16
 template <int RT>
 constexpr int sk_waves() { return RT == 1 ? 16 : kSkWaves; }
 
-// One thread per element of [KB][N]: out[kb * N + n] = â(n * KB + kb).
-__device__ __forceinline__ void recon_elems(const ReconJob& J, int64_t b) {
-  const int64_t e = b * blockDim.x + threadIdx.x;
-  if (e >= J.N * J.KB) return;
-  const int64_t kb = e / J.N, n = e - kb * J.N;
-  J.out[e] = J.f32 ? J.f32[n * J.KB + kb] : absmax_recon(J.q, J.scale, *J.mean, n * J.KB + kb);
+// Block constants rebuilt into [KB][N]: out[kb * N + n] = â(n * KB + kb).
+// Workgroup b takes a tile of 64 rows n x 64 column blocks kb through LDS, so
+// both sides are coalesced: the int8 (or float32) constants are read along
+// kb (64 consecutive per row), the float32 table is written along n.
+constexpr int kReconTile = 64;
+
+__device__ __forceinline__ int64_t recon_blocks(const ReconJob& J) {
+  return ceil_div(J.N, kReconTile) * ceil_div(J.KB, kReconTile);
+}
+
+__device__ __forceinline__ void recon_tile(const ReconJob& J, int64_t b,
+                                           float (*tile)[kReconTile + 1]) {
+  const int64_t tiles_kb = ceil_div(J.KB, kReconTile);
+  const int64_t n0 = (b / tiles_kb) * kReconTile, kb0 = (b % tiles_kb) * kReconTile;
+  const float mu = J.f32 ? 0.f : *J.mean;
+  for (int idx = threadIdx.x; idx < kReconTile * kReconTile; idx += blockDim.x) {
+    const int nl = idx / kReconTile, kl = idx % kReconTile;
+    const int64_t n = n0 + nl, kb = kb0 + kl;
+    if (n < J.N && kb < J.KB) {
+      const int64_t e = n * J.KB + kb;
+      tile[kl][nl] = J.f32 ? J.f32[e] : absmax_recon(J.q, J.scale, mu, e);
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < kReconTile * kReconTile; idx += blockDim.x) {
+    const int kl = idx / kReconTile, nl = idx % kReconTile;
+    const int64_t n = n0 + nl, kb = kb0 + kl;
+    if (n < J.N && kb < J.KB) J.out[kb * J.N + n] = tile[kl][nl];
+  }
 }
 
 
@@ -53,7 +76,166 @@ __global__ __launch_bounds__(sk_waves<RT>() * 64) void k_skinny_slices(SkinnyJob
     if (b < b1) { skinny_slice<RT, sk_waves<RT>(), DROP>(j1, M, r, r32, b); return; }
     b -= b1;
   }
-  if (has_rc) recon_elems(rc, b);
+  if (has_rc) {
+    __shared__ float tile[kReconTile][kReconTile + 1];
+    recon_tile(rc, b, tile);
+  }
+}
+
+// ------------------------------------------------ skinny NT, LDS-staged
+// For ranks 17..64 (RT = 2, 4) over an inner dimension that is a multiple of
+// 64: a workgroup of 8 waves takes 128 rows of T (16 per wave) and one inner
+// slice.  Per 64-wide step both tiles stream into LDS by DMA, three stages
+// deep: T [128 rows][64] (16 KB) and U [16 RT rows][64] (2 RT KB), 16-byte
+// chunks XOR-swizzled by row.  Every wave then reads all of U from LDS, so U
+// crosses the L2 once per 128 rows of T instead of once per 16 (the reason:
+// per 16 rows U is RT times the bytes of T, and those re-reads, not HBM, set
+// the time of the per-wave form).  A wave owns its rows outright: no
+// cross-wave reduction.  Slices write float32 partials [ks][M][16 RT] that
+// k_skinny_finish adds in order.
+constexpr int kSk2Waves = 8;
+constexpr int kSk2Rows = 16 * kSk2Waves;
+constexpr int kSk2Step = 64;
+constexpr int kSk2TBytes = kSk2Rows * kSk2Step * 2;          // 16 KB
+template <int RT>
+constexpr int sk2_stage_bytes() { return kSk2TBytes + RT * 16 * kSk2Step * 2; }
+
+__device__ __forceinline__ uint4 lds_chunk64(const uint16_t* lds, int row, int chunk) {
+  return *reinterpret_cast<const uint4*>(lds + row * kSk2Step + ((chunk ^ (row & 7)) * 8));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14)); }
+
+template <int RT, bool DROP>
+__device__ __forceinline__ void skinny2_slice(const SkinnyJob& J, int64_t M, int r, int r32,
+                                              int64_t b, uint8_t* arena) {
+  constexpr int kU = RT * 16;                  // U rows per tile
+  constexpr int kUw = kU / 8;                  // 1 KB DMA loads of U per step (2 or ...)
+  constexpr int kUper = kUw >= kSk2Waves ? kUw / kSk2Waves : 1;   // per issuing wave
+  constexpr int kUwaves = kUw >= kSk2Waves ? kSk2Waves : kUw;     // waves issuing U loads
+  static_assert(kUper * kUwaves == kUw, "U tile split");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j16 = lane & 15, g = lane >> 4;
+  const int ks = (int)(b % J.ks);
+  const int64_t mbase = (b / J.ks) * kSk2Rows;
+  const int64_t kbeg = (int64_t)ks * J.kslice;
+  const int64_t kend = kbeg + J.kslice < J.kin ? kbeg + J.kslice : J.kin;
+  const int nsteps = (int)((kend - kbeg) / kSk2Step);   // >= 1, every step whole
+  // DMA sources: T load q = 2 wv + i covers tile rows 8q .. 8q + 7; lane t
+  // fetches chunk (t % 8) ^ (t / 8) of row 8q + t / 8 (rows clamped below M)
+  const int c = (lane & 7) ^ (lane >> 3);
+  const uint16_t* tsrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    int64_t m = mbase + 8 * (2 * wv + i) + (lane >> 3);
+    m = m < M ? m : M - 1;
+    tsrc[i] = J.T + m * J.ldt + kbeg + c * 8;
+  }
+  const uint16_t* usrc[kUper];
+#pragma unroll
+  for (int i = 0; i < kUper; ++i) {
+    int u = 8 * (kUper * wv + i) + (lane >> 3);
+    u = u < r ? u : r - 1;   // rows past r feed output columns that are never stored
+    usrc[i] = J.U + (int64_t)u * J.ldu + kbeg + c * 8;
+  }
+  const bool uw = wv < kUwaves;
+  auto issue = [&](int st, int i) {   // DMA of step i into stage st
+    uint8_t* base = arena + st * sk2_stage_bytes<RT>();
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      dma16(tsrc[q] + i * kSk2Step, base + (2 * wv + q) * 1024);
+    if (uw) {
+#pragma unroll
+      for (int q = 0; q < kUper; ++q)
+        dma16(usrc[q] + i * kSk2Step, base + kSk2TBytes + (kUper * wv + q) * 1024);
+    }
+  };
+  // the wait for step i's loads, with step i + 1's (if any) still in flight
+  auto wait_step = [&](bool next) {
+    if (!next) { wait_vm<0>(); return; }
+    if (uw) wait_vm<2 + kUper>();
+    else wait_vm<2>();
+  };
+  const int mw = 16 * wv + j16;                       // this lane's tile row
+  const int64_t mrow = mbase + mw;
+  const bool dj = DROP && J.drop.thr != 0;
+  const uint64_t erow = (uint64_t)(mrow < M ? mrow : M - 1) * (uint64_t)J.drop.cols + 8 * g;
+  const bool wbits = DROP && J.drop.bits_out && mrow < M;
+
+  f32x4_t acc[RT];
+#pragma unroll
+  for (int jt = 0; jt < RT; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  issue(0, 0);
+  if (nsteps > 1) issue(1, 1);
+  for (int i = 0; i < nsteps; ++i) {
+    wait_step(i + 1 < nsteps);
+    __syncthreads();                                   // step i resident; step i - 1 read
+    if (i + 2 < nsteps) issue((i + 2) % 3, i + 2);
+    const uint8_t* base = arena + (i % 3) * sk2_stage_bytes<RT>();
+    const uint16_t* ts = reinterpret_cast<const uint16_t*>(base);
+    const uint16_t* us = reinterpret_cast<const uint16_t*>(base + kSk2TBytes);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      uint4 a = lds_chunk64(ts, mw, 4 * s + g);
+      if constexpr (DROP) {
+        if (dj) {   // dropout of T = X, element m K + k
+          const uint64_t e = erow + kbeg + (int64_t)i * kSk2Step + 32 * s;
+          const uint32_t kb = dropout_byte(e, J.drop);
+          a = and4(a, byte_mask8(kb));
+          if (wbits) J.drop.bits_out[e >> 3] = (uint8_t)kb;
+        }
+      }
+#pragma unroll
+      for (int jt = 0; jt < RT; ++jt)
+        acc[jt] = mfma16x16x32(a, lds_chunk64(us, jt * 16 + j16, 4 * s + g), acc[jt]);
+    }
+  }
+  // lane holds P[mbase + 16 wv + 4 g + v][16 jt + j16]
+  float* part = J.part + (int64_t)ks * M * (RT * 16);
+#pragma unroll
+  for (int jt = 0; jt < RT; ++jt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float sum = acc[jt][v];
+      if constexpr (DROP) sum *= J.drop.inv;
+      const int64_t m = mbase + 16 * wv + 4 * g + v;
+      const int j = jt * 16 + j16;
+      if (J.ks > 1 || J.part_only) {
+        if (m < M) part[m * (RT * 16) + j] = sum;
+        continue;
+      }
+      if (m < M) {
+        if (J.out_s && j < r32) J.out_s[m * r32 + j] = to_bf16(j < r ? J.scale * sum : 0.f);
+        if (J.out && j < r) J.out[m * r + j] = to_bf16(sum);
+      }
+      if (J.out_t && j < r && m < J.ldo_t)
+        J.out_t[(int64_t)j * J.ldo_t + m] = m < M ? to_bf16(sum) : 0;
+    }
+}
+
+__device__ __forceinline__ int64_t skinny2_blocks(const SkinnyJob& J, int64_t M) {
+  return ceil_div(skinny_rows(J, M), kSk2Rows) * J.ks;
+}
+
+// Staged jobs (and optionally the constant table) in one launch; one LDS
+// arena serves whichever branch a workgroup takes.
+template <int RT, bool DROP>
+__global__ __launch_bounds__(kSk2Waves * 64) void k_skinny2(SkinnyJob j0, SkinnyJob j1, int nj,
+                                                            int64_t M, int r, int r32,
+                                                            ReconJob rc, int has_rc) {
+  __shared__ __attribute__((aligned(1024))) uint8_t arena[3 * sk2_stage_bytes<RT>()];
+  int64_t b = blockIdx.x;
+  const int64_t b0 = skinny2_blocks(j0, M);
+  if (b < b0) { skinny2_slice<RT, DROP>(j0, M, r, r32, b, arena); return; }
+  b -= b0;
+  if (nj > 1) {
+    const int64_t b1 = skinny2_blocks(j1, M);
+    if (b < b1) { skinny2_slice<RT, DROP>(j1, M, r, r32, b, arena); return; }
+    b -= b1;
+  }
+  if (has_rc) recon_tile(rc, b, reinterpret_cast<float (*)[kReconTile + 1]>(arena));
 }
 
 // Thread per (row m, column j < r32) of one job: adds the slices in order.
@@ -93,26 +275,48 @@ __global__ __launch_bounds__(256) void k_skinny_finish(SkinnyJob j0, SkinnyJob j
 }
 
 // ------------------------------------------------------------------ prep
-__device__ __forceinline__ void transpose_elem(const TransposeJob& J, int64_t e) {
-  if (e >= J.cols * J.ldo) return;
-  const int64_t j = e / J.ldo, i = e - j * J.ldo;   // output row j (= input column), column i
-  J.out[e] = (i < J.rows) ? J.in[i * J.cols + j] : (uint16_t)0;
+// bf16 transpose [rows, cols] -> [cols, ldo] (zero for i in [rows, ldo)), a
+// 64 x 64 tile per workgroup through LDS: rows of the input are read along
+// cols, rows of the output written along i, both coalesced.
+constexpr int kTrTile = 64;
+
+__device__ __forceinline__ int64_t transpose_blocks(const TransposeJob& J) {
+  return ceil_div(J.ldo, kTrTile) * ceil_div(J.cols, kTrTile);
+}
+
+__device__ __forceinline__ void transpose_tile(const TransposeJob& J, int64_t b,
+                                               uint16_t (*tile)[kTrTile + 2]) {
+  const int64_t tiles_j = ceil_div(J.cols, kTrTile);
+  const int64_t i0 = (b / tiles_j) * kTrTile, j0 = (b % tiles_j) * kTrTile;
+  for (int idx = threadIdx.x; idx < kTrTile * kTrTile; idx += blockDim.x) {
+    const int il = idx / kTrTile, jl = idx % kTrTile;
+    const int64_t i = i0 + il, j = j0 + jl;
+    if (j < J.cols) tile[jl][il] = i < J.rows ? J.in[i * J.cols + j] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < kTrTile * kTrTile; idx += blockDim.x) {
+    const int jl = idx / kTrTile, il = idx % kTrTile;
+    const int64_t i = i0 + il, j = j0 + jl;
+    if (j < J.cols && i < J.ldo) J.out[j * J.ldo + i] = tile[jl][il];
+  }
 }
 
 __global__ __launch_bounds__(256) void k_prep(TransposeJob t0, TransposeJob t1, int nt,
                                               ReconJob rc, int has_rc) {
+  __shared__ float lds[kReconTile * (kReconTile + 1)];
   int64_t b = blockIdx.x;
+  auto tr = reinterpret_cast<uint16_t (*)[kTrTile + 2]>(lds);
   if (nt > 0) {
-    const int64_t n0 = ceil_div(t0.cols * t0.ldo, 256);
-    if (b < n0) { transpose_elem(t0, b * 256 + threadIdx.x); return; }
+    const int64_t n0 = transpose_blocks(t0);
+    if (b < n0) { transpose_tile(t0, b, tr); return; }
     b -= n0;
   }
   if (nt > 1) {
-    const int64_t n1 = ceil_div(t1.cols * t1.ldo, 256);
-    if (b < n1) { transpose_elem(t1, b * 256 + threadIdx.x); return; }
+    const int64_t n1 = transpose_blocks(t1);
+    if (b < n1) { transpose_tile(t1, b, tr); return; }
     b -= n1;
   }
-  if (has_rc) recon_elems(rc, b);
+  if (has_rc) recon_tile(rc, b, reinterpret_cast<float (*)[kReconTile + 1]>(lds));
 }
 
 // ------------------------------------------------------- adapter gradients
@@ -221,7 +425,7 @@ __device__ __forceinline__ void grad_slice(const GradJob& J, int64_t M, int r, i
   // uniform offset), two steps in flight: the next step's loads are issued
   // before this step's MFMAs.
   const int64_t tbytes = M * J.P * 2, ubytes = (int64_t)r * J.ldu * 2;
-  const bool bufs = fast && RT <= 2 && tbytes <= kBufferMax && ubytes <= kBufferMax;
+  const bool bufs = fast && RT <= 4 && tbytes <= kBufferMax && ubytes <= kBufferMax;
   const int64_t cnt_fast = bufs && first + 32 <= mend ? (mend - first - 32) / 128 + 1 : 0;
   if (cnt_fast > 0) {
     const __amdgpu_buffer_rsrc_t tview = buffer_view(J.T, tbytes);
@@ -296,7 +500,9 @@ __device__ __forceinline__ void grad_slice(const GradJob& J, int64_t M, int r, i
           if constexpr (DROP) s *= J.drop.inv;
           const int64_t p = p0 + 8 * (4 * g + v) + t;
           const int j = jt * 16 + i16;
-          if (p < J.P && j < r) base[p * r + j] = s;
+          // partials in the output's own layout, so the reduce reads them
+          // contiguously
+          if (p < J.P && j < r) base[J.transposed ? (int64_t)j * J.P + p : p * r + j] = s;
         }
     }
     __syncthreads();
@@ -325,16 +531,54 @@ __device__ __forceinline__ void grad_reduce_elem(const GradJob& J, int r, int64_
     while (g + 1 < J.groups && p >= J.end[g]) ++g;
     if (j / J.gr != g) { J.out[idx] = 0.f; return; }
   }
-  float s = J.partial[p * r + j];
-  for (int k = 1; k < J.splits; ++k) s += J.partial[(int64_t)k * J.P * r + p * r + j];
+  float s = J.partial[idx];
+  for (int k = 1; k < J.splits; ++k) s += J.partial[(int64_t)k * J.P * r + idx];
   J.out[idx] = J.scale * s;
 }
 
+// Four consecutive elements of the [P][r] (untransposed, ungrouped) output
+// per thread: float4 loads of the partials, in slice order.
+__device__ __forceinline__ void grad_reduce_vec4(const GradJob& J, int r, int64_t idx4) {
+  const int64_t idx = 4 * idx4;
+  const int64_t stride = J.P * r;
+  if (idx >= stride) return;
+  if (idx + 4 > stride) {   // the last, partial group
+    for (int64_t e = idx; e < stride; ++e) grad_reduce_elem(J, r, e);
+    return;
+  }
+  float4 s = *reinterpret_cast<const float4*>(J.partial + idx);
+  for (int k = 1; k < J.splits; ++k) {
+    const float4 v = *reinterpret_cast<const float4*>(J.partial + (int64_t)k * stride + idx);
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  *reinterpret_cast<float4*>(J.out + idx) =
+      make_float4(J.scale * s.x, J.scale * s.y, J.scale * s.z, J.scale * s.w);
+}
+
+__device__ __host__ __forceinline__ bool grad_vec4(const GradJob& J, int r) {
+  // every slice's partials 16-byte aligned too
+  return J.groups == 0 && (J.P * r) % 4 == 0 &&
+         ((reinterpret_cast<uintptr_t>(J.out) | reinterpret_cast<uintptr_t>(J.partial)) & 15) == 0;
+}
+
+__device__ __host__ __forceinline__ int64_t grad_reduce_blocks(const GradJob& J, int r, bool vec) {
+  return ceil_div(vec ? ceil_div(J.P * r, 4) : J.P * r, 256);
+}
+
 __global__ __launch_bounds__(256) void k_lora_grad_reduce(GradJob j0, GradJob j1, int nj, int r) {
-  const int64_t b0 = ceil_div(j0.P * r, 256);
+  const bool v0 = grad_vec4(j0, r);
+  const int64_t b0 = grad_reduce_blocks(j0, r, v0);
   const int64_t b = blockIdx.x;
-  if (b < b0) { grad_reduce_elem(j0, r, b * 256 + threadIdx.x); return; }
-  if (nj > 1) grad_reduce_elem(j1, r, (b - b0) * 256 + threadIdx.x);
+  if (b < b0) {
+    if (v0) grad_reduce_vec4(j0, r, b * 256 + threadIdx.x);
+    else grad_reduce_elem(j0, r, b * 256 + threadIdx.x);
+    return;
+  }
+  if (nj > 1) {
+    const int64_t e = (b - b0) * 256 + threadIdx.x;
+    if (grad_vec4(j1, r)) grad_reduce_vec4(j1, r, e);
+    else grad_reduce_elem(j1, r, e);
+  }
 }
 
 template <int RT>
@@ -342,7 +586,7 @@ hipError_t skinny_rt(const SkinnyJob* jobs, int nj, int64_t M, int r, int r32, c
                      hipStream_t s) {
   int64_t blocks = 0;
   for (int i = 0; i < nj; ++i) blocks += ceil_div(skinny_rows(jobs[i], M), 16) * jobs[i].ks;
-  blocks += rc ? ceil_div(rc->N * rc->KB, sk_waves<RT>() * 64) : 0;
+  blocks += rc ? ceil_div(rc->N, kReconTile) * ceil_div(rc->KB, kReconTile) : 0;
   const ReconJob none{};
   bool drop = false;
   for (int i = 0; i < nj; ++i) drop |= jobs[i].drop.thr != 0;
@@ -350,6 +594,21 @@ hipError_t skinny_rt(const SkinnyJob* jobs, int nj, int64_t M, int r, int r32, c
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(sk_waves<RT>() * 64), 0, s,
                      jobs[0], nj > 1 ? jobs[1] : jobs[0], nj, M, r, r32, rc ? *rc : none,
                      rc ? 1 : 0);
+  return hipGetLastError();
+}
+
+template <int RT>
+hipError_t skinny2_rt(const SkinnyJob* jobs, int nj, int64_t M, int r, int r32,
+                      const ReconJob* rc, hipStream_t s) {
+  int64_t blocks = 0;
+  for (int i = 0; i < nj; ++i) blocks += ceil_div(skinny_rows(jobs[i], M), kSk2Rows) * jobs[i].ks;
+  blocks += rc ? ceil_div(rc->N, kReconTile) * ceil_div(rc->KB, kReconTile) : 0;
+  const ReconJob none{};
+  bool drop = false;
+  for (int i = 0; i < nj; ++i) drop |= jobs[i].drop.thr != 0;
+  const auto kern = drop ? k_skinny2<RT, true> : k_skinny2<RT, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kSk2Waves * 64), 0, s, jobs[0],
+                     nj > 1 ? jobs[1] : jobs[0], nj, M, r, r32, rc ? *rc : none, rc ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -369,7 +628,26 @@ hipError_t grads_rt(const GradJob* jobs, int nj, int64_t M, int r, hipStream_t s
 
 int skinny_rpad(int r) { return r <= 16 ? 16 : r <= 32 ? 32 : r <= 64 ? 64 : 128; }
 
-int skinny_slices(int64_t M, int64_t kin) {
+// The LDS-staged form: ranks 17..64, whole 64-wide steps, 16-byte rows.
+static bool skinny_staged(const SkinnyJob& j, int r) {
+  const int rp = skinny_rpad(r);
+  return (rp == 32 || rp == 64) && j.kin % kSk2Step == 0 && j.ldt % 8 == 0 &&
+         j.ldu % 8 == 0 && (reinterpret_cast<uintptr_t>(j.T) & 15) == 0 &&
+         (reinterpret_cast<uintptr_t>(j.U) & 15) == 0;
+}
+
+// Slices of the staged form: about 256 workgroups, at least 4 steps each.
+static int skinny2_slices(int64_t M, int64_t kin) {
+  const int64_t groups = ceil_div(M, kSk2Rows);
+  const int64_t steps = kin / kSk2Step;
+  int64_t ks = ceil_div(256, groups);
+  const int64_t maxs = steps / 4 > 0 ? steps / 4 : 1;
+  if (ks > maxs) ks = maxs;
+  if (ks < 1) ks = 1;
+  return (int)ks;
+}
+
+static int skinny1_slices(int64_t M, int64_t kin) {
   // one slice once there are enough row groups to spread over the chip (no
   // finish step then); else about 256 workgroups, at least one 128-wide
   // step per wave
@@ -384,28 +662,50 @@ int skinny_slices(int64_t M, int64_t kin) {
   return (int)ks;
 }
 
-size_t skinny_part_floats(int64_t M, int64_t kin, int r) {
-  return (size_t)skinny_slices(M, kin) * (size_t)M * (size_t)skinny_rpad(r);
+int skinny_slices(int64_t M, int64_t kin, int r) {
+  // the larger of the two forms' slice counts (workspace sizing)
+  const int rp = skinny_rpad(r);
+  const int s1 = skinny1_slices(M, kin);
+  const int s2 = (rp == 32 || rp == 64) && kin % kSk2Step == 0 ? skinny2_slices(M, kin) : 1;
+  return s1 > s2 ? s1 : s2;
 }
 
-void skinny_plan(SkinnyJob* j, int64_t M) {
-  const int ks = skinny_slices(M, j->kin);
-  // slice length a multiple of the wave step; every slice non-empty
-  j->kslice = ceil_div(ceil_div(j->kin, ks), kSkStep) * kSkStep;
+size_t skinny_part_floats(int64_t M, int64_t kin, int r) {
+  return (size_t)skinny_slices(M, kin, r) * (size_t)M * (size_t)skinny_rpad(r);
+}
+
+void skinny_plan(SkinnyJob* j, int64_t M, int r) {
+  j->staged = skinny_staged(*j, r) ? 1 : 0;
+  const int ks = j->staged ? skinny2_slices(M, j->kin) : skinny1_slices(M, j->kin);
+  // slice length a multiple of the step; every slice non-empty
+  const int64_t step = j->staged ? kSk2Step : kSkStep;
+  j->kslice = ceil_div(ceil_div(j->kin, ks), step) * step;
   j->ks = (int)ceil_div(j->kin, j->kslice);
 }
 
 hipError_t launch_skinny(const SkinnyJob* jobs, int nj, int64_t M, int r, int r32,
                          const ReconJob* recon, hipStream_t s) {
   const int rpad = skinny_rpad(r);
-  hipError_t e;
-  switch (rpad) {
-    case 16: e = skinny_rt<1>(jobs, nj, M, r, r32, recon, s); break;
-    case 32: e = skinny_rt<2>(jobs, nj, M, r, r32, recon, s); break;
-    case 64: e = skinny_rt<4>(jobs, nj, M, r, r32, recon, s); break;
-    default: e = skinny_rt<8>(jobs, nj, M, r, r32, recon, s); break;
+  // staged jobs in one launch (with the constant table), the rest in another
+  SkinnyJob st[2], pl[2];
+  int ns = 0, np = 0;
+  for (int i = 0; i < nj; ++i) (jobs[i].staged ? st[ns++] : pl[np++]) = jobs[i];
+  hipError_t e = hipSuccess;
+  if (ns > 0) {
+    e = rpad == 32 ? skinny2_rt<2>(st, ns, M, r, r32, recon, s)
+                   : skinny2_rt<4>(st, ns, M, r, r32, recon, s);
+    if (e != hipSuccess) return e;
+    recon = nullptr;
   }
-  if (e != hipSuccess) return e;
+  if (np > 0) {
+    switch (rpad) {
+      case 16: e = skinny_rt<1>(pl, np, M, r, r32, recon, s); break;
+      case 32: e = skinny_rt<2>(pl, np, M, r, r32, recon, s); break;
+      case 64: e = skinny_rt<4>(pl, np, M, r, r32, recon, s); break;
+      default: e = skinny_rt<8>(pl, np, M, r, r32, recon, s); break;
+    }
+    if (e != hipSuccess) return e;
+  }
   bool finish = false;
   for (int i = 0; i < nj; ++i) finish |= jobs[i].ks > 1;
   if (!finish) return hipSuccess;
@@ -418,8 +718,8 @@ hipError_t launch_skinny(const SkinnyJob* jobs, int nj, int64_t M, int r, int r3
 
 hipError_t launch_prep(const TransposeJob* t, int nt, const ReconJob* recon, hipStream_t s) {
   int64_t blocks = 0;
-  for (int i = 0; i < nt; ++i) blocks += ceil_div(t[i].cols * t[i].ldo, 256);
-  blocks += recon ? ceil_div(recon->N * recon->KB, 256) : 0;
+  for (int i = 0; i < nt; ++i) blocks += ceil_div(t[i].ldo, kTrTile) * ceil_div(t[i].cols, kTrTile);
+  blocks += recon ? ceil_div(recon->N, kReconTile) * ceil_div(recon->KB, kReconTile) : 0;
   if (blocks == 0) return hipSuccess;
   const TransposeJob tn{};
   const ReconJob rn{};
@@ -429,11 +729,11 @@ hipError_t launch_prep(const TransposeJob* t, int nt, const ReconJob* recon, hip
 }
 
 int lora_grad_splits(int64_t M, int64_t P) {
-  // about 512 workgroups over the chip, at least 256 tokens per split (two
-  // steps per wave)
+  // about 256 workgroups over the chip per job, at least 512 tokens per split
+  // (four steps per wave)
   const int64_t groups = ceil_div(P, 128);
-  int64_t splits = ceil_div(512, groups);
-  const int64_t maxs = ceil_div(M, 256);
+  int64_t splits = ceil_div(256, groups);
+  const int64_t maxs = ceil_div(M, 512);
   if (splits > maxs) splits = maxs;
   if (splits < 1) splits = 1;
   return (int)splits;
@@ -450,7 +750,7 @@ hipError_t launch_lora_grads(const GradJob* jobs, int nj, int64_t M, int r, hipS
   }
   if (e != hipSuccess) return e;
   int64_t blocks = 0;
-  for (int i = 0; i < nj; ++i) blocks += ceil_div(jobs[i].P * r, 256);
+  for (int i = 0; i < nj; ++i) blocks += grad_reduce_blocks(jobs[i], r, grad_vec4(jobs[i], r));
   hipLaunchKernelGGL(k_lora_grad_reduce, dim3((unsigned)blocks), dim3(256), 0, s, jobs[0],
                      nj > 1 ? jobs[1] : jobs[0], nj, r);
   return hipGetLastError();
