@@ -279,6 +279,19 @@ __global__ __launch_bounds__(256) void k_qlora_decode(DecodeArgs a, NF4Tables ta
   }
 }
 
+// src[0] + src[stride] + ... over the first min(count, 16) terms, in order,
+// with all of their loads issued first (count >= 1)
+__device__ __forceinline__ float sum_first16(const float* src, int64_t stride, int count) {
+  float w[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i] = i < count ? src[i * stride] : 0.f;
+  float v = w[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i)
+    if (i < count) v += w[i];
+  return v;
+}
+
 // Y[m][n] = bf16( sum_split partial + sum_j bf16(s XA[m][j]) B[n][j] ), with
 // XA the slice sum of the down-projection.  Workgroup (n block, token m):
 // first the r values of XA[m] (slices added in order, loads unrolled), then
@@ -296,8 +309,8 @@ __global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__
   if (t < r) {
     const float* src = xa_part + m * rpad + t;
     const int64_t stride = M * rpad;
-    float v = src[0];
-    int k = 1;
+    float v = sum_first16(src, stride, ks);
+    int k = 16;
     for (; k + 8 <= ks; k += 8) {
       float w[8];
 #pragma unroll
@@ -315,8 +328,8 @@ __global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__
   if (n >= N) return;
   const float* src = partial + m * N + n;
   const int64_t stride = M * N;
-  float y = src[0];
-  int k = 1;
+  float y = sum_first16(src, stride, splits);
+  int k = 16;
   for (; k + 8 <= splits; k += 8) {
     float w[8];
 #pragma unroll
@@ -361,10 +374,17 @@ int decode_xa_slices(int64_t K) {
   return (int)ceil_div(K, (int64_t)kXaWaves * kSkStep);
 }
 
+bool decode_needs_consts(int64_t K, bool f32_consts) {
+  (void)K;
+  (void)f32_consts;
+  return false;   // the streamers read the int8 constants of any row length
+}
+
 hipError_t launch_decode(const uint16_t* X, int64_t M, int64_t K, const NF4Ref& W, int64_t N,
                          const uint16_t* A, const uint16_t* B, int r, float scale, int splits,
-                         float* partial, float* xa_part, uint16_t* Y, uint16_t* XA_out,
-                         const DropoutParams& drop, hipStream_t s) {
+                         float* partial, float* xa_part, float* consts, uint16_t* Y,
+                         uint16_t* XA_out, const DropoutParams& drop, hipStream_t s) {
+  (void)consts;
   const int64_t KB = K / kBlock;
   DecodeArgs a{};
   a.X = X; a.M = M; a.K = K; a.N = N;
