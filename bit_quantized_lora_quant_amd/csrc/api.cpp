@@ -88,7 +88,6 @@ struct LinearWs {
   size_t ahat_t, xas, gemv_part, bt, gs, gt, xat, part_a, part_b, gemm_part;
   size_t sk_k, sk_n;          // skinny-product slice partials (inner dim K / N)
   size_t dec_xa;              // decode: down-projection slice partials
-  size_t dec_consts;          // decode: float32 constants (rows of K/64 not a word multiple)
   size_t total;
 };
 
@@ -120,9 +119,6 @@ LinearWs linear_layout(int64_t M, int64_t N, int64_t K, int r) {
   w.dec_xa = off;
   if (M <= 16)
     off = align_up(off + (size_t)decode_xa_slices(K) * M * skinny_rpad(r) * sizeof(float));
-  w.dec_consts = off;
-  if (M <= 16 && decode_needs_consts(K, false))
-    off = align_up(off + (size_t)(K / kBlock) * N * sizeof(float));
   w.total = off;
   return w;
 }
@@ -341,8 +337,8 @@ qlora_status qlora_linear_fwd_dropout(const qlora_nf4_tensor* W, const qlora_bf1
     float* part = at<float>(ws, L.gemv_part);
     float* xa_part = at<float>(ws, L.dec_xa);
     e = traced(QLORA_KERNEL_GEMV, s, [&] {
-      return launch_decode(X, M, K, w, N, A, B, r, scale, L.gemv_splits, part, xa_part,
-                           at<float>(ws, L.dec_consts), Y, XA_out, dp, s);
+      return launch_decode(X, M, K, w, N, A, B, r, scale, L.gemv_splits, part, xa_part, Y,
+                           XA_out, dp, s);
     });
     return hip_status(e);
   }

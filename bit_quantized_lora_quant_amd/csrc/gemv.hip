@@ -374,22 +374,13 @@ int decode_xa_slices(int64_t K) {
   return (int)ceil_div(K, (int64_t)kXaWaves * kSkStep);
 }
 
-bool decode_needs_consts(int64_t K, bool f32_consts) {
-  (void)K;
-  (void)f32_consts;
-  return false;   // the streamers read the int8 constants of any row length
-}
-
 hipError_t launch_decode(const uint16_t* X, int64_t M, int64_t K, const NF4Ref& W, int64_t N,
                          const uint16_t* A, const uint16_t* B, int r, float scale, int splits,
-                         float* partial, float* xa_part, float* consts, uint16_t* Y,
-                         uint16_t* XA_out, const DropoutParams& drop, hipStream_t s) {
-  (void)consts;
-  const int64_t KB = K / kBlock;
+                         float* partial, float* xa_part, uint16_t* Y, uint16_t* XA_out,
+                         const DropoutParams& drop, hipStream_t s) {
   DecodeArgs a{};
   a.X = X; a.M = M; a.K = K; a.N = N;
   a.codes = W.codes; a.q = W.q; a.scale = W.scale; a.mean = W.mean; a.f32 = W.f32;
-  (void)KB;
   a.splits = splits;
   a.partial = partial;
   const int rpad = skinny_rpad(r);

@@ -150,13 +150,10 @@ struct NF4Ref {
 };
 int gemv_splits(int64_t N, int64_t K);
 int decode_xa_slices(int64_t K);
-// whether the decode needs the float32 constant table [N][K/64] (`consts`):
-// double-quantised constants whose rows are not a whole number of 4-byte words
-bool decode_needs_consts(int64_t K, bool f32_consts);
 hipError_t launch_decode(const uint16_t* X, int64_t M, int64_t K, const NF4Ref& W, int64_t N,
                          const uint16_t* A, const uint16_t* B, int r, float scale, int splits,
-                         float* partial, float* xa_part, float* consts, uint16_t* Y,
-                         uint16_t* XA_out, const DropoutParams& drop, hipStream_t s);
+                         float* partial, float* xa_part, uint16_t* Y, uint16_t* XA_out,
+                         const DropoutParams& drop, hipStream_t s);
 
 // merged[n][k] += s * sum_j B[n][j] A[j][k] (float32, j in order, fused
 // multiply-add per term), merged [N, K] float32, A [r, K], B [N, r] bf16
