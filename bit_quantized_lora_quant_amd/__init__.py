@@ -25,7 +25,8 @@ EXPORTS = [
     "qlora_nf4_codebook", "qlora_codebook", "qlora_status_string",
     "qlora_quantize_workspace_bytes",
     "qlora_quantize_nf4", "qlora_quantize_nf4_noalloc", "qlora_dequantize_nf4",
-    "qlora_dequantize_absmax",
+    "qlora_dequantize_absmax", "qlora_quantize_batch_workspace_bytes",
+    "qlora_quantize_nf4_batch", "qlora_dequantize_nf4_batch",
     "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout", "qlora_dropout_mask",
     "qlora_adamw_step", "qlora_adamw8_step", "qlora_host_state_alloc", "qlora_host_state_free",
@@ -102,6 +103,10 @@ def lib():
         L.qlora_quantize_nf4_noalloc.argtypes = [P, D, P]
         L.qlora_dequantize_nf4.argtypes = [D, ctypes.c_int, P, P]
         L.qlora_dequantize_absmax.argtypes = [D, P, P]
+        L.qlora_quantize_batch_workspace_bytes.argtypes = [P, P, I32]
+        L.qlora_quantize_batch_workspace_bytes.restype = SZ
+        L.qlora_quantize_nf4_batch.argtypes = [P, P, I32, P, SZ, P]
+        L.qlora_dequantize_nf4_batch.argtypes = [P, I32, ctypes.c_int, P, P]
         L.qlora_linear_workspace_bytes.argtypes = [I64, I64, I64, I32]
         L.qlora_linear_workspace_bytes.restype = SZ
         L.qlora_linear_fwd.argtypes = [D, P, I64, P, P, I32, F, P, P, P, SZ, P]
@@ -243,6 +248,51 @@ def qlora_dequantize_nf4(q: NF4Tensor, dtype=torch.bfloat16, out: torch.Tensor =
     _check(lib().qlora_dequantize_nf4(ctypes.byref(d), code, _ptr(out), _stream()),
            "qlora_dequantize_nf4")
     return out
+
+
+def qlora_quantize_batch_workspace_bytes(shapes) -> int:
+    """Workspace bytes for qlora_quantize_nf4_batch over (rows, cols) pairs."""
+    shapes = list(shapes)
+    rows = (ctypes.c_int64 * max(len(shapes), 1))(*[r for r, _ in shapes])
+    cols = (ctypes.c_int64 * max(len(shapes), 1))(*[c for _, c in shapes])
+    return int(lib().qlora_quantize_batch_workspace_bytes(rows, cols, len(shapes)))
+
+
+def qlora_quantize_nf4_batch(Ws, qs, ws: torch.Tensor = None):
+    """Quantise float32 [rows, cols] device tensors Ws[i] into the NF4Tensors
+    qs[i], up to 32 tensors per launch; returns the workspace."""
+    Ws, qs = list(Ws), list(qs)
+    assert len(Ws) == len(qs)
+    for W, q in zip(Ws, qs):
+        assert W.dtype == torch.float32 and W.is_contiguous() and W.dim() == 2
+        assert tuple(W.shape) == (q.rows, q.cols)
+    if ws is None:
+        need = qlora_quantize_batch_workspace_bytes([(q.rows, q.cols) for q in qs])
+        ws = workspace(need, Ws[0].device if Ws else "cpu")
+    n = len(qs)
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[_ptr(W) for W in Ws])
+    descs = (NF4Descriptor * max(n, 1))(*[q.descriptor() for q in qs])
+    _check(lib().qlora_quantize_nf4_batch(ptrs, descs, n, _ptr(ws), ws.numel(), _stream()),
+           "qlora_quantize_nf4_batch")
+    return ws
+
+
+def qlora_dequantize_nf4_batch(qs, outs):
+    """Dequantise NF4Tensors qs[i] into contiguous device tensors outs[i]
+    (all bf16 or all float32), up to 32 tensors per launch."""
+    qs, outs = list(qs), list(outs)
+    assert len(qs) == len(outs)
+    dt = outs[0].dtype if outs else torch.bfloat16
+    for q, o in zip(qs, outs):
+        assert o.dtype == dt and dt in (torch.bfloat16, torch.float32) and o.is_contiguous()
+        assert o.numel() == q.numel
+    n = len(qs)
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[_ptr(o) for o in outs])
+    descs = (NF4Descriptor * max(n, 1))(*[q.descriptor() for q in qs])
+    code = QLORA_BF16 if dt == torch.bfloat16 else QLORA_F32
+    _check(lib().qlora_dequantize_nf4_batch(descs, n, code, ptrs, _stream()),
+           "qlora_dequantize_nf4_batch")
+    return outs
 
 
 def qlora_dequantize_absmax(q: NF4Tensor, out: torch.Tensor = None):

@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cmath>
 #include <cstring>
+#include <vector>
 
 #include "../../include/qlora_nf4.h"
 #include "launch.h"
@@ -239,18 +240,74 @@ size_t qlora_quantize_workspace_bytes(int64_t rows, int64_t cols) {
   return quant_layout(rows * cols).total;
 }
 
-// Launch sequence of the quantiser on a workspace the caller has checked.
-static qlora_status quantize_on(const float* W, const qlora_nf4_tensor* q, void* ws,
-                                const QuantWs& L, hipStream_t s);
+// The quantiser's view of a descriptor, with its scratch at ws (layout L).
+static QuantTensor quant_tensor(const float* W, const qlora_nf4_tensor* q, void* ws,
+                                const QuantWs& L) {
+  QuantTensor t{};
+  t.w = W;
+  t.n = q->rows * q->cols;
+  t.kind = q->quant_type;
+  t.codes = q->codes;
+  if (q->dq_block == 0) {
+    t.absmax = q->absmax;          // without double quantisation the exact absmax is stored
+  } else {
+    t.absmax = at<float>(ws, L.absmax);
+    t.q = q->absmax_q;
+    t.scale = q->absmax_scale;
+    t.mean = q->absmax_mean;
+    t.pa = at<double>(ws, L.pa);
+    t.pb = at<double>(ws, L.pb);
+  }
+  return t;
+}
+
+static DequantTensor dequant_tensor(const qlora_nf4_tensor* q, void* out) {
+  return DequantTensor{q->codes, q->absmax_q, q->absmax_scale, q->absmax_mean, f32_consts(q),
+                       q->rows * q->cols, q->quant_type, out};
+}
+
+// Launch sequence of the quantiser on tensors whose arguments and workspace
+// the caller has checked: per group of kQuantBatch tensors, the codes in one
+// launch, then the second-level constants.
+static qlora_status quantize_on(const QuantTensor* t, int64_t count, hipStream_t s) {
+  for (int64_t i = 0; i < count; i += kQuantBatch) {
+    const int m = (int)std::min<int64_t>(kQuantBatch, count - i);
+    hipError_t e = traced(QLORA_KERNEL_QUANTIZE, s, [&] { return launch_quant_codes(t + i, m, s); });
+    if (e == hipSuccess) e = launch_quant_consts(t + i, m, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return QLORA_OK;
+}
+
+// Dequantiser launches: tensors with float32 constants and with the 8-bit
+// state in separate groups (the constant source is a kernel template switch).
+static qlora_status dequantize_on(const qlora_nf4_tensor* q, int64_t count, bool bf16,
+                                  void* const* out, hipStream_t s) {
+  DequantTensor group[kQuantBatch];
+  for (int f32 = 0; f32 < 2; ++f32) {
+    int m = 0;
+    for (int64_t i = 0; i <= count; ++i) {
+      if (i < count && (f32_consts(&q[i]) != nullptr) == (f32 == 1))
+        group[m++] = dequant_tensor(&q[i], out[i]);
+      if (m > 0 && (m == kQuantBatch || i == count)) {
+        const hipError_t e = traced(QLORA_KERNEL_DEQUANT, s,
+                                    [&] { return launch_dequantize(group, m, bf16, s); });
+        if (e != hipSuccess) return hip_status(e);
+        m = 0;
+      }
+    }
+  }
+  return QLORA_OK;
+}
 
 qlora_status qlora_quantize_nf4(const float* W, const qlora_nf4_tensor* q, void* ws,
                                 size_t ws_bytes, void* stream) {
   if (!W || !valid_tensor(q) || !aligned(W, 16)) return QLORA_ERR_INVALID_ARG;
   if (!tensor_fits(q)) return QLORA_ERR_UNSUPPORTED;
-  const int64_t n = q->rows * q->cols;
-  const QuantWs L = quant_layout(n);
+  const QuantWs L = quant_layout(q->rows * q->cols);
   if (!ws || ws_bytes < L.total || !aligned(ws, kAlign)) return QLORA_ERR_WORKSPACE;
-  return quantize_on(W, q, ws, L, static_cast<hipStream_t>(stream));
+  const QuantTensor t = quant_tensor(W, q, ws, L);
+  return quantize_on(&t, 1, static_cast<hipStream_t>(stream));
 }
 
 qlora_status qlora_quantize_nf4_noalloc(const float* W, const qlora_nf4_tensor* q,
@@ -263,21 +320,40 @@ qlora_status qlora_quantize_nf4_noalloc(const float* W, const qlora_nf4_tensor* 
   if (L.total > quant_scratch_bytes()) return QLORA_ERR_UNSUPPORTED;
   void* ws = nullptr;
   if (quant_scratch(&ws) != hipSuccess) return QLORA_ERR_HIP;
-  return quantize_on(W, q, ws, L, static_cast<hipStream_t>(stream));
+  const QuantTensor t = quant_tensor(W, q, ws, L);
+  return quantize_on(&t, 1, static_cast<hipStream_t>(stream));
 }
 
-static qlora_status quantize_on(const float* W, const qlora_nf4_tensor* q, void* ws,
-                                const QuantWs& L, hipStream_t s) {
-  const int64_t n = q->rows * q->cols;
-  // without double quantisation the exact absmax is the stored constant
-  float* absmax = q->dq_block == 0 ? q->absmax : at<float>(ws, L.absmax);
-  hipError_t e = traced(QLORA_KERNEL_QUANTIZE, s, [&] {
-    return launch_quant_absmax(W, n, q->codes, absmax, q->quant_type, s);
-  });
-  if (e != hipSuccess || q->dq_block == 0) return hip_status(e);
-  e = launch_dq(absmax, nblocks(n), q->absmax_q, q->absmax_scale, q->absmax_mean,
-                at<double>(ws, L.pa), at<double>(ws, L.pb), s);
-  return hip_status(e);
+size_t qlora_quantize_batch_workspace_bytes(const int64_t* rows, const int64_t* cols,
+                                            int32_t count) {
+  if (count < 0 || (count > 0 && (!rows || !cols))) return 0;
+  size_t total = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    if (rows[i] < 1 || cols[i] < 1 || !below(rows[i], cols[i], kMaxWeights + 1)) return 0;
+    total += quant_layout(rows[i] * cols[i]).total;
+  }
+  return total;
+}
+
+qlora_status qlora_quantize_nf4_batch(const float* const* W, const qlora_nf4_tensor* q,
+                                      int32_t count, void* ws, size_t ws_bytes, void* stream) {
+  if (count < 0 || (count > 0 && (!W || !q))) return QLORA_ERR_INVALID_ARG;
+  size_t need = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    if (!W[i] || !valid_tensor(&q[i]) || !aligned(W[i], 16)) return QLORA_ERR_INVALID_ARG;
+    if (!tensor_fits(&q[i])) return QLORA_ERR_UNSUPPORTED;
+    need += quant_layout(q[i].rows * q[i].cols).total;
+  }
+  if (count == 0) return QLORA_OK;
+  if (!ws || ws_bytes < need || !aligned(ws, kAlign)) return QLORA_ERR_WORKSPACE;
+  std::vector<QuantTensor> t((size_t)count);
+  size_t off = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const QuantWs L = quant_layout(q[i].rows * q[i].cols);
+    t[i] = quant_tensor(W[i], &q[i], at<uint8_t>(ws, off), L);
+    off += L.total;
+  }
+  return quantize_on(t.data(), count, static_cast<hipStream_t>(stream));
 }
 
 qlora_status qlora_dequantize_nf4(const qlora_nf4_tensor* q, qlora_dtype out_dtype, void* out,
@@ -285,11 +361,18 @@ qlora_status qlora_dequantize_nf4(const qlora_nf4_tensor* q, qlora_dtype out_dty
   if (!valid_tensor(q) || !out || !aligned(out, 16)) return QLORA_ERR_INVALID_ARG;
   if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16) return QLORA_ERR_INVALID_ARG;
   if (!tensor_fits(q)) return QLORA_ERR_UNSUPPORTED;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(traced(QLORA_KERNEL_DEQUANT, s, [&] {
-    return launch_dequant(q->codes, q->absmax_q, q->absmax_scale, q->absmax_mean, f32_consts(q),
-                          q->rows * q->cols, out_dtype == QLORA_BF16, out, q->quant_type, s);
-  }));
+  return dequantize_on(q, 1, out_dtype == QLORA_BF16, &out, static_cast<hipStream_t>(stream));
+}
+
+qlora_status qlora_dequantize_nf4_batch(const qlora_nf4_tensor* q, int32_t count,
+                                        qlora_dtype out_dtype, void* const* out, void* stream) {
+  if (count < 0 || (count > 0 && (!q || !out))) return QLORA_ERR_INVALID_ARG;
+  if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16) return QLORA_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < count; ++i) {
+    if (!valid_tensor(&q[i]) || !out[i] || !aligned(out[i], 16)) return QLORA_ERR_INVALID_ARG;
+    if (!tensor_fits(&q[i])) return QLORA_ERR_UNSUPPORTED;
+  }
+  return dequantize_on(q, count, out_dtype == QLORA_BF16, out, static_cast<hipStream_t>(stream));
 }
 
 qlora_status qlora_dequantize_absmax(const qlora_nf4_tensor* q, float* out, void* stream) {
@@ -540,15 +623,13 @@ qlora_status qlora_merge_requantize(const qlora_nf4_tensor* W, const qlora_bf16*
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* mbuf = merged ? merged : at<float>(ws, 0);
   void* qws = at<uint8_t>(ws, moff);
-  hipError_t e = launch_dequant(W->codes, W->absmax_q, W->absmax_scale, W->absmax_mean,
-                                f32_consts(W), n, 0, mbuf, W->quant_type, s);
+  const DequantTensor d = dequant_tensor(W, mbuf);
+  hipError_t e = launch_dequantize(&d, 1, 0, s);
   if (e == hipSuccess) e = launch_merge_lora_add(mbuf, N, K, A, B, r, alpha / (float)r, s);
   if (e != hipSuccess) return QLORA_ERR_HIP;
-  float* absmax = out->dq_block == 0 ? out->absmax : at<float>(qws, Q.absmax);
-  e = launch_quant_absmax(mbuf, n, out->codes, absmax, out->quant_type, s);
-  if (e == hipSuccess && out->dq_block != 0)
-    e = launch_dq(absmax, nblocks(n), out->absmax_q, out->absmax_scale, out->absmax_mean,
-                  at<double>(qws, Q.pa), at<double>(qws, Q.pb), s);
+  const QuantTensor t = quant_tensor(mbuf, out, qws, Q);
+  e = launch_quant_codes(&t, 1, s);
+  if (e == hipSuccess) e = launch_quant_consts(&t, 1, s);
   return hip_status(e);
 }
 

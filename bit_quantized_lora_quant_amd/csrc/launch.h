@@ -10,15 +10,47 @@ namespace qnf4 {
 // ---------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  All pointers are device.
 
-// kind: kQuantNf4 or kQuantInt4.  f32 (nullable): float32 block constants in
-// place of the double-quantised state (q, scale and mean then unused).
-hipError_t launch_quant_absmax(const float* w, int64_t n, uint8_t* codes, float* absmax,
-                               int kind, hipStream_t s);
-hipError_t launch_dq(const float* absmax, int64_t nb, int8_t* q, float* scale, float* mean,
-                     double* partial_a, double* partial_b, hipStream_t s);
-hipError_t launch_dequant(const uint8_t* codes, const int8_t* q, const float* scale,
-                          const float* mean, const float* f32, int64_t n, int out_bf16,
-                          void* out, int kind, hipStream_t s);
+// The quantiser and dequantiser take up to kQuantBatch tensors per launch
+// (kernel-argument arrays).
+constexpr int kQuantBatch = 32;
+
+// One tensor to quantise.  kind: kQuantNf4 or kQuantInt4.  absmax receives
+// the exact block constants (the stored float32 constants when q is null,
+// i.e. without double quantisation; else scratch of nb floats).  With double
+// quantisation, pa and pb hold the mean tree's float64 partials: at least
+// ceil(nb / 2048) and ceil(nb / 2048^2) values.
+struct QuantTensor {
+  const float* w;
+  int64_t n;
+  int kind;
+  uint8_t* codes;
+  float* absmax;
+  int8_t* q;        // null: no second level (scale, mean, pa, pb unused)
+  float* scale;
+  float* mean;
+  double* pa;
+  double* pb;
+};
+// Codes and exact absmax of count tensors, one launch.
+hipError_t launch_quant_codes(const QuantTensor* t, int count, hipStream_t s);
+// Mean tree (one launch per level) and second-level constants (one launch)
+// of the tensors with double quantisation, after launch_quant_codes.
+hipError_t launch_quant_consts(const QuantTensor* t, int count, hipStream_t s);
+
+// One tensor to dequantise; f32 (nullable): float32 block constants in place
+// of the double-quantised state (q, scale and mean then unused).  All tensors
+// of one launch have f32 set, or none has.
+struct DequantTensor {
+  const uint8_t* codes;
+  const int8_t* q;
+  const float* scale;
+  const float* mean;
+  const float* f32;
+  int64_t n;
+  int kind;
+  void* out;
+};
+hipError_t launch_dequantize(const DequantTensor* t, int count, int out_bf16, hipStream_t s);
 // The quantiser's allocation-free scratch on the current device: its size,
 // and its device address (looked up once per device).
 size_t quant_scratch_bytes();

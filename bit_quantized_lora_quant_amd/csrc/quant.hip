@@ -9,6 +9,7 @@
 // Arithmetic that decides a code or a constant is IEEE float32 with round to
 // nearest even (this file is built with -ffp-contract=off); the one fused
 // operation is the explicit fmaf that rebuilds a constant.
+#include <cstring>
 #include <mutex>
 
 #include "launch.h"
@@ -69,19 +70,56 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
-__global__ __launch_bounds__(kThreads) void k_quant_absmax_nf4(const float* __restrict__ w,
-                                                               int64_t n, NF4Tables tab,
-                                                               uint8_t* __restrict__ codes,
-                                                               float* __restrict__ absmax) {
-  __shared__ Bucket buckets[256];
-  build_buckets(buckets, tab);
+// Job lookup in a batched launch: first[j] is the first work item of job j
+// in the launch's item space (first[0] = 0, first[count] = all items).  The
+// item is wave-uniform, so the search runs on scalar loads of the kernel
+// arguments.
+__device__ __forceinline__ int job_of(const int64_t* first, int count, int64_t item) {
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (first[mid] <= item) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Up to kQuantBatch tensors share a launch: the 1024-weight chunks of all of
+// them form one grid-stride space, so small tensors cost no launch of their
+// own.
+struct QuantJob {
+  const float* w;
+  uint8_t* codes;
+  float* absmax;
+  int64_t n;
+  int kind;
+};
+struct QuantBatch {
+  QuantJob job[kQuantBatch];
+  int64_t first[kQuantBatch + 1];   // first chunk of each tensor
+  int count;
+  NF4Tables tab[2];                 // by kind
+};
+
+__global__ __launch_bounds__(kThreads) void k_quant_absmax_nf4(const QuantBatch b) {
+  __shared__ Bucket buckets[2][256];
+  build_buckets(buckets[0], b.tab[0]);
+  build_buckets(buckets[1], b.tab[1]);
   __syncthreads();
   const int lane = threadIdx.x & 63;
-  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-  const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
-  const int64_t nchunks = ceil_div(n, kQChunk);
-  for (int64_t c = wave; c < nchunks; c += nwaves) {
-    const int64_t base = c * kQChunk;
+  const int64_t wave =
+      (int64_t)blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
+  const int64_t total = b.first[b.count];
+  int j = 0;
+  for (int64_t c = wave; c < total; c += nwaves) {
+    while (c >= b.first[j + 1]) ++j;       // chunks ascend, so the job index only grows
+    const float* __restrict__ w = b.job[j].w;
+    uint8_t* __restrict__ codes = b.job[j].codes;
+    float* __restrict__ absmax = b.job[j].absmax;
+    const int64_t n = b.job[j].n;
+    const Bucket* __restrict__ bk = buckets[b.job[j].kind];
+    const int64_t base = (c - b.first[j]) * kQChunk;
     const bool full = base + kQChunk <= n;
     float v[4][4];
     if (full) {
@@ -110,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_absmax_nf4(const float* __re
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float x = (a == 0.0f) ? 0.0f : v[i][e] / a;
-        packed |= nf4_code(x, buckets) << (4 * e);
+        packed |= nf4_code(x, bk) << (4 * e);
       }
       if (full) {
         *reinterpret_cast<uint16_t*>(codes + (e0 >> 1)) = (uint16_t)packed;
@@ -145,13 +183,28 @@ __device__ __forceinline__ double shfl_xor_f64(double v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// One tree level of several tensors in one launch: a workgroup per chunk.
+struct TreeJob {
+  const void* in;     // float constants (first level) or float64 partials
+  int64_t cnt;
+  double* out;        // one sum per chunk
+  float* mean;        // non-null on the level that leaves one value
+  int64_t mean_count;
+};
+struct TreeBatch {
+  TreeJob job[kQuantBatch];
+  int64_t first[kQuantBatch + 1];   // first chunk of each tensor
+  int count;
+};
+
 template <typename InT>
-__global__ __launch_bounds__(kThreads) void k_tree_sum(const InT* __restrict__ in, int64_t cnt,
-                                                       double* __restrict__ out,
-                                                       float* __restrict__ mean_out,
-                                                       int64_t mean_count) {
+__global__ __launch_bounds__(kThreads) void k_tree_sum(const TreeBatch b) {
   __shared__ double wave_sum[4];
-  const int64_t base = (int64_t)blockIdx.x * kTreeChunk + threadIdx.x * 8;
+  const int j = job_of(b.first, b.count, blockIdx.x);
+  const InT* __restrict__ in = static_cast<const InT*>(b.job[j].in);
+  const int64_t cnt = b.job[j].cnt;
+  const int64_t chunk = (int64_t)blockIdx.x - b.first[j];
+  const int64_t base = chunk * kTreeChunk + threadIdx.x * 8;
   double v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = (base + i < cnt) ? (double)in[base + i] : 0.0;
@@ -164,23 +217,39 @@ __global__ __launch_bounds__(kThreads) void k_tree_sum(const InT* __restrict__ i
   __syncthreads();
   if (threadIdx.x == 0) {
     const double t = (wave_sum[0] + wave_sum[1]) + (wave_sum[2] + wave_sum[3]);
-    out[blockIdx.x] = t;
-    if (mean_out) *mean_out = (float)(t / (double)mean_count);
+    b.job[j].out[chunk] = t;
+    if (b.job[j].mean) *b.job[j].mean = (float)(t / (double)b.job[j].mean_count);
   }
 }
 
 // -------------------------------------------------- second-level constants
 // One wave per 256 constants (4 per lane): deviation from the mean, wave max
 // of |d|, scale = max / 127, q = clamp(rint(d / scale), +-127).
-__global__ __launch_bounds__(kThreads) void k_dq_blocks(const float* __restrict__ absmax,
-                                                        int64_t nb,
-                                                        const float* __restrict__ mean,
-                                                        int8_t* __restrict__ q,
-                                                        float* __restrict__ scale) {
-  const int64_t dqb = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+struct DqJob {
+  const float* absmax;
+  int64_t nb;
+  const float* mean;
+  int8_t* q;
+  float* scale;
+};
+struct DqBatch {
+  DqJob job[kQuantBatch];
+  int64_t first[kQuantBatch + 1];   // first 256-constant block of each tensor
+  int count;
+};
+
+__global__ __launch_bounds__(kThreads) void k_dq_blocks(const DqBatch b) {
+  const int64_t item =
+      (int64_t)blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (item >= b.first[b.count]) return;            // whole waves only
+  const int j = job_of(b.first, b.count, item);
+  const float* __restrict__ absmax = b.job[j].absmax;
+  const int64_t nb = b.job[j].nb;
+  int8_t* __restrict__ q = b.job[j].q;
+  const int64_t dqb = item - b.first[j];
   const int lane = threadIdx.x & 63;
   const int64_t b0 = dqb * kDqBlock + lane * 4;
-  const float mu = *mean;
+  const float mu = *b.job[j].mean;
   float d[4];
   float m = 0.0f;
 #pragma unroll
@@ -190,9 +259,8 @@ __global__ __launch_bounds__(kThreads) void k_dq_blocks(const float* __restrict_
   }
 #pragma unroll
   for (int dd = 1; dd < 64; dd <<= 1) m = fmaxf(m, __shfl_xor(m, dd, 64));
-  if (dqb * kDqBlock >= nb) return;
   const float S = m / 127.0f;
-  if (lane == 0) scale[dqb] = S;
+  if (lane == 0) b.job[j].scale[dqb] = S;
   uint32_t packed = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -219,24 +287,45 @@ constexpr int kDqChunk = 2048;
 // F32: float32 block constants (no double quantisation); a template switch,
 // since a per-load choice between the two constant sources makes the
 // compiler wait for each chunk's loads before the next chunk's.
+struct DeqJob {
+  const uint8_t* codes;
+  const int8_t* q;
+  const float* scale;
+  const float* mean;
+  const float* f32;
+  void* out;
+  int64_t n;
+  int kind;
+};
+struct DeqBatch {
+  DeqJob job[kQuantBatch];
+  int64_t first[kQuantBatch + 1];   // first 2048-weight chunk of each tensor
+  int count;
+  float level[2][16];               // by kind
+};
+
 template <bool BF16, bool F32>
-__global__ __launch_bounds__(kThreads) void k_dequant_nf4(const uint8_t* __restrict__ codes,
-                                                          const int8_t* __restrict__ q,
-                                                          const float* __restrict__ scale,
-                                                          const float* __restrict__ mean,
-                                                          const float* __restrict__ f32,
-                                                          int64_t n, NF4Tables tab,
-                                                          void* __restrict__ out) {
-  __shared__ float lvl[16];
-  if (threadIdx.x < 16) lvl[threadIdx.x] = tab.level[threadIdx.x];
+__global__ __launch_bounds__(kThreads) void k_dequant_nf4(const DeqBatch b) {
+  __shared__ float lvl[2][16];
+  if (threadIdx.x < 32) lvl[threadIdx.x >> 4][threadIdx.x & 15] = b.level[threadIdx.x >> 4][threadIdx.x & 15];
   __syncthreads();
   const int lane = threadIdx.x & 63;
-  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-  const int64_t nwaves = ((int64_t)gridDim.x * kThreads) >> 6;
-  const int64_t nchunks = ceil_div(n, kDqChunk);
-  const float mu = F32 ? 0.0f : *mean;
-  for (int64_t c = wave; c < nchunks; c += nwaves) {
-    const int64_t base = c * kDqChunk;
+  const int64_t wave =
+      (int64_t)blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
+  const int64_t total = b.first[b.count];
+  int j = 0;
+  for (int64_t c = wave; c < total; c += nwaves) {
+    while (c >= b.first[j + 1]) ++j;       // chunks ascend, so the job index only grows
+    const uint8_t* __restrict__ codes = b.job[j].codes;
+    const int8_t* __restrict__ q = b.job[j].q;
+    const float* __restrict__ scale = b.job[j].scale;
+    const float* __restrict__ f32 = b.job[j].f32;
+    void* __restrict__ out = b.job[j].out;
+    const int64_t n = b.job[j].n;
+    const float* __restrict__ tl = lvl[b.job[j].kind];
+    const float mu = F32 ? 0.0f : *b.job[j].mean;
+    const int64_t base = (c - b.first[j]) * kDqChunk;
     const bool full = base + kDqChunk <= n;
     uint32_t cw[4];
     float a[4];
@@ -259,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_nf4(const uint8_t* __restr
       const int64_t e0 = base + 512 * i + 8 * lane;
       float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = lvl[(cw[i] >> (4 * e)) & 15u] * a[i];
+      for (int e = 0; e < 8; ++e) v[e] = tl[(cw[i] >> (4 * e)) & 15u] * a[i];
       if (full || e0 + 8 <= n) {
         if (BF16) {
           uint4 p;
@@ -339,43 +428,93 @@ static int64_t stream_grid(int64_t chunks) {
   return ceil_div(waves > 0 ? waves : 1, kThreads / 64);
 }
 
-hipError_t launch_quant_absmax(const float* w, int64_t n, uint8_t* codes, float* absmax,
-                               int kind, hipStream_t s) {
-  const NF4Tables& tab = host_tables(kind);
-  if (!tab.bucket_ok) return hipErrorInvalidValue;
-  return launch_kernel(k_quant_absmax_nf4, dim3((unsigned)stream_grid(ceil_div(n, kQChunk))),
-                       dim3(kThreads), s, w, n, tab, codes, absmax);
-}
-
-hipError_t launch_dq(const float* absmax, int64_t nb, int8_t* q, float* scale, float* mean,
-                     double* pa, double* pb, hipStream_t s) {
-  // first pass over the float constants, then over float64 partials
-  int64_t cnt = ceil_div(nb, kTreeChunk);
-  hipLaunchKernelGGL(k_tree_sum<float>, dim3((unsigned)cnt), dim3(kThreads), 0, s, absmax, nb, pa,
-                     cnt == 1 ? mean : nullptr, nb);
-  double* src = pa;
-  double* dst = pb;
-  while (cnt > 1) {
-    const int64_t next = ceil_div(cnt, kTreeChunk);
-    hipLaunchKernelGGL(k_tree_sum<double>, dim3((unsigned)next), dim3(kThreads), 0, s, src, cnt,
-                       dst, next == 1 ? mean : nullptr, nb);
-    cnt = next;
-    double* t = src; src = dst; dst = t;
+hipError_t launch_quant_codes(const QuantTensor* t, int count, hipStream_t s) {
+  if (count < 1 || count > kQuantBatch) return hipErrorInvalidValue;
+  QuantBatch b{};
+  b.tab[kQuantNf4] = host_tables(kQuantNf4);
+  b.tab[kQuantInt4] = host_tables(kQuantInt4);
+  int64_t chunks = 0;
+  for (int i = 0; i < count; ++i) {
+    if (!host_tables(t[i].kind).bucket_ok) return hipErrorInvalidValue;
+    b.job[i] = QuantJob{t[i].w, t[i].codes, t[i].absmax, t[i].n, t[i].kind};
+    b.first[i] = chunks;
+    chunks += ceil_div(t[i].n, kQChunk);
   }
-  const int64_t nd = ceil_div(nb, kDqBlock);
-  hipLaunchKernelGGL(k_dq_blocks, dim3((unsigned)ceil_div(nd, kThreads / 64)), dim3(kThreads), 0,
-                     s, absmax, nb, mean, q, scale);
-  return hipGetLastError();
+  b.first[count] = chunks;
+  b.count = count;
+  return launch_kernel(k_quant_absmax_nf4, dim3((unsigned)stream_grid(chunks)), dim3(kThreads),
+                       s, b);
 }
 
-hipError_t launch_dequant(const uint8_t* codes, const int8_t* q, const float* scale,
-                          const float* mean, const float* f32, int64_t n, int out_bf16,
-                          void* out, int kind, hipStream_t s) {
-  const dim3 grid((unsigned)stream_grid(ceil_div(n, kDqChunk)));
+hipError_t launch_quant_consts(const QuantTensor* t, int count, hipStream_t s) {
+  if (count < 0 || count > kQuantBatch) return hipErrorInvalidValue;
+  // the mean tree, one launch per level: the first over the float constants,
+  // the next over the float64 partials of the tensors that still have more
+  // than one (each level's input and output alternate between pa and pb)
+  int64_t cur[kQuantBatch];
+  for (int i = 0; i < count; ++i) cur[i] = t[i].q ? ceil_div(t[i].n, (int64_t)kBlock) : 0;
+  for (int level = 0;; ++level) {
+    TreeBatch b{};
+    int m = 0;
+    int64_t chunks = 0;
+    for (int i = 0; i < count; ++i) {
+      if (!t[i].q || (level > 0 && cur[i] <= 1)) continue;
+      const int64_t next = ceil_div(cur[i], kTreeChunk);
+      const void* in = level == 0 ? static_cast<const void*>(t[i].absmax)
+                                  : (level & 1 ? t[i].pa : t[i].pb);
+      double* out = level & 1 ? t[i].pb : t[i].pa;
+      b.job[m] = TreeJob{in, cur[i], out, next == 1 ? t[i].mean : nullptr,
+                         ceil_div(t[i].n, (int64_t)kBlock)};
+      b.first[m++] = chunks;
+      chunks += next;
+      cur[i] = next;
+    }
+    if (m == 0) break;
+    b.first[m] = chunks;
+    b.count = m;
+    hipError_t e = level == 0
+        ? launch_kernel(k_tree_sum<float>, dim3((unsigned)chunks), dim3(kThreads), s, b)
+        : launch_kernel(k_tree_sum<double>, dim3((unsigned)chunks), dim3(kThreads), s, b);
+    if (e != hipSuccess) return e;
+  }
+  // second-level constants: a wave per 256 constants
+  DqBatch b{};
+  int m = 0;
+  int64_t items = 0;
+  for (int i = 0; i < count; ++i) {
+    if (!t[i].q) continue;
+    const int64_t nb = ceil_div(t[i].n, (int64_t)kBlock);
+    b.job[m] = DqJob{t[i].absmax, nb, t[i].mean, t[i].q, t[i].scale};
+    b.first[m++] = items;
+    items += ceil_div(nb, kDqBlock);
+  }
+  if (m == 0) return hipSuccess;
+  b.first[m] = items;
+  b.count = m;
+  return launch_kernel(k_dq_blocks, dim3((unsigned)ceil_div(items, kThreads / 64)),
+                       dim3(kThreads), s, b);
+}
+
+hipError_t launch_dequantize(const DequantTensor* t, int count, int out_bf16, hipStream_t s) {
+  if (count < 1 || count > kQuantBatch) return hipErrorInvalidValue;
+  const bool f32 = t[0].f32 != nullptr;
+  DeqBatch b{};
+  std::memcpy(b.level[kQuantNf4], host_tables(kQuantNf4).level, sizeof(b.level[0]));
+  std::memcpy(b.level[kQuantInt4], host_tables(kQuantInt4).level, sizeof(b.level[0]));
+  int64_t chunks = 0;
+  for (int i = 0; i < count; ++i) {
+    if ((t[i].f32 != nullptr) != f32) return hipErrorInvalidValue;
+    b.job[i] = DeqJob{t[i].codes, t[i].q, t[i].scale, t[i].mean, t[i].f32, t[i].out, t[i].n,
+                      t[i].kind};
+    b.first[i] = chunks;
+    chunks += ceil_div(t[i].n, kDqChunk);
+  }
+  b.first[count] = chunks;
+  b.count = count;
+  const dim3 grid((unsigned)stream_grid(chunks));
   const auto k = out_bf16 ? (f32 ? k_dequant_nf4<true, true> : k_dequant_nf4<true, false>)
                           : (f32 ? k_dequant_nf4<false, true> : k_dequant_nf4<false, false>);
-  return launch_kernel(k, grid, dim3(kThreads), s, codes, q, scale, mean, f32, n,
-                       host_tables(kind), out);
+  return launch_kernel(k, grid, dim3(kThreads), s, b);
 }
 
 hipError_t launch_absmax_recon(const int8_t* q, const float* scale, const float* mean,

@@ -155,11 +155,40 @@ qlora_status qlora_quantize_nf4(const float* W, const qlora_nf4_tensor* q, void*
 qlora_status qlora_quantize_nf4_noalloc(const float* W, const qlora_nf4_tensor* q,
                                         void* stream);
 
+/* Bytes of workspace qlora_quantize_nf4_batch needs for count tensors of
+ * rows[i] x cols[i] (host arrays): the sum of qlora_quantize_workspace_bytes
+ * over them; 0 for count 0 or when a size is out of range. */
+size_t qlora_quantize_batch_workspace_bytes(const int64_t* rows, const int64_t* cols,
+                                            int32_t count);
+
+/* qlora_quantize_nf4 over count tensors in one call (a model's weights, say):
+ * q[i] receives exactly what qlora_quantize_nf4(W[i], &q[i], ...) would give,
+ * but up to 32 tensors share each launch (their codes in one launch, the
+ * levels of the mean tree and the second-level constants in a few more), so
+ * small tensors cost no launches of their own.
+ *   W   host array of count device pointers, float32[rows*cols] each,
+ *       16-byte aligned, read-only.
+ *   q   host array of count descriptors; no two may share an output buffer.
+ *   ws  device workspace of at least qlora_quantize_batch_workspace_bytes();
+ *       its contents on return are unspecified.
+ * count 0 does nothing.  Errors as qlora_quantize_nf4, for the first tensor
+ * that fails a check, before anything is launched. */
+qlora_status qlora_quantize_nf4_batch(const float* const* W, const qlora_nf4_tensor* q,
+                                      int32_t count, void* ws, size_t ws_bytes, void* stream);
+
 /* Dequantise to float32 or bf16 (round to nearest even) into out[rows*cols]
  * ("Double Quantization" section: NF4 weights converted back to the compute
  * dtype).  The float32 result is the single product level[code] * constant. */
 qlora_status qlora_dequantize_nf4(const qlora_nf4_tensor* q, qlora_dtype out_dtype, void* out,
                                   void* stream);
+
+/* qlora_dequantize_nf4 over count tensors: q[i] (host array of descriptors)
+ * into out[i] (host array of count device pointers, 16-byte aligned, not
+ * overlapping), up to 32 tensors per launch; the results equal count separate
+ * calls.  count 0 does nothing.  Errors as qlora_dequantize_nf4, before
+ * anything is launched. */
+qlora_status qlora_dequantize_nf4_batch(const qlora_nf4_tensor* q, int32_t count,
+                                        qlora_dtype out_dtype, void* const* out, void* stream);
 
 /* The constant each 64-block dequantises with, float32[nb]: reconstructed from
  * the 8-bit state, or a copy of q->absmax without double quantisation. */

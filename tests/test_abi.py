@@ -292,3 +292,39 @@ def test_noalloc_quantise_refuses_past_its_fixed_scratch(q):
             q.QLORA_ERR_UNSUPPORTED, (rows, cols)
     d = _desc(q)
     assert lib.qlora_quantize_nf4_noalloc(None, ctypes.byref(d), None) == q.QLORA_ERR_INVALID_ARG
+
+
+def test_batch_argument_errors(q):
+    """The batched quantiser and dequantiser check every tensor before any
+    launch (fake buffers, never dereferenced), take count 0 as nothing to do,
+    and need the sum of the single-tensor workspaces."""
+    lib = q.lib()
+    P = ctypes.c_void_p
+    fake = 0x100000
+    D2 = q.NF4Descriptor * 2
+    ptrs = (P * 2)(P(fake), P(fake))
+    bad = D2(_desc(q), _desc(q, rows=0))
+    assert lib.qlora_quantize_nf4_batch(ptrs, bad, 2, P(fake), 1 << 30, None) == \
+        q.QLORA_ERR_INVALID_ARG
+    assert lib.qlora_dequantize_nf4_batch(bad, 2, q.QLORA_F32, ptrs, None) == \
+        q.QLORA_ERR_INVALID_ARG
+    good = D2(_desc(q), _desc(q, rows=100, cols=1000))
+    assert lib.qlora_quantize_nf4_batch(ptrs, good, -1, P(fake), 1 << 30, None) == \
+        q.QLORA_ERR_INVALID_ARG
+    assert lib.qlora_quantize_nf4_batch(None, good, 2, P(fake), 1 << 30, None) == \
+        q.QLORA_ERR_INVALID_ARG
+    assert lib.qlora_dequantize_nf4_batch(good, 2, 7, ptrs, None) == q.QLORA_ERR_INVALID_ARG
+    assert lib.qlora_dequantize_nf4_batch(good, 2, q.QLORA_F32, (P * 2)(P(fake), P(fake + 8)),
+                                          None) == q.QLORA_ERR_INVALID_ARG
+    assert lib.qlora_quantize_nf4_batch(None, None, 0, None, 0, None) == q.QLORA_OK
+    assert lib.qlora_dequantize_nf4_batch(None, 0, q.QLORA_BF16, None, None) == q.QLORA_OK
+    need = q.qlora_quantize_batch_workspace_bytes([(64, 64), (100, 1000)])
+    assert need == q.qlora_quantize_workspace_bytes(64, 64) + \
+        q.qlora_quantize_workspace_bytes(100, 1000)
+    assert lib.qlora_quantize_nf4_batch(ptrs, good, 2, P(fake), need - 1, None) == \
+        q.QLORA_ERR_WORKSPACE
+    big = D2(_desc(q), q.NF4Descriptor(1 << 31, 1 << 7, 64, 256, fake, fake, fake, fake, 0, 0, 0))
+    assert lib.qlora_quantize_nf4_batch(ptrs, big, 2, P(fake), 1 << 40, None) == \
+        q.QLORA_ERR_UNSUPPORTED
+    assert q.qlora_quantize_batch_workspace_bytes([(0, 5)]) == 0
+    assert q.qlora_quantize_batch_workspace_bytes([]) == 0
