@@ -47,6 +47,9 @@ def parse():
                     help="all, none, or a comma list of layer8b, quant, variants, dropout, driver, "
                          "adamw, decode")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--headline", choices=["on", "off"], default="on",
+                    help="off: skip the headline step (and the CPU baseline) and print only "
+                         "the legs, for profiling a leg on its own")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run 3 plain device-to-device copies of MIB MiB (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -807,9 +810,9 @@ def main():
     q.lib()
     if args.calibrate_copy:
         calibrate_copy(torch, args.calibrate_copy)
-    head = headline(args, q, torch, workloads)
+    head = headline(args, q, torch, workloads) if args.headline == "on" else None
     cpu = None
-    if args.cpu_baseline == "on":
+    if head is not None and args.cpu_baseline == "on":
         cpu = cpu_baseline(workloads)
         log("cpu baseline: %s tokens/s on %d threads" % (cpu["value"], cpu["cores"]))
     legs = {}
@@ -835,6 +838,9 @@ def main():
         legs["llama8b_adapters_adamw_step"] = leg_adamw(q, torch, workloads)
     if "decode" in want:
         legs["llama70b_decode_gemv"] = leg_decode(q, torch, workloads)
+    if head is None:
+        print(json.dumps({"headline": None, "legs": legs}), flush=True)
+        return
     tokens_s = head["tokens"] / head["sec"]
     tflops = head["flops"] / head["sec"] / 1e12
     line = {

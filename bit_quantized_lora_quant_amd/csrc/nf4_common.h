@@ -49,6 +49,7 @@ constexpr int kDqBlock = 256;  // first-level constants per second-level scale
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // The 16 levels and the 15 decision thresholds, passed by value in the kernel
 // argument segment (they land in scalar registers).  thresh[j] is the largest

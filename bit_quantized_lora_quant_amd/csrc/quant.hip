@@ -125,7 +125,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_absmax_nf4(const QuantBatch 
     if (full) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float4 t = *reinterpret_cast<const float4*>(w + base + 256 * i + 4 * lane);
+        // read once: nontemporal, so the stream does not displace cached lines
+        const f32x4_t t = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4_t*>(w + base + 256 * i + 4 * lane));
         v[i][0] = t.x; v[i][1] = t.y; v[i][2] = t.z; v[i][3] = t.w;
       }
     } else {
@@ -145,10 +147,29 @@ __global__ __launch_bounds__(kThreads) void k_quant_absmax_nf4(const QuantBatch 
       const int64_t blk = e0 / kBlock;
       if ((lane & 15) == 0 && e0 < n) absmax[blk] = a;
       uint32_t packed = 0;
+      // x = w / a, correctly rounded.  When every block of the wave has its
+      // absmax in [2^-60, 2^60] (or 0): one IEEE reciprocal r = 1/a per block
+      // and, per weight, q0 = w r corrected by its residual, fma(w - q0 a, r,
+      // q0) -- the correctly rounded quotient by Markstein's theorem (r within
+      // half an ulp of 1/a, q0 within an ulp of w/a, the residual exact).  The
+      // range keeps r and the residual normal for every quotient of magnitude
+      // 2^-20 or more; smaller ones fall in the zero level's interval of both
+      // tables, whatever their last bits.  Otherwise the IEEE division.
+      const bool tame = a == 0.0f || (a >= 0x1p-60f && a <= 0x1p60f);
+      if (__all(tame)) {
+        const float r = a == 0.0f ? 0.0f : 1.0f / a;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x = (a == 0.0f) ? 0.0f : v[i][e] / a;
-        packed |= nf4_code(x, bk) << (4 * e);
+        for (int e = 0; e < 4; ++e) {
+          const float q0 = v[i][e] * r;
+          const float x = __builtin_fmaf(__builtin_fmaf(-q0, a, v[i][e]), r, q0);
+          packed |= nf4_code(x, bk) << (4 * e);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = (a == 0.0f) ? 0.0f : v[i][e] / a;
+          packed |= nf4_code(x, bk) << (4 * e);
+        }
       }
       if (full) {
         *reinterpret_cast<uint16_t*>(codes + (e0 >> 1)) = (uint16_t)packed;
@@ -333,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_nf4(const DeqBatch b) {
     for (int i = 0; i < 4; ++i) {
       const int64_t e0 = base + 512 * i + 8 * lane;
       if (full) {
-        cw[i] = *reinterpret_cast<const uint32_t*>(codes + (e0 >> 1));
+        cw[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(codes + (e0 >> 1)));
       } else {
         cw[i] = 0;
         for (int64_t k = 0; k < 4; ++k)
@@ -354,11 +375,14 @@ __global__ __launch_bounds__(kThreads) void k_dequant_nf4(const DeqBatch b) {
           uint4 p;
           p.x = pack_bf16x2(v[0], v[1]); p.y = pack_bf16x2(v[2], v[3]);
           p.z = pack_bf16x2(v[4], v[5]); p.w = pack_bf16x2(v[6], v[7]);
-          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + e0) = p;
+          // written once: nontemporal stores
+          const u32x4_t pv = {p.x, p.y, p.z, p.w};
+          __builtin_nontemporal_store(pv, reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(out) + e0));
         } else {
           float* o = reinterpret_cast<float*>(out) + e0;
-          *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
-          *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+          f32x4_t o0 = {v[0], v[1], v[2], v[3]}, o1 = {v[4], v[5], v[6], v[7]};
+          __builtin_nontemporal_store(o0, reinterpret_cast<f32x4_t*>(o));
+          __builtin_nontemporal_store(o1, reinterpret_cast<f32x4_t*>(o + 4));
         }
       } else {
 #pragma unroll
@@ -422,9 +446,10 @@ hipError_t quant_scratch(void** ptr) {
   return hipSuccess;
 }
 
-// Grid-stride launches: about 32 waves per CU, fewer for small tensors.
+// Grid-stride launches: up to 128 waves per CU (four times the resident
+// waves, so the tail of the pass is spread thin), fewer for small tensors.
 static int64_t stream_grid(int64_t chunks) {
-  const int64_t waves = chunks < 8192 ? chunks : 8192;
+  const int64_t waves = chunks < 32768 ? chunks : 32768;
   return ceil_div(waves > 0 ? waves : 1, kThreads / 64);
 }
 

@@ -186,3 +186,33 @@ def test_every_float_in_the_unit_interval(q, kind):
             ref = oracle.quantize(host_w.reshape(-1), kind=kind, dq=False)["codes"]
             assert np.array_equal(codes, ref), "codes differ in chunk at %d (sign %x)" % (start, sign)
             del W
+
+
+@pytest.mark.parametrize("kind", ["nf4", "int4"])
+def test_quotients_next_to_thresholds(q, kind):
+    """Weights within two ulps of threshold x absmax, in blocks whose absmax
+    (first element, either sign) is drawn log-uniformly over 2^-70 .. 2^70:
+    the code decision w / absmax > threshold, taken on the device through a
+    per-block reciprocal with a residual correction (or the division, for
+    absmax outside 2^+-60), equals the oracle's IEEE division for every one."""
+    rng = np.random.default_rng(17 if kind == "nf4" else 18)
+    cb = oracle.codebook(kind).astype(np.float64)
+    thr = (cb[:-1] + cb[1:]) / 2.0
+    thr = thr[np.abs(thr) < 1.0]
+    nb = 1 << 16
+    a = np.exp2(rng.uniform(-70, 70, nb)).astype(np.float32)
+    a *= np.where(rng.random(nb) < 0.5, -1, 1).astype(np.float32)
+    w = np.empty((nb, 64), dtype=np.float32)
+    w[:, 0] = a
+    t = rng.choice(thr, size=(nb, 63))
+    x = (t * np.abs(a)[:, None].astype(np.float64)).astype(np.float32)
+    bits = x.view(np.int32) + rng.integers(-2, 3, size=x.shape).astype(np.int32)
+    x = bits.view(np.float32)
+    x = np.where(np.abs(x) <= np.abs(a)[:, None], x, np.float32(0))
+    w[:, 1:] = x
+    say("quotients next to thresholds %s" % kind)
+    qq, _ = q.qlora_quantize_nf4(to_dev(w), quant_type=kind, double_quant=False)
+    torch.cuda.synchronize()
+    ref = oracle.quantize(w.reshape(-1), kind=kind, dq=False)["codes"]
+    got = host(qq.codes).numpy()
+    assert np.array_equal(got, ref), "codes differ at bytes %s" % (np.nonzero(got != ref)[0][:8],)
