@@ -736,7 +736,8 @@ def leg_variants(q, torch, workloads, passes=3):
 
 def leg_decode(q, torch, workloads, steps=5):
     """Decode forward through 80 layers x 7 70B-shaped linears (distinct NF4
-    weights, ~35 GB) at M = 1, 4, 16 tokens."""
+    weights, ~35 GB) at M = 1, 4, 16 tokens: as 560 separate calls, and as the
+    layer driver (q/k/v and gate/up batched: 4 launch pairs per layer)."""
     dev = "cuda:0"
     wl = workloads.LLAMA70B_DECODE
     r, alpha = wl.r, wl.alpha
@@ -764,10 +765,32 @@ def leg_decode(q, torch, workloads, steps=5):
         X = {K: torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16) for _, K, _ in wl.linears}
         Y = {N: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _, _, N in wl.linears}
         ws = q.workspace(max(q.qlora_linear_workspace_bytes(M, N, K, r) for _, K, N in wl.linears), dev)
+        names = [nm for nm, _, _ in wl.linears]
+        # the layer driver: the projections that read one input (q/k/v, then
+        # gate/up) as one batched call, o and down alone
+        groups = [[names.index(n) for n in g] for g in (("q_proj", "k_proj", "v_proj"),
+                                                         ("o_proj",), ("gate_proj", "up_proj"),
+                                                         ("down_proj",))]
+        Yl = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _, _, N in wl.linears]
+        per = len(wl.linears)
+        bws = q.workspace(max(q.qlora_linear_batch_workspace_bytes(
+            [lin[i][0] for i in g], M, r) for g in groups), dev)
 
         def step():
             for Q, K, N in lin:
                 q.qlora_linear_fwd(Q, X[K], A[K], B[N], alpha, Y=Y[N], ws=ws)
+
+        def step_batched():
+            for layer in range(wl.layers):
+                for g in groups:
+                    jobs = [(lin[layer * per + i][0], X[lin[layer * per + i][1]],
+                             A[lin[layer * per + i][1]], B[lin[layer * per + i][2]], Yl[i])
+                            for i in g]
+                    if len(jobs) == 1:
+                        Q, Xj, Aj, Bj, Yj = jobs[0]
+                        q.qlora_linear_fwd(Q, Xj, Aj, Bj, alpha, Y=Yj, ws=ws)
+                    else:
+                        q.qlora_linear_fwd_batch(jobs, alpha, ws=bws)
 
         step()
         torch.cuda.synchronize()
@@ -776,13 +799,18 @@ def leg_decode(q, torch, workloads, steps=5):
         tr = q.qlora_trace_end()
         # the 560 calls of a token step replayed from one HIP graph
         gstep = graph_of(torch, step)
+        sec_sep = timed(torch, gstep.replay, steps)
+        del gstep
+        gstep = graph_of(torch, step_batched)
         sec = timed(torch, gstep.replay, steps)
         del gstep
         nb = sum(Q.nbytes() + 2 * r * (K + N) + 2 * M * (K + N) for Q, K, N in lin)
         code_bytes = sum(Q.nbytes() for Q, _, _ in lin)
         ent = {"ms_per_token_step": round(sec * 1e3, 3), "tokens/s": round(M / sec, 1),
                "GB/s": round(nb / sec / 1e9, 1), "frac_hbm": round(nb / sec / 1e9 / PEAK_HBM_GBS, 4),
-               "launch": "hip graph", "eager_ms_per_token_step": round(sec_eager * 1e3, 3)}
+               "launch": "hip graph; q/k/v and gate/up as batched calls (4 launch pairs per layer)",
+               "separate_calls_ms_per_token_step": round(sec_sep * 1e3, 3),
+               "eager_ms_per_token_step": round(sec_eager * 1e3, 3)}
         if "gemv" in tr:
             n, ms = tr["gemv"]
             ent["gemv_kernel"] = {"launches": n, "avg_us": round(ms / n * 1e3, 2),

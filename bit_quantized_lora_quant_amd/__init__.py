@@ -28,6 +28,7 @@ EXPORTS = [
     "qlora_dequantize_absmax", "qlora_quantize_batch_workspace_bytes",
     "qlora_quantize_nf4_batch", "qlora_dequantize_nf4_batch",
     "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
+    "qlora_linear_batch_workspace_bytes", "qlora_linear_fwd_batch",
     "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout", "qlora_dropout_mask",
     "qlora_adamw_step", "qlora_adamw8_step", "qlora_host_state_alloc", "qlora_host_state_free",
     "qlora_merge_workspace_bytes", "qlora_merge_requantize",
@@ -110,6 +111,9 @@ def lib():
         L.qlora_linear_workspace_bytes.argtypes = [I64, I64, I64, I32]
         L.qlora_linear_workspace_bytes.restype = SZ
         L.qlora_linear_fwd.argtypes = [D, P, I64, P, P, I32, F, P, P, P, SZ, P]
+        L.qlora_linear_batch_workspace_bytes.argtypes = [P, I32, I64, I32]
+        L.qlora_linear_batch_workspace_bytes.restype = SZ
+        L.qlora_linear_fwd_batch.argtypes = [P, I32, I64, I32, F, P, SZ, P]
         L.qlora_linear_bwd.argtypes = [D, P, I64, P, P, I32, F, P, P, P, P, P, P, SZ, P]
         L.qlora_linear_fwd_dropout.argtypes = [D, P, I64, P, P, I32, F, P, P, P, P, P, SZ, P]
         L.qlora_linear_bwd_dropout.argtypes = [D, P, I64, P, P, I32, F, P, P, P, P, P, P, P, P,
@@ -360,6 +364,51 @@ def qlora_linear_fwd(q: NF4Tensor, X, A, B, alpha: float, Y=None, XA_out=None, w
                                               ws.numel(), _stream()),
                "qlora_linear_fwd_dropout")
     return (Y, XA_out) if return_xa else Y
+
+
+class LinearJob(ctypes.Structure):
+    """qlora_linear_job: one linear of a batched forward."""
+    _fields_ = [("W", ctypes.POINTER(NF4Descriptor)), ("X", ctypes.c_void_p),
+                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("Y", ctypes.c_void_p),
+                ("XA_out", ctypes.c_void_p)]
+
+
+def _linear_jobs(jobs):
+    descs = [q.descriptor() for q, *_ in jobs]
+    arr = (LinearJob * max(len(jobs), 1))()
+    for i, ((q, X, A, B, Y, XA), d) in enumerate(zip(jobs, descs)):
+        arr[i] = LinearJob(ctypes.pointer(d), _ptr(X), _ptr(A), _ptr(B), _ptr(Y), _ptr(XA))
+    return arr, descs
+
+
+def qlora_linear_batch_workspace_bytes(qs, M: int, r: int) -> int:
+    jobs = [(q, None, None, None, None, None) for q in qs]
+    arr, keep = _linear_jobs(jobs)
+    return int(lib().qlora_linear_batch_workspace_bytes(arr, len(jobs), M, r))
+
+
+def qlora_linear_fwd_batch(jobs, alpha: float, ws=None, return_xa: bool = False):
+    """Forward of independent linears (q, X, A, B[, Y]) with one M and rank r;
+    for M <= 16 up to 8 share each launch pair.  Returns the list of Y (or of
+    (Y, XA) with return_xa)."""
+    jobs = list(jobs)
+    M, r = jobs[0][1].shape[0], jobs[0][2].shape[0]
+    full = []
+    for job in jobs:
+        q, X, A, B = job[:4]
+        _bf16(X), _bf16(A), _bf16(B)
+        assert X.shape == (M, q.cols) and A.shape == (r, q.cols) and B.shape == (q.rows, r)
+        Y = job[4] if len(job) > 4 and job[4] is not None else \
+            torch.empty((M, q.rows), dtype=torch.bfloat16, device=X.device)
+        XA = torch.empty((M, r), dtype=torch.bfloat16, device=X.device) if return_xa else None
+        full.append((q, X, A, B, Y, XA))
+    arr, keep = _linear_jobs(full)
+    if ws is None:
+        ws = workspace(lib().qlora_linear_batch_workspace_bytes(arr, len(full), M, r),
+                       jobs[0][1].device)
+    _check(lib().qlora_linear_fwd_batch(arr, len(full), M, r, ctypes.c_float(alpha), _ptr(ws),
+                                        ws.numel(), _stream()), "qlora_linear_fwd_batch")
+    return [(j[4], j[5]) if return_xa else j[4] for j in full]
 
 
 def qlora_linear_bwd(q: NF4Tensor, X, A, B, alpha: float, dY, XA_in=None, need_dx: bool = True,

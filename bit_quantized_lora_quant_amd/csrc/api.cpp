@@ -417,12 +417,9 @@ qlora_status qlora_linear_fwd_dropout(const qlora_nf4_tensor* W, const qlora_bf1
   if (M <= 16) {
     const NF4Ref w{W->codes, W->absmax_q, W->absmax_scale, W->absmax_mean, f32_consts(W),
                    W->quant_type};
-    float* part = at<float>(ws, L.gemv_part);
-    float* xa_part = at<float>(ws, L.dec_xa);
-    e = traced(QLORA_KERNEL_GEMV, s, [&] {
-      return launch_decode(X, M, K, w, N, A, B, r, scale, L.gemv_splits, part, xa_part, Y,
-                           XA_out, dp, s);
-    });
+    const DecodeJob d{X, K, w, N, A, B, at<float>(ws, L.gemv_part), at<float>(ws, L.dec_xa), Y,
+                      XA_out, dp};
+    e = traced(QLORA_KERNEL_GEMV, s, [&] { return launch_decode(&d, 1, M, r, scale, s); });
     return hip_status(e);
   }
   float* ahat_t = at<float>(ws, L.ahat_t);
@@ -445,6 +442,76 @@ qlora_status qlora_linear_fwd_dropout(const qlora_nf4_tensor* W, const qlora_bf1
     e = traced(QLORA_KERNEL_SPLIT_REDUCE, s,
                [&] { return launch_split_reduce(part, L.sf, M * N, Y, s); });
   return hip_status(e);
+}
+
+// Decode workspace of one job of a batch: its split partials, then its
+// down-projection slice partials.
+static size_t decode_job_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
+  return align_up((size_t)gemv_splits(N, K) * M * N * sizeof(float)) +
+         align_up((size_t)decode_xa_slices(K) * M * skinny_rpad(r) * sizeof(float));
+}
+
+size_t qlora_linear_batch_workspace_bytes(const qlora_linear_job* jobs, int32_t count, int64_t M,
+                                          int32_t r) {
+  if (count < 0 || (count > 0 && !jobs) || M < 1 || r < 1 || r > QLORA_MAX_RANK) return 0;
+  size_t total = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const qlora_nf4_tensor* W = jobs[i].W;
+    if (!valid_tensor(W) || !linear_fits(M, W->rows, W->cols)) return 0;
+    const size_t b = M <= 16 ? decode_job_bytes(M, W->rows, W->cols, r)
+                             : linear_layout(M, W->rows, W->cols, r).total;
+    total = M <= 16 ? total + b : std::max(total, b);
+  }
+  return total;
+}
+
+qlora_status qlora_linear_fwd_batch(const qlora_linear_job* jobs, int32_t count, int64_t M,
+                                    int32_t r, float alpha, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  if (count < 0 || (count > 0 && !jobs)) return QLORA_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < count; ++i) {
+    const qlora_linear_job& j = jobs[i];
+    const qlora_status st = check_linear(j.W, j.X, M, j.A, j.B, r, alpha);
+    if (st != QLORA_OK) return st;
+    if (!j.Y || !aligned(j.Y, 16)) return QLORA_ERR_INVALID_ARG;
+  }
+  if (count == 0) return QLORA_OK;
+  const size_t need = qlora_linear_batch_workspace_bytes(jobs, count, M, r);
+  if (!ws || ws_bytes < need || !aligned(ws, kAlign)) return QLORA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M > 16) {
+    // the GEMM path, one linear after another on the one workspace
+    for (int32_t i = 0; i < count; ++i) {
+      const qlora_linear_job& j = jobs[i];
+      const qlora_status st = qlora_linear_fwd_dropout(j.W, j.X, M, j.A, j.B, r, alpha, nullptr,
+                                                       nullptr, j.Y, j.XA_out, ws, ws_bytes,
+                                                       stream);
+      if (st != QLORA_OK) return st;
+    }
+    return QLORA_OK;
+  }
+  const float scale = alpha / (float)r;
+  DecodeJob group[kDecodeBatch];
+  size_t off = 0;
+  int m = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const qlora_linear_job& j = jobs[i];
+    const qlora_nf4_tensor* W = j.W;
+    const int64_t N = W->rows, K = W->cols;
+    const NF4Ref w{W->codes, W->absmax_q, W->absmax_scale, W->absmax_mean, f32_consts(W),
+                   W->quant_type};
+    float* part = at<float>(ws, off);
+    float* xa_part = at<float>(ws, off + align_up((size_t)gemv_splits(N, K) * M * N * sizeof(float)));
+    off += decode_job_bytes(M, N, K, r);
+    group[m++] = DecodeJob{j.X, K, w, N, j.A, j.B, part, xa_part, j.Y, j.XA_out, DropoutParams{}};
+    if (m == kDecodeBatch || i == count - 1) {
+      const hipError_t e =
+          traced(QLORA_KERNEL_GEMV, s, [&] { return launch_decode(group, m, M, r, scale, s); });
+      if (e != hipSuccess) return hip_status(e);
+      m = 0;
+    }
+  }
+  return QLORA_OK;
 }
 
 qlora_status qlora_linear_bwd(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,

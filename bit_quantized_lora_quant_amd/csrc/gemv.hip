@@ -21,6 +21,8 @@
 // The per-block factoring computes sum_b a_b (sum_k x_k bf16(level_k)), where
 // the GEMMs compute sum_k x_k bf16(level_k a_b): both round each weight once
 // to bf16, and both stay inside the forward's tolerance.
+#include <cstring>
+
 #include "skinny.h"
 
 namespace qnf4 {
@@ -56,10 +58,6 @@ struct DecodeArgs {
 // The LDS arena of a streaming workgroup starts with the 16 bf16 levels.
 constexpr int kDecTab = 64;   // bytes reserved for the table (keeps the rest 16-byte aligned)
 constexpr int kDecCodes = kDecRows * kDecBlocks * 32;   // the code tile, 16 KB
-
-__device__ __forceinline__ void build_levels(uint16_t* tab16, const NF4Tables& tab) {
-  if (threadIdx.x < 16) tab16[threadIdx.x] = (uint16_t)(pack_bf16x2(tab.level[threadIdx.x], 0.f) & 0xFFFF);
-}
 
 // 8 codes (one 32-bit word, code 2j in the low nibble of byte j) -> 8 bf16
 // levels as an MFMA operand.  The word is spread into 2 x nibble per byte, the
@@ -262,19 +260,44 @@ __device__ __forceinline__ void xa_slice(const DecodeArgs& a, int r, int64_t sl,
   }
 }
 
+// Up to kDecodeBatch independent linears (each its own W, X, adapters and
+// output; shared M and rank) in one launch: their workgroups follow one
+// another in the grid, and a workgroup finds its job by a scalar search of
+// the kernel arguments.
+struct DecodeBatch {
+  DecodeArgs job[kDecodeBatch];
+  int64_t first[kDecodeBatch + 1];   // first workgroup of each job
+  int kind[kDecodeBatch];
+  int count;
+  float level[2][16];                // by kind
+};
+
+__device__ __forceinline__ int job_index(const int64_t* first, int count, int64_t item) {
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (first[mid] <= item) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
 template <int RT>
-__global__ __launch_bounds__(256) void k_qlora_decode(DecodeArgs a, NF4Tables tab, int r) {
+__global__ __launch_bounds__(256) void k_qlora_decode(const DecodeBatch bt, int r) {
   // one LDS arena (sized per launch) for either branch: [16 bf16 levels |
   // code tile | X rows 0..M, row M zero] or the 4 KB of XA wave partials
   extern __shared__ __attribute__((aligned(16))) uint8_t arena[];
-  const int64_t b = blockIdx.x;
+  const int j = job_index(bt.first, bt.count, blockIdx.x);
+  const DecodeArgs& a = bt.job[j];
+  const int64_t b = (int64_t)blockIdx.x - bt.first[j];
   if (b < a.xa_blocks) {
     xa_slice<RT>(a, r, b, reinterpret_cast<float (*)[4][64]>(arena));
   } else {
     uint16_t* tab16 = reinterpret_cast<uint16_t*>(arena);
     uint8_t* cs = arena + kDecTab;
     uint16_t* xs = reinterpret_cast<uint16_t*>(arena + kDecTab + kDecCodes);
-    build_levels(tab16, tab);
+    if (threadIdx.x < 16)
+      tab16[threadIdx.x] = (uint16_t)(pack_bf16x2(bt.level[bt.kind[j]][threadIdx.x], 0.f) & 0xFFFF);
     decode_rows(a, tab16, cs, xs, b - a.xa_blocks);   // its barrier also covers the table
   }
 }
@@ -292,18 +315,39 @@ __device__ __forceinline__ float sum_first16(const float* src, int64_t stride, i
   return v;
 }
 
+struct FinishJob {
+  const float* partial;   // [splits][M][N]
+  int splits;
+  int64_t N;
+  const float* xa_part;   // [ks][M][rpad]
+  int ks;
+  const uint16_t* B;
+  uint16_t* Y;
+  uint16_t* XA_out;
+};
+struct FinishBatch {
+  FinishJob job[kDecodeBatch];
+  int64_t first[kDecodeBatch + 1];   // first 256-column block of each job
+  int count;
+};
+
 // Y[m][n] = bf16( sum_split partial + sum_j bf16(s XA[m][j]) B[n][j] ), with
 // XA the slice sum of the down-projection.  Workgroup (n block, token m):
 // first the r values of XA[m] (slices added in order, loads unrolled), then
 // one output per thread; the n block 0 workgroups also write bf16(XA).
-__global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__ partial,
-                                                       int splits, int64_t M, int64_t N,
-                                                       const float* __restrict__ xa_part,
-                                                       int ks, int rpad, int r, float scale,
-                                                       const uint16_t* __restrict__ B,
-                                                       uint16_t* __restrict__ Y,
-                                                       uint16_t* __restrict__ XA_out) {
+__global__ __launch_bounds__(256) void k_decode_finish(const FinishBatch fb, int64_t M, int rpad,
+                                                       int r, float scale) {
   __shared__ float xs[128];
+  const int jb = job_index(fb.first, fb.count, blockIdx.x);
+  const float* __restrict__ partial = fb.job[jb].partial;
+  const int splits = fb.job[jb].splits;
+  const int64_t N = fb.job[jb].N;
+  const float* __restrict__ xa_part = fb.job[jb].xa_part;
+  const int ks = fb.job[jb].ks;
+  const uint16_t* __restrict__ B = fb.job[jb].B;
+  uint16_t* __restrict__ Y = fb.job[jb].Y;
+  uint16_t* __restrict__ XA_out = fb.job[jb].XA_out;
+  const int64_t nblock = (int64_t)blockIdx.x - fb.first[jb];
   const int64_t m = blockIdx.y;
   const int t = threadIdx.x;
   if (t < r) {
@@ -321,10 +365,10 @@ __global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__
     for (; k < ks; ++k) v += src[k * stride];
     const uint32_t sb = pack_bf16x2(scale * v, 0.f) & 0xFFFFu;
     xs[t] = __builtin_bit_cast(float, sb << 16);
-    if (blockIdx.x == 0 && XA_out) XA_out[m * r + t] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFF);
+    if (nblock == 0 && XA_out) XA_out[m * r + t] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFF);
   }
   __syncthreads();
-  const int64_t n = (int64_t)blockIdx.x * 256 + t;
+  const int64_t n = nblock * 256 + t;
   if (n >= N) return;
   const float* src = partial + m * N + n;
   const int64_t stride = M * N;
@@ -355,11 +399,11 @@ __global__ __launch_bounds__(256) void k_decode_finish(const float* __restrict__
 }
 
 template <int RT>
-hipError_t decode_rt(const DecodeArgs& a, int r, int64_t blocks, int kind, hipStream_t s) {
-  const size_t stream = kDecTab + kDecCodes + (size_t)(a.M + 1) * kDecXStride * 2;
+hipError_t decode_rt(const DecodeBatch& bt, int64_t M, int r, int64_t blocks, hipStream_t s) {
+  const size_t stream = kDecTab + kDecCodes + (size_t)(M + 1) * kDecXStride * 2;
   const size_t xa = (size_t)kXaWaves * 4 * 64 * 4;
   return launch_kernel_lds(k_qlora_decode<RT>, dim3((unsigned)blocks), dim3(256),
-                           stream > xa ? stream : xa, s, a, host_tables(kind), r);
+                           stream > xa ? stream : xa, s, bt, r);
 }
 
 }  // namespace
@@ -374,32 +418,48 @@ int decode_xa_slices(int64_t K) {
   return (int)ceil_div(K, (int64_t)kXaWaves * kSkStep);
 }
 
-hipError_t launch_decode(const uint16_t* X, int64_t M, int64_t K, const NF4Ref& W, int64_t N,
-                         const uint16_t* A, const uint16_t* B, int r, float scale, int splits,
-                         float* partial, float* xa_part, uint16_t* Y, uint16_t* XA_out,
-                         const DropoutParams& drop, hipStream_t s) {
-  DecodeArgs a{};
-  a.X = X; a.M = M; a.K = K; a.N = N;
-  a.codes = W.codes; a.q = W.q; a.scale = W.scale; a.mean = W.mean; a.f32 = W.f32;
-  a.splits = splits;
-  a.partial = partial;
+hipError_t launch_decode(const DecodeJob* jobs, int count, int64_t M, int r, float scale,
+                         hipStream_t s) {
+  if (count < 1 || count > kDecodeBatch) return hipErrorInvalidValue;
+  DecodeBatch bt{};
+  FinishBatch fb{};
+  std::memcpy(bt.level[kQuantNf4], host_tables(kQuantNf4).level, sizeof(bt.level[0]));
+  std::memcpy(bt.level[kQuantInt4], host_tables(kQuantInt4).level, sizeof(bt.level[0]));
   const int rpad = skinny_rpad(r);
-  const int ks = decode_xa_slices(K);
-  a.xa_blocks = ks;                            // one row group of tokens (M <= 16)
-  a.xa = SkinnyJob{X, K, K, A, K, ks, (int64_t)kXaWaves * kSkStep, xa_part, scale,
-                   nullptr, nullptr, nullptr, 0, 1};
-  a.xa.drop = drop;
-  const int64_t blocks = ks + ceil_div(N, kDecRows) * splits;
+  int64_t blocks = 0, nblocks = 0;
+  for (int i = 0; i < count; ++i) {
+    const DecodeJob& d = jobs[i];
+    DecodeArgs& a = bt.job[i];
+    a.X = d.X; a.M = M; a.K = d.K; a.N = d.N;
+    a.codes = d.W.codes; a.q = d.W.q; a.scale = d.W.scale; a.mean = d.W.mean; a.f32 = d.W.f32;
+    a.splits = gemv_splits(d.N, d.K);
+    a.partial = d.partial;
+    const int ks = decode_xa_slices(d.K);
+    a.xa_blocks = ks;                          // one row group of tokens (M <= 16)
+    a.xa = SkinnyJob{d.X, d.K, d.K, d.A, d.K, ks, (int64_t)kXaWaves * kSkStep, d.xa_part, scale,
+                     nullptr, nullptr, nullptr, 0, 1};
+    a.xa.drop = d.drop;
+    bt.kind[i] = d.W.kind;
+    bt.first[i] = blocks;
+    blocks += ks + ceil_div(d.N, kDecRows) * a.splits;
+    fb.job[i] = FinishJob{d.partial, a.splits, d.N, d.xa_part, ks, d.B, d.Y, d.XA_out};
+    fb.first[i] = nblocks;
+    nblocks += ceil_div(d.N, (int64_t)256);
+  }
+  bt.first[count] = blocks;
+  bt.count = count;
+  fb.first[count] = nblocks;
+  fb.count = count;
   hipError_t e;
   switch (rpad) {
-    case 16: e = decode_rt<1>(a, r, blocks, W.kind, s); break;
-    case 32: e = decode_rt<2>(a, r, blocks, W.kind, s); break;
-    case 64: e = decode_rt<4>(a, r, blocks, W.kind, s); break;
-    default: e = decode_rt<8>(a, r, blocks, W.kind, s); break;
+    case 16: e = decode_rt<1>(bt, M, r, blocks, s); break;
+    case 32: e = decode_rt<2>(bt, M, r, blocks, s); break;
+    case 64: e = decode_rt<4>(bt, M, r, blocks, s); break;
+    default: e = decode_rt<8>(bt, M, r, blocks, s); break;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_decode_finish, dim3((unsigned)ceil_div(N, 256), (unsigned)M), dim3(256), 0,
-                     s, partial, splits, M, N, xa_part, ks, rpad, r, scale, B, Y, XA_out);
+  hipLaunchKernelGGL(k_decode_finish, dim3((unsigned)nblocks, (unsigned)M), dim3(256), 0, s, fb, M,
+                     rpad, r, scale);
   return hipGetLastError();
 }
 

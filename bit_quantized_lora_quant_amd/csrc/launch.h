@@ -182,10 +182,26 @@ struct NF4Ref {
 };
 int gemv_splits(int64_t N, int64_t K);
 int decode_xa_slices(int64_t K);
-hipError_t launch_decode(const uint16_t* X, int64_t M, int64_t K, const NF4Ref& W, int64_t N,
-                         const uint16_t* A, const uint16_t* B, int r, float scale, int splits,
-                         float* partial, float* xa_part, uint16_t* Y, uint16_t* XA_out,
-                         const DropoutParams& drop, hipStream_t s);
+// One linear of a decode launch: partial holds gemv_splits(N, K) x M x N
+// floats, xa_part decode_xa_slices(K) x M x skinny_rpad(r).
+struct DecodeJob {
+  const uint16_t* X;
+  int64_t K;
+  NF4Ref W;
+  int64_t N;
+  const uint16_t* A;
+  const uint16_t* B;
+  float* partial;
+  float* xa_part;
+  uint16_t* Y;
+  uint16_t* XA_out;
+  DropoutParams drop;
+};
+// Independent linears with one M and rank per launch pair (streaming, then
+// finish); count <= kDecodeBatch.
+constexpr int kDecodeBatch = 8;
+hipError_t launch_decode(const DecodeJob* jobs, int count, int64_t M, int r, float scale,
+                         hipStream_t s);
 
 // merged[n][k] += s * sum_j B[n][j] A[j][k] (float32, j in order, fused
 // multiply-add per term), merged [N, K] float32, A [r, K], B [N, r] bf16

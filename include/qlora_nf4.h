@@ -214,6 +214,38 @@ qlora_status qlora_linear_fwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
                               qlora_bf16* Y, qlora_bf16* XA_out, void* ws, size_t ws_bytes,
                               void* stream);
 
+/* Several independent adapted linears with one token count M and one rank
+ * (a layer's query, key and value projections, or its gate and up
+ * projections, each with its own 4-bit weight, input and adapter pair: LoRA
+ * adapts all seven projections, "Fine-Tuning Memory Requirements: Full
+ * Training vs LoRA vs QLoRA", section "LoRA: freeze the base, train small
+ * adapters").
+ * For M <= 16 (decode) up to 8 of them share one weight-streaming launch and
+ * one finish launch, so the small ones cost no launches of their own; each
+ * Y (and XA) equals what qlora_linear_fwd gives for that job alone.  For
+ * M > 16 the jobs run one after another through qlora_linear_fwd.
+ *   jobs   host array of count jobs; per job W, X [M, K], A [r, K], B [N, r],
+ *          Y [M, N] (16-byte aligned) and XA_out [M, r] or NULL, all device
+ *          memory, as in qlora_linear_fwd; no two jobs may share an output.
+ *   ws     device workspace of at least qlora_linear_batch_workspace_bytes()
+ *          (the jobs' decode partials side by side; for M > 16 the largest
+ *          single-linear workspace).
+ * Without dropout.  count 0 does nothing.  Errors as qlora_linear_fwd, for
+ * the first job that fails a check, before anything is launched. */
+typedef struct qlora_linear_job {
+  const qlora_nf4_tensor* W;
+  const qlora_bf16* X;
+  const qlora_bf16* A;
+  const qlora_bf16* B;
+  qlora_bf16* Y;
+  qlora_bf16* XA_out;
+} qlora_linear_job;
+size_t qlora_linear_batch_workspace_bytes(const qlora_linear_job* jobs, int32_t count, int64_t M,
+                                          int32_t r);
+qlora_status qlora_linear_fwd_batch(const qlora_linear_job* jobs, int32_t count, int64_t M,
+                                    int32_t r, float alpha, void* ws, size_t ws_bytes,
+                                    void* stream);
+
 /* Backward of the same layer with W frozen (no gradient for W; the gradient
  * flows through W' into the adapters):
  *     G  = dY . B

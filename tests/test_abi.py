@@ -328,3 +328,42 @@ def test_batch_argument_errors(q):
         q.QLORA_ERR_UNSUPPORTED
     assert q.qlora_quantize_batch_workspace_bytes([(0, 5)]) == 0
     assert q.qlora_quantize_batch_workspace_bytes([]) == 0
+
+
+def test_linear_batch_argument_errors(q):
+    """The batched forward checks every job before any launch (fake buffers),
+    takes count 0 as nothing to do, and sizes its workspace as the jobs'
+    decode partials side by side (M <= 16) or the largest single-linear
+    workspace (M > 16)."""
+    lib = q.lib()
+    P = ctypes.c_void_p
+    fake = 0x100000
+    d1, d2 = _desc(q, rows=1024, cols=4096), _desc(q, rows=4096, cols=1024)
+    J = q.LinearJob * 2
+    good = J(q.LinearJob(ctypes.pointer(d1), P(fake), P(fake), P(fake), P(fake), None),
+             q.LinearJob(ctypes.pointer(d2), P(fake), P(fake), P(fake), P(fake), None))
+    for M in (1, 16):
+        need = lib.qlora_linear_batch_workspace_bytes(good, 2, M, 16)
+        parts = []
+        for rows, cols in ((1024, 4096), (4096, 1024)):
+            parts.append(-(-(cols // 512) * M * rows * 4 // 256) * 256 +
+                         -(-(cols // 512) * M * 16 * 4 // 256) * 256)
+        assert need == sum(parts), (M, need, parts)
+        assert lib.qlora_linear_fwd_batch(good, 2, M, 16, ctypes.c_float(32.0), P(fake), need - 1,
+                                          None) == q.QLORA_ERR_WORKSPACE
+    big = lib.qlora_linear_batch_workspace_bytes(good, 2, 64, 16)
+    assert big == max(q.qlora_linear_workspace_bytes(64, 1024, 4096, 16),
+                      q.qlora_linear_workspace_bytes(64, 4096, 1024, 16))
+    bad = J(good[0], q.LinearJob(ctypes.pointer(d2), P(fake), P(fake), P(fake), None, None))
+    assert lib.qlora_linear_fwd_batch(bad, 2, 1, 16, ctypes.c_float(32.0), P(fake), 1 << 30,
+                                      None) == q.QLORA_ERR_INVALID_ARG
+    d3 = _desc(q, rows=64, cols=96)        # K not a multiple of 64
+    odd = J(good[0], q.LinearJob(ctypes.pointer(d3), P(fake), P(fake), P(fake), P(fake), None))
+    assert lib.qlora_linear_fwd_batch(odd, 2, 1, 16, ctypes.c_float(32.0), P(fake), 1 << 30,
+                                      None) == q.QLORA_ERR_UNSUPPORTED
+    assert lib.qlora_linear_fwd_batch(good, -1, 1, 16, ctypes.c_float(32.0), P(fake), 1 << 30,
+                                      None) == q.QLORA_ERR_INVALID_ARG
+    assert lib.qlora_linear_fwd_batch(good, 2, 1, 0, ctypes.c_float(32.0), P(fake), 1 << 30,
+                                      None) == q.QLORA_ERR_INVALID_ARG
+    assert lib.qlora_linear_fwd_batch(None, 0, 1, 16, ctypes.c_float(32.0), None, 0, None) == \
+        q.QLORA_OK
