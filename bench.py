@@ -277,22 +277,43 @@ def headline(args, q, torch, workloads):
     A = {K: ((torch.rand((r, K), generator=g, device=dev) * 2 - 1) * K ** -0.5).to(torch.bfloat16)
          for K, _ in shp}
     B = {N: (torch.randn((N, r), generator=g, device=dev) * 0.01).to(torch.bfloat16) for _, N in shp}
-    Y = {N: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _, N in shp}
+    # one output and XA per projection of a layer (the batched forward writes
+    # several at once)
+    Y = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _, _, N in wl.linears]
+    XA = [torch.empty((M, r), dtype=torch.bfloat16, device=dev) for _ in wl.linears]
     dX = {K: torch.empty((M, K), dtype=torch.bfloat16, device=dev) for K, _ in shp}
     dA = {K: torch.empty((r, K), dtype=torch.float32, device=dev) for K, _ in shp}
     dB = {N: torch.empty((N, r), dtype=torch.float32, device=dev) for _, N in shp}
-    XA = {K: torch.empty((M, r), dtype=torch.bfloat16, device=dev) for K, _ in shp}
     ws = q.workspace(max(q.qlora_linear_workspace_bytes(M, N, K, r) for K, N in shp), dev)
+    # the layer driver's forward: the projections that read one input (q/k/v,
+    # gate/up) as one batched call, whose consecutive same-K pairs share a
+    # GEMM launch (q+k, gate+up: 5 forward GEMM launches per layer)
+    names = [nm for nm, _, _ in wl.linears]
+    groups = [[names.index(n) for n in grp] for grp in (("q_proj", "k_proj", "v_proj"),
+                                                         ("o_proj",), ("gate_proj", "up_proj"),
+                                                         ("down_proj",))]
+    per = len(wl.linears)
+    bws = q.workspace(max(q.qlora_linear_batch_workspace_bytes([lin[i][0] for i in grp], M, r)
+                          for grp in groups), dev)
+    fwd_launches = wl.layers * sum((len(grp) + 1) // 2 for grp in groups)
     torch.cuda.synchronize()
     log("headline inputs ready (%d linears, %.1f GB of quantised weights)"
         % (len(lin), sum(Q.nbytes() for Q, _, _ in lin) / 1e9))
 
     def step():
-        for Q, K, N in lin:
-            q.qlora_linear_fwd(Q, X[K], A[K], B[N], alpha, Y=Y[N], XA_out=XA[K], ws=ws,
-                               return_xa=True)
-        for Q, K, N in reversed(lin):
-            q.qlora_linear_bwd(Q, X[K], A[K], B[N], alpha, dY[N], XA_in=XA[K], dX=dX[K],
+        for layer in range(wl.layers):
+            for grp in groups:
+                jobs = [(lin[layer * per + t][0], X[lin[layer * per + t][1]],
+                         A[lin[layer * per + t][1]], B[lin[layer * per + t][2]], Y[t]) for t in grp]
+                if len(jobs) == 1:
+                    Q, Xj, Aj, Bj, Yj = jobs[0]
+                    q.qlora_linear_fwd(Q, Xj, Aj, Bj, alpha, Y=Yj, XA_out=XA[grp[0]], ws=ws,
+                                       return_xa=True)
+                else:
+                    q.qlora_linear_fwd_batch(jobs, alpha, ws=bws, XA_out=[XA[t] for t in grp])
+        for i in reversed(range(len(lin))):
+            Q, K, N = lin[i]
+            q.qlora_linear_bwd(Q, X[K], A[K], B[N], alpha, dY[N], XA_in=XA[i % per], dX=dX[K],
                                dA=dA[K], dB=dB[N], ws=ws)
 
     sec, tr, sampled = timed_steps(args, q, torch, step, ["fwd_gemm", "dx_gemm", "split_reduce"],
@@ -301,12 +322,12 @@ def headline(args, q, torch, workloads):
     # per-kernel algorithmic flops: fwd GEMM 2MN(K + r), dX GEMM 2MK(N + r)
     kflops = {"fwd_gemm": sum(2 * M * N * (K + r) for _, K, N in lin),
               "dx_gemm": sum(2 * M * K * (N + r) for _, K, N in lin)}
-    kern = kernel_table(tr, kflops, {"fwd_gemm": len(lin), "dx_gemm": len(lin)}, sampled)
+    kern = kernel_table(tr, kflops, {"fwd_gemm": fwd_launches, "dx_gemm": len(lin)}, sampled)
     roof = roofline_of(kern)
     roof["timed_steps"] = sampled
     log("headline: %.4f s/step, %.1f TFLOP/s" % (sec, flops / sec / 1e12))
     res = dict(sec=sec, tokens=M, flops=flops, roofline=roof, kernels=kern)
-    del lin, X, dY, A, B, Y, dX, dA, dB, XA, ws
+    del lin, X, dY, A, B, Y, dX, dA, dB, XA, ws, bws
     torch.cuda.empty_cache()
     return res
 

@@ -387,10 +387,11 @@ def qlora_linear_batch_workspace_bytes(qs, M: int, r: int) -> int:
     return int(lib().qlora_linear_batch_workspace_bytes(arr, len(jobs), M, r))
 
 
-def qlora_linear_fwd_batch(jobs, alpha: float, ws=None, return_xa: bool = False):
+def qlora_linear_fwd_batch(jobs, alpha: float, ws=None, return_xa: bool = False, XA_out=None):
     """Forward of independent linears (q, X, A, B[, Y]) with one M and rank r;
-    for M <= 16 up to 8 share each launch pair.  Returns the list of Y (or of
-    (Y, XA) with return_xa)."""
+    for M <= 16 up to 8 share each launch pair, for M > 16 consecutive pairs
+    of one K share a GEMM launch.  XA_out (optional): one [M, r] buffer per
+    job.  Returns the list of Y (or of (Y, XA) with return_xa)."""
     jobs = list(jobs)
     M, r = jobs[0][1].shape[0], jobs[0][2].shape[0]
     full = []
@@ -400,7 +401,10 @@ def qlora_linear_fwd_batch(jobs, alpha: float, ws=None, return_xa: bool = False)
         assert X.shape == (M, q.cols) and A.shape == (r, q.cols) and B.shape == (q.rows, r)
         Y = job[4] if len(job) > 4 and job[4] is not None else \
             torch.empty((M, q.rows), dtype=torch.bfloat16, device=X.device)
-        XA = torch.empty((M, r), dtype=torch.bfloat16, device=X.device) if return_xa else None
+        if XA_out is not None:
+            XA = XA_out[len(full)]
+        else:
+            XA = torch.empty((M, r), dtype=torch.bfloat16, device=X.device) if return_xa else None
         full.append((q, X, A, B, Y, XA))
     arr, keep = _linear_jobs(full)
     if ws is None:

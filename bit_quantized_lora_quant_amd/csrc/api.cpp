@@ -397,6 +397,25 @@ qlora_status qlora_linear_fwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
                                   ws_bytes, stream);
 }
 
+// The forward's work before its GEMM (M > 16): X.A^T -> bf16(s.XA) [M, r32]
+// (GEMM tail) and bf16(XA) [M, r] (caller), with the block constants
+// reconstructed in the same launch; fills the GEMM job of the linear.
+static hipError_t fwd_prep(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
+                           const qlora_bf16* A, const qlora_bf16* B, int32_t r, float scale,
+                           const DropoutParams& dp, qlora_bf16* Y, qlora_bf16* XA_out, void* ws,
+                           const LinearWs& L, hipStream_t s, FwdGemmJob* job) {
+  const int64_t N = W->rows, K = W->cols;
+  float* ahat_t = at<float>(ws, L.ahat_t);
+  uint16_t* xas = at<uint16_t>(ws, L.xas);
+  SkinnyJob xa{X, K, K, A, K, 0, 0, at<float>(ws, L.sk_k), scale, xas, XA_out, nullptr, 0};
+  xa.drop = dp;
+  skinny_plan(&xa, M, r);
+  const ReconJob rc{W->absmax_q, W->absmax_scale, W->absmax_mean, N, K / kBlock, ahat_t,
+                    f32_consts(W)};
+  *job = FwdGemmJob{X, W->codes, N, ahat_t, xas, B, Y};
+  return launch_skinny(&xa, 1, M, r, L.r32, &rc, s);
+}
+
 qlora_status qlora_linear_fwd_dropout(const qlora_nf4_tensor* W, const qlora_bf16* X, int64_t M,
                                       const qlora_bf16* A, const qlora_bf16* B, int32_t r,
                                       float alpha, const qlora_dropout* drop,
@@ -422,21 +441,12 @@ qlora_status qlora_linear_fwd_dropout(const qlora_nf4_tensor* W, const qlora_bf1
     e = traced(QLORA_KERNEL_GEMV, s, [&] { return launch_decode(&d, 1, M, r, scale, s); });
     return hip_status(e);
   }
-  float* ahat_t = at<float>(ws, L.ahat_t);
-  uint16_t* xas = at<uint16_t>(ws, L.xas);
-  // X.A^T -> bf16(s.XA) [M, r32] (GEMM tail) and bf16(XA) [M, r] (caller),
-  // with the block constants reconstructed in the same launch
-  SkinnyJob xa{X, K, K, A, K, 0, 0, at<float>(ws, L.sk_k), scale, xas, XA_out, nullptr, 0};
-  xa.drop = dp;
-  skinny_plan(&xa, M, r);
-  const ReconJob rc{W->absmax_q, W->absmax_scale, W->absmax_mean, N, K / kBlock, ahat_t,
-                    f32_consts(W)};
-  e = launch_skinny(&xa, 1, M, r, L.r32, &rc, s);
-  if (e != hipSuccess) return QLORA_ERR_HIP;
+  FwdGemmJob job;
+  if (fwd_prep(W, X, M, A, B, r, scale, dp, Y, XA_out, ws, L, s, &job) != hipSuccess)
+    return QLORA_ERR_HIP;
   float* part = at<float>(ws, L.gemm_part);
   e = traced(QLORA_KERNEL_FWD_GEMM, s, [&] {
-    return launch_fwd_gemm(X, M, K, W->codes, N, ahat_t, xas, B, r, L.r32, Y, L.sf, part,
-                           W->quant_type, s);
+    return launch_fwd_gemm(&job, 1, M, K, r, L.r32, L.sf, part, W->quant_type, s);
   });
   if (e == hipSuccess && L.sf > 1)
     e = traced(QLORA_KERNEL_SPLIT_REDUCE, s,
@@ -458,9 +468,8 @@ size_t qlora_linear_batch_workspace_bytes(const qlora_linear_job* jobs, int32_t 
   for (int32_t i = 0; i < count; ++i) {
     const qlora_nf4_tensor* W = jobs[i].W;
     if (!valid_tensor(W) || !linear_fits(M, W->rows, W->cols)) return 0;
-    const size_t b = M <= 16 ? decode_job_bytes(M, W->rows, W->cols, r)
-                             : linear_layout(M, W->rows, W->cols, r).total;
-    total = M <= 16 ? total + b : std::max(total, b);
+    total += M <= 16 ? decode_job_bytes(M, W->rows, W->cols, r)
+                     : linear_layout(M, W->rows, W->cols, r).total;
   }
   return total;
 }
@@ -479,18 +488,50 @@ qlora_status qlora_linear_fwd_batch(const qlora_linear_job* jobs, int32_t count,
   const size_t need = qlora_linear_batch_workspace_bytes(jobs, count, M, r);
   if (!ws || ws_bytes < need || !aligned(ws, kAlign)) return QLORA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const float scale = alpha / (float)r;
   if (M > 16) {
-    // the GEMM path, one linear after another on the one workspace
-    for (int32_t i = 0; i < count; ++i) {
-      const qlora_linear_job& j = jobs[i];
-      const qlora_status st = qlora_linear_fwd_dropout(j.W, j.X, M, j.A, j.B, r, alpha, nullptr,
-                                                       nullptr, j.Y, j.XA_out, ws, ws_bytes,
-                                                       stream);
-      if (st != QLORA_OK) return st;
+    // the GEMM path, each job on its own workspace region; two consecutive
+    // jobs with one K and table kind and no split share one GEMM launch
+    size_t off = 0;
+    for (int32_t i = 0; i < count;) {
+      const qlora_linear_job& a = jobs[i];
+      const LinearWs La = linear_layout(M, a.W->rows, a.W->cols, r);
+      void* wa = at<uint8_t>(ws, off);
+      bool pair = false;
+      LinearWs Lb{};
+      if (i + 1 < count) {
+        const qlora_linear_job& b = jobs[i + 1];
+        Lb = linear_layout(M, b.W->rows, b.W->cols, r);
+        pair = b.W->cols == a.W->cols && b.W->quant_type == a.W->quant_type && La.sf == 1 &&
+               Lb.sf == 1;
+      }
+      if (!pair) {
+        const qlora_status st = qlora_linear_fwd_dropout(a.W, a.X, M, a.A, a.B, r, alpha,
+                                                         nullptr, nullptr, a.Y, a.XA_out, wa,
+                                                         La.total, stream);
+        if (st != QLORA_OK) return st;
+        off += La.total;
+        i += 1;
+        continue;
+      }
+      const qlora_linear_job& b = jobs[i + 1];
+      void* wb = at<uint8_t>(ws, off + La.total);
+      FwdGemmJob g[2];
+      hipError_t e = fwd_prep(a.W, a.X, M, a.A, a.B, r, scale, DropoutParams{}, a.Y, a.XA_out,
+                              wa, La, s, &g[0]);
+      if (e == hipSuccess)
+        e = fwd_prep(b.W, b.X, M, b.A, b.B, r, scale, DropoutParams{}, b.Y, b.XA_out, wb, Lb, s,
+                     &g[1]);
+      if (e == hipSuccess)
+        e = traced(QLORA_KERNEL_FWD_GEMM, s, [&] {
+          return launch_fwd_gemm(g, 2, M, a.W->cols, r, La.r32, 1, nullptr, a.W->quant_type, s);
+        });
+      if (e != hipSuccess) return hip_status(e);
+      off += La.total + Lb.total;
+      i += 2;
     }
     return QLORA_OK;
   }
-  const float scale = alpha / (float)r;
   DecodeJob group[kDecodeBatch];
   size_t off = 0;
   int m = 0;

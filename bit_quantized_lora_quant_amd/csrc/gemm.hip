@@ -217,11 +217,8 @@ constexpr int kThreadsW8 = 512;
 
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreadsW8, kThreadsW8),
                           amdgpu_waves_per_eu(2, 2)))
-void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
-                    const uint8_t* __restrict__ codes, int64_t N,
-                    const float* __restrict__ ahat_t, NF4Tables tab,
-                    const uint16_t* __restrict__ xas, const uint16_t* __restrict__ B, int r,
-                    int r32, uint16_t* __restrict__ Y, int splits, int ksteps,
+void k_qlora_fwd_nt(const FwdGemmJob j0, const FwdGemmJob j1, int64_t tn_split, int64_t M,
+                    int64_t K, NF4Tables tab, int r, int r32, int splits, int ksteps,
                     float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint16_t xs0[kTile * kStep];
   __shared__ __attribute__((aligned(16))) uint16_t xs1[kTile * kStep];
@@ -240,6 +237,17 @@ void k_qlora_fwd_nt(const uint16_t* __restrict__ X, int64_t M, int64_t K,
   int64_t tm, tn;
   int split;
   tile_coords_split(ceil_div(M, kTile), splits, tm, tn, split);
+  // two linears in one launch: the column tiles of the second follow the first's
+  const bool second = tn >= tn_split;
+  if (second) tn -= tn_split;
+  const FwdGemmJob& J = second ? j1 : j0;
+  const uint16_t* __restrict__ X = J.X;
+  const uint8_t* __restrict__ codes = J.codes;
+  const int64_t N = J.N;
+  const float* __restrict__ ahat_t = J.ahat_t;
+  const uint16_t* __restrict__ xas = J.xas;
+  const uint16_t* __restrict__ B = J.B;
+  uint16_t* __restrict__ Y = J.Y;
   const int64_t m0 = tm * kTile, n0 = tn * kTile;
   if (tid < 16) lvl[tid] = tab.level[tid];
   if (tid < 256) lvlp[tid] = make_float2(tab.level[tid & 15], tab.level[tid >> 4]);
@@ -1055,14 +1063,16 @@ int dx_splits(int64_t M, int64_t N, int64_t K) {
   return fwd_splits(M, K, N);
 }
 
-hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes,
-                           int64_t N, const float* ahat_t, const uint16_t* xas, const uint16_t* B,
-                           int r, int r32, uint16_t* Y, int splits, float* part, int kind,
-                           hipStream_t s) {
+hipError_t launch_fwd_gemm(const FwdGemmJob* jobs, int count, int64_t M, int64_t K, int r,
+                           int r32, int splits, float* part, int kind, hipStream_t s) {
+  if (count < 1 || count > 2 || (count == 2 && splits != 1)) return hipErrorInvalidValue;
   const int ksteps = (int)ceil_div(K / kStep, splits);
-  const int64_t grid = ceil_div(M, kTile) * ceil_div(N, kTile) * splits;
-  return launch_kernel(k_qlora_fwd_nt, dim3((unsigned)grid), dim3(kThreadsW8), s, X, M, K, codes, N,
-                       ahat_t, host_tables(kind), xas, B, r, r32, Y, splits, ksteps, part);
+  const int64_t tn0 = ceil_div(jobs[0].N, kTile);
+  const int64_t tn = tn0 + (count == 2 ? ceil_div(jobs[1].N, kTile) : 0);
+  const int64_t grid = ceil_div(M, kTile) * tn * splits;
+  return launch_kernel(k_qlora_fwd_nt, dim3((unsigned)grid), dim3(kThreadsW8), s, jobs[0],
+                       count == 2 ? jobs[1] : jobs[0], tn0, M, K, host_tables(kind), r, r32,
+                       splits, ksteps, part);
 }
 
 hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes,

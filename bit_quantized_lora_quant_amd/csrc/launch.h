@@ -152,10 +152,21 @@ hipError_t launch_lora_grads(const GradJob* jobs, int njobs, int64_t M, int r, h
 // The *_splits functions return the slice count (every slice non-empty).
 int fwd_splits(int64_t M, int64_t N, int64_t K);
 int dx_splits(int64_t M, int64_t N, int64_t K);
-hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, int64_t K, const uint8_t* codes,
-                           int64_t N, const float* ahat_t, const uint16_t* xas, const uint16_t* B,
-                           int r, int r32, uint16_t* Y, int splits, float* part, int kind,
-                           hipStream_t s);
+// One linear of a forward GEMM launch: X [M, K], the 4-bit codes and the
+// reconstructed constants [K/64][N] of W, bf16(s XA) [M, r32], B [N, r],
+// Y [M, N].  A launch takes one linear, or two with one M, K, rank and table
+// kind (and no split), the second's column tiles after the first's.
+struct FwdGemmJob {
+  const uint16_t* X;
+  const uint8_t* codes;
+  int64_t N;
+  const float* ahat_t;
+  const uint16_t* xas;
+  const uint16_t* B;
+  uint16_t* Y;
+};
+hipError_t launch_fwd_gemm(const FwdGemmJob* jobs, int count, int64_t M, int64_t K, int r,
+                           int r32, int splits, float* part, int kind, hipStream_t s);
 // drop (nullable): the LoRA term of dX passes through the dropout of X,
 // dX = dY . W' + keep / (1 - p) * (s.G . A), element by element.
 hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, int64_t N, const uint8_t* codes,

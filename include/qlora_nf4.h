@@ -223,13 +223,15 @@ qlora_status qlora_linear_fwd(const qlora_nf4_tensor* W, const qlora_bf16* X, in
  * For M <= 16 (decode) up to 8 of them share one weight-streaming launch and
  * one finish launch, so the small ones cost no launches of their own; each
  * Y (and XA) equals what qlora_linear_fwd gives for that job alone.  For
- * M > 16 the jobs run one after another through qlora_linear_fwd.
+ * M > 16 two consecutive jobs with one K and 4-bit type, large enough to need
+ * no split of K, share one GEMM launch (their column tiles in one grid, so a
+ * partial last round of one fills with the other's tiles); the results equal
+ * the single calls' as well.
  *   jobs   host array of count jobs; per job W, X [M, K], A [r, K], B [N, r],
  *          Y [M, N] (16-byte aligned) and XA_out [M, r] or NULL, all device
  *          memory, as in qlora_linear_fwd; no two jobs may share an output.
  *   ws     device workspace of at least qlora_linear_batch_workspace_bytes()
- *          (the jobs' decode partials side by side; for M > 16 the largest
- *          single-linear workspace).
+ *          (the jobs' own workspaces side by side).
  * Without dropout.  count 0 does nothing.  Errors as qlora_linear_fwd, for
  * the first job that fails a check, before anything is launched. */
 typedef struct qlora_linear_job {

@@ -332,9 +332,8 @@ def test_batch_argument_errors(q):
 
 def test_linear_batch_argument_errors(q):
     """The batched forward checks every job before any launch (fake buffers),
-    takes count 0 as nothing to do, and sizes its workspace as the jobs'
-    decode partials side by side (M <= 16) or the largest single-linear
-    workspace (M > 16)."""
+    takes count 0 as nothing to do, and sizes its workspace as the jobs' own
+    workspaces side by side (decode partials for M <= 16)."""
     lib = q.lib()
     P = ctypes.c_void_p
     fake = 0x100000
@@ -352,8 +351,8 @@ def test_linear_batch_argument_errors(q):
         assert lib.qlora_linear_fwd_batch(good, 2, M, 16, ctypes.c_float(32.0), P(fake), need - 1,
                                           None) == q.QLORA_ERR_WORKSPACE
     big = lib.qlora_linear_batch_workspace_bytes(good, 2, 64, 16)
-    assert big == max(q.qlora_linear_workspace_bytes(64, 1024, 4096, 16),
-                      q.qlora_linear_workspace_bytes(64, 4096, 1024, 16))
+    assert big == q.qlora_linear_workspace_bytes(64, 1024, 4096, 16) + \
+        q.qlora_linear_workspace_bytes(64, 4096, 1024, 16)
     bad = J(good[0], q.LinearJob(ctypes.pointer(d2), P(fake), P(fake), P(fake), None, None))
     assert lib.qlora_linear_fwd_batch(bad, 2, 1, 16, ctypes.c_float(32.0), P(fake), 1 << 30,
                                       None) == q.QLORA_ERR_INVALID_ARG

@@ -73,3 +73,55 @@ def test_batch_of_a_70b_layer_attention_inputs(q):
     torch.cuda.synchronize()
     for i, (Yb, Ys) in enumerate(zip(got, single)):
         assert torch.equal(Yb.view(torch.int16), Ys.view(torch.int16)), "Y of job %d" % i
+
+
+PAIR_SHAPES = [(1000, 512, "nf4", True), (777, 512, "nf4", True), (640, 512, "int4", True),
+               (300, 512, "int4", False), (1500, 1024, "nf4", True), (256, 512, "nf4", True)]
+
+
+def test_gemm_pairs_equal_single_calls(q):
+    """M = 300 tokens with K = 512 (no split of K at any N): consecutive jobs
+    of one K and table share a GEMM launch -- (1000, 777) and (640, 300),
+    then 1500 alone (another K) and 256 alone -- and every Y and XA equals
+    the single call's bit for bit; two of them also against the oracle."""
+    M = 300
+    jobs = _jobs(q, M, PAIR_SHAPES, seed=300)
+    say("linear batch GEMM pairs M=%d" % M)
+    got = q.qlora_linear_fwd_batch([j[:4] for j in jobs], ALPHA, return_xa=True)
+    single = [q.qlora_linear_fwd(qq, X, A, B, ALPHA, return_xa=True) for qq, X, A, B, *_ in jobs]
+    torch.cuda.synchronize()
+    for i, ((Yb, XAb), (Ys, XAs)) in enumerate(zip(got, single)):
+        assert torch.equal(Yb.view(torch.int16), Ys.view(torch.int16)), "Y of job %d" % i
+        assert torch.equal(XAb.view(torch.int16), XAs.view(torch.int16)), "XA of job %d" % i
+    for i in (1, 3):
+        qq, X, A, B, w, kind, dq = jobs[i]
+        wd = oracle.dequantize(oracle.quantize(w.reshape(-1), kind=kind, dq=dq)).reshape(w.shape)
+        y_ref, xa_ref = oracle.linear_fwd(wd.astype(np.float64), bf16_np(X), bf16_np(A),
+                                          bf16_np(B), ALPHA)
+        assert_close("Y", bf16_np(got[i][0]), y_ref)
+        assert_close("XA", bf16_np(got[i][1]), xa_ref)
+
+
+def test_gemm_pair_of_the_65b_gate_and_up(q):
+    """The LLaMA-65B gate and up projections (8192 -> 22016 each, r = 64) at
+    4096 tokens as one paired GEMM launch (2752 tiles): both outputs equal
+    the single calls' bit for bit."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(65)
+    M, K, N, r = 4096, 8192, 22016, 64
+    say("linear batch 65B gate/up pair")
+    jobs = []
+    for _ in range(2):
+        W = torch.randn((N, K), generator=g, device=DEV) * 0.02
+        qq, _ = q.qlora_quantize_nf4(W)
+        del W
+        X = torch.randn((M, K), generator=g, device=DEV).to(torch.bfloat16)
+        A = (torch.randn((r, K), generator=g, device=DEV) * 0.01).to(torch.bfloat16)
+        B = (torch.randn((N, r), generator=g, device=DEV) * 0.01).to(torch.bfloat16)
+        jobs.append((qq, X, A, B))
+    jobs[1] = (jobs[1][0], jobs[0][1], jobs[1][2], jobs[1][3])   # one shared input
+    got = q.qlora_linear_fwd_batch(jobs, 16.0)
+    single = [q.qlora_linear_fwd(*j, 16.0) for j in jobs]
+    torch.cuda.synchronize()
+    for i in range(2):
+        assert torch.equal(got[i].view(torch.int16), single[i].view(torch.int16)), "Y %d" % i
