@@ -727,7 +727,8 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
                        const uint16_t* __restrict__ gs, const uint16_t* __restrict__ A, int r,
                        int r32, uint16_t* __restrict__ dX, int splits, int nsteps,
                        float* __restrict__ part, DropoutParams drop) {
-  __shared__ __attribute__((aligned(1024))) float lvl[16];   // at LDS address 0
+  __shared__ __attribute__((aligned(2048))) float2 lvlp[256];   // at LDS address 0
+  __shared__ float lvl[16];
   __shared__ __attribute__((aligned(16))) uint16_t ys0[kTile * kStep];
   __shared__ __attribute__((aligned(16))) uint16_t ys1[kTile * kStep];
   __shared__ __attribute__((aligned(16))) uint16_t ys2[kTile * kStep];
@@ -745,6 +746,7 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
   tile_coords_split(ceil_div(M, kTile), splits, tm, tn, split);
   const int64_t m0 = tm * kTile, k0 = tn * kTile;
   if (tid < 16) lvl[tid] = tab.level[tid];
+  lvlp[tid] = make_float2(tab.level[tid & 15], tab.level[tid >> 4]);
 
   const int64_t kc = k0 + 64 * wv + 4 * j16;      // first of this lane's 4 columns
   const bool kvalid = kc < K;                       // K % 64 == 0: all 4 or none
@@ -842,29 +844,28 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
   // Slice i (0..31) of a step builds bop[s ^ 1][t = i & 3][q = (i >> 2) & 3]
   // from pair-word k = i >> 2 of the step's sequence: this step's sub-step 1
   // (k < 4), the next step's sub-step 0 (k < 8), and for the lookahead the
-  // next step's sub-step 1 (k = 8, 9).  Group schedule and lookup addressing
-  // as in the forward kernel; a pair-word spreads into 4 x nibble bytes
-  // [row 2q: t0 t2, row 2q+1: t0 t2] and [.. t1 t3 ..].
-  auto lvl_at = [&](uint32_t off) { return *reinterpret_cast<const float*>(
-                                        reinterpret_cast<const char*>(lvl) + off); };
+  // next step's sub-step 1 (k = 8, 9).  Group schedule as in the forward
+  // kernel.  Byte 2 hi + c of a pair-word holds row 2q + hi at columns 2c
+  // (low nibble) and 2c + 1, so an even slice looks up both rows' level
+  // pairs (256-entry table at LDS address 0) for itself and the next slice:
+  // half the lookups of a 16-entry table, bit-identical, about 6% faster.
+  auto pair_at = [&](uint32_t off) { return *reinterpret_cast<const float2*>(
+                                         reinterpret_cast<const char*>(lvlp) + off); };
   auto word = [&](int k) -> uint32_t {
     const int q = k & 3;
     return k < 4 ? cc[4 + q] : (k < 8 ? cn[q] : cn[4 + q]);
   };
-  uint32_t w4lo[2], w4hi[2];
+  uint32_t wev[2], wod[2];
   auto spread = [&](int k) {
     const uint32_t w = word(k);
-    w4lo[k & 1] = (w << 2) & 0x3C3C3C3Cu;
-    w4hi[k & 1] = (w >> 2) & 0x3C3C3C3Cu;
-    asm volatile("" : "+v"(w4lo[k & 1]), "+v"(w4hi[k & 1]));
+    wev[k & 1] = (w & 0x00FF00FFu) << 3;
+    wod[k & 1] = (w >> 5) & 0x07F807F8u;
+    asm volatile("" : "+v"(wev[k & 1]), "+v"(wod[k & 1]));
   };
-  auto byte_of = [](uint32_t w, int b) -> uint32_t {
-    return b == 0 ? (w & 0xFFu) : (b == 3 ? (w >> 24) : ((w >> (8 * b)) & 0xFFu));
-  };
-  // row (hi) of column t in a spread pair-word
-  auto lookup = [&](int k, int t, int hi) {
-    const uint32_t w = (t & 1) ? w4hi[k & 1] : w4lo[k & 1];
-    return lvl_at(byte_of(w, 2 * hi + (t >> 1)));
+  // row (hi) at columns t and t + 1 (t even): byte 2 hi + t / 2 of the pair-word
+  auto pair_lookup = [&](int k, int t, int hi) {
+    const uint32_t w = (t & 2) ? wod[k & 1] : wev[k & 1];
+    return pair_at(hi ? (w >> 16) : (w & 0xFFFFu));
   };
   constexpr int kD = 4;
   uint4 aq[kD];
@@ -874,8 +875,11 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
 #pragma unroll
   for (int d = 0; d < kD; ++d) {
     aq[d] = lds_chunk(ys0, d * 16 + j16, g);
-    lqa[d] = lookup(0, d, 0);
-    lqb[d] = lookup(0, d, 1);
+    if ((d & 1) == 0) {
+      const float2 pa = pair_lookup(0, d, 0), pb = pair_lookup(0, d, 1);
+      lqa[d] = pa.x; lqa[d + 1] = pa.y;
+      lqb[d] = pb.x; lqb[d + 1] = pb.y;
+    }
   }
 
   auto step = [&](uint32_t it, const uint16_t* yb, uint16_t* yd, uint8_t* cd, float* ad,
@@ -888,7 +892,11 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
       const int ia = i + kD, ka = ia >> 2;
       mfma_acc(acc[mt][0], aq[qd], u32x4v_t{bop[s][0][0], bop[s][0][1], bop[s][0][2], bop[s][0][3]});
       __builtin_amdgcn_sched_barrier(0);
-      lqa[ia & 7] = lookup(ka, ia & 3, 0);
+      if ((ia & 1) == 0) {
+        const float2 pa = pair_lookup(ka, ia & 3, 0);
+        lqa[ia & 7] = pa.x;
+        lqa[(ia + 1) & 7] = pa.y;
+      }
       if ((i & 7) == 0) {   // dY tile it+2: two of this wave's eight loads
 #pragma unroll
         for (int l = 2 * (i >> 3); l < 2 * (i >> 3) + 2; ++l)
@@ -897,7 +905,11 @@ void k_qlora_dx_nn_dma(const uint16_t* __restrict__ dY, int64_t M, int64_t N,
       __builtin_amdgcn_sched_barrier(0);
       mfma_acc(acc[mt][1], aq[qd], u32x4v_t{bop[s][1][0], bop[s][1][1], bop[s][1][2], bop[s][1][3]});
       __builtin_amdgcn_sched_barrier(0);
-      lqb[ia & 7] = lookup(ka, ia & 3, 1);
+      if ((ia & 1) == 0) {
+        const float2 pb = pair_lookup(ka, ia & 3, 1);
+        lqb[ia & 7] = pb.x;
+        lqb[(ia + 1) & 7] = pb.y;
+      }
       if ((i & 3) == 0) spread((i >> 2) + 2);
       if (i == 4) issue_codes(tc, cd, ad);
       __builtin_amdgcn_sched_barrier(0);
