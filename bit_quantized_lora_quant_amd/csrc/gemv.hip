@@ -283,7 +283,7 @@ __device__ __forceinline__ int job_index(const int64_t* first, int count, int64_
 }
 
 template <int RT>
-__global__ __launch_bounds__(256) void k_qlora_decode(const DecodeBatch bt, int r) {
+__device__ __forceinline__ void decode_body(const DecodeBatch& bt, int r) {
   // one LDS arena (sized per launch) for either branch: [16 bf16 levels |
   // code tile | X rows 0..M, row M zero] or the 4 KB of XA wave partials
   extern __shared__ __attribute__((aligned(16))) uint8_t arena[];
@@ -300,6 +300,20 @@ __global__ __launch_bounds__(256) void k_qlora_decode(const DecodeBatch bt, int 
       tab16[threadIdx.x] = (uint16_t)(pack_bf16x2(bt.level[bt.kind[j]][threadIdx.x], 0.f) & 0xFFFF);
     decode_rows(a, tab16, cs, xs, b - a.xa_blocks);   // its barrier also covers the table
   }
+}
+
+// Two entry points of one body: up to 4 tokens, where the arena fits 7-8
+// workgroups per CU, the registers are held to 64 so that as many fit (3%
+// faster at one token than the 6 that 74 registers allow); from 5 tokens the
+// X rows limit the workgroups per CU anyway and the registers are left free.
+template <int RT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void k_qlora_decode_narrow(const DecodeBatch bt, int r) {
+  decode_body<RT>(bt, r);
+}
+template <int RT>
+__global__ __launch_bounds__(256) void k_qlora_decode(const DecodeBatch bt, int r) {
+  decode_body<RT>(bt, r);
 }
 
 // src[0] + src[stride] + ... over the first min(count, 16) terms, in order,
@@ -402,8 +416,8 @@ template <int RT>
 hipError_t decode_rt(const DecodeBatch& bt, int64_t M, int r, int64_t blocks, hipStream_t s) {
   const size_t stream = kDecTab + kDecCodes + (size_t)(M + 1) * kDecXStride * 2;
   const size_t xa = (size_t)kXaWaves * 4 * 64 * 4;
-  return launch_kernel_lds(k_qlora_decode<RT>, dim3((unsigned)blocks), dim3(256),
-                           stream > xa ? stream : xa, s, bt, r);
+  return launch_kernel_lds(M <= 4 ? k_qlora_decode_narrow<RT> : k_qlora_decode<RT>,
+                           dim3((unsigned)blocks), dim3(256), stream > xa ? stream : xa, s, bt, r);
 }
 
 }  // namespace
