@@ -677,6 +677,34 @@ def leg_adamw(q, torch, workloads, reps=10):
         ts = None
         flat.free()
         del flat
+    # the placement policy: an HBM budget of half the 8-bit statistics' bytes;
+    # the largest tensors' statistics stay on the device, the rest are mapped
+    # from host memory
+    numels = [a * b for a, b in shapes]
+    need = sum(q.adamw8_state_bytes(n) for n in numels)
+    states = q.adamw8_states(numels, dev, hbm_budget=need // 2)
+    ts, off = [], 0
+    for n, st in zip(numels, states):
+        ts.append((P[off:off + n], G[off:off + n], st, PB[off:off + n]))
+        off += n
+
+    def step_half():
+        q.qlora_adamw8_step(ts, 1, 2e-4, 0.9, 0.999, 1e-8, 0.01)
+
+    step_half()
+    gr = graph_of(torch, step_half)
+    sec = timed(torch, gr.replay, reps)
+    del gr
+    on_host = sum(st.nbytes() for st in states if st.on_host)
+    res["half_hbm_statistics_8bit"] = {
+        "step_ms": round(sec * 1e3, 4), "hbm_budget_bytes": need // 2,
+        "host_state_bytes": on_host, "host_tensors": sum(1 for st in states if st.on_host),
+        "placement": "plan_state_placement: largest tensors in HBM until the budget is spent"}
+    torch.cuda.synchronize()
+    ts = None
+    for st in states:
+        st.free()
+    del states
     del P, G, PB
     torch.cuda.empty_cache()
     log("adamw leg: %.3f / %.3f ms with float32 / 8-bit device statistics, %.3f / %.3f ms "

@@ -614,6 +614,7 @@ class AdamW8State:
     def __init__(self, numel: int, device, host: bool = False):
         nb = (numel + ADAMW8_BLOCK - 1) // ADAMW8_BLOCK
         self.numel = numel
+        self.on_host = bool(host)
         self._host = []
         if host:
             bufs = [HostState(numel, torch.int8), HostState(nb, torch.float32),
@@ -638,6 +639,40 @@ class AdamW8State:
         for b in self._host:
             b.free()
         self._host = []
+
+
+def adamw8_state_bytes(numel: int) -> int:
+    """Bytes of the 8-bit statistics of `numel` parameters (two codes per
+    parameter, two float32 scales per 256)."""
+    return 2 * numel + 8 * ((numel + ADAMW8_BLOCK - 1) // ADAMW8_BLOCK)
+
+
+def plan_state_placement(state_bytes, hbm_budget: int):
+    """Placement of optimiser statistics under an HBM budget (the paged
+    optimiser of the pages, made explicit: this part has no managed memory to
+    migrate pages on demand).  Every step reads and writes every tensor's
+    statistics once, so the bytes left in host memory cross the host link each
+    step; keeping the largest tensors in HBM first leaves the fewest of them
+    there for a given budget.  Returns, per tensor in the given order, True
+    when its statistics go to pinned, device-mapped host memory.  No tensor
+    placed in host memory would have fit in the budget left over."""
+    sizes = [int(b) for b in state_bytes]
+    left = int(hbm_budget)
+    host = [True] * len(sizes)
+    for i in sorted(range(len(sizes)), key=lambda i: (-sizes[i], i)):
+        if sizes[i] <= left:
+            host[i] = False
+            left -= sizes[i]
+    return host
+
+
+def adamw8_states(numels, device, hbm_budget: int = None):
+    """AdamW8State for each tensor size, placed by plan_state_placement
+    (all in HBM without a budget)."""
+    numels = [int(n) for n in numels]
+    host = ([False] * len(numels) if hbm_budget is None else
+            plan_state_placement([adamw8_state_bytes(n) for n in numels], hbm_budget))
+    return [AdamW8State(n, device, host=h) for n, h in zip(numels, host)]
 
 
 def qlora_trace_begin(kernels, capacity: int = 4096):

@@ -35,14 +35,15 @@ def _run(q, sizes, steps, host_state=False, offset=0, seed=0):
     tensor `offset` elements into its buffer (the element-wise path)."""
     rng = np.random.default_rng(seed)
     dev_t, ora = [], []
-    for n in sizes:
+    for i, n in enumerate(sizes):
         p0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
         pbuf = torch.zeros(n + offset, dtype=torch.float32, device=DEV)
         p = pbuf[offset:]
         p.copy_(torch.from_numpy(p0))
         gbuf = torch.zeros(n + offset, dtype=torch.float32, device=DEV)
         pbb = torch.zeros(n + offset, dtype=torch.bfloat16, device=DEV)
-        st = q.AdamW8State(n, DEV, host=host_state)
+        on_host = host_state[i] if isinstance(host_state, (list, tuple)) else host_state
+        st = q.AdamW8State(n, DEV, host=on_host)
         dev_t.append((p, gbuf, st, pbb[offset:], offset))
         z = (n + 255) // 256
         ora.append([p0, np.zeros(n, np.int8), np.zeros(z, np.float32), np.zeros(n, np.uint8),
@@ -80,6 +81,20 @@ def test_bit_exact_over_steps(q):
 
 def test_host_resident_state(q):
     _run(q, [256, 1000, 70001], steps=3, host_state=True, seed=1)
+
+
+def test_statistics_split_by_an_hbm_budget(q):
+    """Half the statistics' bytes in HBM, the rest mapped from host memory, in
+    one launch: the placement changes no bit."""
+    sizes = [70001, 256, 4099, 1000, 65536 + 17, 3, 30000]
+    need = sum(q.adamw8_state_bytes(n) for n in sizes)
+    flags = q.plan_state_placement([q.adamw8_state_bytes(n) for n in sizes], need // 2)
+    assert any(flags) and not all(flags)
+    states = q.adamw8_states(sizes, DEV, hbm_budget=need // 2)
+    assert [st.on_host for st in states] == flags
+    for st in states:
+        st.free()
+    _run(q, sizes, steps=3, host_state=flags, seed=4)
 
 
 def test_more_tensors_than_one_launch(q):
