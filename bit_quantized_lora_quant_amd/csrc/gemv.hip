@@ -28,6 +28,14 @@
 namespace qnf4 {
 namespace {
 
+// dma16 marked non-temporal: the code tiles are streamed once and no other
+// workgroup reads them again (2% faster decode than the default policy).
+__device__ __forceinline__ void dma16_nt(const void* g, const void* lds) {
+  const uint32_t a = (uint32_t)(uintptr_t)(lds_void_t*)lds;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :: "v"(g), "s"(a) : "m0", "memory");
+}
+
 constexpr int kDecRows = 64;      // weight rows per streaming workgroup (4 waves x 16)
 // 8 blocks (a 16 KB code tile) rather than 16: twice the workgroups fit in
 // LDS at once, so more tiles are in flight while others compute (14-18%
@@ -121,7 +129,7 @@ __device__ __forceinline__ void decode_rows(const DecodeArgs& a, const uint16_t*
       nr = nr < a.N ? nr : a.N - 1;
       int q = (lane % kDecRowChunks) ^ (r & 15);
       q = q < 2 * nblk ? q : 2 * nblk - 1;
-      dma16(a.codes + nr * (a.K / 2) + 32 * kb0 + 16 * q, cs + jj * 1024);
+      dma16_nt(a.codes + nr * (a.K / 2) + 32 * kb0 + 16 * q, cs + jj * 1024);
     }
   }
   // X[m][64 kb0 .. 64 (kb0 + 16)) into LDS rows 0..M-1 by DMA: two 1 KB
