@@ -24,8 +24,11 @@ constexpr int kThreads = 256;
 // reads the float4 at chunk + 256 i + 4 l, so each load instruction covers 1
 // KB contiguously and a lane has eight 16-byte loads in flight (2% faster
 // than four); the 16 lanes of a DPP row then hold exactly one 64-block,
-// whose absmax is four DPP max steps.  The 4 codes of a lane and load leave
-// as one 16-bit store (128 contiguous bytes per wave).
+// whose absmax is four DPP max steps.  In a whole chunk the 4 codes of a
+// lane and load go to a per-wave LDS stage, and the chunk's 1 KB of codes
+// leaves as one non-temporal 16-byte store per lane (3% faster than sixteen-
+// bit stores straight from the coding loop); its 32 block constants leave as
+// one 4-byte store on 32 lanes.  A ragged chunk stores element by element.
 constexpr int kQChunk = 2048;
 
 // Nearest-level code of x in [-1, 1] = number of thresholds below x, found
@@ -104,12 +107,18 @@ struct QuantBatch {
 
 __global__ __launch_bounds__(kThreads) void k_quant_absmax_nf4(const QuantBatch b) {
   __shared__ Bucket buckets[2][256];
+  // per wave: the chunk's codes and block constants, staged so that they
+  // leave as one 16-byte store per lane and one 4-byte store per lane
+  __shared__ __attribute__((aligned(16))) uint8_t cstage[kThreads / 64][kQChunk / 2];
+  __shared__ float astage[kThreads / 64][kQChunk / kBlock];
   build_buckets(buckets[0], b.tab[0]);
   build_buckets(buckets[1], b.tab[1]);
   __syncthreads();
   const int lane = threadIdx.x & 63;
-  const int64_t wave =
-      (int64_t)blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wi = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t* const cst = cstage[wi];
+  float* const ast = astage[wi];
+  const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + wi;
   const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
   const int64_t total = b.first[b.count];
   int j = 0;
@@ -146,7 +155,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_absmax_nf4(const QuantBatch 
       const float a = row16_max(m);
       const int64_t e0 = base + 256 * i + 4 * lane;          // first element of this lane
       const int64_t blk = e0 / kBlock;
-      if ((lane & 15) == 0 && e0 < n) absmax[blk] = a;
+      if ((lane & 15) == 0) {
+        if (full) ast[4 * i + (lane >> 4)] = a;
+        else if (e0 < n) absmax[blk] = a;
+      }
       uint32_t packed = 0;
       // x = w / a, correctly rounded.  When every block of the wave has its
       // absmax in [2^-60, 2^60] (or 0): one IEEE reciprocal r = 1/a per block
@@ -173,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_absmax_nf4(const QuantBatch 
         }
       }
       if (full) {
-        *reinterpret_cast<uint16_t*>(codes + (e0 >> 1)) = (uint16_t)packed;
+        *reinterpret_cast<uint16_t*>(cst + 128 * i + 2 * lane) = (uint16_t)packed;
       } else {
         // bytes holding elements (e0, e0+1) and (e0+2, e0+3); a missing odd
         // element leaves its high nibble 0
@@ -187,6 +199,16 @@ __global__ __launch_bounds__(kThreads) void k_quant_absmax_nf4(const QuantBatch 
           }
         }
       }
+    }
+    if (full) {
+      // lane l stores bytes 16 l .. 16 l + 15 of the chunk's codes, and lanes
+      // 0..31 its 32 block constants (the stage is this wave's own)
+      __builtin_amdgcn_wave_barrier();
+      const uint4 o = *reinterpret_cast<const uint4*>(cst + 16 * lane);
+      __builtin_nontemporal_store(u32x4_t{o.x, o.y, o.z, o.w},
+                                  reinterpret_cast<u32x4_t*>(codes + (base >> 1) + 16 * lane));
+      if (lane < kQChunk / kBlock) absmax[base / kBlock + lane] = ast[lane];
+      __builtin_amdgcn_wave_barrier();
     }
   }
 }
