@@ -4,8 +4,8 @@
 // Two launches per call.  The first holds two kinds of workgroup:
 //  * LoRA down-projection slices: X . A^T over inner-index slices (first in
 //    the grid, so they start early and leave no tail);
-//  * weight streamers: 64 rows of W by at most 8 64-blocks (512 inner
-//    indices).  A streamer stages its code tile and its slice of X in LDS
+//  * weight streamers: 64 rows of W (128 beyond 4 tokens) by at most 8
+//    64-blocks (512 inner indices), 16 rows per wave.  A streamer stages its code tile and its slice of X in LDS
 //    by DMA (4 rows x 256 contiguous bytes per load), then per 64-block turns each lane's
 //    16 codes into bf16 levels through a 16-entry LDS table at address 0
 //    (one conflict-free 16-bit lookup per code, no multiply: a 256-entry
@@ -36,7 +36,11 @@ __device__ __forceinline__ void dma16_nt(const void* g, const void* lds) {
                :: "v"(g), "s"(a) : "m0", "memory");
 }
 
-constexpr int kDecRows = 64;      // weight rows per streaming workgroup (4 waves x 16)
+// Weight rows per streaming workgroup: 16 per wave, 4 waves up to 4 tokens
+// and 8 beyond, where the X slice in LDS is as large as the code tile and
+// twice the rows share it (3% faster at 16 tokens; 3-4% slower at one, where
+// the smaller workgroups keep more tiles in flight).
+constexpr int dec_waves(int64_t M) { return M <= 4 ? 4 : 8; }
 // 8 blocks (a 16 KB code tile) rather than 16: twice the workgroups fit in
 // LDS at once, so more tiles are in flight while others compute (14-18%
 // faster at 16 tokens, 6-10% at one)
@@ -65,7 +69,7 @@ struct DecodeArgs {
 
 // The LDS arena of a streaming workgroup starts with the 16 bf16 levels.
 constexpr int kDecTab = 64;   // bytes reserved for the table (keeps the rest 16-byte aligned)
-constexpr int kDecCodes = kDecRows * kDecBlocks * 32;   // the code tile, 16 KB
+constexpr int dec_codes(int W) { return 16 * W * kDecBlocks * 32; }   // the code tile, 16 or 32 KB
 
 // 8 codes (one 32-bit word, code 2j in the low nibble of byte j) -> 8 bf16
 // levels as an MFMA operand.  The word is spread into 2 x nibble per byte, the
@@ -88,13 +92,15 @@ __device__ __forceinline__ uint4 levels8(uint32_t c, const uint16_t* tab16) {
   return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
+template <int W>
 __device__ __forceinline__ void decode_rows(const DecodeArgs& a, const uint16_t* tab16,
                                             uint8_t* cs, uint16_t* xs, int64_t b) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j16 = lane & 15, g = lane >> 4;
   const int split = (int)(b % a.splits);
-  const int64_t n = (b / a.splits) * kDecRows + 16 * wv + j16;
+  constexpr int kRows = 16 * W;
+  const int64_t n = (b / a.splits) * kRows + 16 * wv + j16;
   const int64_t nl = n < a.N ? n : a.N - 1;
   const int64_t KB = a.K / kBlock;
   const int64_t kb0 = (int64_t)split * kDecBlocks;
@@ -120,8 +126,8 @@ __device__ __forceinline__ void decode_rows(const DecodeArgs& a, const uint16_t*
   // of row R is stored at position q ^ (R & 15) instead.  Chunks past the
   // range re-read the last valid one (their blocks meet zero constants).
   {
-    const int64_t n0 = (b / a.splits) * kDecRows;
-    constexpr int kLoads = kDecRows / kDecDmaRows / 4;   // per wave
+    const int64_t n0 = (b / a.splits) * kRows;
+    constexpr int kLoads = kRows / kDecDmaRows / W;   // per wave
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int jj = kLoads * wv + i, r = kDecDmaRows * jj + lane / kDecRowChunks;
@@ -138,7 +144,7 @@ __device__ __forceinline__ void decode_rows(const DecodeArgs& a, const uint16_t*
   const int64_t kx = 64 * kb0;
   const int clim = 64 * nblk - 8;                 // last valid 8-element chunk
 #pragma unroll 1
-  for (int j = wv; j < kDecXPieces * (int)a.M; j += 4) {
+  for (int j = wv; j < kDecXPieces * (int)a.M; j += W) {
     const int m = j / kDecXPieces, pc = j % kDecXPieces, col = 512 * pc + 8 * lane;
     dma16(a.X + m * a.K + kx + (col < clim ? col : clim), xs + m * kDecXStride + 512 * pc);
   }
@@ -162,7 +168,7 @@ __device__ __forceinline__ void decode_rows(const DecodeArgs& a, const uint16_t*
     return i < nblk ? v : 0.f;
   };
   // row M stays zero: the padding token rows of the MFMA read it
-  for (int e = tid; e < kDecXStride / 8; e += 256)
+  for (int e = tid; e < kDecXStride / 8; e += 64 * W)
     *reinterpret_cast<uint4*>(xs + a.M * kDecXStride + 8 * e) = make_uint4(0u, 0u, 0u, 0u);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA pieces have landed
   __syncthreads();
@@ -212,6 +218,7 @@ __device__ __forceinline__ void xa_slice(const DecodeArgs& a, int r, int64_t sl,
   const int j16 = lane & 15, g = lane >> 4;
   const int64_t K = a.K;
   const int64_t k = sl * (kXaWaves * kSkStep) + (int64_t)wv * kSkStep;
+  const bool kwave = wv < kXaWaves;   // further waves only meet the barriers
   const bool tok = j16 < a.M;
   const uint32_t keep = tok ? 0xFFFFFFFFu : 0u;
   const uint16_t* xrow = a.X + (int64_t)(tok ? j16 : 0) * K;
@@ -219,7 +226,7 @@ __device__ __forceinline__ void xa_slice(const DecodeArgs& a, int r, int64_t sl,
   f32x4_t acc[RT];
 #pragma unroll
   for (int jt = 0; jt < RT; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (k < K) {
+  if (kwave && k < K) {
     uint4 x[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -251,7 +258,8 @@ __device__ __forceinline__ void xa_slice(const DecodeArgs& a, int r, int64_t sl,
 #pragma unroll
   for (int jt = 0; jt < RT; ++jt) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[wv][v][lane] = acc[jt][v];
+    for (int v = 0; v < 4; ++v)
+      if (kwave) red[wv][v][lane] = acc[jt][v];
     __syncthreads();
     if (wv == 0) {
 #pragma unroll
@@ -290,7 +298,7 @@ __device__ __forceinline__ int job_index(const int64_t* first, int count, int64_
   return lo;
 }
 
-template <int RT>
+template <int RT, int W>
 __device__ __forceinline__ void decode_body(const DecodeBatch& bt, int r) {
   // one LDS arena (sized per launch) for either branch: [16 bf16 levels |
   // code tile | X rows 0..M, row M zero] or the 4 KB of XA wave partials
@@ -303,25 +311,26 @@ __device__ __forceinline__ void decode_body(const DecodeBatch& bt, int r) {
   } else {
     uint16_t* tab16 = reinterpret_cast<uint16_t*>(arena);
     uint8_t* cs = arena + kDecTab;
-    uint16_t* xs = reinterpret_cast<uint16_t*>(arena + kDecTab + kDecCodes);
+    uint16_t* xs = reinterpret_cast<uint16_t*>(arena + kDecTab + dec_codes(W));
     if (threadIdx.x < 16)
       tab16[threadIdx.x] = (uint16_t)(pack_bf16x2(bt.level[bt.kind[j]][threadIdx.x], 0.f) & 0xFFFF);
-    decode_rows(a, tab16, cs, xs, b - a.xa_blocks);   // its barrier also covers the table
+    decode_rows<W>(a, tab16, cs, xs, b - a.xa_blocks);   // its barrier also covers the table
   }
 }
 
-// Two entry points of one body: up to 4 tokens, where the arena fits 7-8
-// workgroups per CU, the registers are held to 64 so that as many fit (3%
-// faster at one token than the 6 that 74 registers allow); from 5 tokens the
-// X rows limit the workgroups per CU anyway and the registers are left free.
+// Two entry points of one body: up to 4 tokens (4 waves), where the arena
+// fits 7-8 workgroups per CU, the registers are held to 64 so that as many
+// fit (3% faster at one token than the 6 that 74 registers allow); from 5
+// tokens (8 waves) the X rows limit the workgroups per CU anyway and the
+// registers are left free.
 template <int RT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void k_qlora_decode_narrow(const DecodeBatch bt, int r) {
-  decode_body<RT>(bt, r);
+  decode_body<RT, 4>(bt, r);
 }
 template <int RT>
-__global__ __launch_bounds__(256) void k_qlora_decode(const DecodeBatch bt, int r) {
-  decode_body<RT>(bt, r);
+__global__ __launch_bounds__(512) void k_qlora_decode(const DecodeBatch bt, int r) {
+  decode_body<RT, 8>(bt, r);
 }
 
 // src[0] + src[stride] + ... over the first min(count, 16) terms, in order,
@@ -422,10 +431,12 @@ __global__ __launch_bounds__(256) void k_decode_finish(const FinishBatch fb, int
 
 template <int RT>
 hipError_t decode_rt(const DecodeBatch& bt, int64_t M, int r, int64_t blocks, hipStream_t s) {
-  const size_t stream = kDecTab + kDecCodes + (size_t)(M + 1) * kDecXStride * 2;
+  const int W = dec_waves(M);
+  const size_t stream = kDecTab + dec_codes(W) + (size_t)(M + 1) * kDecXStride * 2;
   const size_t xa = (size_t)kXaWaves * 4 * 64 * 4;
-  return launch_kernel_lds(M <= 4 ? k_qlora_decode_narrow<RT> : k_qlora_decode<RT>,
-                           dim3((unsigned)blocks), dim3(256), stream > xa ? stream : xa, s, bt, r);
+  return launch_kernel_lds(W == 4 ? k_qlora_decode_narrow<RT> : k_qlora_decode<RT>,
+                           dim3((unsigned)blocks), dim3(64 * W), stream > xa ? stream : xa, s, bt,
+                           r);
 }
 
 }  // namespace
@@ -463,7 +474,7 @@ hipError_t launch_decode(const DecodeJob* jobs, int count, int64_t M, int r, flo
     a.xa.drop = d.drop;
     bt.kind[i] = d.W.kind;
     bt.first[i] = blocks;
-    blocks += ks + ceil_div(d.N, kDecRows) * a.splits;
+    blocks += ks + ceil_div(d.N, (int64_t)16 * dec_waves(M)) * a.splits;
     fb.job[i] = FinishJob{d.partial, a.splits, d.N, d.xa_part, ks, d.B, d.Y, d.XA_out};
     fb.first[i] = nblocks;
     nblocks += ceil_div(d.N, (int64_t)256);
