@@ -73,6 +73,11 @@ RAGGED = [  # M, N, K, r
     # few output tiles: the inner loop is split across workgroups, with uneven
     # slices (17 = 9 + 8, 65 = 7 x 9 + 2, 19 = 10 + 9 steps of 64)
     (300, 1216, 1088, 24), (70, 512, 4160, 16), (40, 4096, 256, 8),
+    # decode path: partial last row tiles of the 4-wave (up to 4 tokens) and
+    # 8-wave (5..16 tokens) streamers, ragged last inner ranges, block
+    # counts that do not group by four (the per-block constant path)
+    (7, 200, 320, 8), (16, 1000, 576, 64), (12, 129, 64, 3), (3, 65, 1088, 16),
+    (16, 8, 4160, 32),
 ]
 
 
